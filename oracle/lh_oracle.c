@@ -1,0 +1,589 @@
+/*
+ * Lighthouse attention: plain CPU oracle.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test-suite, the smoke check and the
+ * benchmark's CPU-baseline leg may load this library.  It shares no code,
+ * header, table or helper with the GPU path and must never be used as a
+ * fallback for it.
+ *
+ * Source: "Long Context Pre-Training with Lighthouse Attention" (Peng, Ghosh,
+ * Quesnelle; arXiv 2605.06554), as mirrored on the pages
+ *   P1  bittide.aicompass.dev article (translation of the arXiv HTML):
+ *       Sec. 1 (Introduction), Fig. 1, Sec. 3, Sec. 3.1 / Eq. (1), Fig. 2;
+ *   P3  alphasignal.ai summary ("Pyramid Pool" bullet);
+ *   P4  aibriefing.imbch.dev summary ("three key points").
+ * Everything is fp64 except the selection scores, which are fp32 in a fixed
+ * reduction order so that the selected index set is reproducible bit for bit.
+ *
+ * Readings taken where the pages leave a step open (each one is listed with
+ * its reason in the design notes that ship with the repository):
+ *   R1 score of an entry = ||q||^2 + ||k||^2 of its leaves (no sqrt: monotone),
+ *      coarser levels take the max over their p children (Fig. 2 "l2 norm +
+ *      max-pool");
+ *   R2 selection is top-down: K entries per level and per head, ordered by
+ *      (score descending, index ascending); a selected entry is replaced by
+ *      its p children, an unselected candidate is kept as it is, so the kept
+ *      entries partition [0, N) (Fig. 2 "bitonic argsort + tree-prune");
+ *   R3 kept entries are ordered by their first token to form the causal
+ *      sub-sequence (Fig. 1 caption; P4 "hole-free causal sequence");
+ *   R4 attention on the sub-sequence is Eq. (1) with scale 1/sqrt(d) and the
+ *      ordinary lower-triangular mask;
+ *   R5 scatter copies each output to the p^l tokens its entry covers
+ *      (Sec. 3 stage (iv)); the gradient of the mean-pool divides by p^l.
+ *
+ * dtype codes: 0 = bf16 (raw uint16 bit patterns), 1 = fp32.
+ * Tensors q, k, v, dO, O, dq, dk, dv are [N][H][d] (token-major); the
+ * sub-sequence tensors are [H][S][d]; scores are [H][n_l] per level.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define LHO_OK 0
+#define LHO_ERR_ARG (-1)
+#define LHO_ERR_MEM (-2)
+
+/* ---------------------------------------------------------------- helpers */
+
+static int64_t ipow(int64_t b, int e) {
+    int64_t r = 1;
+    for (int i = 0; i < e; ++i) r *= b;
+    return r;
+}
+
+/* Exact conversion of one stored element to fp32. */
+static float load_f32(const void* x, int dtype, int64_t i) {
+    if (dtype == 0) {
+        uint32_t b = (uint32_t)((const uint16_t*)x)[i] << 16;
+        float f;
+        memcpy(&f, &b, sizeof f);
+        return f;
+    }
+    return ((const float*)x)[i];
+}
+
+static int check_shape(int N, int H, int d, int dtype, int p, int L, int K) {
+    if (N <= 0 || H <= 0 || p < 2 || L < 1 || K < 0) return LHO_ERR_ARG;
+    if (dtype != 0 && dtype != 1) return LHO_ERR_ARG;
+    if (d < 8 || d % 8 != 0) return LHO_ERR_ARG;
+    int G = d / 8;
+    if (G & (G - 1)) return LHO_ERR_ARG;      /* groups combine by a power-of-two butterfly */
+    int64_t top = ipow(p, L - 1);
+    if (top > N || N % top != 0) return LHO_ERR_ARG;
+    return LHO_OK;
+}
+
+/* ------------------------------------------------------- sub-sequence size */
+
+/* Number of kept entries S for (N, p, L, K) under reading R2: start with all
+ * N/p^(L-1) top entries; each of the min(K, #candidates) selections at a
+ * level replaces one entry by p children. */
+int64_t lho_subseq_len(int N, int p, int L, int K) {
+    if (N <= 0 || p < 2 || L < 1 || K < 0) return -1;
+    int64_t top = ipow(p, L - 1);
+    if (top > N || N % top != 0) return -1;
+    int64_t n = N / top, S = n, cand = n;
+    for (int l = L - 1; l >= 1; --l) {
+        int64_t sel = cand < K ? cand : K;
+        S += sel * (p - 1);
+        cand = sel * p;
+    }
+    return S;
+}
+
+/* ------------------------------------------------------------- pyramid (O1) */
+
+/* Mean of the p children one level down, recursively (Sec. 3 stage (i),
+ * Fig. 2 step 1: level l averages p^l tokens).  `scratch` holds (lev)*d
+ * doubles for the recursion. */
+static void pooled_row(const void* x, int dtype, int H, int d, int h, int p,
+                       int lev, int64_t j, double* out, double* scratch) {
+    if (lev == 0) {
+        int64_t base = (j * H + h) * (int64_t)d;
+        for (int e = 0; e < d; ++e) out[e] = (double)load_f32(x, dtype, base + e);
+        return;
+    }
+    double* child = scratch;
+    for (int e = 0; e < d; ++e) out[e] = 0.0;
+    for (int c = 0; c < p; ++c) {
+        pooled_row(x, dtype, H, d, h, p, lev - 1, (int64_t)p * j + c, child, scratch + d);
+        for (int e = 0; e < d; ++e) out[e] += child[e];
+    }
+    for (int e = 0; e < d; ++e) out[e] /= (double)p;
+}
+
+/* Full pyramid, levels 1..L-1, each [N/p^l][H][d] fp64, concatenated. */
+int lho_pyramid(const void* x, int N, int H, int d, int dtype, int p, int L, double* out) {
+    int rc = check_shape(N, H, d, dtype, p, L, 0);
+    if (rc) return rc;
+    int64_t off = 0;
+    double* scratch = (double*)malloc(sizeof(double) * (size_t)d * (size_t)(L + 1));
+    if (!scratch) return LHO_ERR_MEM;
+    for (int l = 1; l < L; ++l) {
+        int64_t n = N / ipow(p, l);
+        for (int64_t j = 0; j < n; ++j)
+            for (int h = 0; h < H; ++h)
+                pooled_row(x, dtype, H, d, h, p, l, j, out + off + (j * H + h) * (int64_t)d, scratch);
+        off += n * H * (int64_t)d;
+    }
+    free(scratch);
+    return LHO_OK;
+}
+
+/* --------------------------------------------------------------- scores (O2, O3) */
+
+/* Sum of squares of d exact fp32 values in the fixed order of reading R1:
+ * groups of 8 consecutive elements, each accumulated by fmaf from +0 in
+ * element order, then the d/8 group sums combined by a xor butterfly
+ * (a_g <- a_g + a_(g^off) for off = G/2 .. 1); the result is a_0. */
+static float ssq_fixed_order(const float* x, int d) {
+    int G = d / 8;
+    float a[64], b[64];
+    for (int g = 0; g < G; ++g) {
+        float acc = 0.0f;
+        for (int e = 0; e < 8; ++e) acc = fmaf(x[8 * g + e], x[8 * g + e], acc);
+        a[g] = acc;
+    }
+    for (int off = G / 2; off >= 1; off /= 2) {
+        for (int g = 0; g < G; ++g) b[g] = a[g] + a[g ^ off];
+        for (int g = 0; g < G; ++g) a[g] = b[g];
+    }
+    return a[0];
+}
+
+static void head_leaf_scores(const void* q, const void* k, int N, int H, int d, int dtype, int h, float* s0) {
+    float xq[512], xk[512];
+    for (int64_t t = 0; t < N; ++t) {
+        int64_t base = (t * H + h) * (int64_t)d;
+        for (int e = 0; e < d; ++e) {
+            xq[e] = load_f32(q, dtype, base + e);
+            xk[e] = load_f32(k, dtype, base + e);
+        }
+        s0[t] = ssq_fixed_order(xq, d) + ssq_fixed_order(xk, d);
+    }
+}
+
+/* Same quantity in fp64 with a plain sum, for the near-tie report only. */
+static void head_leaf_scores64(const void* q, const void* k, int N, int H, int d, int dtype, int h, double* s0) {
+    for (int64_t t = 0; t < N; ++t) {
+        int64_t base = (t * H + h) * (int64_t)d;
+        double acc = 0.0;
+        for (int e = 0; e < d; ++e) {
+            double a = load_f32(q, dtype, base + e), b = load_f32(k, dtype, base + e);
+            acc += a * a + b * b;
+        }
+        s0[t] = acc;
+    }
+}
+
+/* Leaf scores for every head: s0 is [H][N]. */
+int lho_leaf_scores(const void* q, const void* k, int N, int H, int d, int dtype, float* s0) {
+    int rc = check_shape(N, H, d, dtype, 2, 1, 0);
+    if (rc) return rc;
+    if (d > 512) return LHO_ERR_ARG;
+    for (int h = 0; h < H; ++h) head_leaf_scores(q, k, N, H, d, dtype, h, s0 + (int64_t)h * N);
+    return LHO_OK;
+}
+
+/* Score of a level-l entry = max of its p children (Fig. 2 step 2). */
+static void max_pool_levels_f32(float** lev, int N, int p, int L) {
+    for (int l = 1; l < L; ++l) {
+        int64_t n = N / ipow(p, l);
+        for (int64_t j = 0; j < n; ++j) {
+            float m = lev[l - 1][(int64_t)p * j];
+            for (int c = 1; c < p; ++c) {
+                float v = lev[l - 1][(int64_t)p * j + c];
+                if (v > m) m = v;
+            }
+            lev[l][j] = m;
+        }
+    }
+}
+
+static void max_pool_levels_f64(double** lev, int N, int p, int L) {
+    for (int l = 1; l < L; ++l) {
+        int64_t n = N / ipow(p, l);
+        for (int64_t j = 0; j < n; ++j) {
+            double m = lev[l - 1][(int64_t)p * j];
+            for (int c = 1; c < p; ++c) {
+                double v = lev[l - 1][(int64_t)p * j + c];
+                if (v > m) m = v;
+            }
+            lev[l][j] = m;
+        }
+    }
+}
+
+/* ----------------------------------------------------------- selection (O4, O5) */
+
+typedef struct {
+    uint32_t bits;   /* fp32 score bit pattern; scores are >= +0 so this orders them */
+    int64_t idx;
+} key_t_;
+
+static int key_cmp(const void* pa, const void* pb) {
+    const key_t_* a = (const key_t_*)pa;
+    const key_t_* b = (const key_t_*)pb;
+    if (a->bits != b->bits) return a->bits > b->bits ? -1 : 1;   /* larger score first */
+    if (a->idx != b->idx) return a->idx < b->idx ? -1 : 1;       /* then lower index   */
+    return 0;
+}
+
+static int i64_cmp(const void* pa, const void* pb) {
+    int64_t a = *(const int64_t*)pa, b = *(const int64_t*)pb;
+    return a < b ? -1 : (a > b ? 1 : 0);
+}
+
+typedef struct {
+    int64_t start;
+    int level;
+} entry_t;
+
+static int entry_cmp(const void* pa, const void* pb) {
+    const entry_t* a = (const entry_t*)pa;
+    const entry_t* b = (const entry_t*)pb;
+    return a->start < b->start ? -1 : (a->start > b->start ? 1 : 0);
+}
+
+static uint32_t f32_bits(float f) {
+    uint32_t b;
+    memcpy(&b, &f, sizeof b);
+    return b;
+}
+
+/* Top-down tree selection for one head (reading R2), then ordering by start
+ * (reading R3).  lev[l] holds the fp32 scores of level l.  Writes S entries
+ * to start/level and returns S (or -1 on allocation failure).  lev64 (may be
+ * NULL) gives fp64 scores for the near-tie count. */
+static int64_t head_select(float** lev, double** lev64, int N, int p, int L, int K,
+                           int32_t* start_out, int8_t* level_out, int* near_ties) {
+    int64_t n_top = N / ipow(p, L - 1);
+    int64_t cap = n_top > (int64_t)K * p ? n_top : (int64_t)K * p;
+    int64_t S_max = lho_subseq_len(N, p, L, K);
+    int64_t* cand = (int64_t*)malloc(sizeof(int64_t) * (size_t)cap);
+    int64_t* next = (int64_t*)malloc(sizeof(int64_t) * (size_t)cap);
+    int64_t* sel = (int64_t*)malloc(sizeof(int64_t) * (size_t)(K + 1));
+    key_t_* keys = (key_t_*)malloc(sizeof(key_t_) * (size_t)cap);
+    entry_t* E = (entry_t*)malloc(sizeof(entry_t) * (size_t)S_max);
+    if (!cand || !next || !sel || !keys || !E) {
+        free(cand); free(next); free(sel); free(keys); free(E);
+        return -1;
+    }
+    int64_t ncand = n_top, nE = 0;
+    for (int64_t j = 0; j < n_top; ++j) cand[j] = j;
+    for (int l = L - 1; l >= 1; --l) {
+        for (int64_t c = 0; c < ncand; ++c) {
+            keys[c].bits = f32_bits(lev[l][cand[c]]);
+            keys[c].idx = cand[c];
+        }
+        qsort(keys, (size_t)ncand, sizeof(key_t_), key_cmp);
+        int64_t nsel = ncand < K ? ncand : K;
+        if (near_ties && lev64 && nsel > 0 && nsel < ncand) {
+            double a = lev64[l][keys[nsel - 1].idx], b = lev64[l][keys[nsel].idx];
+            if (fabs(a - b) <= 1e-6 * fabs(a)) ++*near_ties;
+        }
+        for (int64_t s = 0; s < nsel; ++s) sel[s] = keys[s].idx;
+        qsort(sel, (size_t)nsel, sizeof(int64_t), i64_cmp);
+        /* candidates not selected are kept at this level (cand is ascending) */
+        int64_t s = 0;
+        for (int64_t c = 0; c < ncand; ++c) {
+            if (s < nsel && sel[s] == cand[c]) { ++s; continue; }
+            E[nE].start = cand[c] * ipow(p, l);
+            E[nE].level = l;
+            ++nE;
+        }
+        /* children of the selected entries become the next candidates */
+        int64_t nn = 0;
+        for (int64_t i = 0; i < nsel; ++i)
+            for (int c = 0; c < p; ++c) next[nn++] = sel[i] * p + c;
+        int64_t* tmp = cand; cand = next; next = tmp;
+        ncand = nn;
+    }
+    for (int64_t c = 0; c < ncand; ++c) {        /* level 0: every candidate is kept */
+        E[nE].start = cand[c];
+        E[nE].level = 0;
+        ++nE;
+    }
+    qsort(E, (size_t)nE, sizeof(entry_t), entry_cmp);
+    for (int64_t i = 0; i < nE; ++i) {
+        start_out[i] = (int32_t)E[i].start;
+        level_out[i] = (int8_t)E[i].level;
+    }
+    free(cand); free(next); free(sel); free(keys); free(E);
+    return nE;
+}
+
+/* ------------------------------------------------------------ attention (O6, O8) */
+
+/* Eq. (1) on one head's sub-sequence with the causal mask: two-pass softmax. */
+static void head_attention_fwd(int64_t S, int d, const double* Q, const double* K, const double* V,
+                               double* O, double* lse, double* logit) {
+    double scale = 1.0 / sqrt((double)d);
+    for (int64_t i = 0; i < S; ++i) {
+        double m = -INFINITY;
+        for (int64_t j = 0; j <= i; ++j) {
+            double acc = 0.0;
+            for (int e = 0; e < d; ++e) acc += Q[i * d + e] * K[j * d + e];
+            logit[j] = acc * scale;
+            if (logit[j] > m) m = logit[j];
+        }
+        double sum = 0.0;
+        for (int64_t j = 0; j <= i; ++j) sum += exp(logit[j] - m);
+        for (int e = 0; e < d; ++e) O[i * d + e] = 0.0;
+        for (int64_t j = 0; j <= i; ++j) {
+            double w = exp(logit[j] - m) / sum;
+            for (int e = 0; e < d; ++e) O[i * d + e] += w * V[j * d + e];
+        }
+        if (lse) lse[i] = m + log(sum);
+    }
+}
+
+/* Gradient of the above: P = softmax, dV = P^T dO, dP = dO V^T,
+ * dS = P o (dP - rowsum(dO o O)), dQ = dS K / sqrt(d), dK = dS^T Q / sqrt(d). */
+static void head_attention_bwd(int64_t S, int d, const double* Q, const double* K, const double* V,
+                               const double* O, const double* dO, double* dQ, double* dK, double* dV,
+                               double* logit) {
+    double scale = 1.0 / sqrt((double)d);
+    memset(dQ, 0, sizeof(double) * (size_t)(S * d));
+    memset(dK, 0, sizeof(double) * (size_t)(S * d));
+    memset(dV, 0, sizeof(double) * (size_t)(S * d));
+    for (int64_t i = 0; i < S; ++i) {
+        double m = -INFINITY;
+        for (int64_t j = 0; j <= i; ++j) {
+            double acc = 0.0;
+            for (int e = 0; e < d; ++e) acc += Q[i * d + e] * K[j * d + e];
+            logit[j] = acc * scale;
+            if (logit[j] > m) m = logit[j];
+        }
+        double sum = 0.0;
+        for (int64_t j = 0; j <= i; ++j) sum += exp(logit[j] - m);
+        double D = 0.0;
+        for (int e = 0; e < d; ++e) D += dO[i * d + e] * O[i * d + e];
+        for (int64_t j = 0; j <= i; ++j) {
+            double P = exp(logit[j] - m) / sum;
+            double dP = 0.0;
+            for (int e = 0; e < d; ++e) dP += dO[i * d + e] * V[j * d + e];
+            double dS = P * (dP - D);
+            for (int e = 0; e < d; ++e) {
+                dQ[i * d + e] += dS * K[j * d + e] * scale;
+                dK[j * d + e] += dS * Q[i * d + e] * scale;
+                dV[j * d + e] += P * dO[i * d + e];
+            }
+        }
+    }
+}
+
+/* ------------------------------------------------------------- per-head work */
+
+typedef struct {
+    const void *q, *k, *v, *dout;
+    int N, H, d, dtype, p, L, K;
+    int64_t S;
+} ctx_t;
+
+/* Scores, levels and the selection for head h.  Returns 0 or an error. */
+static int head_scores_select(const ctx_t* c, int h, float* levels_out, int32_t* st, int8_t* lv,
+                              int* near_ties) {
+    int L = c->L;
+    float** lev = (float**)calloc((size_t)L, sizeof(float*));
+    double** lev64 = near_ties ? (double**)calloc((size_t)L, sizeof(double*)) : NULL;
+    int rc = LHO_OK;
+    if (!lev || (near_ties && !lev64)) { rc = LHO_ERR_MEM; goto done; }
+    for (int l = 0; l < L; ++l) {
+        lev[l] = (float*)malloc(sizeof(float) * (size_t)(c->N / ipow(c->p, l)));
+        if (!lev[l]) { rc = LHO_ERR_MEM; goto done; }
+        if (lev64) {
+            lev64[l] = (double*)malloc(sizeof(double) * (size_t)(c->N / ipow(c->p, l)));
+            if (!lev64[l]) { rc = LHO_ERR_MEM; goto done; }
+        }
+    }
+    head_leaf_scores(c->q, c->k, c->N, c->H, c->d, c->dtype, h, lev[0]);
+    max_pool_levels_f32(lev, c->N, c->p, L);
+    if (lev64) {
+        head_leaf_scores64(c->q, c->k, c->N, c->H, c->d, c->dtype, h, lev64[0]);
+        max_pool_levels_f64(lev64, c->N, c->p, L);
+    }
+    if (levels_out) {
+        /* level l of head h lives at H*sum_{l'<l} n_l' + h*n_l */
+        int64_t off = 0;
+        for (int l = 0; l < L; ++l) {
+            int64_t n = c->N / ipow(c->p, l);
+            memcpy(levels_out + off + (int64_t)h * n, lev[l], sizeof(float) * (size_t)n);
+            off += n * c->H;
+        }
+    }
+    if (st) {
+        int64_t S = head_select(lev, lev64, c->N, c->p, L, c->K, st, lv, near_ties);
+        if (S != c->S) rc = LHO_ERR_MEM;
+    }
+done:
+    if (lev) for (int l = 0; l < L; ++l) free(lev[l]);
+    if (lev64) for (int l = 0; l < L; ++l) free(lev64[l]);
+    free(lev);
+    free(lev64);
+    return rc;
+}
+
+/* Gather (O5): row i of the sub-sequence is the level-l_i pyramid entry that
+ * starts at token start_i. */
+static void head_gather(const ctx_t* c, const void* x, int h, const int32_t* st, const int8_t* lv,
+                        double* out, double* scratch) {
+    for (int64_t i = 0; i < c->S; ++i) {
+        int l = lv[i];
+        int64_t j = st[i] / ipow(c->p, l);
+        pooled_row(x, c->dtype, c->H, c->d, h, c->p, l, j, out + i * c->d, scratch);
+    }
+}
+
+/* ----------------------------------------------------------------- public API */
+
+/*
+ * Forward pass (Fig. 1 forward path).  Output pointers may be NULL.
+ *   score_levels [sum_l H*N/p^l] fp32, level-major then [H][n_l]
+ *   sel_start, sel_level [H][S]: written unless given_sel != 0, in which case
+ *       they are read (the selection is frozen; used for finite differences)
+ *   Qt, Kt, Vt, Ot [H][S][d], lse [H][S]
+ *   O [N][H][d]
+ *   near_ties [H]: count of selection boundaries whose fp64 scores are within
+ *       1e-6 relative (reported, not an error)
+ */
+int lho_forward(const void* q, const void* k, const void* v, int N, int H, int d, int dtype,
+                int p, int L, int K, int given_sel, float* score_levels,
+                int32_t* sel_start, int8_t* sel_level, double* Qt, double* Kt, double* Vt,
+                double* Ot, double* lse, double* O, int* near_ties, int nthreads) {
+    int rc = check_shape(N, H, d, dtype, p, L, K);
+    if (rc) return rc;
+    if (d > 512 || !sel_start || !sel_level) return LHO_ERR_ARG;
+    ctx_t c = {q, k, v, NULL, N, H, d, dtype, p, L, K, lho_subseq_len(N, p, L, K)};
+    int64_t S = c.S;
+    int err = 0;
+#ifdef _OPENMP
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+#else
+    (void)nthreads;
+#endif
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : err)
+    for (int h = 0; h < H; ++h) {
+        int32_t* st = sel_start + (int64_t)h * S;
+        int8_t* lv = sel_level + (int64_t)h * S;
+        if (near_ties) near_ties[h] = 0;
+        if (!given_sel || score_levels) {
+            if (head_scores_select(&c, h, score_levels, given_sel ? NULL : st, given_sel ? NULL : lv,
+                                   (near_ties && !given_sel) ? &near_ties[h] : NULL)) {
+                err |= 1;
+                continue;
+            }
+        }
+        int need_attn = Ot || lse || O;
+        if (!(Qt || Kt || Vt || need_attn)) continue;
+        size_t sd = (size_t)(S * d);
+        double* scratch = (double*)malloc(sizeof(double) * (size_t)d * (size_t)(L + 1));
+        double* Qh = (double*)malloc(sizeof(double) * sd);
+        double* Kh = (double*)malloc(sizeof(double) * sd);
+        double* Vh = (double*)malloc(sizeof(double) * sd);
+        double* Oh = (double*)malloc(sizeof(double) * sd);
+        double* lh = (double*)malloc(sizeof(double) * (size_t)S);
+        double* logit = (double*)malloc(sizeof(double) * (size_t)S);
+        if (!scratch || !Qh || !Kh || !Vh || !Oh || !lh || !logit) {
+            err |= 1;
+        } else {
+            head_gather(&c, q, h, st, lv, Qh, scratch);
+            head_gather(&c, k, h, st, lv, Kh, scratch);
+            head_gather(&c, v, h, st, lv, Vh, scratch);
+            if (Qt) memcpy(Qt + (int64_t)h * S * d, Qh, sizeof(double) * sd);
+            if (Kt) memcpy(Kt + (int64_t)h * S * d, Kh, sizeof(double) * sd);
+            if (Vt) memcpy(Vt + (int64_t)h * S * d, Vh, sizeof(double) * sd);
+            if (need_attn) {
+                head_attention_fwd(S, d, Qh, Kh, Vh, Oh, lh, logit);
+                if (Ot) memcpy(Ot + (int64_t)h * S * d, Oh, sizeof(double) * sd);
+                if (lse) memcpy(lse + (int64_t)h * S, lh, sizeof(double) * (size_t)S);
+                if (O) {
+                    /* scatter (O7): every token of entry i receives row i */
+                    for (int64_t i = 0; i < S; ++i) {
+                        int64_t len = ipow(p, lv[i]);
+                        for (int64_t t = st[i]; t < st[i] + len; ++t)
+                            memcpy(O + (t * H + h) * (int64_t)d, Oh + i * d, sizeof(double) * (size_t)d);
+                    }
+                }
+            }
+        }
+        free(scratch); free(Qh); free(Kh); free(Vh); free(Oh); free(lh); free(logit);
+    }
+    return err ? LHO_ERR_MEM : LHO_OK;
+}
+
+/*
+ * Backward pass (Fig. 1 gradient path: O -> scatter -> attention -> gather ->
+ * pool).  The selection (sel_start, sel_level from lho_forward) is an input:
+ * indices carry no gradient.  Output pointers may be NULL.
+ *   dOt, dQt, dKt, dVt [H][S][d];  dq, dk, dv [N][H][d]
+ */
+int lho_backward(const void* q, const void* k, const void* v, const void* dout, int N, int H, int d,
+                 int dtype, int p, int L, int K, const int32_t* sel_start, const int8_t* sel_level,
+                 double* dOt, double* dQt, double* dKt, double* dVt, double* dq, double* dk, double* dv,
+                 int nthreads) {
+    int rc = check_shape(N, H, d, dtype, p, L, K);
+    if (rc) return rc;
+    if (d > 512 || !sel_start || !sel_level || !dout) return LHO_ERR_ARG;
+    ctx_t c = {q, k, v, dout, N, H, d, dtype, p, L, K, lho_subseq_len(N, p, L, K)};
+    int64_t S = c.S;
+    int err = 0;
+#ifdef _OPENMP
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+#else
+    (void)nthreads;
+#endif
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : err)
+    for (int h = 0; h < H; ++h) {
+        const int32_t* st = sel_start + (int64_t)h * S;
+        const int8_t* lv = sel_level + (int64_t)h * S;
+        size_t sd = (size_t)(S * d);
+        double* scratch = (double*)malloc(sizeof(double) * (size_t)d * (size_t)(L + 1));
+        double* buf = (double*)malloc(sizeof(double) * sd * 8);
+        double* lse = (double*)malloc(sizeof(double) * (size_t)S);
+        double* logit = (double*)malloc(sizeof(double) * (size_t)S);
+        if (!scratch || !buf || !lse || !logit) {
+            err |= 1;
+            free(scratch); free(buf); free(lse); free(logit);
+            continue;
+        }
+        double *Qh = buf, *Kh = buf + sd, *Vh = buf + 2 * sd, *Oh = buf + 3 * sd;
+        double *dOh = buf + 4 * sd, *dQh = buf + 5 * sd, *dKh = buf + 6 * sd, *dVh = buf + 7 * sd;
+        head_gather(&c, q, h, st, lv, Qh, scratch);
+        head_gather(&c, k, h, st, lv, Kh, scratch);
+        head_gather(&c, v, h, st, lv, Vh, scratch);
+        head_attention_fwd(S, d, Qh, Kh, Vh, Oh, lse, logit);
+        /* adjoint of the scatter: an entry's gradient is the sum over its tokens */
+        for (int64_t i = 0; i < S; ++i) {
+            int64_t len = ipow(p, lv[i]);
+            for (int e = 0; e < d; ++e) dOh[i * d + e] = 0.0;
+            for (int64_t t = st[i]; t < st[i] + len; ++t) {
+                int64_t base = (t * H + h) * (int64_t)d;
+                for (int e = 0; e < d; ++e) dOh[i * d + e] += (double)load_f32(dout, dtype, base + e);
+            }
+        }
+        head_attention_bwd(S, d, Qh, Kh, Vh, Oh, dOh, dQh, dKh, dVh, logit);
+        if (dOt) memcpy(dOt + (int64_t)h * S * d, dOh, sizeof(double) * sd);
+        if (dQt) memcpy(dQt + (int64_t)h * S * d, dQh, sizeof(double) * sd);
+        if (dKt) memcpy(dKt + (int64_t)h * S * d, dKh, sizeof(double) * sd);
+        if (dVt) memcpy(dVt + (int64_t)h * S * d, dVh, sizeof(double) * sd);
+        /* adjoint of the mean-pool: each of the p^l tokens gets 1/p^l of it */
+        for (int64_t i = 0; i < S; ++i) {
+            int64_t len = ipow(p, lv[i]);
+            for (int64_t t = st[i]; t < st[i] + len; ++t) {
+                int64_t base = (t * H + h) * (int64_t)d;
+                for (int e = 0; e < d; ++e) {
+                    if (dq) dq[base + e] = dQh[i * d + e] / (double)len;
+                    if (dk) dk[base + e] = dKh[i * d + e] / (double)len;
+                    if (dv) dv[base + e] = dVh[i * d + e] / (double)len;
+                }
+            }
+        }
+        free(scratch); free(buf); free(lse); free(logit);
+    }
+    return err ? LHO_ERR_MEM : LHO_OK;
+}
