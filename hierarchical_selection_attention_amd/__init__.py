@@ -1,0 +1,9 @@
+"""Lighthouse attention layer on MI355X (gfx950): HIP kernels behind a C ABI.
+
+Import fails loudly when liblighthouse.so has not been built
+(`python -m hierarchical_selection_attention_amd.build`); there is no
+fallback implementation.
+"""
+from ._lib import *  # noqa: F401,F403
+from ._lib import (EXPORTS, LIB_PATH, LighthouseError, alloc_workspace, backward, dense_backward,  # noqa: F401
+                   dense_forward, dtype_code, forward, workspace_tensor)

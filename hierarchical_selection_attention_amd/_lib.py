@@ -1,0 +1,220 @@
+"""ctypes binding of liblighthouse.so (include/lighthouse.h).
+
+The raw functions keep the C names and take plain integers (device pointers as
+ints, stream handle as int).  The helpers below them only marshal torch tensors
+into those pointers; every step of the layer runs in the HIP kernels.  There is
+no fallback: if the library is missing, importing raises.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "liblighthouse.so")
+
+LH_OK, LH_ERR_ARG, LH_ERR_SHAPE, LH_ERR_DTYPE, LH_ERR_WORKSPACE, LH_ERR_HIP = 0, -1, -2, -3, -4, -5
+LH_BF16, LH_FP32 = 0, 1
+LH_SCATTER_FP_ATOMIC, LH_SCATTER_INT_ATOMIC = 0, 1
+VIEWS = {"scores": 0, "sel_start": 1, "sel_level": 2, "qsub": 3, "ksub": 4, "vsub": 5, "osub": 6,
+         "lse": 7, "dosub": 8, "dqsub": 9, "dksub": 10, "dvsub": 11, "block_first": 12}
+
+EXPORTS = ("lh_subseq_len", "lh_workspace_bytes", "lh_forward", "lh_backward", "lh_workspace_view",
+           "lh_dense_workspace_bytes", "lh_dense_attn_fwd", "lh_dense_attn_bwd", "lh_stage_timing",
+           "lh_stage_timing_read", "lh_stage_name", "lh_status_str")
+
+
+class LighthouseError(RuntimeError):
+    pass
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run `python -m hierarchical_selection_attention_amd.build`")
+    L = C.CDLL(LIB_PATH)
+    i, i64, sz, vp = C.c_int, C.c_int64, C.c_size_t, C.c_void_p
+    sig = {
+        "lh_subseq_len": (i64, [i, i, i, i]),
+        "lh_workspace_bytes": (sz, [i, i, i, i, i, i, i]),
+        "lh_forward": (i, [vp, vp, vp, vp, i, i, i, i, i, i, i, vp, sz, vp]),
+        "lh_backward": (i, [vp, vp, vp, vp, i, i, i, i, i, i, i, i, vp, sz, vp]),
+        "lh_workspace_view": (i, [vp, i, i, i, i, i, i, i, i, C.POINTER(vp), C.POINTER(sz)]),
+        "lh_dense_workspace_bytes": (sz, [i, i, i, i]),
+        "lh_dense_attn_fwd": (i, [vp, vp, vp, vp, vp, i, i, i, i, vp, sz, vp]),
+        "lh_dense_attn_bwd": (i, [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, vp, sz, vp]),
+        "lh_stage_timing": (i, [i]),
+        "lh_stage_timing_read": (i, [C.POINTER(C.c_double), C.POINTER(C.c_int), i]),
+        "lh_stage_name": (C.c_char_p, [i]),
+        "lh_status_str": (C.c_char_p, [i]),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(L, name)
+        f.restype = res
+        f.argtypes = args
+    return L
+
+
+_L = _load()
+
+# ---------------------------------------------------------------- raw C names
+lh_subseq_len = _L.lh_subseq_len
+lh_workspace_bytes = _L.lh_workspace_bytes
+lh_forward = _L.lh_forward
+lh_backward = _L.lh_backward
+lh_dense_workspace_bytes = _L.lh_dense_workspace_bytes
+lh_dense_attn_fwd = _L.lh_dense_attn_fwd
+lh_dense_attn_bwd = _L.lh_dense_attn_bwd
+lh_stage_timing = _L.lh_stage_timing
+
+
+def lh_status_str(rc: int) -> str:
+    return _L.lh_status_str(rc).decode()
+
+
+def lh_stage_name(stage: int) -> str:
+    return _L.lh_stage_name(stage).decode()
+
+
+def lh_workspace_view(ws_ptr, N, H, d, p, L, K, dtype, view):
+    ptr, nbytes = C.c_void_p(), C.c_size_t()
+    rc = _L.lh_workspace_view(ws_ptr, N, H, d, p, L, K, dtype, view, C.byref(ptr), C.byref(nbytes))
+    _check(rc, "lh_workspace_view")
+    return ptr.value, nbytes.value
+
+
+def lh_stage_timing_read(n: int = 16):
+    ms = (C.c_double * n)()
+    cnt = (C.c_int * n)()
+    rc = _L.lh_stage_timing_read(ms, cnt, n)
+    if rc < 0:
+        raise LighthouseError(f"lh_stage_timing_read: {lh_status_str(rc)}")
+    return {lh_stage_name(s): (ms[s], cnt[s]) for s in range(min(rc, n)) if cnt[s] > 0}
+
+
+def _check(rc, what):
+    if rc != LH_OK:
+        raise LighthouseError(f"{what} failed: {lh_status_str(rc)} ({rc})")
+
+
+# ------------------------------------------------------- torch marshalling
+def _torch():
+    import torch
+    return torch
+
+
+def dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return LH_BF16
+    if t.dtype == torch.float32:
+        return LH_FP32
+    raise LighthouseError(f"unsupported dtype {t.dtype}")
+
+
+def _stream_handle(stream):
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def _dev_tensor_check(*ts):
+    for t in ts:
+        if not t.is_cuda or not t.is_contiguous():
+            raise LighthouseError("tensors must be contiguous device tensors")
+
+
+def alloc_workspace(N, H, d, p, L, K, dtype, device="cuda"):
+    torch = _torch()
+    nbytes = lh_workspace_bytes(N, H, d, p, L, K, dtype)
+    if nbytes == 0:
+        raise LighthouseError("invalid layer parameters")
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+def forward(q, k, v, p, L, K, ws=None, out=None, stream=None):
+    """o = Lighthouse layer(q, k, v) for [N, H, d] tensors.  Returns (o, ws)."""
+    torch = _torch()
+    _dev_tensor_check(q, k, v)
+    N, H, d = q.shape
+    dt = dtype_code(q)
+    if ws is None:
+        ws = alloc_workspace(N, H, d, p, L, K, dt, q.device)
+    if out is None:
+        out = torch.empty_like(q)
+    rc = lh_forward(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), N, H, d, p, L, K, dt,
+                    ws.data_ptr(), ws.numel(), _stream_handle(stream))
+    _check(rc, "lh_forward")
+    return out, ws
+
+
+def backward(dout, p, L, K, ws, mode=LH_SCATTER_FP_ATOMIC, grads=None, stream=None):
+    """(dq, dk, dv) of the Lighthouse layer; ws must come from the matching forward()."""
+    torch = _torch()
+    _dev_tensor_check(dout)
+    N, H, d = dout.shape
+    dt = dtype_code(dout)
+    if grads is None:
+        grads = tuple(torch.empty_like(dout) for _ in range(3))
+    dq, dk, dv = grads
+    rc = lh_backward(dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), N, H, d, p, L, K, dt, mode,
+                     ws.data_ptr(), ws.numel(), _stream_handle(stream))
+    _check(rc, "lh_backward")
+    return dq, dk, dv
+
+
+def workspace_tensor(ws, N, H, d, p, L, K, dtype, view):
+    """A typed torch view of one intermediate inside the workspace (see lh_view)."""
+    torch = _torch()
+    vid = VIEWS[view] if isinstance(view, str) else int(view)
+    ptr, nbytes = lh_workspace_view(ws.data_ptr(), N, H, d, p, L, K, dtype, vid)
+    off = ptr - ws.data_ptr()
+    raw = ws[off: off + nbytes]
+    S = int(lh_subseq_len(N, p, L, K))
+    Sp = (S + 63) // 64 * 64
+    name = [k for k, v in VIEWS.items() if v == vid][0]
+    if name == "scores":
+        return raw.view(torch.float32)
+    if name == "sel_start":
+        return raw.view(torch.int32).view(H, S)
+    if name == "sel_level":
+        return raw.view(H, S)
+    if name in ("qsub", "ksub", "vsub", "osub"):
+        return raw.view(torch.float32).view(H, Sp, d)
+    if name == "lse":
+        return raw.view(torch.float32).view(H, Sp)
+    if name in ("dosub", "dqsub", "dksub", "dvsub"):
+        return raw.view(torch.float32).view(H, Sp, d)
+    if name == "block_first":
+        return raw.view(torch.int32).view(H, -1)
+    raise LighthouseError(f"unknown view {view}")
+
+
+def dense_forward(q, k, v, ws=None, out=None, lse=None, stream=None):
+    torch = _torch()
+    _dev_tensor_check(q, k, v)
+    N, H, d = q.shape
+    dt = dtype_code(q)
+    if ws is None:
+        ws = torch.empty(lh_dense_workspace_bytes(N, H, d, dt), dtype=torch.uint8, device=q.device)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((H, N), dtype=torch.float32, device=q.device)
+    rc = lh_dense_attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), N, H, d, dt,
+                           ws.data_ptr(), ws.numel(), _stream_handle(stream))
+    _check(rc, "lh_dense_attn_fwd")
+    return out, lse, ws
+
+
+def dense_backward(q, k, v, o, lse, dout, ws, grads=None, stream=None):
+    torch = _torch()
+    N, H, d = q.shape
+    dt = dtype_code(q)
+    if grads is None:
+        grads = tuple(torch.empty_like(q) for _ in range(3))
+    dq, dk, dv = grads
+    rc = lh_dense_attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), dout.data_ptr(),
+                           dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), N, H, d, dt, ws.data_ptr(), ws.numel(),
+                           _stream_handle(stream))
+    _check(rc, "lh_dense_attn_bwd")
+    return dq, dk, dv

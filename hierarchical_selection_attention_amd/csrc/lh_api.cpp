@@ -1,0 +1,521 @@
+// C ABI of the Lighthouse layer (declared in include/lighthouse.h): argument
+// validation, workspace layout and the launch order of the stages on the
+// caller's stream.  Stage order follows Fig. 1 of "Long Context Pre-Training
+// with Lighthouse Attention": pyramid pool -> selector -> dense gather ->
+// attention -> back-scatter, and the reverse for the gradient.
+#include <math.h>
+#include <stdint.h>
+#include <mutex>
+#include <vector>
+
+#include "lighthouse.h"
+#include "lh_internal.h"
+
+namespace lh {
+
+static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+int64_t subseq_len(int N, int p, int L, int K) {
+    if (N <= 0 || p < 2 || L < 1 || L > kMaxLevels || K < 0) return LH_ERR_ARG;
+    int64_t top = 1;
+    for (int l = 0; l < L - 1; ++l) {
+        top *= p;
+        if (top > N) return LH_ERR_SHAPE;
+    }
+    if (N % top != 0) return LH_ERR_SHAPE;
+    int64_t n = N / top, S = n, cand = n;
+    for (int l = L - 1; l >= 1; --l) {
+        const int64_t sel = cand < K ? cand : K;
+        S += sel * (p - 1);
+        cand = sel * p;
+    }
+    return S;
+}
+
+int make_plan(int N, int H, int d, int p, int L, int K, int dtype, Plan* P) {
+    if (dtype != BF16 && dtype != FP32) return LH_ERR_DTYPE;
+    if (N <= 0 || H <= 0 || p < 2 || L < 1 || L > kMaxLevels || K < 0) return LH_ERR_ARG;
+    if (d != 64 && d != 128) return LH_ERR_SHAPE;
+    if ((int64_t)H * d > 8192) return LH_ERR_SHAPE;
+    const int64_t S = subseq_len(N, p, L, K);
+    if (S < 0) return (int)S;
+    Plan& pl = *P;
+    pl = Plan{};
+    pl.N = N; pl.H = H; pl.d = d; pl.p = p; pl.L = L; pl.K = K; pl.dtype = dtype;
+    pl.esz = dtype == BF16 ? 2 : 4;
+    pl.S = S;
+    pl.Sp = (S + kRowPad - 1) / kRowPad * kRowPad;
+    pl.pw[0] = 1;
+    for (int l = 1; l < L; ++l) pl.pw[l] = pl.pw[l - 1] * p;
+    for (int l = 0; l < L; ++l) pl.n[l] = N / pl.pw[l];
+    pl.ntop = pl.n[L - 1];
+    int m = 0;
+    while (m + 1 <= L - 1 && pl.pw[m + 1] <= kChunkTokMax && pl.pw[m + 1] * H <= kChunkScoreMax) ++m;
+    if (L > 1 && m < 1) return LH_ERR_SHAPE;
+    pl.m = m;
+    pl.tok = pl.pw[m];
+    // candidate counts per level; the top-K network handles K <= kMaxK
+    int64_t nc = pl.ntop, cap = pl.ntop;
+    for (int l = L - 1; l >= 1; --l) {
+        if (nc > K && K > kMaxK) return LH_ERR_SHAPE;
+        nc = (nc < K ? nc : K) * p;
+        if (nc > cap) cap = nc;
+    }
+    pl.tk_cap = cap > 0 ? cap : 1;
+
+    const size_t HSd = (size_t)H * pl.Sp * d;
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        const size_t o = off;
+        off = align256(off + bytes);
+        return o;
+    };
+    size_t nscore = 0;
+    for (int l = 0; l < L; ++l) {
+        pl.lev_off[l] = nscore;
+        nscore += (size_t)H * pl.n[l];
+    }
+    pl.off_scores = take(sizeof(float) * nscore);
+    pl.off_pool_m = take(m >= 1 ? sizeof(float) * 3 * (size_t)pl.n[m] * H * d : 0);
+    pl.off_pool_top = (m == L - 1) ? pl.off_pool_m : take(sizeof(float) * 3 * (size_t)pl.ntop * H * d);
+    pl.off_start = take(sizeof(int32_t) * (size_t)H * S);
+    pl.off_level = take((size_t)H * S);
+    pl.off_bfirst = take(sizeof(int32_t) * (size_t)H * (pl.ntop + 1));
+    pl.off_tk = take(sizeof(int32_t) * (size_t)H * L * 5 * pl.tk_cap);
+    pl.off_qs = take(sizeof(float) * HSd);
+    pl.off_ks = take(sizeof(float) * HSd);
+    pl.off_vs = take(sizeof(float) * HSd);
+    const size_t h16 = dtype == BF16 ? 2 * HSd : 0;
+    pl.off_qh = take(h16); pl.off_ql = take(h16);
+    pl.off_kh = take(h16); pl.off_kl = take(h16);
+    pl.off_vh = take(h16); pl.off_vl = take(h16);
+    pl.off_vTh = take(h16); pl.off_vTl = take(h16);
+    pl.off_kTh = take(h16); pl.off_kTl = take(h16);
+    pl.off_qTbh = take(h16); pl.off_qTbl = take(h16);
+    pl.off_hmax = take(sizeof(uint32_t) * 8 * (size_t)H);
+    pl.off_hscale = take(sizeof(float) * 4 * (size_t)H);
+    pl.off_os = take(sizeof(float) * HSd);
+    pl.off_lse = take(sizeof(float) * (size_t)H * pl.Sp);
+    pl.off_lse2 = take(sizeof(float) * (size_t)H * pl.Sp);
+    pl.off_acc = take(8 * HSd);
+    pl.off_dos = take(sizeof(float) * HSd);
+    pl.off_doh = take(h16); pl.off_dol = take(h16);
+    pl.off_doTh = take(h16); pl.off_doTl = take(h16);
+    pl.off_D = take(sizeof(float) * (size_t)H * pl.Sp);
+    pl.off_rowdown = take(sizeof(float) * (size_t)H * pl.Sp);
+    pl.off_dq = take(sizeof(float) * HSd);
+    pl.off_dk = take(sizeof(float) * HSd);
+    pl.off_dv = take(sizeof(float) * HSd);
+    pl.total = off;
+    return LH_OK;
+}
+
+// ------------------------------------------------------------ stage timing
+namespace {
+struct TimedLaunch {
+    int stage;
+    hipEvent_t a, b;
+};
+std::mutex g_mu;
+bool g_timing = false;
+std::vector<TimedLaunch> g_recs;
+std::vector<hipEvent_t> g_pool;
+
+hipEvent_t take_event() {
+    if (!g_pool.empty()) {
+        hipEvent_t e = g_pool.back();
+        g_pool.pop_back();
+        return e;
+    }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    return e;
+}
+
+const char* kStageNames[ST_COUNT] = {
+    "pool_score", "pool_up", "topk", "gather", "sub_prep", "attn_fwd", "scatter_fwd",
+    "zero_acc", "scatter_bwd", "bwd_prep", "attn_bwd_dkdv", "attn_bwd_dq", "pool_bwd"};
+
+// Runs `fn` (which enqueues one stage) between two timing events when enabled.
+template <class F>
+hipError_t stage(int id, hipStream_t s, F&& fn) {
+    hipEvent_t a = nullptr, b = nullptr;
+    {
+        std::lock_guard<std::mutex> g(g_mu);
+        if (g_timing) {
+            a = take_event();
+            b = take_event();
+        }
+    }
+    if (a && b) (void)hipEventRecord(a, s);
+    hipError_t e = fn();
+    if (a && b) {
+        (void)hipEventRecord(b, s);
+        std::lock_guard<std::mutex> g(g_mu);
+        g_recs.push_back({id, a, b});
+    }
+    return e;
+}
+}  // namespace
+
+}  // namespace lh
+
+using namespace lh;
+
+#define LH_TRY(expr)                               \
+    do {                                           \
+        if ((expr) != hipSuccess) return LH_ERR_HIP; \
+    } while (0)
+
+extern "C" {
+
+int64_t lh_subseq_len(int N, int p, int L, int K) { return subseq_len(N, p, L, K); }
+
+size_t lh_workspace_bytes(int N, int H, int d, int p, int L, int K, int dtype) {
+    Plan P;
+    if (make_plan(N, H, d, p, L, K, dtype, &P) != LH_OK) return 0;
+    return P.total;
+}
+
+static int check_ws(const Plan& P, const void* ws, size_t ws_bytes) {
+    if (!ws) return LH_ERR_WORKSPACE;
+    if (reinterpret_cast<uintptr_t>(ws) % 256 != 0) return LH_ERR_WORKSPACE;
+    if (ws_bytes < P.total) return LH_ERR_WORKSPACE;
+    return LH_OK;
+}
+
+static bool aligned16(const void* p) { return reinterpret_cast<uintptr_t>(p) % 16 == 0; }
+
+static const uint16_t* u16(char* w, size_t off) { return reinterpret_cast<const uint16_t*>(w + off); }
+static uint16_t* u16m(char* w, size_t off) { return reinterpret_cast<uint16_t*>(w + off); }
+static float* f32(char* w, size_t off) { return reinterpret_cast<float*>(w + off); }
+
+static AttnArgs sub_attn_args(const Plan& P, char* w) {
+    AttnArgs a{};
+    a.qh = u16(w, P.off_qh); a.ql = u16(w, P.off_ql);
+    a.kh = u16(w, P.off_kh); a.kl = u16(w, P.off_kl);
+    a.vh = u16(w, P.off_vh); a.vl = u16(w, P.off_vl);
+    a.doh = u16(w, P.off_doh); a.dol = u16(w, P.off_dol);
+    a.vTh = u16(w, P.off_vTh); a.vTl = u16(w, P.off_vTl);
+    a.kTh = u16(w, P.off_kTh); a.kTl = u16(w, P.off_kTl);
+    a.doTh = u16(w, P.off_doTh); a.doTl = u16(w, P.off_doTl);
+    a.qTbh = u16(w, P.off_qTbh); a.qTbl = u16(w, P.off_qTbl);
+    a.hscale = f32(w, P.off_hscale);
+    a.o = f32(w, P.off_os);
+    a.lse = f32(w, P.off_lse);
+    a.lse2 = f32(w, P.off_lse2);
+    a.D = f32(w, P.off_D);
+    a.rowdown = f32(w, P.off_rowdown);
+    a.dq = f32(w, P.off_dq); a.dk = f32(w, P.off_dk); a.dv = f32(w, P.off_dv);
+    a.rows = P.S; a.Sp = P.Sp;
+    a.H = P.H; a.d = P.d;
+    a.split = true;
+    a.fp32_path = P.dtype == FP32;
+    a.scale = 1.0f / sqrtf((float)P.d);
+    a.qf = f32(w, P.off_qs); a.kf = f32(w, P.off_ks); a.vf = f32(w, P.off_vs); a.dof = f32(w, P.off_dos);
+    return a;
+}
+
+// fp16 hi/lo copy of one [H][Sp][d] fp32 tensor (rows and optionally a transposed copy)
+static hipError_t split_sub(const Plan& P, char* w, size_t src, unsigned int* hmax, int slot, size_t rh, size_t rl,
+                            size_t th, size_t tl, int t_bf16, hipStream_t s) {
+    SplitSpec sp{};
+    sp.src = w + src; sp.ld = P.d; sp.hs = P.Sp * P.d; sp.rows = P.Sp; sp.Sp = P.Sp;
+    sp.d = P.d; sp.H = P.H; sp.src_bf16 = 0;
+    sp.hmax = hmax; sp.hscale = f32(w, P.off_hscale); sp.slot = slot;
+    sp.rh = u16m(w, rh); sp.rl = u16m(w, rl); sp.th = u16m(w, th); sp.tl = u16m(w, tl);
+    sp.t_bf16 = t_bf16;
+    return launch_split(sp, s);
+}
+
+int lh_forward(const void* q, const void* k, const void* v, void* o, int N, int H, int d, int p, int L,
+               int K, int dtype, void* ws, size_t ws_bytes, void* stream) {
+    Plan P;
+    int rc = make_plan(N, H, d, p, L, K, dtype, &P);
+    if (rc) return rc;
+    if (!q || !k || !v || !o) return LH_ERR_ARG;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return LH_ERR_ARG;
+    if ((rc = check_ws(P, ws, ws_bytes))) return rc;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    char* w = reinterpret_cast<char*>(ws);
+    LH_TRY(stage(ST_POOL_SCORE, s, [&] { return launch_pool_score(P, q, k, v, w, s); }));
+    if (L > 1 && P.m < L - 1) LH_TRY(stage(ST_POOL_UP, s, [&] { return launch_pool_up(P, w, s); }));
+    LH_TRY(stage(ST_TOPK, s, [&] { return launch_topk(P, w, s); }));
+    LH_TRY(stage(ST_GATHER, s, [&] { return launch_gather(P, q, k, v, w, s); }));
+    unsigned int* hmax = reinterpret_cast<unsigned int*>(w + P.off_hmax);
+    LH_TRY(stage(ST_SUB_PREP, s, [&] {
+        hipError_t e = launch_fill_zero(hmax, sizeof(uint32_t) * 8 * (size_t)H, s);
+        if (e != hipSuccess || dtype != BF16) return e;
+        const size_t src[3] = {P.off_qs, P.off_ks, P.off_vs};
+        for (int t = 0; t < 3 && e == hipSuccess; ++t)
+            e = launch_maxabs(w + src[t], false, P.d, P.Sp * P.d, P.Sp, P.d, H, hmax + t, s);
+        if (e == hipSuccess) e = split_sub(P, w, P.off_qs, hmax, 0, P.off_qh, P.off_ql, P.off_qTbh, P.off_qTbl, 1, s);
+        if (e == hipSuccess) e = split_sub(P, w, P.off_ks, hmax, 1, P.off_kh, P.off_kl, P.off_kTh, P.off_kTl, 0, s);
+        if (e == hipSuccess) e = split_sub(P, w, P.off_vs, hmax, 2, P.off_vh, P.off_vl, P.off_vTh, P.off_vTl, 0, s);
+        return e;
+    }));
+    AttnArgs a = sub_attn_args(P, w);
+    LH_TRY(stage(ST_ATTN_FWD, s, [&] { return launch_attn_fwd(a, s); }));
+    LH_TRY(stage(ST_SCATTER_FWD, s, [&] { return launch_scatter_fwd(P, w, o, s); }));
+    return LH_OK;
+}
+
+int lh_backward(const void* dout, void* dq, void* dk, void* dv, int N, int H, int d, int p, int L, int K,
+                int dtype, int scatter_mode, void* ws, size_t ws_bytes, void* stream) {
+    Plan P;
+    int rc = make_plan(N, H, d, p, L, K, dtype, &P);
+    if (rc) return rc;
+    if (scatter_mode != LH_SCATTER_FP_ATOMIC && scatter_mode != LH_SCATTER_INT_ATOMIC) return LH_ERR_DTYPE;
+    if (!dout || !dq || !dk || !dv) return LH_ERR_ARG;
+    if (!aligned16(dout) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv)) return LH_ERR_ARG;
+    if ((rc = check_ws(P, ws, ws_bytes))) return rc;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    char* w = reinterpret_cast<char*>(ws);
+    const size_t HSd = (size_t)H * P.Sp * d;
+    unsigned int* hmax = reinterpret_cast<unsigned int*>(w + P.off_hmax);
+    unsigned int* hmax_b = hmax + 4 * (size_t)H;
+    LH_TRY(stage(ST_ZERO_ACC, s, [&] { return launch_fill_zero(w + P.off_acc, 8 * HSd, s); }));
+    LH_TRY(stage(ST_SCATTER_BWD, s, [&] { return launch_scatter_bwd(P, dout, scatter_mode, w, s); }));
+    LH_TRY(stage(ST_BWD_PREP, s, [&] {
+        RowPrepSpec rp{};
+        rp.acc = w + P.off_acc; rp.o = w + P.off_os;
+        rp.dos = f32(w, P.off_dos); rp.D = f32(w, P.off_D); rp.rowdown = f32(w, P.off_rowdown);
+        rp.vmax = hmax; rp.S = P.S; rp.Sp = P.Sp; rp.H = H; rp.d = d; rp.mode = scatter_mode; rp.dense = 0;
+        hipError_t e = launch_row_prep(rp, s);
+        if (e != hipSuccess || dtype != BF16) return e;
+        e = launch_fill_zero(hmax_b, sizeof(uint32_t) * 4 * (size_t)H, s);
+        if (e == hipSuccess) e = launch_maxabs(w + P.off_dos, false, P.d, P.Sp * P.d, P.Sp, P.d, H, hmax_b + 3, s);
+        if (e == hipSuccess) e = split_sub(P, w, P.off_dos, hmax_b, 3, P.off_doh, P.off_dol, P.off_doTh, P.off_doTl, 0, s);
+        return e;
+    }));
+    AttnArgs a = sub_attn_args(P, w);
+    LH_TRY(stage(ST_ATTN_BWD_DKDV, s, [&] { return launch_attn_bwd(a, s, 0); }));
+    if (dtype == BF16) LH_TRY(stage(ST_ATTN_BWD_DQ, s, [&] { return launch_attn_bwd(a, s, 1); }));
+    LH_TRY(stage(ST_POOL_BWD, s, [&] { return launch_pool_bwd(P, w, dq, dk, dv, s); }));
+    return LH_OK;
+}
+
+int lh_workspace_view(void* ws, int N, int H, int d, int p, int L, int K, int dtype, int view, void** ptr,
+                      size_t* bytes) {
+    Plan P;
+    int rc = make_plan(N, H, d, p, L, K, dtype, &P);
+    if (rc) return rc;
+    if (!ws || !ptr || !bytes) return LH_ERR_ARG;
+    char* w = reinterpret_cast<char*>(ws);
+    const size_t HSd = (size_t)H * P.Sp * d;
+    size_t off = 0, n = 0;
+    switch (view) {
+        case LH_VIEW_SCORES: {
+            off = P.off_scores;
+            size_t tot = 0;
+            for (int l = 0; l < L; ++l) tot += (size_t)H * P.n[l];
+            n = sizeof(float) * tot;
+            break;
+        }
+        case LH_VIEW_SEL_START: off = P.off_start; n = sizeof(int32_t) * (size_t)H * P.S; break;
+        case LH_VIEW_SEL_LEVEL: off = P.off_level; n = (size_t)H * P.S; break;
+        case LH_VIEW_QSUB: off = P.off_qs; n = sizeof(float) * HSd; break;
+        case LH_VIEW_KSUB: off = P.off_ks; n = sizeof(float) * HSd; break;
+        case LH_VIEW_VSUB: off = P.off_vs; n = sizeof(float) * HSd; break;
+        case LH_VIEW_OSUB: off = P.off_os; n = sizeof(float) * HSd; break;
+        case LH_VIEW_LSE: off = P.off_lse; n = sizeof(float) * (size_t)H * P.Sp; break;
+        case LH_VIEW_DOSUB: off = P.off_dos; n = sizeof(float) * HSd; break;
+        case LH_VIEW_DQSUB: off = P.off_dq; n = sizeof(float) * HSd; break;
+        case LH_VIEW_DKSUB: off = P.off_dk; n = sizeof(float) * HSd; break;
+        case LH_VIEW_DVSUB: off = P.off_dv; n = sizeof(float) * HSd; break;
+        case LH_VIEW_BLOCK_FIRST: off = P.off_bfirst; n = sizeof(int32_t) * (size_t)H * (P.ntop + 1); break;
+        default: return LH_ERR_ARG;
+    }
+    *ptr = w + off;
+    *bytes = n;
+    return LH_OK;
+}
+
+// ------------------------------------------------------------ dense path
+static int dense_check(int N, int H, int d, int dtype) {
+    if (dtype != BF16) return LH_ERR_DTYPE;
+    if (N <= 0 || H <= 0) return LH_ERR_ARG;
+    if (d != 64 && d != 128) return LH_ERR_SHAPE;
+    if (N % 64 != 0 || (int64_t)H * d > 8192) return LH_ERR_SHAPE;
+    return LH_OK;
+}
+
+struct DenseLayout {
+    size_t qh, kh, vh, doh, vTh, kTh, doTh, qTbh, o32, hmax, hscale, lse2, D, rowdown, total;
+};
+static DenseLayout dense_layout(int N, int H, int d) {
+    DenseLayout L{};
+    const size_t t = 2 * (size_t)H * d * N;
+    const size_t r = sizeof(float) * (size_t)H * N;
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        const size_t o = off;
+        off = align256(off + bytes);
+        return o;
+    };
+    L.qh = take(t); L.kh = take(t); L.vh = take(t); L.doh = take(t);
+    L.vTh = take(t); L.kTh = take(t); L.doTh = take(t); L.qTbh = take(t);
+    L.o32 = take(2 * t);
+    L.hmax = take(sizeof(uint32_t) * 4 * (size_t)H);
+    L.hscale = take(sizeof(float) * 4 * (size_t)H);
+    L.lse2 = take(r); L.D = take(r); L.rowdown = take(r);
+    L.total = off;
+    return L;
+}
+
+size_t lh_dense_workspace_bytes(int N, int H, int d, int dtype) {
+    if (dense_check(N, H, d, dtype)) return 0;
+    return dense_layout(N, H, d).total;
+}
+
+// Dense operands are bf16 inputs [N][H][d]: exact in the 16-bit formats, so
+// no lo parts are needed.
+static hipError_t dense_split(const void* src, int N, int H, int d, char* w, const DenseLayout& DL, int slot,
+                              size_t rh, size_t th, int t_bf16, hipStream_t s) {
+    SplitSpec sp{};
+    sp.src = src; sp.ld = (int64_t)H * d; sp.hs = d; sp.rows = N; sp.Sp = N;
+    sp.d = d; sp.H = H; sp.src_bf16 = 1;
+    sp.hmax = reinterpret_cast<const unsigned int*>(w + DL.hmax);
+    sp.hscale = f32(w, DL.hscale); sp.slot = slot;
+    sp.rh = rh == SIZE_MAX ? nullptr : u16m(w, rh);
+    sp.th = th == SIZE_MAX ? nullptr : u16m(w, th);
+    sp.t_bf16 = t_bf16;
+    return launch_split(sp, s);
+}
+
+static AttnArgs dense_args(int N, int H, int d, char* w, const DenseLayout& DL) {
+    AttnArgs a{};
+    a.qh = u16(w, DL.qh); a.kh = u16(w, DL.kh); a.vh = u16(w, DL.vh); a.doh = u16(w, DL.doh);
+    a.vTh = u16(w, DL.vTh); a.kTh = u16(w, DL.kTh); a.doTh = u16(w, DL.doTh); a.qTbh = u16(w, DL.qTbh);
+    a.hscale = f32(w, DL.hscale);
+    a.lse2 = f32(w, DL.lse2); a.D = f32(w, DL.D); a.rowdown = f32(w, DL.rowdown);
+    a.rows = N; a.Sp = N; a.ld_o = (int64_t)H * d; a.hs_o = d;
+    a.H = H; a.d = d; a.split = false; a.fp32_path = false;
+    a.scale = 1.0f / sqrtf((float)d);
+    return a;
+}
+
+// Per-head max |x| of the given bf16 [N][H][d] tensors into slots first..n-1
+// (the slots are cleared first; other slots are kept).
+static hipError_t dense_maxabs(const void* const* src, int n, int N, int H, int d, char* w, const DenseLayout& DL,
+                               hipStream_t s, int first = 0) {
+    unsigned int* hmax = reinterpret_cast<unsigned int*>(w + DL.hmax);
+    hipError_t e = hipSuccess;
+    if (first == 0) e = launch_fill_zero(hmax, sizeof(uint32_t) * 4 * (size_t)H, s);
+    else e = launch_clear_slot(hmax, H, first, s);
+    for (int t = first; t < n && e == hipSuccess; ++t)
+        if (src[t]) e = launch_maxabs(src[t], true, (int64_t)H * d, d, N, d, H, hmax + t, s);
+    return e;
+}
+
+int lh_dense_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int N, int H, int d,
+                      int dtype, void* ws, size_t ws_bytes, void* stream) {
+    int rc = dense_check(N, H, d, dtype);
+    if (rc) return rc;
+    if (!q || !k || !v || !o || !lse) return LH_ERR_ARG;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return LH_ERR_ARG;
+    const DenseLayout DL = dense_layout(N, H, d);
+    if (!ws || reinterpret_cast<uintptr_t>(ws) % 256 || ws_bytes < DL.total) return LH_ERR_WORKSPACE;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    char* w = reinterpret_cast<char*>(ws);
+    const void* src[3] = {q, k, v};
+    LH_TRY(dense_maxabs(src, 3, N, H, d, w, DL, s));
+    // every q/k/v copy the matching backward needs is made here
+    LH_TRY(dense_split(q, N, H, d, w, DL, 0, DL.qh, DL.qTbh, 1, s));
+    LH_TRY(dense_split(k, N, H, d, w, DL, 1, DL.kh, DL.kTh, 0, s));
+    LH_TRY(dense_split(v, N, H, d, w, DL, 2, DL.vh, DL.vTh, 0, s));
+    AttnArgs a = dense_args(N, H, d, w, DL);
+    a.o_bf16 = reinterpret_cast<uint16_t*>(o);
+    a.o = f32(w, DL.o32);
+    a.lse = lse;
+    LH_TRY(launch_attn_fwd(a, s));
+    return LH_OK;
+}
+
+int lh_dense_attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                      const void* dout, void* dq, void* dk, void* dv, int N, int H, int d, int dtype, void* ws,
+                      size_t ws_bytes, void* stream) {
+    int rc = dense_check(N, H, d, dtype);
+    if (rc) return rc;
+    if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv) return LH_ERR_ARG;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dout) || !aligned16(dq) ||
+        !aligned16(dk) || !aligned16(dv))
+        return LH_ERR_ARG;
+    const DenseLayout DL = dense_layout(N, H, d);
+    if (!ws || reinterpret_cast<uintptr_t>(ws) % 256 || ws_bytes < DL.total) return LH_ERR_WORKSPACE;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    char* w = reinterpret_cast<char*>(ws);
+    // q, k, v copies and the fp32 output come from the matching forward's workspace
+    const void* src[4] = {nullptr, nullptr, nullptr, dout};
+    LH_TRY(dense_maxabs(src, 4, N, H, d, w, DL, s, 3));
+    LH_TRY(dense_split(dout, N, H, d, w, DL, 3, DL.doh, DL.doTh, 0, s));
+    RowPrepSpec rp{};
+    rp.dout = dout; rp.o = w + DL.o32; rp.ld = (int64_t)H * d; rp.hs = d;
+    rp.D = f32(w, DL.D); rp.rowdown = f32(w, DL.rowdown);
+    rp.vmax = reinterpret_cast<const unsigned int*>(w + DL.hmax);
+    rp.lse_in = lse; rp.lse2 = f32(w, DL.lse2);
+    rp.S = N; rp.Sp = N; rp.H = H; rp.d = d; rp.dense = 1;
+    LH_TRY(launch_row_prep(rp, s));
+    AttnArgs a = dense_args(N, H, d, w, DL);
+    a.dq_b = reinterpret_cast<uint16_t*>(dq);
+    a.dk_b = reinterpret_cast<uint16_t*>(dk);
+    a.dv_b = reinterpret_cast<uint16_t*>(dv);
+    LH_TRY(launch_attn_bwd(a, s, 0));
+    LH_TRY(launch_attn_bwd(a, s, 1));
+    return LH_OK;
+}
+
+// ------------------------------------------------------------ timing / misc
+int lh_stage_timing(int enable) {
+    std::lock_guard<std::mutex> g(g_mu);
+    for (auto& r : g_recs) {
+        g_pool.push_back(r.a);
+        g_pool.push_back(r.b);
+    }
+    g_recs.clear();
+    g_timing = enable != 0;
+    return LH_OK;
+}
+
+int lh_stage_timing_read(double* ms, int* count, int n) {
+    std::vector<TimedLaunch> recs;
+    {
+        std::lock_guard<std::mutex> g(g_mu);
+        recs.swap(g_recs);
+    }
+    int rc = ST_COUNT;
+    for (auto& r : recs) {
+        float t = 0.f;
+        if (hipEventSynchronize(r.b) != hipSuccess || hipEventElapsedTime(&t, r.a, r.b) != hipSuccess) {
+            rc = LH_ERR_HIP;
+        } else if (r.stage < n) {
+            if (ms) ms[r.stage] += t;
+            if (count) count[r.stage] += 1;
+        }
+    }
+    std::lock_guard<std::mutex> g(g_mu);
+    for (auto& r : recs) {
+        g_pool.push_back(r.a);
+        g_pool.push_back(r.b);
+    }
+    return rc;
+}
+
+const char* lh_stage_name(int stage) {
+    if (stage < 0 || stage >= ST_COUNT) return "unknown";
+    return kStageNames[stage];
+}
+
+const char* lh_status_str(int status) {
+    switch (status) {
+        case LH_OK: return "ok";
+        case LH_ERR_ARG: return "invalid argument";
+        case LH_ERR_SHAPE: return "unsupported shape";
+        case LH_ERR_DTYPE: return "unknown dtype or mode";
+        case LH_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
+        case LH_ERR_HIP: return "HIP launch or runtime error";
+        default: return "unknown status";
+    }
+}
+
+}  // extern "C"

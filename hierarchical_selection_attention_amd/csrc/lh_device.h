@@ -1,0 +1,84 @@
+// Device-side helpers for the gfx950 kernels: vector types, bf16 conversion,
+// wavefront shuffles.  Wave size is 64 on CDNA.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace lh {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+// bf16 bits -> fp32, exact.
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// fp32 -> bf16 bits, round to nearest even (inputs are finite).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+    uint32_t u = __float_as_uint(f);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+}
+
+// 8 consecutive elements of a row as fp32.  bf16: one 16-byte load; fp32: two.
+template <int DT>
+__device__ __forceinline__ void load8(const void* base, int64_t elem, float (&x)[8]) {
+    if constexpr (DT == 0) {
+        u32x4 w = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(base) + elem);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            x[2 * i] = bf16_lo(w[i]);
+            x[2 * i + 1] = bf16_hi(w[i]);
+        }
+    } else {
+        const f32x4* p = reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(base) + elem);
+        f32x4 a = p[0], b = p[1];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            x[i] = a[i];
+            x[4 + i] = b[i];
+        }
+    }
+}
+
+template <int DT>
+__device__ __forceinline__ void store8(void* base, int64_t elem, const float (&x)[8]) {
+    if constexpr (DT == 0) {
+        u32x4 w;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) w[i] = pack_bf16x2(x[2 * i], x[2 * i + 1]);
+        *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(base) + elem) = w;
+    } else {
+        f32x4* p = reinterpret_cast<f32x4*>(reinterpret_cast<float*>(base) + elem);
+        p[0] = f32x4{x[0], x[1], x[2], x[3]};
+        p[1] = f32x4{x[4], x[5], x[6], x[7]};
+    }
+}
+
+__device__ __forceinline__ void load8f(const float* base, int64_t elem, float (&x)[8]) {
+    const f32x4* p = reinterpret_cast<const f32x4*>(base + elem);
+    f32x4 a = p[0], b = p[1];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        x[i] = a[i];
+        x[4 + i] = b[i];
+    }
+}
+__device__ __forceinline__ void store8f(float* base, int64_t elem, const float (&x)[8]) {
+    f32x4* p = reinterpret_cast<f32x4*>(base + elem);
+    p[0] = f32x4{x[0], x[1], x[2], x[3]};
+    p[1] = f32x4{x[4], x[5], x[6], x[7]};
+}
+
+__device__ __forceinline__ float shfl_xor_f(float v, int mask) {
+    return __shfl_xor(v, mask, 64);
+}
+
+}  // namespace lh

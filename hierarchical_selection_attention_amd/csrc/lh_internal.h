@@ -1,0 +1,125 @@
+// Internal plan of the Lighthouse layer on gfx950: shapes, workspace layout
+// and the host-side launchers of every kernel.  Shared by the kernel sources
+// and the C ABI (lh_api.cpp); not installed.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace lh {
+
+constexpr int kMaxLevels = 24;
+constexpr int kMaxK = 2048;        // largest K the top-K network sorts (when K < #candidates)
+constexpr int kRowPad = 64;        // sub-sequence rows are padded to a multiple of this
+constexpr int kChunkTokMax = 256;  // tokens per workgroup in the pooling/scoring pass
+constexpr int kChunkScoreMax = 8192;  // tokens*heads of leaf scores kept in LDS per workgroup
+
+enum Dtype { BF16 = 0, FP32 = 1 };
+
+// Stage ids for event timing (order of launch).
+enum Stage {
+    ST_POOL_SCORE = 0, ST_POOL_UP, ST_TOPK, ST_GATHER, ST_SUB_PREP, ST_ATTN_FWD,
+    ST_SCATTER_FWD, ST_ZERO_ACC, ST_SCATTER_BWD, ST_BWD_PREP, ST_ATTN_BWD_DKDV,
+    ST_ATTN_BWD_DQ, ST_POOL_BWD, ST_COUNT
+};
+
+struct Plan {
+    int N, H, d, p, L, K, dtype, esz;
+    int64_t S, Sp;
+    int m;                  // pyramid level produced per workgroup by the pooling pass
+    int64_t tok;            // p^m tokens per pooling workgroup
+    int64_t ntop;           // N / p^(L-1)
+    int64_t n[kMaxLevels];  // entries at level l
+    int64_t pw[kMaxLevels]; // p^l
+    int64_t tk_cap;         // capacity of one level's candidate list in the selection scratch
+    // byte offsets inside the workspace
+    size_t off_scores;
+    size_t lev_off[kMaxLevels];   // float offset of level l inside the score block
+    size_t off_pool_m;            // fp32 [3][n_m][H][d]
+    size_t off_pool_top;          // fp32 [3][ntop][H][d] (aliases off_pool_m when m == L-1)
+    size_t off_start, off_level, off_bfirst;
+    size_t off_tk;                // selection scratch: [H][L][5][tk_cap] int32
+    size_t off_qs, off_ks, off_vs;   // fp32 [H][Sp][d] gathered sub-sequence
+    // 16-bit operand copies (bf16 path): fp16 hi/lo rows [H][Sp][d], transposed [H][d][Sp]
+    size_t off_qh, off_ql, off_kh, off_kl, off_vh, off_vl;
+    size_t off_vTh, off_vTl, off_kTh, off_kTl, off_qTbh, off_qTbl;
+    size_t off_hmax;              // uint32 [2][H][4]: forward (q, k, v) and backward (dO) max |x|
+    size_t off_hscale;            // fp32 [H][4]: per-head multipliers of the fp16 copies
+    size_t off_os;                // fp32 [H][Sp][d]
+    size_t off_lse, off_lse2;     // fp32 [H][Sp]
+    size_t off_acc;               // 8 bytes x [H][Sp][d]: fp32 or int64 accumulators of dO~
+    size_t off_dos;               // fp32 [H][Sp][d]
+    size_t off_doh, off_dol, off_doTh, off_doTl;   // fp16 copies of dO~
+    size_t off_D, off_rowdown;    // fp32 [H][Sp]
+    size_t off_dq, off_dk, off_dv;   // fp32 [H][Sp][d]
+    size_t total;
+};
+
+// Fills `pl`; returns 0 or a negative lh_status.
+int make_plan(int N, int H, int d, int p, int L, int K, int dtype, Plan* pl);
+int64_t subseq_len(int N, int p, int L, int K);
+
+// ------------------------------------------------------------ launchers
+// Each returns hipSuccess or the launch error.  All pointers are device
+// pointers; `ws` is the workspace base.
+
+hipError_t launch_pool_score(const Plan& P, const void* q, const void* k, const void* v, char* ws,
+                             hipStream_t s);
+hipError_t launch_pool_up(const Plan& P, char* ws, hipStream_t s);
+hipError_t launch_topk(const Plan& P, char* ws, hipStream_t s);
+hipError_t launch_gather(const Plan& P, const void* q, const void* k, const void* v, char* ws,
+                         hipStream_t s);
+hipError_t launch_scatter_fwd(const Plan& P, char* ws, void* o, hipStream_t s);
+hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
+hipError_t launch_scatter_bwd(const Plan& P, const void* dout, int mode, char* ws, hipStream_t s);
+hipError_t launch_pool_bwd(const Plan& P, char* ws, void* dq, void* dk, void* dv, hipStream_t s);
+
+// Attention operands: 16-bit copies laid out [H][Sp][d] (rows) and
+// [H][d][Sp] (transposed); lo parts are used when `split`.
+struct AttnArgs {
+    const uint16_t *qh, *ql, *kh, *kl, *vh, *vl, *doh, *dol;
+    const uint16_t *vTh, *vTl, *kTh, *kTl, *doTh, *doTl, *qTbh, *qTbl;
+    const float* hscale;
+    float* o;                  // fp32 [H][Sp][d] or null
+    uint16_t* o_bf16;          // bf16 output rows (ld_o, hs_o) or null
+    float *lse, *lse2;
+    const float *D, *rowdown;
+    float *dq, *dk, *dv;       // fp32 [H][Sp][d] or null
+    uint16_t *dq_b, *dk_b, *dv_b;   // bf16 rows (ld_o, hs_o) or null
+    int64_t rows, Sp, ld_o, hs_o;
+    int H, d;
+    bool split, fp32_path;
+    float scale;
+    const float *qf, *kf, *vf, *dof;   // fp32 path operands [H][Sp][d]
+};
+hipError_t launch_attn_fwd(const AttnArgs& a, hipStream_t s);
+hipError_t launch_attn_bwd(const AttnArgs& a, hipStream_t s, int part);   // part 0: dK/dV, 1: dQ
+
+struct SplitSpec {
+    const void* src;
+    int64_t ld, hs, rows, Sp;
+    int d, H, src_bf16;
+    const unsigned int* hmax;
+    float* hscale;
+    int slot;
+    uint16_t *rh, *rl, *th, *tl;
+    int t_bf16;
+};
+struct RowPrepSpec {
+    const void *acc, *dout, *o;
+    int64_t ld, hs;
+    float *dos, *D, *rowdown;
+    const float* lse_in;       // dense: natural-log lse [H][N] -> lse2 (base 2)
+    float* lse2;
+    const unsigned int* vmax;
+    int64_t S, Sp;
+    int H, d, mode, dense;
+};
+hipError_t launch_maxabs(const void* src, bool src_bf16, int64_t ld, int64_t hs, int64_t rows, int d, int H,
+                         unsigned int* out, hipStream_t s);
+hipError_t launch_split(const SplitSpec& sp, hipStream_t s);
+hipError_t launch_clear_slot(unsigned int* hmax, int H, int slot, hipStream_t s);
+hipError_t launch_row_prep(const RowPrepSpec& sp, hipStream_t s);
+
+}  // namespace lh

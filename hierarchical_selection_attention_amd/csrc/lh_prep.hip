@@ -1,0 +1,250 @@
+// Operand preparation for the attention kernels on gfx950: per-head scale
+// exponents, hi/lo splits into 16-bit formats (row-major and transposed), and
+// the per-row quantities of the backward pass (D_i and the dS down-scale).
+#include "lh_device.h"
+#include "lh_internal.h"
+
+namespace lh {
+
+// ---------------------------------------------------------------- max |x|
+// Per-head maximum of |x| over [rows][d] (fp32 [H][Sp][d] or bf16 rows with
+// strides), accumulated as float bits with atomicMax (values are >= 0).
+template <int SRC_BF16>
+__global__ void __launch_bounds__(256) k_maxabs(const void* src, int64_t ld, int64_t hs, int64_t rows, int d,
+                                                unsigned int* out) {
+    const int h = blockIdx.y;
+    const int64_t r0 = (int64_t)blockIdx.x * 64;
+    const int G = d / 8;
+    float mx = 0.f;
+    for (int idx = threadIdx.x; idx < 64 * G; idx += 256) {
+        const int64_t r = r0 + idx / G;
+        if (r >= rows) break;
+        float x[8];
+        const int64_t el = h * hs + r * ld + (idx % G) * 8;
+        if constexpr (SRC_BF16) load8<0>(src, el, x);
+        else load8f(reinterpret_cast<const float*>(src), el, x);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) mx = fmaxf(mx, fabsf(x[e]));
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, shfl_xor_f(mx, off));
+    __shared__ float wm[4];
+    if ((threadIdx.x & 63) == 0) wm[threadIdx.x >> 6] = mx;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const float m = fmaxf(fmaxf(wm[0], wm[1]), fmaxf(wm[2], wm[3]));
+        atomicMax(out + h * 4, __float_as_uint(m));
+    }
+}
+
+// Power of two s with max|x| * s in [2^13, 2^14) (1 when max is 0).
+__device__ __forceinline__ float down_scale(float mx) {
+    if (!(mx > 0.f)) return 1.0f;
+    int ex;
+    frexpf(mx, &ex);           // mx = f * 2^ex, f in [0.5, 1)
+    return ldexpf(1.0f, 14 - ex);
+}
+
+// ---------------------------------------------------------------- splits
+// One 64x64 tile of head h: x = src * down (down = power-of-two scale of the
+// head); writes fp16 hi/lo rows, and a transposed copy as fp16 hi/lo (scaled)
+// or bf16 hi/lo (unscaled).  Rows >= `rows` are written as zeros.
+struct SplitArgs {
+    const void* src;
+    int64_t ld, hs, rows, Sp;
+    int d, src_bf16;
+    const unsigned int* hmax;   // [H][4], slot `slot`
+    float* hscale;              // [H][4]: stored * hscale = true value
+    int slot;
+    uint16_t *rh, *rl;          // fp16 [H][Sp][d] (scaled) or null
+    uint16_t *th, *tl;          // [H][d][Sp] or null
+    int t_bf16;                 // transposed copy in bf16, unscaled
+};
+
+__device__ __forceinline__ uint16_t h16(float x) { return __builtin_bit_cast(uint16_t, (_Float16)x); }
+__device__ __forceinline__ float f16f(uint16_t b) { return (float)__builtin_bit_cast(_Float16, b); }
+
+__global__ void __launch_bounds__(256) k_split(SplitArgs a) {
+    __shared__ uint16_t th[64][64 + 2];
+    __shared__ uint16_t tl[64][64 + 2];
+    const int h = blockIdx.z;
+    const int64_t r0 = (int64_t)blockIdx.x * 64;
+    const int c0 = blockIdx.y * 64;
+    const float mx = __uint_as_float(a.hmax[h * 4 + a.slot]);
+    const float down = down_scale(mx);
+    if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) a.hscale[h * 4 + a.slot] = 1.0f / down;
+    const float tdown = a.t_bf16 ? 1.0f : down;
+    // each thread: 2 (row, 8-column chunk) items of the 64x64 tile
+    for (int it = threadIdx.x; it < 64 * 8; it += 256) {
+        const int r = it / 8, cc = (it % 8) * 8;
+        float x[8];
+        if (r0 + r < a.rows) {
+            const int64_t el = h * a.hs + (r0 + r) * a.ld + c0 + cc;
+            if (a.src_bf16) load8<0>(a.src, el, x);
+            else load8f(reinterpret_cast<const float*>(a.src), el, x);
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) x[e] = 0.f;
+        }
+        if (a.rh) {
+            u32x4 wh, wl;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float x0 = x[2 * e] * down, x1 = x[2 * e + 1] * down;
+                const uint16_t h0 = h16(x0), h1 = h16(x1);
+                wh[e] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+                wl[e] = (uint32_t)h16(x0 - f16f(h0)) | ((uint32_t)h16(x1 - f16f(h1)) << 16);
+            }
+            const int64_t o = ((int64_t)h * a.Sp + r0 + r) * a.d + c0 + cc;
+            *reinterpret_cast<u32x4*>(a.rh + o) = wh;
+            if (a.rl) *reinterpret_cast<u32x4*>(a.rl + o) = wl;
+        }
+        if (a.th) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float xs = x[e] * tdown;
+                uint16_t hb, lb;
+                if (a.t_bf16) {
+                    hb = (uint16_t)f32_to_bf16_bits(xs);
+                    lb = (uint16_t)f32_to_bf16_bits(xs - bf16_lo(hb));
+                } else {
+                    hb = h16(xs);
+                    lb = h16(xs - f16f(hb));
+                }
+                th[cc + e][r] = hb;
+                tl[cc + e][r] = lb;
+            }
+        }
+    }
+    if (!a.th) return;
+    __syncthreads();
+    for (int it = threadIdx.x; it < 64 * 8; it += 256) {
+        const int col = it / 8, rr = (it % 8) * 8;
+        u32x4 wh, wl;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            wh[e] = (uint32_t)th[col][rr + 2 * e] | ((uint32_t)th[col][rr + 2 * e + 1] << 16);
+            wl[e] = (uint32_t)tl[col][rr + 2 * e] | ((uint32_t)tl[col][rr + 2 * e + 1] << 16);
+        }
+        const int64_t o = ((int64_t)h * a.d + c0 + col) * a.Sp + r0 + rr;
+        *reinterpret_cast<u32x4*>(a.th + o) = wh;
+        if (a.tl) *reinterpret_cast<u32x4*>(a.tl + o) = wl;
+    }
+}
+
+// ---------------------------------------------------------- backward rows
+// Per sub-sequence row: finish dO~ (fp32 or 64-bit fixed-point accumulator),
+// D_i = <dO~_i, O~_i> in double, and the power-of-two down-scale of row i of
+// dS, from |dS_ij| <= ||dO~_i|| * sqrt(d) * max|V~| + |D_i|.
+struct RowPrepArgs {
+    const void* acc;       // [H][Sp][d] fp32 (mode 0) or int64 (mode 1); unused when dense
+    const void* dout;      // dense: bf16 rows with strides ld/hs
+    const void* o;         // fp32 [H][Sp][d] attention output
+    int64_t ld, hs;        // dense strides of dout
+    float* dos;            // fp32 [H][Sp][d] finished dO~ (sub-sequence) or null
+    float *D, *rowdown;    // [H][Sp]
+    const float* lse_in;   // dense: natural-log lse [H][N], converted to base 2 in lse2
+    float* lse2;
+    const unsigned int* vmax;  // [H][4] slot 2: max |V|
+    int64_t S, Sp;
+    int H, d, mode, dense;
+};
+
+template <int G>
+__global__ void __launch_bounds__(256) k_row_prep(RowPrepArgs a) {
+    constexpr int d = G * 8;
+    const int c = threadIdx.x % G;
+    const int64_t r = (int64_t)blockIdx.x * (256 / G) + threadIdx.x / G;   // over [H][Sp]
+    const bool live = r < (int64_t)a.H * a.Sp;
+    const int64_t h = live ? r / a.Sp : 0;
+    const int64_t i = live ? r % a.Sp : 0;
+    float x[8], o[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = o[e] = 0.f;
+    if (live && i < a.S) {
+        if (a.dense) {
+            load8<0>(a.dout, h * a.hs + i * a.ld + c * 8, x);
+            load8f(reinterpret_cast<const float*>(a.o), r * d + c * 8, o);
+        } else {
+            const int64_t el = r * d + c * 8;
+            if (a.mode == 0) {
+                load8f(reinterpret_cast<const float*>(a.acc), el, x);
+            } else {
+                const long long* p = reinterpret_cast<const long long*>(a.acc) + el;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) x[e] = (float)((double)p[e] * (1.0 / 4294967296.0));
+            }
+            load8f(reinterpret_cast<const float*>(a.o), el, o);
+        }
+    }
+    if (live && a.dos) store8f(a.dos, r * d + c * 8, x);
+    double dot = 0.0, nrm = 0.0;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        dot = fma((double)x[e], (double)o[e], dot);
+        nrm = fma((double)x[e], (double)x[e], nrm);
+    }
+#pragma unroll
+    for (int off = G / 2; off >= 1; off >>= 1) {
+        dot += __shfl_xor(dot, off, 64);
+        nrm += __shfl_xor(nrm, off, 64);
+    }
+    if (live && c == 0) {
+        if (a.lse_in) a.lse2[r] = a.lse_in[r] * 1.4426950408889634f;
+        a.D[r] = (float)dot;
+        const float vm = __uint_as_float(a.vmax[h * 4 + 2]);
+        const float bound = (float)(sqrt(nrm) * sqrt((double)d) * (double)vm + fabs(dot));
+        float down = 1.0f;
+        if (bound > 0.f) {
+            int ex;
+            frexpf(bound, &ex);
+            down = ldexpf(1.0f, 13 - ex);
+        }
+        a.rowdown[r] = down;
+    }
+}
+
+__global__ void k_clear_slot(unsigned int* hmax, int H, int slot) {
+    const int h = blockIdx.x * blockDim.x + threadIdx.x;
+    if (h < H) hmax[h * 4 + slot] = 0u;
+}
+
+// ------------------------------------------------------------------ launchers
+hipError_t launch_clear_slot(unsigned int* hmax, int H, int slot, hipStream_t s) {
+    hipLaunchKernelGGL(k_clear_slot, dim3((unsigned)((H + 63) / 64)), dim3(64), 0, s, hmax, H, slot);
+    return hipGetLastError();
+}
+
+hipError_t launch_maxabs(const void* src, bool src_bf16, int64_t ld, int64_t hs, int64_t rows, int d, int H,
+                         unsigned int* out, hipStream_t s) {
+    dim3 grid((unsigned)((rows + 63) / 64), (unsigned)H);
+    if (src_bf16) hipLaunchKernelGGL(k_maxabs<1>, grid, dim3(256), 0, s, src, ld, hs, rows, d, out);
+    else hipLaunchKernelGGL(k_maxabs<0>, grid, dim3(256), 0, s, src, ld, hs, rows, d, out);
+    return hipGetLastError();
+}
+
+hipError_t launch_split(const SplitSpec& sp, hipStream_t s) {
+    SplitArgs a{};
+    a.src = sp.src; a.ld = sp.ld; a.hs = sp.hs; a.rows = sp.rows; a.Sp = sp.Sp;
+    a.d = sp.d; a.src_bf16 = sp.src_bf16; a.hmax = sp.hmax; a.hscale = sp.hscale; a.slot = sp.slot;
+    a.rh = sp.rh; a.rl = sp.rl; a.th = sp.th; a.tl = sp.tl; a.t_bf16 = sp.t_bf16;
+    dim3 grid((unsigned)(sp.Sp / 64), (unsigned)(sp.d / 64), (unsigned)sp.H);
+    hipLaunchKernelGGL(k_split, grid, dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_row_prep(const RowPrepSpec& sp, hipStream_t s) {
+    RowPrepArgs a{};
+    a.acc = sp.acc; a.dout = sp.dout; a.o = sp.o; a.ld = sp.ld; a.hs = sp.hs;
+    a.dos = sp.dos; a.D = sp.D; a.rowdown = sp.rowdown; a.vmax = sp.vmax;
+    a.lse_in = sp.lse_in; a.lse2 = sp.lse2;
+    a.S = sp.S; a.Sp = sp.Sp; a.H = sp.H; a.d = sp.d; a.mode = sp.mode; a.dense = sp.dense;
+    const int G = sp.d / 8;
+    const int64_t rows = (int64_t)sp.H * sp.Sp;
+    dim3 grid((unsigned)((rows + (256 / G) - 1) / (256 / G)));
+    if (G == 16) hipLaunchKernelGGL(k_row_prep<16>, grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL(k_row_prep<8>, grid, dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+}  // namespace lh

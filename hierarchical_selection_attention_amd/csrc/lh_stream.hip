@@ -1,0 +1,662 @@
+// Bandwidth-bound stages of the Lighthouse layer on gfx950.
+//
+// Paper: "Long Context Pre-Training with Lighthouse Attention" (arXiv
+// 2605.06554), Sec. 3 stages (i) pooling and (iv) scatter, Fig. 1 (gather,
+// back-scatter, gradient path) and Fig. 2 (mean-pool by p^l, l2 norm +
+// max-pool).  Every kernel streams [N][H][d] rows with 16-byte vector
+// accesses: a row is split over G = d/8 consecutive lanes (8 elements each),
+// so one wavefront instruction touches 64*16 contiguous bytes of bf16.
+#include "lh_device.h"
+#include "lh_internal.h"
+
+namespace lh {
+
+// ---------------------------------------------------------------------------
+// Pooling + scoring pass (stage (i) and the scorer of stage (ii)).
+// One workgroup per chunk of `tok` = p^m tokens, all heads.  Thread
+// (ts, h, c): token lane ts, head h, 8-element chunk c.  Outputs: leaf scores
+// and their max-pool for levels 0..m, and the level-m means of q, k, v (fp32).
+// The leaf score is ||q||^2 + ||k||^2 in fp32 in a fixed order: fma over the 8
+// elements of a lane from +0, then a xor butterfly over the G lanes of the row,
+// then one add of the q and k parts.
+struct PoolScoreArgs {
+    const void *q, *k, *v;
+    float* lev[kMaxLevels];   // level l scores, [H][n_l]
+    float* pool_m;            // fp32 [3][n_m][H][d]
+    int64_t n[kMaxLevels];
+    int N, H, HG, p, m, tok, mt;
+    int64_t pw[kMaxLevels];
+};
+
+template <int DT, int G>
+__global__ void __launch_bounds__(256) k_pool_score(PoolScoreArgs a) {
+    extern __shared__ float smem[];
+    const int d = G * 8;
+    const int tid = threadIdx.x;
+    const int c = tid % G;
+    const int row = tid / G;
+    const int HG = a.HG;              // heads handled by this workgroup
+    const int hl = row % HG;          // local head
+    const int h = blockIdx.y * HG + hl;
+    const int ts = row / HG;
+    const int H = a.H;
+    const int64_t t0 = (int64_t)blockIdx.x * a.tok;
+    const int iters = a.tok / a.mt;
+    float* sc = smem;   // [tok][H] leaf scores
+
+    float aq[8], ak[8], av[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) aq[e] = ak[e] = av[e] = 0.f;
+
+    constexpr int U = 4;
+    for (int i0 = 0; i0 < iters; i0 += U) {
+        float xq[U][8], xk[U][8], xv[U][8];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if (i0 + u < iters) {
+                int64_t t = t0 + ts + (int64_t)a.mt * (i0 + u);
+                int64_t el = (t * H + h) * d + c * 8;
+                load8<DT>(a.q, el, xq[u]);
+                load8<DT>(a.k, el, xk[u]);
+                load8<DT>(a.v, el, xv[u]);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if (i0 + u < iters) {
+                float sq = 0.f, sk = 0.f;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    sq = __builtin_fmaf(xq[u][e], xq[u][e], sq);
+                    sk = __builtin_fmaf(xk[u][e], xk[u][e], sk);
+                }
+#pragma unroll
+                for (int off = G / 2; off >= 1; off >>= 1) {
+                    sq = sq + shfl_xor_f(sq, off);
+                    sk = sk + shfl_xor_f(sk, off);
+                }
+                if (c == 0) sc[(ts + a.mt * (i0 + u)) * HG + hl] = sq + sk;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    aq[e] += xq[u][e];
+                    ak[e] += xk[u][e];
+                    av[e] += xv[u][e];
+                }
+            }
+        }
+    }
+    __syncthreads();
+
+    // scores of levels 0..m for this chunk: max over the covered leaves
+    for (int l = 0; l <= a.m; ++l) {
+        const int per = a.tok / (int)a.pw[l];
+        const int span = (int)a.pw[l];
+        const int64_t j0 = t0 / span;
+        for (int idx = tid; idx < HG * per; idx += blockDim.x) {
+            int hh = idx / per, j = idx % per;
+            float mx = sc[(j * span) * HG + hh];
+            for (int u = 1; u < span; ++u) mx = fmaxf(mx, sc[(j * span + u) * HG + hh]);
+            a.lev[l][(int64_t)(blockIdx.y * HG + hh) * a.n[l] + j0 + j] = mx;
+        }
+    }
+
+    // level-m means of q, k, v (only needed when the pyramid has levels)
+    if (a.m >= 1) {
+        float* red = smem + a.tok * HG;   // [mt][HG][d]
+        const float inv = 1.0f / (float)a.tok;
+        const int64_t blk = blockIdx.x;
+        float* accs[3] = {aq, ak, av};
+#pragma unroll
+        for (int t = 0; t < 3; ++t) {
+            float* acc = accs[t];
+            float* dst = a.pool_m + ((int64_t)t * a.n[a.m] + blk) * H * d;
+            if (a.mt == 1) {
+                float o[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) o[e] = acc[e] * inv;
+                store8f(dst, (int64_t)h * d + c * 8, o);
+            } else {
+                __syncthreads();
+#pragma unroll
+                for (int e = 0; e < 8; ++e) red[(ts * HG + hl) * d + c * 8 + e] = acc[e];
+                __syncthreads();
+                if (ts == 0) {
+                    float o[8];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        float s = 0.f;
+                        for (int z = 0; z < a.mt; ++z) s += red[(z * HG + hl) * d + c * 8 + e];
+                        o[e] = s * inv;
+                    }
+                    store8f(dst, (int64_t)h * d + c * 8, o);
+                }
+            }
+        }
+    }
+}
+
+// Levels m+1..L-1 from level m: top-level means of q, k, v and max-pooled
+// scores.  One workgroup per top-level block.
+struct PoolUpArgs {
+    float* lev[kMaxLevels];
+    const float* pool_m;   // [3][n_m][H][d]
+    float* pool_top;       // [3][ntop][H][d]
+    int64_t n[kMaxLevels];
+    int64_t pw[kMaxLevels];
+    int H, d, p, m, L;
+};
+
+__global__ void __launch_bounds__(256) k_pool_up(PoolUpArgs a) {
+    const int64_t b = blockIdx.x;
+    const int R = (int)(a.pw[a.L - 1] / a.pw[a.m]);   // level-m rows per top block
+    const int HD = a.H * a.d;
+    const float inv = 1.0f / (float)R;
+    for (int t = 0; t < 3; ++t) {
+        const float* src = a.pool_m + ((int64_t)t * a.n[a.m] + b * R) * HD;
+        float* dst = a.pool_top + ((int64_t)t * a.n[a.L - 1] + b) * HD;
+        for (int idx = threadIdx.x; idx < HD; idx += blockDim.x) {
+            float s = 0.f;
+            for (int r = 0; r < R; ++r) s += src[(int64_t)r * HD + idx];
+            dst[idx] = s * inv;
+        }
+    }
+    for (int l = a.m + 1; l < a.L; ++l) {
+        const int per = (int)(a.pw[a.L - 1] / a.pw[l]);   // level-l entries per top block
+        for (int idx = threadIdx.x; idx < a.H * per; idx += blockDim.x) {
+            int h = idx / per, j = idx % per;
+            int64_t jj = b * per + j;
+            const float* prev = a.lev[l - 1] + h * a.n[l - 1] + jj * a.p;
+            float mx = prev[0];
+            for (int c = 1; c < a.p; ++c) mx = fmaxf(mx, prev[c]);
+            a.lev[l][h * a.n[l] + jj] = mx;
+        }
+        __syncthreads();
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Gather (Fig. 1 "Dense Gather"): sub-sequence row i of head h is the mean of
+// the pyramid entry (start_i, level_i).  One wavefront per row; the entry is
+// read from the stored top level, from the stored level m (p^(l-m) rows), or
+// from the input tokens (p^l rows).  Rows i in [S, Sp) are written as zeros.
+struct GatherArgs {
+    const void *q, *k, *v;
+    const float* pool_m;
+    const float* pool_top;
+    const int32_t* start;
+    const uint8_t* level;
+    float *qs, *ks, *vs;   // fp32 [H][Sp][d]
+    int64_t S, Sp, n_m, ntop;
+    int64_t pw[kMaxLevels];
+    int H, m, L;
+};
+
+template <int DT, int G>
+__global__ void __launch_bounds__(256) k_gather(GatherArgs a) {
+    constexpr int d = G * 8;
+    constexpr int NR = 64 / G;   // rows read per wavefront instruction
+    const int lane = threadIdx.x & 63;
+    const int c = lane % G, rs = lane / G;
+    const int h = blockIdx.y;
+    const int64_t i = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (i >= a.Sp) return;
+    const int64_t orow = ((int64_t)h * a.Sp + i) * d + c * 8;
+    if (i >= a.S) {
+        if (rs == 0) {
+            float z[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+            store8f(a.qs, orow, z);
+            store8f(a.ks, orow, z);
+            store8f(a.vs, orow, z);
+        }
+        return;
+    }
+    const int64_t st = a.start[h * a.S + i];
+    const int l = a.level[h * a.S + i];
+    const int H = a.H;
+    float acc[3][8];
+#pragma unroll
+    for (int t = 0; t < 3; ++t)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[t][e] = 0.f;
+    int64_t R;
+    if (l >= 1 && l == a.L - 1) {
+        R = 1;
+        if (rs == 0) {
+            const int64_t el = ((st / a.pw[l]) * H + h) * d + c * 8;
+#pragma unroll
+            for (int t = 0; t < 3; ++t) load8f(a.pool_top + t * a.ntop * H * d, el, acc[t]);
+        }
+    } else if (l >= 1 && l >= a.m) {
+        R = a.pw[l] / a.pw[a.m];
+        const int64_t r0 = st / a.pw[a.m];
+        for (int64_t r = rs; r < R; r += NR) {
+            const int64_t el = ((r0 + r) * H + h) * d + c * 8;
+#pragma unroll
+            for (int t = 0; t < 3; ++t) {
+                float x[8];
+                load8f(a.pool_m + t * a.n_m * H * d, el, x);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) acc[t][e] += x[e];
+            }
+        }
+    } else {
+        R = a.pw[l];
+        const void* src[3] = {a.q, a.k, a.v};
+        constexpr int U = 4;
+        for (int64_t r0 = rs; r0 < R; r0 += NR * U) {
+            float x[U][3][8];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int64_t r = r0 + (int64_t)u * NR;
+                if (r < R) {
+                    const int64_t el = ((st + r) * H + h) * d + c * 8;
+#pragma unroll
+                    for (int t = 0; t < 3; ++t) load8<DT>(src[t], el, x[u][t]);
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                if (r0 + (int64_t)u * NR < R) {
+#pragma unroll
+                    for (int t = 0; t < 3; ++t)
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) acc[t][e] += x[u][t][e];
+                }
+            }
+        }
+    }
+    if (R > 1) {
+#pragma unroll
+        for (int off = G; off < 64; off <<= 1)
+#pragma unroll
+            for (int t = 0; t < 3; ++t)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) acc[t][e] += shfl_xor_f(acc[t][e], off);
+    }
+    if (rs == 0) {
+        float* dst[3] = {a.qs, a.ks, a.vs};
+#pragma unroll
+        for (int t = 0; t < 3; ++t) {
+            float o[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) o[e] = (R > 1) ? acc[t][e] / (float)R : acc[t][e];
+            store8f(dst[t], orow, o);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Token-range mapping shared by the scatter-type kernels: a workgroup covers
+// kTileTok consecutive tokens of every head; thread (ts, h, c) walks the
+// contiguous sub-range ts of length kTileTok/mt with a cursor over the
+// position-sorted sub-sequence of head h.
+constexpr int kTileTok = 64;
+
+struct TokMap {
+    int c, h, ts;
+    int64_t tb, te;
+};
+
+template <int G>
+__device__ __forceinline__ TokMap tok_map(int HG, int mt, int64_t N) {
+    TokMap m;
+    const int tid = threadIdx.x;
+    m.c = tid % G;
+    const int row = tid / G;
+    m.h = blockIdx.y * HG + row % HG;
+    m.ts = row / HG;
+    const int span = kTileTok / mt;
+    m.tb = (int64_t)blockIdx.x * kTileTok + (int64_t)m.ts * span;
+    m.te = m.tb + span;
+    if (m.te > N) m.te = N;
+    return m;
+}
+
+// Last slot whose start is <= t (starts are strictly increasing, start[0] = 0).
+__device__ __forceinline__ int64_t find_slot(const int32_t* st, int64_t S, int64_t t) {
+    int64_t lo = 0, hi = S - 1;
+    while (lo < hi) {
+        int64_t mid = (lo + hi + 1) >> 1;
+        if (st[mid] <= t) lo = mid; else hi = mid - 1;
+    }
+    return lo;
+}
+
+// Scatter forward (stage (iv)): o[t][h] = O~[h][slot_h(t)], rounded once from
+// the fp32 sub-sequence output to the I/O dtype.
+struct ScatterArgs {
+    const int32_t* start;
+    const float* src;     // fp32 [H][Sp][d]
+    void* dst;            // dtype [N][H][d]
+    int64_t N, S, Sp;
+    int H, HG, mt;
+};
+
+template <int DT, int G>
+__global__ void __launch_bounds__(256) k_scatter_fwd(ScatterArgs a) {
+    constexpr int d = G * 8;
+    const TokMap tm = tok_map<G>(a.HG, a.mt, a.N);
+    if (tm.tb >= tm.te) return;
+    const int32_t* st = a.start + (int64_t)tm.h * a.S;
+    int64_t slot = find_slot(st, a.S, tm.tb);
+    int64_t nxt = slot + 1 < a.S ? st[slot + 1] : a.N;
+    const int64_t sbase = (int64_t)tm.h * a.Sp * d + tm.c * 8;
+    const int64_t H = a.H;
+    float x[8];
+    load8f(a.src, sbase + slot * d, x);
+    for (int64_t t = tm.tb; t < tm.te; ++t) {
+        if (t >= nxt) {
+            ++slot;
+            nxt = slot + 1 < a.S ? st[slot + 1] : a.N;
+            load8f(a.src, sbase + slot * d, x);
+        }
+        store8<DT>(a.dst, (t * H + tm.h) * d + tm.c * 8, x);
+    }
+}
+
+// Adjoint of the scatter: dO~[h][i] = sum over the tokens of entry i of dO.
+// Each thread sums its contiguous token range per entry in fp32 (token order);
+// an entry that lies wholly inside the range is stored, one that crosses the
+// range's ends is added atomically: fp32 atomics (mode 0) or exact 64-bit
+// fixed-point integer atomics, scale 2^32 (mode 1, order-independent).
+struct ScatterBwdArgs {
+    const int32_t* start;
+    const void* dout;     // dtype [N][H][d]
+    void* acc;            // fp32 or int64 [H][Sp][d]
+    int64_t N, S, Sp;
+    int H, HG, mt;
+};
+
+__device__ __forceinline__ long long to_fixed(float x) {
+    return (long long)__builtin_rint((double)x * 4294967296.0);
+}
+
+template <int DT, int G, int MODE>
+__device__ __forceinline__ void flush_entry(const ScatterBwdArgs& a, int h, int c, int64_t slot, bool whole,
+                                            const float (&s)[8]) {
+    constexpr int d = G * 8;
+    const int64_t el = ((int64_t)h * a.Sp + slot) * d + c * 8;
+    if constexpr (MODE == 0) {
+        float* p = reinterpret_cast<float*>(a.acc) + el;
+        if (whole) {
+            store8f(reinterpret_cast<float*>(a.acc), el, s);
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) unsafeAtomicAdd(p + e, s[e]);
+        }
+    } else {
+        unsigned long long* p = reinterpret_cast<unsigned long long*>(a.acc) + el;
+        if (whole) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) p[e] = (unsigned long long)to_fixed(s[e]);
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) atomicAdd(p + e, (unsigned long long)to_fixed(s[e]));
+        }
+    }
+}
+
+template <int DT, int G, int MODE>
+__global__ void __launch_bounds__(256) k_scatter_bwd(ScatterBwdArgs a) {
+    constexpr int d = G * 8;
+    const TokMap tm = tok_map<G>(a.HG, a.mt, a.N);
+    if (tm.tb >= tm.te) return;
+    const int32_t* st = a.start + (int64_t)tm.h * a.S;
+    int64_t slot = find_slot(st, a.S, tm.tb);
+    int64_t beg = st[slot];
+    int64_t nxt = slot + 1 < a.S ? st[slot + 1] : a.N;
+    float s[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) s[e] = 0.f;
+    const int64_t H = a.H;
+    constexpr int U = 8;
+    for (int64_t t0 = tm.tb; t0 < tm.te; t0 += U) {
+        float x[U][8];
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            if (t0 + u < tm.te) load8<DT>(a.dout, ((t0 + u) * H + tm.h) * d + tm.c * 8, x[u]);
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t t = t0 + u;
+            if (t < tm.te) {
+                if (t >= nxt) {
+                    flush_entry<DT, G, MODE>(a, tm.h, tm.c, slot, beg >= tm.tb && nxt <= tm.te, s);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) s[e] = 0.f;
+                    ++slot;
+                    beg = nxt;
+                    nxt = slot + 1 < a.S ? st[slot + 1] : a.N;
+                }
+#pragma unroll
+                for (int e = 0; e < 8; ++e) s[e] += x[u][e];
+            }
+        }
+    }
+    flush_entry<DT, G, MODE>(a, tm.h, tm.c, slot, beg >= tm.tb && nxt <= tm.te, s);
+}
+
+// Adjoint of gather + mean-pool: dX[t][h] = dX~[h][slot_h(t)] / p^level.
+struct PoolBwdArgs {
+    const int32_t* start;
+    const uint8_t* level;
+    const float *dqs, *dks, *dvs;   // fp32 [H][Sp][d]
+    void *dq, *dk, *dv;             // dtype [N][H][d]
+    int64_t N, S, Sp;
+    int H, HG, mt, p;
+};
+
+template <int DT, int G>
+__global__ void __launch_bounds__(256) k_pool_bwd(PoolBwdArgs a) {
+    constexpr int d = G * 8;
+    const TokMap tm = tok_map<G>(a.HG, a.mt, a.N);
+    if (tm.tb >= tm.te) return;
+    const int32_t* st = a.start + (int64_t)tm.h * a.S;
+    int64_t slot = find_slot(st, a.S, tm.tb);
+    int64_t nxt = slot + 1 < a.S ? st[slot + 1] : a.N;
+    float g[3][8];
+    const float* srcs[3] = {a.dqs, a.dks, a.dvs};
+    void* dsts[3] = {a.dq, a.dk, a.dv};
+    auto load_slot = [&](int64_t sl) {
+        const int lv = a.level[(int64_t)tm.h * a.S + sl];
+        float den = 1.0f;
+        for (int z = 0; z < lv; ++z) den *= (float)a.p;
+        const int64_t el = ((int64_t)tm.h * a.Sp + sl) * d + tm.c * 8;
+#pragma unroll
+        for (int t = 0; t < 3; ++t) {
+            load8f(srcs[t], el, g[t]);
+            if (lv > 0) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) g[t][e] = g[t][e] / den;
+            }
+        }
+    };
+    load_slot(slot);
+    const int64_t H = a.H;
+    for (int64_t t = tm.tb; t < tm.te; ++t) {
+        if (t >= nxt) {
+            ++slot;
+            nxt = slot + 1 < a.S ? st[slot + 1] : a.N;
+            load_slot(slot);
+        }
+        const int64_t el = (t * H + tm.h) * d + tm.c * 8;
+#pragma unroll
+        for (int z = 0; z < 3; ++z) store8<DT>(dsts[z], el, g[z]);
+    }
+}
+
+__global__ void k_fill_zero(u32x4* p, int64_t n16) {
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += (int64_t)gridDim.x * blockDim.x)
+        p[i] = u32x4{0, 0, 0, 0};
+}
+
+// ------------------------------------------------------------------ launchers
+
+// Heads per workgroup: the largest divisor of H with HG * G <= 256 threads.
+static int head_group(int H, int G) {
+    int hg = 1;
+    for (int c = 1; c <= H; ++c)
+        if (H % c == 0 && c * G <= 256) hg = c;
+    return hg;
+}
+
+static int pick_mt(int rows_threads, int limit) {
+    // token lanes per workgroup: largest power of two keeping <= 256 threads
+    int mt = 1;
+    while (rows_threads * mt * 2 <= 256 && mt * 2 <= limit) mt *= 2;
+    return mt;
+}
+
+hipError_t launch_pool_score(const Plan& P, const void* q, const void* k, const void* v, char* ws,
+                             hipStream_t s) {
+    PoolScoreArgs a{};
+    a.q = q; a.k = k; a.v = v;
+    float* sc = reinterpret_cast<float*>(ws + P.off_scores);
+    for (int l = 0; l < P.L; ++l) {
+        a.lev[l] = sc + P.lev_off[l];
+        a.n[l] = P.n[l];
+        a.pw[l] = P.pw[l];
+    }
+    a.pool_m = reinterpret_cast<float*>(ws + P.off_pool_m);
+    a.N = P.N; a.H = P.H; a.p = P.p; a.m = P.m; a.tok = (int)P.tok;
+    const int G = P.d / 8;
+    a.HG = head_group(P.H, G);
+    // token lanes must divide tok (a power of p): use powers of p
+    int mt = 1;
+    while (a.HG * G * mt * P.p <= 256 && mt * P.p <= P.tok) mt *= P.p;
+    a.mt = mt;
+    const int threads = a.HG * G * mt;
+    size_t lds = sizeof(float) * (size_t)P.tok * a.HG;
+    if (P.m >= 1 && mt > 1) lds += sizeof(float) * (size_t)mt * a.HG * P.d;
+    dim3 grid((unsigned)(P.N / P.tok), (unsigned)(P.H / a.HG));
+    if (P.dtype == BF16) {
+        if (G == 16) hipLaunchKernelGGL((k_pool_score<0, 16>), grid, dim3(threads), lds, s, a);
+        else hipLaunchKernelGGL((k_pool_score<0, 8>), grid, dim3(threads), lds, s, a);
+    } else {
+        if (G == 16) hipLaunchKernelGGL((k_pool_score<1, 16>), grid, dim3(threads), lds, s, a);
+        else hipLaunchKernelGGL((k_pool_score<1, 8>), grid, dim3(threads), lds, s, a);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_pool_up(const Plan& P, char* ws, hipStream_t s) {
+    PoolUpArgs a{};
+    float* sc = reinterpret_cast<float*>(ws + P.off_scores);
+    for (int l = 0; l < P.L; ++l) {
+        a.lev[l] = sc + P.lev_off[l];
+        a.n[l] = P.n[l];
+        a.pw[l] = P.pw[l];
+    }
+    a.pool_m = reinterpret_cast<const float*>(ws + P.off_pool_m);
+    a.pool_top = reinterpret_cast<float*>(ws + P.off_pool_top);
+    a.H = P.H; a.d = P.d; a.p = P.p; a.m = P.m; a.L = P.L;
+    hipLaunchKernelGGL(k_pool_up, dim3((unsigned)P.ntop), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_gather(const Plan& P, const void* q, const void* k, const void* v, char* ws,
+                         hipStream_t s) {
+    GatherArgs a{};
+    a.q = q; a.k = k; a.v = v;
+    a.pool_m = reinterpret_cast<const float*>(ws + P.off_pool_m);
+    a.pool_top = reinterpret_cast<const float*>(ws + P.off_pool_top);
+    a.start = reinterpret_cast<const int32_t*>(ws + P.off_start);
+    a.level = reinterpret_cast<const uint8_t*>(ws + P.off_level);
+    a.qs = reinterpret_cast<float*>(ws + P.off_qs);
+    a.ks = reinterpret_cast<float*>(ws + P.off_ks);
+    a.vs = reinterpret_cast<float*>(ws + P.off_vs);
+    a.S = P.S; a.Sp = P.Sp; a.n_m = P.n[P.m]; a.ntop = P.ntop;
+    for (int l = 0; l < P.L; ++l) a.pw[l] = P.pw[l];
+    a.H = P.H; a.m = P.m; a.L = P.L;
+    dim3 grid((unsigned)((P.Sp + 3) / 4), (unsigned)P.H);
+    const int G = P.d / 8;
+    if (P.dtype == BF16) {
+        if (G == 16) hipLaunchKernelGGL((k_gather<0, 16>), grid, dim3(256), 0, s, a);
+        else hipLaunchKernelGGL((k_gather<0, 8>), grid, dim3(256), 0, s, a);
+    } else {
+        if (G == 16) hipLaunchKernelGGL((k_gather<1, 16>), grid, dim3(256), 0, s, a);
+        else hipLaunchKernelGGL((k_gather<1, 8>), grid, dim3(256), 0, s, a);
+    }
+    return hipGetLastError();
+}
+
+static int scatter_threads(const Plan& P, int* hg_out, int* mt_out) {
+    const int G = P.d / 8;
+    const int hg = head_group(P.H, G);
+    const int mt = pick_mt(hg * G, kTileTok);
+    *hg_out = hg;
+    *mt_out = mt;
+    return hg * G * mt;
+}
+
+hipError_t launch_scatter_fwd(const Plan& P, char* ws, void* o, hipStream_t s) {
+    ScatterArgs a{};
+    a.start = reinterpret_cast<const int32_t*>(ws + P.off_start);
+    a.src = reinterpret_cast<const float*>(ws + P.off_os);
+    a.dst = o;
+    a.N = P.N; a.S = P.S; a.Sp = P.Sp; a.H = P.H;
+    const int threads = scatter_threads(P, &a.HG, &a.mt);
+    dim3 grid((unsigned)((P.N + kTileTok - 1) / kTileTok), (unsigned)(P.H / a.HG));
+    const int G = P.d / 8;
+    if (P.dtype == BF16) {
+        if (G == 16) hipLaunchKernelGGL((k_scatter_fwd<0, 16>), grid, dim3(threads), 0, s, a);
+        else hipLaunchKernelGGL((k_scatter_fwd<0, 8>), grid, dim3(threads), 0, s, a);
+    } else {
+        if (G == 16) hipLaunchKernelGGL((k_scatter_fwd<1, 16>), grid, dim3(threads), 0, s, a);
+        else hipLaunchKernelGGL((k_scatter_fwd<1, 8>), grid, dim3(threads), 0, s, a);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s) {
+    const int64_t n16 = (int64_t)(bytes / 16);
+    int64_t blocks = (n16 + 255) / 256;
+    if (blocks > 4096) blocks = 4096;
+    if (blocks < 1) blocks = 1;
+    hipLaunchKernelGGL(k_fill_zero, dim3((unsigned)blocks), dim3(256), 0, s, reinterpret_cast<u32x4*>(p), n16);
+    return hipGetLastError();
+}
+
+hipError_t launch_scatter_bwd(const Plan& P, const void* dout, int mode, char* ws, hipStream_t s) {
+    ScatterBwdArgs a{};
+    a.start = reinterpret_cast<const int32_t*>(ws + P.off_start);
+    a.dout = dout;
+    a.acc = ws + P.off_acc;
+    a.N = P.N; a.S = P.S; a.Sp = P.Sp; a.H = P.H;
+    const int threads = scatter_threads(P, &a.HG, &a.mt);
+    dim3 grid((unsigned)((P.N + kTileTok - 1) / kTileTok), (unsigned)(P.H / a.HG));
+    const int G = P.d / 8;
+#define LH_SB(DT, GG, MD) hipLaunchKernelGGL((k_scatter_bwd<DT, GG, MD>), grid, dim3(threads), 0, s, a)
+    if (P.dtype == BF16) {
+        if (G == 16) { if (mode == 0) LH_SB(0, 16, 0); else LH_SB(0, 16, 1); }
+        else { if (mode == 0) LH_SB(0, 8, 0); else LH_SB(0, 8, 1); }
+    } else {
+        if (G == 16) { if (mode == 0) LH_SB(1, 16, 0); else LH_SB(1, 16, 1); }
+        else { if (mode == 0) LH_SB(1, 8, 0); else LH_SB(1, 8, 1); }
+    }
+#undef LH_SB
+    return hipGetLastError();
+}
+
+hipError_t launch_pool_bwd(const Plan& P, char* ws, void* dq, void* dk, void* dv, hipStream_t s) {
+    PoolBwdArgs a{};
+    a.start = reinterpret_cast<const int32_t*>(ws + P.off_start);
+    a.level = reinterpret_cast<const uint8_t*>(ws + P.off_level);
+    a.dqs = reinterpret_cast<const float*>(ws + P.off_dq);
+    a.dks = reinterpret_cast<const float*>(ws + P.off_dk);
+    a.dvs = reinterpret_cast<const float*>(ws + P.off_dv);
+    a.dq = dq; a.dk = dk; a.dv = dv;
+    a.N = P.N; a.S = P.S; a.Sp = P.Sp; a.H = P.H; a.p = P.p;
+    const int threads = scatter_threads(P, &a.HG, &a.mt);
+    dim3 grid((unsigned)((P.N + kTileTok - 1) / kTileTok), (unsigned)(P.H / a.HG));
+    const int G = P.d / 8;
+    if (P.dtype == BF16) {
+        if (G == 16) hipLaunchKernelGGL((k_pool_bwd<0, 16>), grid, dim3(threads), 0, s, a);
+        else hipLaunchKernelGGL((k_pool_bwd<0, 8>), grid, dim3(threads), 0, s, a);
+    } else {
+        if (G == 16) hipLaunchKernelGGL((k_pool_bwd<1, 16>), grid, dim3(threads), 0, s, a);
+        else hipLaunchKernelGGL((k_pool_bwd<1, 8>), grid, dim3(threads), 0, s, a);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace lh

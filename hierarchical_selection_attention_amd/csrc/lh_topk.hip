@@ -1,0 +1,265 @@
+// Hierarchical selector (stage (ii) of Sec. 3; Fig. 2 step 3 "bitonic argsort
+// + tree-prune") on gfx950.  One workgroup of 1024 threads per head.
+//
+// From the top level down, the candidates of a level are scored by 64-bit
+// keys (fp32 score bits << 32 | ~index): scores are >= +0 so the bit pattern
+// orders them, and the complemented index makes equal scores rank the lower
+// index first; keys are unique, so the selected set does not depend on how the
+// network orders ties.  The K largest keys are found with a chunked bitonic
+// network in LDS: each chunk of up to 2048 keys is sorted descending, merged
+// into the running top-K list (elementwise max against the reversed chunk
+// head, then a bitonic merge).  Selected entries are replaced by their p
+// children, the others are kept; finally every kept entry gets its slot in
+// the position-ordered sub-sequence from entry counts (bottom-up) and prefix
+// offsets (top-down).
+#include "lh_device.h"
+#include "lh_internal.h"
+
+namespace lh {
+
+constexpr int kTopkThreads = 1024;
+constexpr int kChunk = 2048;
+
+struct TopkArgs {
+    const float* lev[kMaxLevels];   // scores of level l: [H][n_l]
+    int32_t* start;                 // [H][S]
+    uint8_t* level;                 // [H][S]
+    int32_t* bfirst;                // [H][ntop + 1]
+    int32_t* scratch;               // [H][L][5][cap]
+    int64_t n[kMaxLevels];
+    int64_t pw[kMaxLevels];
+    int64_t ncand[kMaxLevels];      // candidates at level l: ntop at the top, p*min(K, .) below
+    int64_t S, cap, ntop;
+    int L, p, K;
+};
+
+__device__ __forceinline__ uint64_t make_key(float s, int32_t idx) {
+    return ((uint64_t)__float_as_uint(s) << 32) | (uint64_t)(uint32_t)(~idx);
+}
+
+// Sort n (power of two) keys in LDS descending.
+__device__ void bitonic_sort_desc(uint64_t* b, int n) {
+    for (int k = 2; k <= n; k <<= 1) {
+        for (int j = k >> 1; j > 0; j >>= 1) {
+            for (int i = threadIdx.x; i < n / 2; i += blockDim.x) {
+                const int lo = 2 * i - (i & (j - 1));
+                const int hi = lo + j;
+                const bool desc = (lo & k) == 0;
+                const uint64_t x = b[lo], y = b[hi];
+                if (desc ? (x < y) : (x > y)) {
+                    b[lo] = y;
+                    b[hi] = x;
+                }
+            }
+            __syncthreads();
+        }
+    }
+}
+
+// Sort a bitonic sequence of n (power of two) keys descending.
+__device__ void bitonic_merge_desc(uint64_t* b, int n) {
+    for (int j = n >> 1; j > 0; j >>= 1) {
+        for (int i = threadIdx.x; i < n / 2; i += blockDim.x) {
+            const int lo = 2 * i - (i & (j - 1));
+            const int hi = lo + j;
+            const uint64_t x = b[lo], y = b[hi];
+            if (x < y) {
+                b[lo] = y;
+                b[hi] = x;
+            }
+        }
+        __syncthreads();
+    }
+}
+
+// Exclusive prefix sum of in[0..n) into out[0..n); returns the total.
+__device__ int64_t block_scan_excl(const int32_t* in, int32_t* out, int64_t n, int32_t* wsum) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nw = blockDim.x >> 6;
+    int64_t carry = 0;
+    for (int64_t base = 0; base < n; base += blockDim.x) {
+        const int64_t i = base + tid;
+        const int32_t v = i < n ? in[i] : 0;
+        int32_t x = v;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            int32_t y = __shfl_up(x, off, 64);
+            if (lane >= off) x += y;
+        }
+        if (lane == 63) wsum[wave] = x;
+        __syncthreads();
+        if (tid == 0) {
+            int32_t acc = 0;
+            for (int w = 0; w < nw; ++w) {
+                int32_t t = wsum[w];
+                wsum[w] = acc;
+                acc += t;
+            }
+            wsum[nw] = acc;
+        }
+        __syncthreads();
+        if (i < n) out[i] = (int32_t)(carry + wsum[wave] + x - v);
+        carry += wsum[nw];
+        __syncthreads();
+    }
+    return carry;
+}
+
+__global__ void __launch_bounds__(kTopkThreads) k_topk(TopkArgs a) {
+    __shared__ uint64_t chunk[kChunk];
+    __shared__ uint64_t top[kMaxK];
+    __shared__ int32_t wsum[kTopkThreads / 64 + 1];
+    const int h = blockIdx.x;
+    const int tid = threadIdx.x;
+    const int L = a.L, p = a.p, K = a.K;
+    const int64_t cap = a.cap;
+    int32_t* base = a.scratch + (int64_t)h * L * 5 * cap;
+    auto arr = [&](int l, int which) { return base + ((int64_t)l * 5 + which) * cap; };
+    // which: 0 idx, 1 flag, 2 rank, 3 cnt, 4 first
+    const int64_t* ncand = a.ncand;
+
+    for (int64_t i = tid; i < a.ntop; i += blockDim.x) arr(L - 1, 0)[i] = (int32_t)i;
+    __syncthreads();
+
+    for (int l = L - 1; l >= 1; --l) {
+        int32_t* idx = arr(l, 0);
+        int32_t* flag = arr(l, 1);
+        const float* sc = a.lev[l] + (int64_t)h * a.n[l];
+        const int64_t nc = ncand[l];
+        const int64_t nsel = nc < K ? nc : K;   // equals ncand[l-1] / p
+        if (nc <= K || K == 0) {
+            const int32_t all = nc <= K ? 1 : 0;
+            for (int64_t i = tid; i < nc; i += blockDim.x) flag[i] = all;
+        } else {
+            int KP = 1;
+            while (KP < K) KP <<= 1;
+            for (int i = tid; i < KP; i += blockDim.x) top[i] = 0;
+            __syncthreads();
+            for (int64_t c0 = 0; c0 < nc; c0 += kChunk) {
+                const int cnt = (int)((nc - c0) < kChunk ? (nc - c0) : kChunk);
+                int NP = 1;
+                while (NP < cnt) NP <<= 1;
+                if (NP < KP) NP = KP;
+                for (int i = tid; i < NP; i += blockDim.x) {
+                    uint64_t key = 0;
+                    if (i < cnt) {
+                        const int32_t j = idx[c0 + i];
+                        key = make_key(sc[j], j);
+                    }
+                    chunk[i] = key;
+                }
+                __syncthreads();
+                bitonic_sort_desc(chunk, NP);
+                for (int i = tid; i < KP; i += blockDim.x) {
+                    const uint64_t x = top[i], y = chunk[KP - 1 - i];
+                    top[i] = x > y ? x : y;
+                }
+                __syncthreads();
+                bitonic_merge_desc(top, KP);
+            }
+            const uint64_t tau = top[K - 1];
+            for (int64_t i = tid; i < nc; i += blockDim.x) {
+                const int32_t j = idx[i];
+                flag[i] = make_key(sc[j], j) >= tau ? 1 : 0;
+            }
+        }
+        __syncthreads();
+        block_scan_excl(flag, arr(l, 2), nc, wsum);
+        // children of the selected candidates, in index order
+        int32_t* rank = arr(l, 2);
+        int32_t* nidx = arr(l - 1, 0);
+        for (int64_t i = tid; i < nc; i += blockDim.x) {
+            if (flag[i]) {
+                const int64_t r = rank[i];
+                const int32_t j = idx[i];
+                for (int c = 0; c < p; ++c) nidx[r * p + c] = j * p + c;
+            }
+        }
+        (void)nsel;
+        __syncthreads();
+    }
+
+    // entry counts, bottom-up
+    for (int64_t i = tid; i < ncand[0]; i += blockDim.x) arr(0, 3)[i] = 1;
+    __syncthreads();
+    for (int l = 1; l < L; ++l) {
+        const int32_t* flag = arr(l, 1);
+        const int32_t* rank = arr(l, 2);
+        const int32_t* ccnt = arr(l - 1, 3);
+        int32_t* cnt = arr(l, 3);
+        for (int64_t i = tid; i < ncand[l]; i += blockDim.x) {
+            int32_t c = 1;
+            if (flag[i]) {
+                c = 0;
+                const int64_t r = rank[i];
+                for (int z = 0; z < p; ++z) c += ccnt[r * p + z];
+            }
+            cnt[i] = c;
+        }
+        __syncthreads();
+    }
+    // slots, top-down
+    block_scan_excl(arr(L - 1, 3), arr(L - 1, 4), ncand[L - 1], wsum);
+    __syncthreads();
+    for (int l = L - 1; l >= 1; --l) {
+        const int32_t* flag = arr(l, 1);
+        const int32_t* rank = arr(l, 2);
+        const int32_t* first = arr(l, 4);
+        const int32_t* ccnt = arr(l - 1, 3);
+        int32_t* cfirst = arr(l - 1, 4);
+        for (int64_t i = tid; i < ncand[l]; i += blockDim.x) {
+            if (flag[i]) {
+                const int64_t r = rank[i];
+                int32_t f = first[i];
+                for (int z = 0; z < p; ++z) {
+                    cfirst[r * p + z] = f;
+                    f += ccnt[r * p + z];
+                }
+            }
+        }
+        __syncthreads();
+    }
+    // emit kept entries
+    int32_t* st = a.start + (int64_t)h * a.S;
+    uint8_t* lv = a.level + (int64_t)h * a.S;
+    for (int l = 0; l < L; ++l) {
+        const int32_t* idx = arr(l, 0);
+        const int32_t* flag = arr(l, 1);
+        const int32_t* first = arr(l, 4);
+        for (int64_t i = tid; i < ncand[l]; i += blockDim.x) {
+            if (l == 0 || !flag[i]) {
+                const int32_t s = first[i];
+                st[s] = (int32_t)(idx[i] * a.pw[l]);
+                lv[s] = (uint8_t)l;
+            }
+        }
+    }
+    int32_t* bf = a.bfirst + (int64_t)h * (a.ntop + 1);
+    const int32_t* tfirst = arr(L - 1, 4);
+    for (int64_t i = tid; i < a.ntop; i += blockDim.x) bf[i] = tfirst[i];
+    if (tid == 0) bf[a.ntop] = (int32_t)a.S;
+}
+
+hipError_t launch_topk(const Plan& P, char* ws, hipStream_t s) {
+    TopkArgs a{};
+    const float* sc = reinterpret_cast<const float*>(ws + P.off_scores);
+    for (int l = 0; l < P.L; ++l) {
+        a.lev[l] = sc + P.lev_off[l];
+        a.n[l] = P.n[l];
+        a.pw[l] = P.pw[l];
+    }
+    a.start = reinterpret_cast<int32_t*>(ws + P.off_start);
+    a.level = reinterpret_cast<uint8_t*>(ws + P.off_level);
+    a.bfirst = reinterpret_cast<int32_t*>(ws + P.off_bfirst);
+    a.scratch = reinterpret_cast<int32_t*>(ws + P.off_tk);
+    a.S = P.S; a.cap = P.tk_cap; a.ntop = P.ntop;
+    a.L = P.L; a.p = P.p; a.K = P.K;
+    int64_t nc = P.ntop;
+    for (int l = P.L - 1; l >= 0; --l) {
+        a.ncand[l] = nc;
+        nc = (nc < P.K ? nc : P.K) * P.p;
+    }
+    hipLaunchKernelGGL(k_topk, dim3((unsigned)P.H), dim3(kTopkThreads), 0, s, a);
+    return hipGetLastError();
+}
+
+}  // namespace lh

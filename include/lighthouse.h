@@ -1,0 +1,145 @@
+/*
+ * lighthouse.h — C ABI of the MI355X (gfx950) Lighthouse attention layer.
+ *
+ * The layer follows "Long Context Pre-Training with Lighthouse Attention"
+ * (Peng, Ghosh, Quesnelle, arXiv 2605.06554; read from the P1 mirror of the
+ * arXiv HTML, Sec. 3, Sec. 3.1 Eq. (1), Fig. 1 and Fig. 2, and the P3/P4
+ * summaries).  It replaces softmax attention by four stages around an
+ * unmodified causal attention kernel:
+ *   (i)   average-pool q, k and v symmetrically into an L-level pyramid with
+ *         factor p (level l averages p^l tokens; level 0 is the input);
+ *   (ii)  score every pyramid entry without parameters (squared l2 norm of
+ *         q and k, max-pooled up the levels) and select, from the top level
+ *         down, the K best entries per level and head; a selected entry is
+ *         replaced by its p children, so the kept entries partition [0, N);
+ *   (iii) order the kept entries by first token into a hole-free causal
+ *         sub-sequence of length S (see lh_subseq_len), gather their pooled
+ *         q, k, v and run ordinary causal softmax attention (Eq. (1), scale
+ *         1/sqrt(d)) on it;
+ *   (iv)  scatter every sub-sequence output back to the p^l tokens of its
+ *         entry.
+ * Gradients flow through (iv), (iii), the gather and the pooling; the
+ * selection carries none (Fig. 1, gradient path).
+ *
+ * Conventions for every entry point below:
+ *   - q, k, v, o, dout, dq, dk, dv are device pointers to contiguous
+ *     [N][H][d] tensors (token-major, one batch element), 16-byte aligned,
+ *     in the element type given by `dtype` (lh_dtype).
+ *   - `stream` is a hipStream_t (NULL = the legacy default stream).  Every
+ *     call only enqueues work on it and returns; nothing synchronises.
+ *   - The library never allocates device memory on these paths: the caller
+ *     provides a workspace of at least lh_workspace_bytes(...) bytes
+ *     (256-byte aligned).  lh_backward reads what lh_forward left in the
+ *     workspace, so the workspace must stay untouched between the two and
+ *     both calls must use the same parameters and stream order.
+ *   - Arguments are validated on the host before any launch; on error the
+ *     call returns a negative lh_status and enqueues nothing.  Launch
+ *     failures return LH_ERR_HIP.  Faults inside kernels surface at the
+ *     caller's next synchronisation.
+ *   - Supported shapes: d in {64, 128}; 1 <= H, H*d <= 8192; p >= 2; L >= 1;
+ *     p^(L-1) divides N; N < 2^31; K >= 0, and K <= 2048 unless K covers
+ *     every candidate at every level.
+ */
+#ifndef LIGHTHOUSE_H
+#define LIGHTHOUSE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    LH_OK = 0,
+    LH_ERR_ARG = -1,        /* null pointer or parameter out of range            */
+    LH_ERR_SHAPE = -2,      /* shape not supported (d, H, N divisibility, sizes)  */
+    LH_ERR_DTYPE = -3,      /* unknown dtype or scatter mode                      */
+    LH_ERR_WORKSPACE = -4,  /* workspace missing, misaligned or too small         */
+    LH_ERR_HIP = -5         /* a HIP launch or runtime call failed                */
+} lh_status;
+
+typedef enum { LH_BF16 = 0, LH_FP32 = 1 } lh_dtype;
+
+/* How the adjoint of the scatter sums dO over the tokens of an entry when a
+ * block of tokens is split over several workgroups (Sec. 1 contributions and
+ * the P4 summary: fp-atomic by default, a deterministic int-atomic variant). */
+typedef enum {
+    LH_SCATTER_FP_ATOMIC = 0,   /* fp32 atomic adds: fastest, not bit-reproducible   */
+    LH_SCATTER_INT_ATOMIC = 1   /* 64-bit fixed-point atomic adds: bit-reproducible  */
+} lh_scatter_mode;
+
+/* Length S of the gathered sub-sequence (Sec. 1: S = O(LpK + N/p^(L-1))):
+ * N/p^(L-1) top entries, plus (p-1) for every selection made.  Host only.
+ * Returns S, or a negative lh_status for invalid arguments. */
+int64_t lh_subseq_len(int N, int p, int L, int K);
+
+/* Bytes of workspace lh_forward/lh_backward need; 0 for invalid arguments. */
+size_t lh_workspace_bytes(int N, int H, int d, int p, int L, int K, int dtype);
+
+/* Forward pass, stages (i)-(iv).  Writes o [N][H][d] and keeps the selection,
+ * the gathered sub-sequence, its output and log-sum-exp in the workspace. */
+int lh_forward(const void* q, const void* k, const void* v, void* o,
+               int N, int H, int d, int p, int L, int K, int dtype,
+               void* ws, size_t ws_bytes, void* stream);
+
+/* Backward pass through the scatter, the attention, the gather and the pool
+ * (Fig. 1 gradient path).  q, k, v are not needed: everything is read from
+ * the workspace of the matching lh_forward.  Writes dq, dk, dv [N][H][d]. */
+int lh_backward(const void* dout, void* dq, void* dk, void* dv,
+                int N, int H, int d, int p, int L, int K, int dtype, int scatter_mode,
+                void* ws, size_t ws_bytes, void* stream);
+
+/* Locations of intermediate results inside a workspace, for inspection.
+ * Host only; pure address arithmetic on `ws`. */
+typedef enum {
+    LH_VIEW_SCORES = 0,     /* fp32, levels 0..L-1 concatenated, each [H][N/p^l]   */
+    LH_VIEW_SEL_START = 1,  /* int32 [H][S]: first token of each kept entry        */
+    LH_VIEW_SEL_LEVEL = 2,  /* uint8 [H][S]: pyramid level of each kept entry      */
+    LH_VIEW_QSUB = 3,       /* fp32 [H][Sp][d]: gathered q (rows >= S are zero)    */
+    LH_VIEW_KSUB = 4,       /* fp32 [H][Sp][d]                                     */
+    LH_VIEW_VSUB = 5,       /* fp32 [H][Sp][d]                                     */
+    LH_VIEW_OSUB = 6,       /* fp32 [H][Sp][d]: attention output on the sub-seq.   */
+    LH_VIEW_LSE = 7,        /* fp32 [H][Sp]: natural-log log-sum-exp per row       */
+    LH_VIEW_DOSUB = 8,      /* fp32 [H][Sp][d]: dO summed over each entry's tokens */
+    LH_VIEW_DQSUB = 9,      /* fp32 [H][Sp][d]: gradient of the gathered q         */
+    LH_VIEW_DKSUB = 10,     /* fp32 [H][Sp][d]                                     */
+    LH_VIEW_DVSUB = 11,     /* fp32 [H][Sp][d]                                     */
+    LH_VIEW_BLOCK_FIRST = 12 /* int32 [H][N/p^(L-1)+1]: first slot of each top block */
+} lh_view;
+
+/* Sp = S rounded up to a multiple of 64 (row padding of the sub-sequence). */
+int lh_workspace_view(void* ws, int N, int H, int d, int p, int L, int K, int dtype,
+                      int view, void** ptr, size_t* bytes);
+
+/* Dense causal attention over all N tokens with the same attention kernels
+ * (the comparison path of the benchmark).  lse is fp32 [H][N] (natural log);
+ * N must be a multiple of 64; bf16 only.  Workspace: lh_dense_workspace_bytes.
+ * lh_dense_attn_bwd reads the operand copies and the fp32 output that the
+ * matching lh_dense_attn_fwd left in the workspace (same workspace, same
+ * stream order); q, k, v and o must be the tensors of that forward call. */
+size_t lh_dense_workspace_bytes(int N, int H, int d, int dtype);
+int lh_dense_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                      int N, int H, int d, int dtype, void* ws, size_t ws_bytes, void* stream);
+int lh_dense_attn_bwd(const void* q, const void* k, const void* v, const void* o,
+                      const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                      int N, int H, int d, int dtype, void* ws, size_t ws_bytes, void* stream);
+
+/* Per-stage timing with HIP events recorded on the caller's stream around
+ * each kernel of lh_forward/lh_backward.  enable != 0 starts recording (and
+ * clears earlier results); lh_stage_timing_read synchronises on the recorded
+ * events, adds each stage's elapsed milliseconds into ms[stage] and its
+ * launch count into count[stage] for stage < n, and returns the number of
+ * stages.  lh_stage_name gives a stage's kernel name. */
+int lh_stage_timing(int enable);
+int lh_stage_timing_read(double* ms, int* count, int n);
+const char* lh_stage_name(int stage);
+
+/* Human-readable text for an lh_status value. */
+const char* lh_status_str(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIGHTHOUSE_H */

@@ -50,7 +50,7 @@ def lib():
                                   vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32]
         L.lho_backward.restype = i32
         L.lho_backward.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, vp, vp,
-                                   vp, vp, vp, vp, vp, vp, vp, i32]
+                                   vp, vp, vp, vp, vp, vp, vp, vp, i32]
         _lib = L
         del dp, fp
     return _lib
@@ -160,7 +160,12 @@ def forward(q, k, v, p, L, K, dtype="bf16", want=("sel",), selection=None, nthre
 
 
 def backward(q, k, v, dout, p, L, K, selection, dtype="bf16", want=("sub",), nthreads=0):
-    """Oracle backward with a given selection.  want: "sub" (dOt, dQt, dKt, dVt), "full" (dq, dk, dv)."""
+    """Oracle backward with a given selection.
+
+    want: "sub" (dOt, dQt, dKt, dVt), "full" (dq, dk, dv), "cond" (absolute term sums
+    cO, cdQ, cdK, cdV [H, S, d]: the scale of the rounding error of each output, used
+    only to set comparison tolerances).
+    """
     q, k, v, dout = _in(q, dtype), _in(k, dtype), _in(v, dtype), _in(dout, dtype)
     N, H, d = q.shape
     S = subseq_len(N, p, L, K)
@@ -170,9 +175,10 @@ def backward(q, k, v, dout, p, L, K, selection, dtype="bf16", want=("sub",), nth
     full = "full" in want
     dOt, dQt, dKt, dVt = ((np.zeros((H, S, d)) if sub else None) for _ in range(4))
     dq, dk, dv = ((np.zeros((N, H, d)) if full else None) for _ in range(3))
+    cond = np.zeros((4, H, S, d)) if "cond" in want else None
     rc = lib().lho_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), N, H, d, DTYPES[dtype], p, L, K,
                             _ptr(st), _ptr(lv), _ptr(dOt), _ptr(dQt), _ptr(dKt), _ptr(dVt),
-                            _ptr(dq), _ptr(dk), _ptr(dv), nthreads)
+                            _ptr(dq), _ptr(dk), _ptr(dv), _ptr(cond), nthreads)
     if rc:
         raise RuntimeError(f"lho_backward failed ({rc})")
     res = {"S": S}
@@ -180,4 +186,6 @@ def backward(q, k, v, dout, p, L, K, selection, dtype="bf16", want=("sub",), nth
         res.update(dOt=dOt, dQt=dQt, dKt=dKt, dVt=dVt)
     if full:
         res.update(dq=dq, dk=dk, dv=dv)
+    if cond is not None:
+        res.update(cO=cond[0], cdQ=cond[1], cdK=cond[2], cdV=cond[3])
     return res

@@ -343,14 +343,24 @@ static void head_attention_fwd(int64_t S, int d, const double* Q, const double* 
 }
 
 /* Gradient of the above: P = softmax, dV = P^T dO, dP = dO V^T,
- * dS = P o (dP - rowsum(dO o O)), dQ = dS K / sqrt(d), dK = dS^T Q / sqrt(d). */
+ * dS = P o (dP - rowsum(dO o O)), dQ = dS K / sqrt(d), dK = dS^T Q / sqrt(d).
+ *
+ * cond (may be NULL) receives, for the tolerance of finite-precision
+ * comparisons only, the sums of absolute values of the terms each output is
+ * made of (4 arrays of S*d: O, dQ, dK, dV).  With A_ij = sum |dO_i||V_j|,
+ * B_i = sum |dO_i||O_i| and w_ij = P_ij (A_ij + B_i):
+ *   cO_i = sum_j P_ij |V_j|,  cdQ_i = sum_j w_ij |K_j| / sqrt(d),
+ *   cdK_j = sum_i w_ij |Q_i| / sqrt(d),  cdV_j = sum_i P_ij |dO_i|.
+ * A computation in precision u with length-n dot products has error of order
+ * n u times these sums (the standard forward error bound of a dot product). */
 static void head_attention_bwd(int64_t S, int d, const double* Q, const double* K, const double* V,
                                const double* O, const double* dO, double* dQ, double* dK, double* dV,
-                               double* logit) {
+                               double* logit, double* cond) {
     double scale = 1.0 / sqrt((double)d);
     memset(dQ, 0, sizeof(double) * (size_t)(S * d));
     memset(dK, 0, sizeof(double) * (size_t)(S * d));
     memset(dV, 0, sizeof(double) * (size_t)(S * d));
+    if (cond) memset(cond, 0, sizeof(double) * (size_t)(4 * S * d));
     for (int64_t i = 0; i < S; ++i) {
         double m = -INFINITY;
         for (int64_t j = 0; j <= i; ++j) {
@@ -361,17 +371,33 @@ static void head_attention_bwd(int64_t S, int d, const double* Q, const double* 
         }
         double sum = 0.0;
         for (int64_t j = 0; j <= i; ++j) sum += exp(logit[j] - m);
-        double D = 0.0;
-        for (int e = 0; e < d; ++e) D += dO[i * d + e] * O[i * d + e];
+        double D = 0.0, B = 0.0;
+        for (int e = 0; e < d; ++e) {
+            D += dO[i * d + e] * O[i * d + e];
+            B += fabs(dO[i * d + e] * O[i * d + e]);
+        }
         for (int64_t j = 0; j <= i; ++j) {
             double P = exp(logit[j] - m) / sum;
-            double dP = 0.0;
-            for (int e = 0; e < d; ++e) dP += dO[i * d + e] * V[j * d + e];
+            double dP = 0.0, A = 0.0;
+            for (int e = 0; e < d; ++e) {
+                dP += dO[i * d + e] * V[j * d + e];
+                A += fabs(dO[i * d + e] * V[j * d + e]);
+            }
             double dS = P * (dP - D);
             for (int e = 0; e < d; ++e) {
                 dQ[i * d + e] += dS * K[j * d + e] * scale;
                 dK[j * d + e] += dS * Q[i * d + e] * scale;
                 dV[j * d + e] += P * dO[i * d + e];
+            }
+            if (cond) {
+                double w = P * (A + B);
+                double *cO = cond, *cQ = cond + S * d, *cK = cond + 2 * S * d, *cV = cond + 3 * S * d;
+                for (int e = 0; e < d; ++e) {
+                    cO[i * d + e] += P * fabs(V[j * d + e]);
+                    cQ[i * d + e] += w * fabs(K[j * d + e]) * scale;
+                    cK[j * d + e] += w * fabs(Q[i * d + e]) * scale;
+                    cV[j * d + e] += P * fabs(dO[i * d + e]);
+                }
             }
         }
     }
@@ -521,11 +547,13 @@ int lho_forward(const void* q, const void* k, const void* v, int N, int H, int d
  * pool).  The selection (sel_start, sel_level from lho_forward) is an input:
  * indices carry no gradient.  Output pointers may be NULL.
  *   dOt, dQt, dKt, dVt [H][S][d];  dq, dk, dv [N][H][d]
+ *   cond [4][H][S][d]: absolute term sums of O~, dQ~, dK~, dV~ (see
+ *   head_attention_bwd); a tolerance aid, not part of the layer.
  */
 int lho_backward(const void* q, const void* k, const void* v, const void* dout, int N, int H, int d,
                  int dtype, int p, int L, int K, const int32_t* sel_start, const int8_t* sel_level,
                  double* dOt, double* dQt, double* dKt, double* dVt, double* dq, double* dk, double* dv,
-                 int nthreads) {
+                 double* cond, int nthreads) {
     int rc = check_shape(N, H, d, dtype, p, L, K);
     if (rc) return rc;
     if (d > 512 || !sel_start || !sel_level || !dout) return LHO_ERR_ARG;
@@ -566,7 +594,13 @@ int lho_backward(const void* q, const void* k, const void* v, const void* dout, 
                 for (int e = 0; e < d; ++e) dOh[i * d + e] += (double)load_f32(dout, dtype, base + e);
             }
         }
-        head_attention_bwd(S, d, Qh, Kh, Vh, Oh, dOh, dQh, dKh, dVh, logit);
+        double* ch = cond ? (double*)malloc(sizeof(double) * sd * 4) : NULL;
+        head_attention_bwd(S, d, Qh, Kh, Vh, Oh, dOh, dQh, dKh, dVh, logit, ch);
+        if (ch) {
+            for (int z = 0; z < 4; ++z)
+                memcpy(cond + ((int64_t)z * H + h) * S * d, ch + (int64_t)z * S * d, sizeof(double) * sd);
+            free(ch);
+        }
         if (dOt) memcpy(dOt + (int64_t)h * S * d, dOh, sizeof(double) * sd);
         if (dQt) memcpy(dQt + (int64_t)h * S * d, dQh, sizeof(double) * sd);
         if (dKt) memcpy(dKt + (int64_t)h * S * d, dKh, sizeof(double) * sd);

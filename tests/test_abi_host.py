@@ -1,0 +1,98 @@
+"""Host-side checks of the C ABI: the library loads, exports every function the
+header declares, and validates arguments before any launch (no GPU needed)."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+import oracle
+import synth_inputs as si
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _lh():
+    import hierarchical_selection_attention_amd as lh
+    return lh
+
+
+def test_library_exports_every_declared_function():
+    lh = _lh()
+    header = open(os.path.join(ROOT, "include", "lighthouse.h")).read()
+    header = re.sub(r"/\*.*?\*/", "", header, flags=re.S)
+    declared = set(re.findall(r"\b(lh_[a-z_]+)\s*\(", header))
+    assert declared, "no declarations found"
+    raw = C.CDLL(lh.LIB_PATH)
+    for name in sorted(declared):
+        assert hasattr(raw, name), f"{name} declared in lighthouse.h but not exported"
+    assert declared == set(lh.EXPORTS)
+
+
+@pytest.mark.parametrize("N,p,L,K", [(2048, 4, 3, 16), (2048, 4, 3, 512), (524288, 4, 5, 128), (1048576, 4, 6, 128),
+                                     (1080, 3, 4, 5), (16384, 2, 3, 100), (512, 4, 1, 7), (2048, 4, 3, 0),
+                                     (4096, 2, 8, 3), (98304, 4, 4, 128), (32768, 4, 4, 64)])
+def test_subseq_len_matches_oracle(N, p, L, K):
+    lh = _lh()
+    assert lh.lh_subseq_len(N, p, L, K) == oracle.subseq_len(N, p, L, K)
+
+
+def test_subseq_len_and_workspace_reject_bad_arguments():
+    lh = _lh()
+    assert lh.lh_subseq_len(2047, 4, 3, 5) == lh.LH_ERR_SHAPE       # p^(L-1) does not divide N
+    assert lh.lh_subseq_len(64, 4, 5, 5) == lh.LH_ERR_SHAPE         # p^(L-1) > N
+    assert lh.lh_subseq_len(2048, 1, 3, 5) == lh.LH_ERR_ARG         # p < 2
+    assert lh.lh_subseq_len(2048, 4, 0, 5) == lh.LH_ERR_ARG         # L < 1
+    assert lh.lh_subseq_len(2048, 4, 3, -1) == lh.LH_ERR_ARG        # K < 0
+    assert lh.lh_workspace_bytes(2048, 2, 96, 4, 3, 16, 0) == 0     # d not in {64, 128}
+    assert lh.lh_workspace_bytes(2048, 2, 64, 4, 3, 16, 7) == 0     # unknown dtype
+    assert lh.lh_workspace_bytes(2048, 128, 128, 4, 3, 16, 0) == 0  # H*d > 8192
+    assert lh.lh_workspace_bytes(1 << 20, 2, 64, 2, 3, 4096, 0) == 0  # K > 2048 with a real choice
+    for idx, w in si.WORKLOADS.items():
+        code = 0 if w["dtype"] == "bf16" else 1
+        assert lh.lh_workspace_bytes(w["N"], w["H"], w["d"], w["p"], w["L"], w["K"], code) > 0
+
+
+def test_entry_points_validate_before_launching():
+    """Invalid calls return their status without touching the GPU (this runs on a CPU host)."""
+    lh = _lh()
+    N, H, d, p, L, K = 2048, 2, 64, 4, 3, 16
+    nb = lh.lh_workspace_bytes(N, H, d, p, L, K, 1)
+    fake = 1 << 20          # never dereferenced: every call below fails validation first
+    aligned_ws = 1 << 24
+    assert lh.lh_forward(None, fake, fake, fake, N, H, d, p, L, K, 1, aligned_ws, nb, None) == lh.LH_ERR_ARG
+    assert lh.lh_forward(fake, fake, fake, fake, N, H, 96, p, L, K, 1, aligned_ws, nb, None) == lh.LH_ERR_SHAPE
+    assert lh.lh_forward(fake, fake, fake, fake, 2047, H, d, p, L, K, 1, aligned_ws, nb, None) == lh.LH_ERR_SHAPE
+    assert lh.lh_forward(fake, fake, fake, fake, N, H, d, p, L, K, 3, aligned_ws, nb, None) == lh.LH_ERR_DTYPE
+    assert lh.lh_forward(fake, fake, fake, fake, N, H, d, p, L, K, 1, aligned_ws, nb - 1, None) == lh.LH_ERR_WORKSPACE
+    assert lh.lh_forward(fake, fake, fake, fake, N, H, d, p, L, K, 1, aligned_ws + 16, nb, None) == lh.LH_ERR_WORKSPACE
+    assert lh.lh_forward(fake, fake, fake, fake, N, H, d, p, L, K, 1, None, nb, None) == lh.LH_ERR_WORKSPACE
+    assert lh.lh_forward(fake + 2, fake, fake, fake, N, H, d, p, L, K, 1, aligned_ws, nb, None) == lh.LH_ERR_ARG
+    assert lh.lh_backward(fake, fake, fake, fake, N, H, d, p, L, K, 1, 2, aligned_ws, nb, None) == lh.LH_ERR_DTYPE
+    assert lh.lh_backward(fake, None, fake, fake, N, H, d, p, L, K, 1, 0, aligned_ws, nb, None) == lh.LH_ERR_ARG
+    assert lh.lh_backward(fake, fake, fake, fake, N, H, d, p, L, K, 1, 0, aligned_ws, 0, None) == lh.LH_ERR_WORKSPACE
+    assert lh.lh_dense_workspace_bytes(1000, 2, 64, 0) == 0          # N not a multiple of 64
+    assert lh.lh_dense_workspace_bytes(1024, 2, 64, 1) == 0          # dense path is bf16
+    assert lh.lh_dense_attn_fwd(fake, fake, fake, fake, fake, 1000, 2, 64, 0, aligned_ws, 1 << 30, None) \
+        == lh.LH_ERR_SHAPE
+
+
+def test_workspace_views_are_inside_the_workspace():
+    lh = _lh()
+    for idx, w in si.WORKLOADS.items():
+        code = 0 if w["dtype"] == "bf16" else 1
+        args = (w["N"], w["H"], w["d"], w["p"], w["L"], w["K"], code)
+        nb = lh.lh_workspace_bytes(*args)
+        base = 1 << 32
+        for name, vid in lh.VIEWS.items():
+            ptr, n = lh.lh_workspace_view(base, *args, vid)
+            assert base <= ptr and ptr + n <= base + nb, name
+            assert (ptr - base) % 256 == 0
+
+
+def test_status_strings_and_stage_names():
+    lh = _lh()
+    for rc in (0, -1, -2, -3, -4, -5):
+        assert lh.lh_status_str(rc) and lh.lh_status_str(rc) != "unknown status"
+    assert lh.lh_stage_name(0) == "pool_score"
+    assert lh.lh_stage_name(99) == "unknown"

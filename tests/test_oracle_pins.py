@@ -407,3 +407,24 @@ def test_adjoints_conserve_mass():
         for i, (a, l) in enumerate(zip(r["start"][h].tolist(), r["level"][h].tolist())):
             for n, sub in (("dq", "dQt"), ("dk", "dKt"), ("dv", "dVt")):
                 np.testing.assert_allclose(b[n][a:a + p ** l, h].sum(0), b[sub][h, i], rtol=1e-10, atol=1e-12)
+
+
+def test_condition_sums_bound_and_match_nonnegative_cases():
+    """The absolute term sums used for tolerances bound each output, and equal it when
+    every term is nonnegative (v >= 0 gives cO = O; dO >= 0 gives cdV = dV)."""
+    N, H, d, p, L, K = 256, 2, 16, 4, 3, 4
+    x = _inputs(N, H, d, "fp32", 61, dout=True)
+    r = oracle.forward(x["q"], x["k"], x["v"], p, L, K, "fp32", want=("sel", "ot"))
+    sel = (r["start"], r["level"])
+    b = oracle.backward(x["q"], x["k"], x["v"], x["dout"], p, L, K, sel, "fp32", want=("sub", "cond"))
+    assert np.all(b["cO"] >= np.abs(r["Ot"]) * (1 - 1e-12))
+    assert np.all(b["cdQ"] >= np.abs(b["dQt"]) * (1 - 1e-12))
+    assert np.all(b["cdK"] >= np.abs(b["dKt"]) * (1 - 1e-12))
+    assert np.all(b["cdV"] >= np.abs(b["dVt"]) * (1 - 1e-12))
+    vpos = np.abs(x["v"])
+    dpos = np.abs(x["dout"])
+    r2 = oracle.forward(x["q"], x["k"], vpos, p, L, K, "fp32", want=("sel", "ot"))
+    b2 = oracle.backward(x["q"], x["k"], vpos, dpos, p, L, K, (r2["start"], r2["level"]), "fp32",
+                         want=("sub", "cond"))
+    np.testing.assert_allclose(b2["cO"], r2["Ot"], rtol=1e-12)
+    np.testing.assert_allclose(b2["cdV"], b2["dVt"], rtol=1e-12)
