@@ -102,16 +102,109 @@ struct AttnK {
     const float *qf, *kf, *vf, *dof;
 };
 
+// ------------------------------------------------------------ LDS tiles
+// Streamed operands move through double-buffered LDS in blocks of kBN
+// sequence positions, shared by the 4 wavefronts of a workgroup.  Row tiles
+// hold kBN rows of d elements; transposed tiles hold d rows of kBN elements.
+// 16-byte slots are XOR-swizzled by row so the 16 rows a fragment read
+// touches fall into different banks.
+constexpr int kBN = 32;
+
+template <int D>
+struct Tiles {
+    static constexpr int NSLOT = D / 8;              // 16-byte slots per row-tile row
+    static constexpr int ROW = kBN * D;              // elements of a row tile
+    static constexpr int TR = D * kBN;               // elements of a transposed tile
+    static constexpr int CH_ROW = kBN * NSLOT / 256; // 16-byte chunks per thread
+    static constexpr int CH_T = D * 4 / 256;
+};
+
+__device__ __forceinline__ int swz_row(int r, int slot, int nslot) { return slot ^ (r & (nslot - 1)); }
+__device__ __forceinline__ int swz_t(int r, int slot) { return slot ^ ((r >> 1) & 3); }
+
+// global [rows][D] (head base `g`, first row r0) -> registers
+template <int D>
+__device__ __forceinline__ void fetch_row(const uint16_t* g, int64_t r0, u32x4 (&reg)[Tiles<D>::CH_ROW]) {
+    constexpr int NSLOT = Tiles<D>::NSLOT;
+#pragma unroll
+    for (int i = 0; i < Tiles<D>::CH_ROW; ++i) {
+        const int c = threadIdx.x + 256 * i;
+        const int r = c / NSLOT, slot = c % NSLOT;
+        reg[i] = *reinterpret_cast<const u32x4*>(g + (r0 + r) * D + swz_row(r, slot, NSLOT) * 8);
+    }
+}
+template <int D>
+__device__ __forceinline__ void store_row(uint16_t* lds, const u32x4 (&reg)[Tiles<D>::CH_ROW]) {
+#pragma unroll
+    for (int i = 0; i < Tiles<D>::CH_ROW; ++i) {
+        const int c = threadIdx.x + 256 * i;
+        *reinterpret_cast<u32x4*>(lds + c * 8) = reg[i];
+    }
+}
+// global transposed [D][Sp] (head base `g`), columns c0..c0+kBN-1 -> registers
+template <int D>
+__device__ __forceinline__ void fetch_t(const uint16_t* g, int64_t Sp, int64_t c0, u32x4 (&reg)[Tiles<D>::CH_T]) {
+#pragma unroll
+    for (int i = 0; i < Tiles<D>::CH_T; ++i) {
+        const int c = threadIdx.x + 256 * i;
+        const int r = c / 4, slot = c % 4;
+        reg[i] = *reinterpret_cast<const u32x4*>(g + (int64_t)r * Sp + c0 + swz_t(r, slot) * 8);
+    }
+}
+template <int D>
+__device__ __forceinline__ void store_t(uint16_t* lds, const u32x4 (&reg)[Tiles<D>::CH_T]) {
+#pragma unroll
+    for (int i = 0; i < Tiles<D>::CH_T; ++i) {
+        const int c = threadIdx.x + 256 * i;
+        *reinterpret_cast<u32x4*>(lds + c * 8) = reg[i];
+    }
+}
+// fragment of row tile: row r, global 16-byte chunk c
+template <int D>
+__device__ __forceinline__ u32x4 frag_row(const uint16_t* lds, int r, int c) {
+    return *reinterpret_cast<const u32x4*>(lds + r * D + swz_row(r, c, Tiles<D>::NSLOT) * 8);
+}
+// fragment of transposed tile: row r, elements {4g..4g+3} and {16+4g..16+4g+3}
+__device__ __forceinline__ u32x4 frag_t(const uint16_t* lds, int r, int g) {
+    const uint16_t* row = lds + r * kBN;
+    const u32x2 lo = *reinterpret_cast<const u32x2*>(row + swz_t(r, g >> 1) * 8 + (g & 1) * 4);
+    const u32x2 hi = *reinterpret_cast<const u32x2*>(row + swz_t(r, 2 + (g >> 1)) * 8 + (g & 1) * 4);
+    return u32x4{lo[0], lo[1], hi[0], hi[1]};
+}
+
+// Work item -> (head, 64-row tile).  When H is a multiple of 8, the workgroups
+// of a head are all dispatched to the same XCD (workgroup i runs on XCD i % 8),
+// so the head's streamed operands stay in that XCD's L2.  `heavy_last_tile`
+// orders the longest causal rows first.
+__device__ __forceinline__ void work_item(int nT, int H, bool heavy_last_tile, int& h, int& tile) {
+    const int i = blockIdx.x;
+    int j;
+    if (H % 8 == 0) {
+        const int x = i % 8, q = i / 8;
+        h = x + 8 * (q / nT);
+        j = q % nT;
+    } else {
+        h = i / nT;
+        j = i % nT;
+    }
+    tile = heavy_last_tile ? nT - 1 - j : j;
+}
+
 // ------------------------------------------------------------------ forward
 template <int D, bool SPLIT>
 __global__ void __launch_bounds__(256) k_attn_fwd(AttnK a) {
+    using T = Tiles<D>;
     constexpr int NS = D / 32, NV = D / 16;
+    constexpr int NA = SPLIT ? 2 : 1;
+    constexpr int STAGE = NA * (T::ROW + T::TR);
+    __shared__ __attribute__((aligned(16))) uint16_t sm[2 * STAGE];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int lq = lane & 15, lg = lane >> 4;
-    const int h = blockIdx.y;
     const int64_t Sp = a.Sp;
-    const int64_t qt = gridDim.x - 1 - blockIdx.x;   // longest rows first
-    const int64_t q0 = qt * 64 + wave * 16;
+    const int nT = (int)(Sp / 64);
+    int h, qt;
+    work_item(nT, gridDim.x / nT, true, h, qt);
+    const int64_t q0 = (int64_t)qt * 64 + wave * 16;
     const int64_t myq = q0 + lq;
     const int64_t hb = (int64_t)h * Sp * D;
     const float mq = a.hscale[h * 4 + 0], mk = a.hscale[h * 4 + 1], mv = a.hscale[h * 4 + 2];
@@ -129,63 +222,92 @@ __global__ void __launch_bounds__(256) k_attn_fwd(AttnK a) {
     for (int v = 0; v < NV; ++v) o[v] = f32x4{0.f, 0.f, 0.f, 0.f};
     float m = -INFINITY, lsum = 0.f;
 
-    for (int64_t kb = 0; kb < q0 + 16; kb += 64) {
-        f32x4 sc[4];
+    const int nblk = (int)(((int64_t)qt * 64 + 64) / kBN);
+    u32x4 rkh[T::CH_ROW], rkl[T::CH_ROW], rvh[T::CH_T], rvl[T::CH_T];
+    auto fetch = [&](int b) {
+        const int64_t kb = (int64_t)b * kBN;
+        fetch_row<D>(a.kh + hb, kb, rkh);
+        fetch_t<D>(a.vTh + hb, Sp, kb, rvh);
+        if constexpr (SPLIT) {
+            fetch_row<D>(a.kl + hb, kb, rkl);
+            fetch_t<D>(a.vTl + hb, Sp, kb, rvl);
+        }
+    };
+    auto store = [&](int buf) {
+        uint16_t* base = sm + buf * STAGE;
+        store_row<D>(base, rkh);
+        store_t<D>(base + NA * T::ROW, rvh);
+        if constexpr (SPLIT) {
+            store_row<D>(base + T::ROW, rkl);
+            store_t<D>(base + NA * T::ROW + T::TR, rvl);
+        }
+    };
+    fetch(0);
+    store(0);
+    __syncthreads();
+    for (int b = 0; b < nblk; ++b) {
+        const int buf = b & 1;
+        if (b + 1 < nblk) fetch(b + 1);
+        const int64_t kb = (int64_t)b * kBN;
+        if (kb < q0 + 16) {
+            const uint16_t* Kh = sm + buf * STAGE;
+            const uint16_t* Kl = Kh + T::ROW;
+            const uint16_t* Vh = Kh + NA * T::ROW;
+            const uint16_t* Vl = Vh + T::TR;
+            f32x4 sc[2];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            sc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
-            const int64_t off = hb + (kb + 16 * u + lq) * D + 8 * lg;
+            for (int u = 0; u < 2; ++u) {
+                sc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+                const int r = 16 * u + lq;
 #pragma unroll
-            for (int s = 0; s < NS; ++s) {
-                const f16x8 kh = ld_f16x8(a.kh + off + 32 * s);
-                sc[u] = mma_h(kh, qfh[s], sc[u]);
-                if constexpr (SPLIT) {
-                    sc[u] = mma_h(kh, qfl[s], sc[u]);
-                    sc[u] = mma_h(ld_f16x8(a.kl + off + 32 * s), qfh[s], sc[u]);
+                for (int st = 0; st < NS; ++st) {
+                    const f16x8 kh = __builtin_bit_cast(f16x8, frag_row<D>(Kh, r, 4 * st + lg));
+                    sc[u] = mma_h(kh, qfh[st], sc[u]);
+                    if constexpr (SPLIT) {
+                        sc[u] = mma_h(kh, qfl[st], sc[u]);
+                        sc[u] = mma_h(__builtin_bit_cast(f16x8, frag_row<D>(Kl, r, 4 * st + lg)), qfh[st], sc[u]);
+                    }
                 }
             }
-        }
-        float mx = -INFINITY;
+            float mx = -INFINITY;
 #pragma unroll
-        for (int u = 0; u < 4; ++u)
+            for (int u = 0; u < 2; ++u)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int64_t key = kb + 16 * u + 4 * lg + r;
-                float x = sc[u][r] * c2;
-                x = key > myq ? -INFINITY : x;
-                sc[u][r] = x;
-                mx = fmaxf(mx, x);
-            }
-        mx = fmaxf(mx, shfl_xor_f(mx, 16));
-        mx = fmaxf(mx, shfl_xor_f(mx, 32));
-        const float mnew = fmaxf(m, mx);
-        const float alpha = exp2f(m - mnew);
-        m = mnew;
-        lsum *= alpha;
+                for (int r = 0; r < 4; ++r) {
+                    const int64_t key = kb + 16 * u + 4 * lg + r;
+                    float x = sc[u][r] * c2;
+                    x = key > myq ? -INFINITY : x;
+                    sc[u][r] = x;
+                    mx = fmaxf(mx, x);
+                }
+            mx = fmaxf(mx, shfl_xor_f(mx, 16));
+            mx = fmaxf(mx, shfl_xor_f(mx, 32));
+            const float mnew = fmaxf(m, mx);
+            const float alpha = exp2f(m - mnew);
+            m = mnew;
+            lsum *= alpha;
 #pragma unroll
-        for (int v = 0; v < NV; ++v) o[v] *= alpha;
+            for (int v = 0; v < NV; ++v) o[v] *= alpha;
 #pragma unroll
-        for (int u = 0; u < 4; ++u)
+            for (int u = 0; u < 2; ++u)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const float pr = exp2f(sc[u][r] - m);
-                lsum += pr;
-                sc[u][r] = pr;
-            }
-#pragma unroll
-        for (int w = 0; w < 2; ++w) {
+                for (int r = 0; r < 4; ++r) {
+                    const float pr = exp2f(sc[u][r] - m);
+                    lsum += pr;
+                    sc[u][r] = pr;
+                }
             f16x8 ph, pl;
-            split_h(sc[2 * w], sc[2 * w + 1], ph, pl);
-            const int64_t col = kb + 32 * w + 4 * lg;
+            split_h(sc[0], sc[1], ph, pl);
 #pragma unroll
             for (int v = 0; v < NV; ++v) {
-                const int64_t off = hb + (int64_t)(16 * v + lq) * Sp + col;
-                const f16x8 vh = __builtin_bit_cast(f16x8, ld_split_raw(a.vTh + off));
+                const f16x8 vh = __builtin_bit_cast(f16x8, frag_t(Vh, 16 * v + lq, lg));
                 o[v] = mma_h(vh, ph, o[v]);
                 o[v] = mma_h(vh, pl, o[v]);
-                if constexpr (SPLIT) o[v] = mma_h(__builtin_bit_cast(f16x8, ld_split_raw(a.vTl + off)), ph, o[v]);
+                if constexpr (SPLIT) o[v] = mma_h(__builtin_bit_cast(f16x8, frag_t(Vl, 16 * v + lq, lg)), ph, o[v]);
             }
         }
+        if (b + 1 < nblk) store(buf ^ 1);
+        __syncthreads();
     }
     lsum += shfl_xor_f(lsum, 16);
     lsum += shfl_xor_f(lsum, 32);
@@ -212,16 +334,23 @@ __global__ void __launch_bounds__(256) k_attn_fwd(AttnK a) {
 }
 
 // ------------------------------------------------------- backward: dK, dV
-// Key-stationary: wave w owns keys k0..k0+15 (lane column = key) and walks the
-// query blocks at or after its keys.
+// Key-stationary: wave w owns keys k0..k0+15 (lane column = key); the query
+// blocks at or after the workgroup's keys stream through LDS.
 template <int D, bool SPLIT, bool OUT_BF16>
 __global__ void __launch_bounds__(256) k_attn_dkdv(AttnK a) {
+    using T = Tiles<D>;
     constexpr int NS = D / 32, NV = D / 16;
+    constexpr int NA = SPLIT ? 2 : 1;
+    // stage: q rows, dO rows, q^T (bf16), dO^T
+    constexpr int STAGE = NA * (2 * T::ROW + 2 * T::TR);
+    __shared__ __attribute__((aligned(16))) uint16_t sm[2 * STAGE];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int lq = lane & 15, lg = lane >> 4;
-    const int h = blockIdx.y;
     const int64_t Sp = a.Sp;
-    const int64_t k0 = (int64_t)blockIdx.x * 64 + wave * 16;
+    const int nT = (int)(Sp / 64);
+    int h, kt;
+    work_item(nT, gridDim.x / nT, false, h, kt);
+    const int64_t k0 = (int64_t)kt * 64 + wave * 16;
     const int64_t mykey = k0 + lq;
     const int64_t hb = (int64_t)h * Sp * D;
     const float mq = a.hscale[h * 4 + 0], mk = a.hscale[h * 4 + 1], mv = a.hscale[h * 4 + 2],
@@ -246,56 +375,127 @@ __global__ void __launch_bounds__(256) k_attn_dkdv(AttnK a) {
 #pragma unroll
     for (int v = 0; v < NV; ++v) dk[v] = dv[v] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    for (int64_t qb = k0 & ~(int64_t)31; qb < a.rows; qb += 32) {
+    const int64_t qfirst = (int64_t)kt * 64;              // first query that can see the workgroup's keys
+    const int nblk = (int)((a.rows - qfirst + kBN - 1) / kBN);
+    u32x4 rA[4][T::CH_ROW];   // q h/l, dO h/l rows
+    u32x4 rB[4][T::CH_T];     // q^T h/l (bf16), dO^T h/l
+    auto fetchA = [&](int b) {
+        const int64_t qb = qfirst + (int64_t)b * kBN;
+        fetch_row<D>(a.qh + hb, qb, rA[0]);
+        fetch_row<D>(a.doh + hb, qb, rA[2]);
+        if constexpr (SPLIT) {
+            fetch_row<D>(a.ql + hb, qb, rA[1]);
+            fetch_row<D>(a.dol + hb, qb, rA[3]);
+        }
+    };
+    auto fetchB = [&](int b) {
+        const int64_t qb = qfirst + (int64_t)b * kBN;
+        fetch_t<D>(a.qTbh + hb, Sp, qb, rB[0]);
+        fetch_t<D>(a.doTh + hb, Sp, qb, rB[2]);
+        if constexpr (SPLIT) {
+            fetch_t<D>(a.qTbl + hb, Sp, qb, rB[1]);
+            fetch_t<D>(a.doTl + hb, Sp, qb, rB[3]);
+        }
+    };
+    // stage layout: [qh][ql?][doh][dol?] rows, then [qTh][qTl?][doTh][doTl?]
+    auto storeA = [&](int buf) {
+        uint16_t* base = sm + buf * STAGE;
+        store_row<D>(base, rA[0]);
+        store_row<D>(base + NA * T::ROW, rA[2]);
+        if constexpr (SPLIT) {
+            store_row<D>(base + T::ROW, rA[1]);
+            store_row<D>(base + 3 * T::ROW, rA[3]);
+        }
+    };
+    auto storeB = [&](int buf) {
+        uint16_t* base = sm + buf * STAGE + NA * 2 * T::ROW;
+        store_t<D>(base, rB[0]);
+        store_t<D>(base + NA * T::TR, rB[2]);
+        if constexpr (SPLIT) {
+            store_t<D>(base + T::TR, rB[1]);
+            store_t<D>(base + 3 * T::TR, rB[3]);
+        }
+    };
+    if (nblk > 0) {
+        fetchA(0);
+        fetchB(0);
+        storeA(0);
+        storeB(0);
+    }
+    __syncthreads();
+    for (int b = 0; b < nblk; ++b) {
+        const int buf = b & 1;
+        const bool more = b + 1 < nblk;
+        if (more) fetchA(b + 1);
+        const int64_t qb = qfirst + (int64_t)b * kBN;
+        const bool active = qb + kBN > k0;   // some query of the block sees some key of the wave
+        const uint16_t* base = sm + buf * STAGE;
+        const uint16_t* Qh = base;
+        const uint16_t* Ql = base + T::ROW;
+        const uint16_t* Oh = base + NA * T::ROW;
+        const uint16_t* Ol = Oh + T::ROW;
+        const uint16_t* QTh = base + NA * 2 * T::ROW;
+        const uint16_t* QTl = QTh + T::TR;
+        const uint16_t* OTh = QTh + NA * T::TR;
+        const uint16_t* OTl = OTh + T::TR;
         f32x4 P[2], dS[2];
+        if (active) {
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            f32x4 s = {0.f, 0.f, 0.f, 0.f}, dp = {0.f, 0.f, 0.f, 0.f};
-            const int64_t off = hb + (qb + 16 * u + lq) * D + 8 * lg;
+            for (int u = 0; u < 2; ++u) {
+                f32x4 s = {0.f, 0.f, 0.f, 0.f}, dp = {0.f, 0.f, 0.f, 0.f};
+                const int r = 16 * u + lq;
 #pragma unroll
-            for (int st = 0; st < NS; ++st) {
-                const f16x8 qh = ld_f16x8(a.qh + off + 32 * st);
-                const f16x8 oh = ld_f16x8(a.doh + off + 32 * st);
-                s = mma_h(qh, kfh[st], s);
-                dp = mma_h(oh, vfh[st], dp);
-                if constexpr (SPLIT) {
-                    s = mma_h(qh, kfl[st], s);
-                    s = mma_h(ld_f16x8(a.ql + off + 32 * st), kfh[st], s);
-                    dp = mma_h(oh, vfl[st], dp);
-                    dp = mma_h(ld_f16x8(a.dol + off + 32 * st), vfh[st], dp);
+                for (int st = 0; st < NS; ++st) {
+                    const f16x8 qh = __builtin_bit_cast(f16x8, frag_row<D>(Qh, r, 4 * st + lg));
+                    const f16x8 oh = __builtin_bit_cast(f16x8, frag_row<D>(Oh, r, 4 * st + lg));
+                    s = mma_h(qh, kfh[st], s);
+                    dp = mma_h(oh, vfh[st], dp);
+                    if constexpr (SPLIT) {
+                        s = mma_h(qh, kfl[st], s);
+                        s = mma_h(__builtin_bit_cast(f16x8, frag_row<D>(Ql, r, 4 * st + lg)), kfh[st], s);
+                        dp = mma_h(oh, vfl[st], dp);
+                        dp = mma_h(__builtin_bit_cast(f16x8, frag_row<D>(Ol, r, 4 * st + lg)), vfh[st], dp);
+                    }
+                }
+                const int64_t qq = qb + 16 * u + 4 * lg;
+                const f32x4 l4 = *reinterpret_cast<const f32x4*>(lse2 + qq);
+                const f32x4 d4 = *reinterpret_cast<const f32x4*>(Dv + qq);
+#pragma unroll
+                for (int r2 = 0; r2 < 4; ++r2) {
+                    const int64_t q = qq + r2;
+                    float pr = exp2f(s[r2] * cS - l4[r2]);
+                    pr = (q >= mykey && q < a.rows) ? pr : 0.f;
+                    P[u][r2] = pr;
+                    dS[u][r2] = pr * (dp[r2] * cP - d4[r2]);
                 }
             }
-            const int64_t qq = qb + 16 * u + 4 * lg;
-            const f32x4 l4 = *reinterpret_cast<const f32x4*>(lse2 + qq);
-            const f32x4 d4 = *reinterpret_cast<const f32x4*>(Dv + qq);
+        }
+        if (more) {
+            storeA(buf ^ 1);
+            fetchB(b + 1);
+        }
+        if (active) {
+            f16x8 ph, pl;
+            split_h(P[0], P[1], ph, pl);
+            bf16x8 sh, sl;
+            split_b(dS[0], dS[1], sh, sl);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int64_t q = qq + r;
-                float pr = exp2f(s[r] * cS - l4[r]);
-                pr = (q >= mykey && q < a.rows) ? pr : 0.f;
-                P[u][r] = pr;
-                dS[u][r] = pr * (dp[r] * cP - d4[r]);
+            for (int v = 0; v < NV; ++v) {
+                const int r = 16 * v + lq;
+                const f16x8 oth = __builtin_bit_cast(f16x8, frag_t(OTh, r, lg));
+                dv[v] = mma_h(oth, ph, dv[v]);
+                dv[v] = mma_h(oth, pl, dv[v]);
+                const bf16x8 qth = __builtin_bit_cast(bf16x8, frag_t(QTh, r, lg));
+                dk[v] = mma_b(qth, sh, dk[v]);
+                dk[v] = mma_b(qth, sl, dk[v]);
+                if constexpr (SPLIT) {
+                    dv[v] = mma_h(__builtin_bit_cast(f16x8, frag_t(OTl, r, lg)), ph, dv[v]);
+                    dk[v] = mma_b(__builtin_bit_cast(bf16x8, frag_t(QTl, r, lg)), sh, dk[v]);
+                }
             }
         }
-        f16x8 ph, pl;
-        split_h(P[0], P[1], ph, pl);
-        bf16x8 sh, sl;
-        split_b(dS[0], dS[1], sh, sl);
-        const int64_t col = qb + 4 * lg;
-#pragma unroll
-        for (int v = 0; v < NV; ++v) {
-            const int64_t off = hb + (int64_t)(16 * v + lq) * Sp + col;
-            const f16x8 oth = __builtin_bit_cast(f16x8, ld_split_raw(a.doTh + off));
-            dv[v] = mma_h(oth, ph, dv[v]);
-            dv[v] = mma_h(oth, pl, dv[v]);
-            const bf16x8 qth = __builtin_bit_cast(bf16x8, ld_split_raw(a.qTbh + off));
-            dk[v] = mma_b(qth, sh, dk[v]);
-            dk[v] = mma_b(qth, sl, dk[v]);
-            if constexpr (SPLIT) {
-                dv[v] = mma_h(__builtin_bit_cast(f16x8, ld_split_raw(a.doTl + off)), ph, dv[v]);
-                dk[v] = mma_b(__builtin_bit_cast(bf16x8, ld_split_raw(a.qTbl + off)), sh, dk[v]);
-            }
-        }
+        if (more) storeB(buf ^ 1);
+        __syncthreads();
     }
     // dk[v][r], dv[v][r] hold the gradients of key mykey at d-index 16v + 4g + r
     if (mykey < a.rows) {
@@ -319,18 +519,25 @@ __global__ void __launch_bounds__(256) k_attn_dkdv(AttnK a) {
 }
 
 // ---------------------------------------------------------- backward: dQ
-// Query-stationary: wave w owns queries q0..q0+15 and walks the keys up to the
-// diagonal.  dS rows are scaled down by a power of two (rowdown) before the
-// fp16 split, so they cannot overflow; the scale is undone at the end.
+// Query-stationary: wave w owns queries q0..q0+15 and the key blocks up to the
+// diagonal stream through LDS.  dS rows are scaled down by a power of two
+// (rowdown) before the fp16 split, so they cannot overflow; the scale is undone
+// at the end.
 template <int D, bool SPLIT, bool OUT_BF16>
 __global__ void __launch_bounds__(256) k_attn_dq(AttnK a) {
+    using T = Tiles<D>;
     constexpr int NS = D / 32, NV = D / 16;
+    constexpr int NA = SPLIT ? 2 : 1;
+    // stage: k rows, v rows, k^T
+    constexpr int STAGE = NA * (2 * T::ROW + T::TR);
+    __shared__ __attribute__((aligned(16))) uint16_t sm[2 * STAGE];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int lq = lane & 15, lg = lane >> 4;
-    const int h = blockIdx.y;
     const int64_t Sp = a.Sp;
-    const int64_t qt = gridDim.x - 1 - blockIdx.x;
-    const int64_t q0 = qt * 64 + wave * 16;
+    const int nT = (int)(Sp / 64);
+    int h, qt;
+    work_item(nT, gridDim.x / nT, true, h, qt);
+    const int64_t q0 = (int64_t)qt * 64 + wave * 16;
     const int64_t myq = q0 + lq;
     const int64_t hb = (int64_t)h * Sp * D;
     const float mq = a.hscale[h * 4 + 0], mk = a.hscale[h * 4 + 1], mv = a.hscale[h * 4 + 2],
@@ -356,43 +563,100 @@ __global__ void __launch_bounds__(256) k_attn_dq(AttnK a) {
 #pragma unroll
     for (int v = 0; v < NV; ++v) dq[v] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    for (int64_t kb = 0; kb < q0 + 16; kb += 32) {
+    const int nblk = (int)(((int64_t)qt * 64 + 64) / kBN);
+    u32x4 rA[4][T::CH_ROW];   // k h/l, v h/l rows
+    u32x4 rB[2][T::CH_T];     // k^T h/l
+    auto fetchA = [&](int b) {
+        const int64_t kb = (int64_t)b * kBN;
+        fetch_row<D>(a.kh + hb, kb, rA[0]);
+        fetch_row<D>(a.vh + hb, kb, rA[2]);
+        if constexpr (SPLIT) {
+            fetch_row<D>(a.kl + hb, kb, rA[1]);
+            fetch_row<D>(a.vl + hb, kb, rA[3]);
+        }
+    };
+    auto fetchB = [&](int b) {
+        const int64_t kb = (int64_t)b * kBN;
+        fetch_t<D>(a.kTh + hb, Sp, kb, rB[0]);
+        if constexpr (SPLIT) fetch_t<D>(a.kTl + hb, Sp, kb, rB[1]);
+    };
+    auto storeA = [&](int buf) {
+        uint16_t* base = sm + buf * STAGE;
+        store_row<D>(base, rA[0]);
+        store_row<D>(base + NA * T::ROW, rA[2]);
+        if constexpr (SPLIT) {
+            store_row<D>(base + T::ROW, rA[1]);
+            store_row<D>(base + 3 * T::ROW, rA[3]);
+        }
+    };
+    auto storeB = [&](int buf) {
+        uint16_t* base = sm + buf * STAGE + NA * 2 * T::ROW;
+        store_t<D>(base, rB[0]);
+        if constexpr (SPLIT) store_t<D>(base + T::TR, rB[1]);
+    };
+    fetchA(0);
+    fetchB(0);
+    storeA(0);
+    storeB(0);
+    __syncthreads();
+    for (int b = 0; b < nblk; ++b) {
+        const int buf = b & 1;
+        const bool more = b + 1 < nblk;
+        if (more) fetchA(b + 1);
+        const int64_t kb = (int64_t)b * kBN;
+        const bool active = kb < q0 + 16;
+        const uint16_t* base = sm + buf * STAGE;
+        const uint16_t* Kh = base;
+        const uint16_t* Kl = base + T::ROW;
+        const uint16_t* Vh = base + NA * T::ROW;
+        const uint16_t* Vl = Vh + T::ROW;
+        const uint16_t* KTh = base + NA * 2 * T::ROW;
+        const uint16_t* KTl = KTh + T::TR;
         f32x4 dS[2];
+        if (active) {
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            f32x4 s = {0.f, 0.f, 0.f, 0.f}, dp = {0.f, 0.f, 0.f, 0.f};
-            const int64_t off = hb + (kb + 16 * u + lq) * D + 8 * lg;
+            for (int u = 0; u < 2; ++u) {
+                f32x4 s = {0.f, 0.f, 0.f, 0.f}, dp = {0.f, 0.f, 0.f, 0.f};
+                const int r = 16 * u + lq;
 #pragma unroll
-            for (int st = 0; st < NS; ++st) {
-                const f16x8 kh = ld_f16x8(a.kh + off + 32 * st);
-                const f16x8 vh = ld_f16x8(a.vh + off + 32 * st);
-                s = mma_h(kh, qfh[st], s);
-                dp = mma_h(vh, dfh[st], dp);
-                if constexpr (SPLIT) {
-                    s = mma_h(kh, qfl[st], s);
-                    s = mma_h(ld_f16x8(a.kl + off + 32 * st), qfh[st], s);
-                    dp = mma_h(vh, dfl[st], dp);
-                    dp = mma_h(ld_f16x8(a.vl + off + 32 * st), dfh[st], dp);
+                for (int st = 0; st < NS; ++st) {
+                    const f16x8 kh = __builtin_bit_cast(f16x8, frag_row<D>(Kh, r, 4 * st + lg));
+                    const f16x8 vh = __builtin_bit_cast(f16x8, frag_row<D>(Vh, r, 4 * st + lg));
+                    s = mma_h(kh, qfh[st], s);
+                    dp = mma_h(vh, dfh[st], dp);
+                    if constexpr (SPLIT) {
+                        s = mma_h(kh, qfl[st], s);
+                        s = mma_h(__builtin_bit_cast(f16x8, frag_row<D>(Kl, r, 4 * st + lg)), qfh[st], s);
+                        dp = mma_h(vh, dfl[st], dp);
+                        dp = mma_h(__builtin_bit_cast(f16x8, frag_row<D>(Vl, r, 4 * st + lg)), dfh[st], dp);
+                    }
+                }
+#pragma unroll
+                for (int r2 = 0; r2 < 4; ++r2) {
+                    const int64_t key = kb + 16 * u + 4 * lg + r2;
+                    float pr = exp2f(s[r2] * cS - l2);
+                    pr = key <= myq ? pr : 0.f;
+                    dS[u][r2] = pr * (dp[r2] * cP - Dq) * down;
                 }
             }
+        }
+        if (more) {
+            storeA(buf ^ 1);
+            fetchB(b + 1);
+        }
+        if (active) {
+            f16x8 sh, sl;
+            split_h(dS[0], dS[1], sh, sl);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int64_t key = kb + 16 * u + 4 * lg + r;
-                float pr = exp2f(s[r] * cS - l2);
-                pr = key <= myq ? pr : 0.f;
-                dS[u][r] = pr * (dp[r] * cP - Dq) * down;
+            for (int v = 0; v < NV; ++v) {
+                const f16x8 kth = __builtin_bit_cast(f16x8, frag_t(KTh, 16 * v + lq, lg));
+                dq[v] = mma_h(kth, sh, dq[v]);
+                dq[v] = mma_h(kth, sl, dq[v]);
+                if constexpr (SPLIT) dq[v] = mma_h(__builtin_bit_cast(f16x8, frag_t(KTl, 16 * v + lq, lg)), sh, dq[v]);
             }
         }
-        f16x8 sh, sl;
-        split_h(dS[0], dS[1], sh, sl);
-#pragma unroll
-        for (int v = 0; v < NV; ++v) {
-            const int64_t off = hb + (int64_t)(16 * v + lq) * Sp + kb + 4 * lg;
-            const f16x8 kth = __builtin_bit_cast(f16x8, ld_split_raw(a.kTh + off));
-            dq[v] = mma_h(kth, sh, dq[v]);
-            dq[v] = mma_h(kth, sl, dq[v]);
-            if constexpr (SPLIT) dq[v] = mma_h(__builtin_bit_cast(f16x8, ld_split_raw(a.kTl + off)), sh, dq[v]);
-        }
+        if (more) storeB(buf ^ 1);
+        __syncthreads();
     }
     if (myq < a.rows) {
         const float mul = a.scale * mk / down;
@@ -550,7 +814,7 @@ hipError_t launch_attn_fwd(const AttnArgs& x, hipStream_t s) {
         if (x.d == 128) hipLaunchKernelGGL(k_attn_fwd_f32<128>, grid, dim3(256), 0, s, a);
         else hipLaunchKernelGGL(k_attn_fwd_f32<64>, grid, dim3(256), 0, s, a);
     } else {
-        dim3 grid((unsigned)(x.Sp / 64), (unsigned)x.H);
+        dim3 grid((unsigned)(x.Sp / 64 * x.H));
         LH_ATTN_DISPATCH(k_attn_fwd, grid);
     }
     return hipGetLastError();
@@ -565,7 +829,7 @@ hipError_t launch_attn_bwd(const AttnArgs& x, hipStream_t s, int part) {
         else hipLaunchKernelGGL(k_attn_bwd_f32<64>, grid, dim3(256), 0, s, a);
         return hipGetLastError();
     }
-    dim3 grid((unsigned)(x.Sp / 64), (unsigned)x.H);
+    dim3 grid((unsigned)(x.Sp / 64 * x.H));
     const bool ob = x.dq_b != nullptr;
     if (part == 0) {
         if (ob) LH_ATTN_DISPATCH(k_attn_dkdv, grid, , true);
