@@ -1,7 +1,7 @@
 """Lighthouse attention layer on MI355X (gfx950): HIP kernels behind a C ABI.
 
 Import fails loudly when liblighthouse.so has not been built
-(`python -m hierarchical_selection_attention_amd.build`); there is no
+(`python hierarchical_selection_attention_amd/build.py`); there is no
 fallback implementation.
 """
 from ._lib import *  # noqa: F401,F403

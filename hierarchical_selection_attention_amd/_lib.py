@@ -30,7 +30,7 @@ class LighthouseError(RuntimeError):
 
 def _load():
     if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is not built; run `python -m hierarchical_selection_attention_amd.build`")
+        raise ImportError(f"{LIB_PATH} is not built; run `python hierarchical_selection_attention_amd/build.py`")
     L = C.CDLL(LIB_PATH)
     i, i64, sz, vp = C.c_int, C.c_int64, C.c_size_t, C.c_void_p
     sig = {

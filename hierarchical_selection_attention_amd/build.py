@@ -1,6 +1,7 @@
 """Build liblighthouse.so (the gfx950 HIP kernels and the C ABI) in-tree with hipcc.
 
-Usage: python -m hierarchical_selection_attention_amd.build
+Usage: python hierarchical_selection_attention_amd/build.py [-v]
+(run as a file: the package itself refuses to import until the library exists)
 """
 from __future__ import annotations
 

@@ -48,17 +48,47 @@ __device__ __forceinline__ void load8(const void* base, int64_t elem, float (&x)
     }
 }
 
+// Same as load8 with non-temporal loads: streamed inputs that are read once.
 template <int DT>
+__device__ __forceinline__ void load8_nt(const void* base, int64_t elem, float (&x)[8]) {
+    if constexpr (DT == 0) {
+        u32x4 w = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(base) + elem));
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            x[2 * i] = bf16_lo(w[i]);
+            x[2 * i + 1] = bf16_hi(w[i]);
+        }
+    } else {
+        const f32x4* p = reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(base) + elem);
+        f32x4 a = __builtin_nontemporal_load(p), b = __builtin_nontemporal_load(p + 1);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            x[i] = a[i];
+            x[4 + i] = b[i];
+        }
+    }
+}
+
+// Store of 8 elements in the I/O dtype; NT selects non-temporal stores.
+template <int DT, bool NT = false>
 __device__ __forceinline__ void store8(void* base, int64_t elem, const float (&x)[8]) {
     if constexpr (DT == 0) {
         u32x4 w;
 #pragma unroll
         for (int i = 0; i < 4; ++i) w[i] = pack_bf16x2(x[2 * i], x[2 * i + 1]);
-        *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(base) + elem) = w;
+        u32x4* p = reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(base) + elem);
+        if constexpr (NT) __builtin_nontemporal_store(w, p);
+        else *p = w;
     } else {
         f32x4* p = reinterpret_cast<f32x4*>(reinterpret_cast<float*>(base) + elem);
-        p[0] = f32x4{x[0], x[1], x[2], x[3]};
-        p[1] = f32x4{x[4], x[5], x[6], x[7]};
+        const f32x4 a = {x[0], x[1], x[2], x[3]}, b = {x[4], x[5], x[6], x[7]};
+        if constexpr (NT) {
+            __builtin_nontemporal_store(a, p);
+            __builtin_nontemporal_store(b, p + 1);
+        } else {
+            p[0] = a;
+            p[1] = b;
+        }
     }
 }
 
@@ -77,8 +107,29 @@ __device__ __forceinline__ void store8f(float* base, int64_t elem, const float (
     p[1] = f32x4{x[4], x[5], x[6], x[7]};
 }
 
+// 8 bf16 values packed in 4 dwords -> fp32, exact.
+__device__ __forceinline__ void unpack8(const u32x4& w, float (&x)[8]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        x[2 * i] = bf16_lo(w[i]);
+        x[2 * i + 1] = bf16_hi(w[i]);
+    }
+}
+
 __device__ __forceinline__ float shfl_xor_f(float v, int mask) {
     return __shfl_xor(v, mask, 64);
+}
+
+// Value of lane (lane ^ OFF) for OFF in {1, 2, 4, 8, 16}: DPP quad permutes for
+// 1 and 2, ds_swizzle (bit mode, xor mask) for 4..16.  Exact moves.
+template <int OFF>
+__device__ __forceinline__ float xor_lane(float v) {
+    const int b = __float_as_int(v);
+    int r;
+    if constexpr (OFF == 1) r = __builtin_amdgcn_mov_dpp(b, 0xB1, 0xF, 0xF, false);       // [1,0,3,2]
+    else if constexpr (OFF == 2) r = __builtin_amdgcn_mov_dpp(b, 0x4E, 0xF, 0xF, false);  // [2,3,0,1]
+    else r = __builtin_amdgcn_ds_swizzle(b, (OFF << 10) | 0x1F);
+    return __int_as_float(r);
 }
 
 }  // namespace lh

@@ -48,41 +48,99 @@ __global__ void __launch_bounds__(256) k_pool_score(PoolScoreArgs a) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) aq[e] = ak[e] = av[e] = 0.f;
 
-    constexpr int U = 4;
-    for (int i0 = 0; i0 < iters; i0 += U) {
-        float xq[U][8], xk[U][8], xv[U][8];
+    // one token: fixed-order fp32 score and running sums of the pooled rows
+    auto consume = [&](int tl, const float (&xq)[8], const float (&xk)[8], const float (&xv)[8]) {
+        float sq = 0.f, sk = 0.f;
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            if (i0 + u < iters) {
-                int64_t t = t0 + ts + (int64_t)a.mt * (i0 + u);
-                int64_t el = (t * H + h) * d + c * 8;
-                load8<DT>(a.q, el, xq[u]);
-                load8<DT>(a.k, el, xk[u]);
-                load8<DT>(a.v, el, xv[u]);
-            }
+        for (int e = 0; e < 8; ++e) {
+            sq = __builtin_fmaf(xq[e], xq[e], sq);
+            sk = __builtin_fmaf(xk[e], xk[e], sk);
         }
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            if (i0 + u < iters) {
-                float sq = 0.f, sk = 0.f;
+        for (int off = G / 2; off >= 1; off >>= 1) {
+            sq = sq + shfl_xor_f(sq, off);
+            sk = sk + shfl_xor_f(sk, off);
+        }
+        if (c == 0) sc[tl * HG + hl] = sq + sk;
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    sq = __builtin_fmaf(xq[u][e], xq[u][e], sq);
-                    sk = __builtin_fmaf(xk[u][e], xk[u][e], sk);
-                }
+        for (int e = 0; e < 8; ++e) {
+            aq[e] += xq[e];
+            ak[e] += xk[e];
+            av[e] += xv[e];
+        }
+    };
+    if constexpr (DT == 0) {
+        // bf16: U tokens of raw 16-byte non-temporal loads in flight (read once);
+        // the butterflies of the U tokens are interleaved so the cross-lane moves overlap
+        constexpr int U = 8;
+        const int64_t tstride = (int64_t)a.mt * H * d;
+        const int64_t el0 = ((t0 + ts) * H + h) * d + c * 8;
+        const uint16_t* Q = reinterpret_cast<const uint16_t*>(a.q) + el0;
+        const uint16_t* Kp = reinterpret_cast<const uint16_t*>(a.k) + el0;
+        const uint16_t* V = reinterpret_cast<const uint16_t*>(a.v) + el0;
+        for (int i0 = 0; i0 < iters; i0 += U) {
+            u32x4 rq[U], rk[U], rv[U];
 #pragma unroll
-                for (int off = G / 2; off >= 1; off >>= 1) {
-                    sq = sq + shfl_xor_f(sq, off);
-                    sk = sk + shfl_xor_f(sk, off);
-                }
-                if (c == 0) sc[(ts + a.mt * (i0 + u)) * HG + hl] = sq + sk;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    aq[e] += xq[u][e];
-                    ak[e] += xk[u][e];
-                    av[e] += xv[u][e];
+            for (int u = 0; u < U; ++u) {
+                if (i0 + u < iters) {
+                    const int64_t off = (int64_t)(i0 + u) * tstride;
+                    rq[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(Q + off));
+                    rk[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(Kp + off));
+                    rv[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(V + off));
                 }
             }
+            float sq[U], sk[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                float xq[8], xk[8], xv[8];
+                unpack8(rq[u], xq);
+                unpack8(rk[u], xk);
+                unpack8(rv[u], xv);
+                float a1 = 0.f, a2 = 0.f;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    a1 = __builtin_fmaf(xq[e], xq[e], a1);
+                    a2 = __builtin_fmaf(xk[e], xk[e], a2);
+                }
+                sq[u] = a1;
+                sk[u] = a2;
+                if (i0 + u < iters) {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        aq[e] += xq[e];
+                        ak[e] += xk[e];
+                        av[e] += xv[e];
+                    }
+                }
+            }
+            // a_g <- a_g + a_(g^off), off = G/2 .. 1
+#define LH_BFLY(OFF)                                                        \
+            if constexpr (G / 2 >= OFF) {                                   \
+                _Pragma("unroll") for (int u = 0; u < U; ++u) {             \
+                    sq[u] = sq[u] + xor_lane<OFF>(sq[u]);                   \
+                    sk[u] = sk[u] + xor_lane<OFF>(sk[u]);                   \
+                }                                                           \
+            }
+            LH_BFLY(8)
+            LH_BFLY(4)
+            LH_BFLY(2)
+            LH_BFLY(1)
+#undef LH_BFLY
+            if (c == 0) {
+#pragma unroll
+                for (int u = 0; u < U; ++u)
+                    if (i0 + u < iters) sc[(ts + a.mt * (i0 + u)) * HG + hl] = sq[u] + sk[u];
+            }
+        }
+    } else {
+        for (int i = 0; i < iters; ++i) {
+            const int64_t t = t0 + ts + (int64_t)a.mt * i;
+            const int64_t el = (t * H + h) * d + c * 8;
+            float xq[8], xk[8], xv[8];
+            load8_nt<DT>(a.q, el, xq);
+            load8_nt<DT>(a.k, el, xk);
+            load8_nt<DT>(a.v, el, xv);
+            consume(ts + a.mt * i, xq, xk, xv);
         }
     }
     __syncthreads();
@@ -350,21 +408,23 @@ __global__ void __launch_bounds__(256) k_scatter_fwd(ScatterArgs a) {
             nxt = slot + 1 < a.S ? st[slot + 1] : a.N;
             load8f(a.src, sbase + slot * d, x);
         }
-        store8<DT>(a.dst, (t * H + tm.h) * d + tm.c * 8, x);
+        store8<DT, true>(a.dst, (t * H + tm.h) * d + tm.c * 8, x);
     }
 }
 
 // Adjoint of the scatter: dO~[h][i] = sum over the tokens of entry i of dO.
-// Each thread sums its contiguous token range per entry in fp32 (token order);
-// an entry that lies wholly inside the range is stored, one that crosses the
-// range's ends is added atomically: fp32 atomics (mode 0) or exact 64-bit
-// fixed-point integer atomics, scale 2^32 (mode 1, order-independent).
+// A thread owns one block of p^m tokens (the pooling chunk) for one
+// (head, 8-element chunk) and sums dO over each entry in token order in fp32.
+// Entries at levels <= m lie inside one block and are stored directly; only
+// coarser entries span blocks, and their partial sums are added atomically:
+// fp32 atomics (mode 0) or exact 64-bit fixed-point integer atomics with
+// scale 2^32 (mode 1, independent of the order of the additions).
 struct ScatterBwdArgs {
     const int32_t* start;
     const void* dout;     // dtype [N][H][d]
     void* acc;            // fp32 or int64 [H][Sp][d]
-    int64_t N, S, Sp;
-    int H, HG, mt;
+    int64_t N, S, Sp, tok;
+    int H, HG;
 };
 
 __device__ __forceinline__ long long to_fixed(float x) {
@@ -399,10 +459,13 @@ __device__ __forceinline__ void flush_entry(const ScatterBwdArgs& a, int h, int 
 template <int DT, int G, int MODE>
 __global__ void __launch_bounds__(256) k_scatter_bwd(ScatterBwdArgs a) {
     constexpr int d = G * 8;
-    const TokMap tm = tok_map<G>(a.HG, a.mt, a.N);
-    if (tm.tb >= tm.te) return;
-    const int32_t* st = a.start + (int64_t)tm.h * a.S;
-    int64_t slot = find_slot(st, a.S, tm.tb);
+    const int tid = threadIdx.x;
+    const int c = tid % G;
+    const int h = blockIdx.y * a.HG + tid / G;
+    const int64_t tb = (int64_t)blockIdx.x * a.tok;
+    const int64_t te = tb + a.tok;
+    const int32_t* st = a.start + (int64_t)h * a.S;
+    int64_t slot = find_slot(st, a.S, tb);
     int64_t beg = st[slot];
     int64_t nxt = slot + 1 < a.S ? st[slot + 1] : a.N;
     float s[8];
@@ -410,17 +473,17 @@ __global__ void __launch_bounds__(256) k_scatter_bwd(ScatterBwdArgs a) {
     for (int e = 0; e < 8; ++e) s[e] = 0.f;
     const int64_t H = a.H;
     constexpr int U = 8;
-    for (int64_t t0 = tm.tb; t0 < tm.te; t0 += U) {
+    for (int64_t t0 = tb; t0 < te; t0 += U) {
         float x[U][8];
 #pragma unroll
         for (int u = 0; u < U; ++u)
-            if (t0 + u < tm.te) load8<DT>(a.dout, ((t0 + u) * H + tm.h) * d + tm.c * 8, x[u]);
+            if (t0 + u < te) load8_nt<DT>(a.dout, ((t0 + u) * H + h) * d + c * 8, x[u]);
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int64_t t = t0 + u;
-            if (t < tm.te) {
+            if (t < te) {
                 if (t >= nxt) {
-                    flush_entry<DT, G, MODE>(a, tm.h, tm.c, slot, beg >= tm.tb && nxt <= tm.te, s);
+                    flush_entry<DT, G, MODE>(a, h, c, slot, beg >= tb && nxt <= te, s);
 #pragma unroll
                     for (int e = 0; e < 8; ++e) s[e] = 0.f;
                     ++slot;
@@ -432,7 +495,7 @@ __global__ void __launch_bounds__(256) k_scatter_bwd(ScatterBwdArgs a) {
             }
         }
     }
-    flush_entry<DT, G, MODE>(a, tm.h, tm.c, slot, beg >= tm.tb && nxt <= tm.te, s);
+    flush_entry<DT, G, MODE>(a, h, c, slot, beg >= tb && nxt <= te, s);
 }
 
 // Adjoint of gather + mean-pool: dX[t][h] = dX~[h][slot_h(t)] / p^level.
@@ -480,7 +543,7 @@ __global__ void __launch_bounds__(256) k_pool_bwd(PoolBwdArgs a) {
         }
         const int64_t el = (t * H + tm.h) * d + tm.c * 8;
 #pragma unroll
-        for (int z = 0; z < 3; ++z) store8<DT>(dsts[z], el, g[z]);
+        for (int z = 0; z < 3; ++z) store8<DT, true>(dsts[z], el, g[z]);
     }
 }
 
@@ -621,10 +684,11 @@ hipError_t launch_scatter_bwd(const Plan& P, const void* dout, int mode, char* w
     a.start = reinterpret_cast<const int32_t*>(ws + P.off_start);
     a.dout = dout;
     a.acc = ws + P.off_acc;
-    a.N = P.N; a.S = P.S; a.Sp = P.Sp; a.H = P.H;
-    const int threads = scatter_threads(P, &a.HG, &a.mt);
-    dim3 grid((unsigned)((P.N + kTileTok - 1) / kTileTok), (unsigned)(P.H / a.HG));
+    a.N = P.N; a.S = P.S; a.Sp = P.Sp; a.H = P.H; a.tok = P.tok;
     const int G = P.d / 8;
+    a.HG = head_group(P.H, G);
+    const int threads = a.HG * G;
+    dim3 grid((unsigned)(P.N / P.tok), (unsigned)(P.H / a.HG));
 #define LH_SB(DT, GG, MD) hipLaunchKernelGGL((k_scatter_bwd<DT, GG, MD>), grid, dim3(threads), 0, s, a)
     if (P.dtype == BF16) {
         if (G == 16) { if (mode == 0) LH_SB(0, 16, 0); else LH_SB(0, 16, 1); }
