@@ -69,6 +69,17 @@ __device__ __forceinline__ void load8_nt(const void* base, int64_t elem, float (
     }
 }
 
+// Raw buffer resource over `bytes` bytes from `base` (no stride; dword3 value
+// for the gfx9 family).  Loads through it take a scalar base, a per-lane 32-bit
+// offset and a uniform scalar offset, so per-token addresses cost no VGPRs.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+// 16-byte non-temporal load (cache policy bit 1 = nt) at lane offset + uniform offset.
+__device__ __forceinline__ u32x4 buf_ld16_nt(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 2);
+}
+
 // Store of 8 elements in the I/O dtype; NT selects non-temporal stores.
 template <int DT, bool NT = false>
 __device__ __forceinline__ void store8(void* base, int64_t elem, const float (&x)[8]) {

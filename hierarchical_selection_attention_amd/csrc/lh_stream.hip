@@ -28,6 +28,13 @@ struct PoolScoreArgs {
     int64_t pw[kMaxLevels];
 };
 
+// Tokens per load batch of the bf16 pooling pass (two batches in flight per wave).
+// One is fastest on MI355X at d = 128: 90 VGPRs, five waves per SIMD; the read
+// stream is not latency bound at that depth, larger batches only cost occupancy.
+#ifndef LH_POOL_U
+#define LH_POOL_U 1
+#endif
+
 template <int DT, int G>
 __global__ void __launch_bounds__(256) k_pool_score(PoolScoreArgs a) {
     extern __shared__ float smem[];
@@ -42,7 +49,7 @@ __global__ void __launch_bounds__(256) k_pool_score(PoolScoreArgs a) {
     const int H = a.H;
     const int64_t t0 = (int64_t)blockIdx.x * a.tok;
     const int iters = a.tok / a.mt;
-    float* sc = smem;   // [tok][H] leaf scores
+    float* sc = smem;   // [HG][tok] leaf scores of this chunk (head-major)
 
     float aq[8], ak[8], av[8];
 #pragma unroll
@@ -61,7 +68,7 @@ __global__ void __launch_bounds__(256) k_pool_score(PoolScoreArgs a) {
             sq = sq + shfl_xor_f(sq, off);
             sk = sk + shfl_xor_f(sk, off);
         }
-        if (c == 0) sc[tl * HG + hl] = sq + sk;
+        if (c == 0) sc[hl * a.tok + tl] = sq + sk;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             aq[e] += xq[e];
@@ -71,31 +78,37 @@ __global__ void __launch_bounds__(256) k_pool_score(PoolScoreArgs a) {
     };
     if constexpr (DT == 0) {
         // bf16: U tokens of raw 16-byte non-temporal loads in flight (read once);
-        // the butterflies of the U tokens are interleaved so the cross-lane moves overlap
-        constexpr int U = 8;
-        const int64_t tstride = (int64_t)a.mt * H * d;
-        const int64_t el0 = ((t0 + ts) * H + h) * d + c * 8;
-        const uint16_t* Q = reinterpret_cast<const uint16_t*>(a.q) + el0;
-        const uint16_t* Kp = reinterpret_cast<const uint16_t*>(a.k) + el0;
-        const uint16_t* V = reinterpret_cast<const uint16_t*>(a.v) + el0;
-        for (int i0 = 0; i0 < iters; i0 += U) {
-            u32x4 rq[U], rk[U], rv[U];
+        // the butterflies of the U tokens are interleaved so the cross-lane moves
+        // overlap.  Loads go through buffer resources over this workgroup's chunk:
+        // one lane offset, and a uniform offset per token.
+        const int64_t base0 = (t0 * H + (int64_t)blockIdx.y * HG) * d;
+        const uint32_t chunk_bytes = (uint32_t)((((int64_t)a.tok - 1) * H + HG) * d * 2);
+        const uint32_t tstride = (uint32_t)(a.mt * H * d * 2);
+        const uint32_t lane_off = (uint32_t)(((ts * H + hl) * d + c * 8) * 2);
+        const auto Q = make_rsrc(reinterpret_cast<const uint16_t*>(a.q) + base0, chunk_bytes);
+        const auto Kp = make_rsrc(reinterpret_cast<const uint16_t*>(a.k) + base0, chunk_bytes);
+        const auto V = make_rsrc(reinterpret_cast<const uint16_t*>(a.v) + base0, chunk_bytes);
+        // loads of tokens i0 .. i0+U-1 into r (q, k, v per token)
+        auto issue = [&](u32x4* r, int i0, auto Uc) {
+            constexpr int U = decltype(Uc)::value;
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                if (i0 + u < iters) {
-                    const int64_t off = (int64_t)(i0 + u) * tstride;
-                    rq[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(Q + off));
-                    rk[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(Kp + off));
-                    rv[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(V + off));
-                }
+                const uint32_t off = (uint32_t)(i0 + u) * tstride;
+                r[3 * u + 0] = buf_ld16_nt(Q, lane_off, off);
+                r[3 * u + 1] = buf_ld16_nt(Kp, lane_off, off);
+                r[3 * u + 2] = buf_ld16_nt(V, lane_off, off);
             }
+        };
+        // scores and pooled sums of tokens i0 .. i0+U-1 held in r
+        auto consume_batch = [&](const u32x4* r, int i0, auto Uc) {
+            constexpr int U = decltype(Uc)::value;
             float sq[U], sk[U];
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 float xq[8], xk[8], xv[8];
-                unpack8(rq[u], xq);
-                unpack8(rk[u], xk);
-                unpack8(rv[u], xv);
+                unpack8(r[3 * u + 0], xq);
+                unpack8(r[3 * u + 1], xk);
+                unpack8(r[3 * u + 2], xv);
                 float a1 = 0.f, a2 = 0.f;
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
@@ -104,13 +117,11 @@ __global__ void __launch_bounds__(256) k_pool_score(PoolScoreArgs a) {
                 }
                 sq[u] = a1;
                 sk[u] = a2;
-                if (i0 + u < iters) {
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        aq[e] += xq[e];
-                        ak[e] += xk[e];
-                        av[e] += xv[e];
-                    }
+                for (int e = 0; e < 8; ++e) {
+                    aq[e] += xq[e];
+                    ak[e] += xk[e];
+                    av[e] += xv[e];
                 }
             }
             // a_g <- a_g + a_(g^off), off = G/2 .. 1
@@ -128,9 +139,37 @@ __global__ void __launch_bounds__(256) k_pool_score(PoolScoreArgs a) {
 #undef LH_BFLY
             if (c == 0) {
 #pragma unroll
-                for (int u = 0; u < U; ++u)
-                    if (i0 + u < iters) sc[(ts + a.mt * (i0 + u)) * HG + hl] = sq[u] + sk[u];
+                for (int u = 0; u < U; ++u) sc[hl * a.tok + ts + a.mt * (i0 + u)] = sq[u] + sk[u];
             }
+        };
+        // full batches of UB tokens, double-buffered: the loads of batch b+1 are
+        // issued before batch b is consumed; then single tokens
+        constexpr int UB = LH_POOL_U;
+        using UBc = std::integral_constant<int, UB>;
+        const int nb = iters / UB;
+        u32x4 ra[3 * UB], rb[3 * UB];
+        // (no branch between a prefetch and the consume after it, so the waits stay exact)
+        if (nb > 0) issue(ra, 0, UBc{});
+        int b = 0;
+        for (; b + 2 < nb; b += 2) {
+            issue(rb, (b + 1) * UB, UBc{});
+            __builtin_amdgcn_sched_barrier(0);
+            consume_batch(ra, b * UB, UBc{});
+            issue(ra, (b + 2) * UB, UBc{});
+            __builtin_amdgcn_sched_barrier(0);
+            consume_batch(rb, (b + 1) * UB, UBc{});
+        }
+        if (b + 1 < nb) {
+            issue(rb, (b + 1) * UB, UBc{});
+            __builtin_amdgcn_sched_barrier(0);
+            consume_batch(ra, b * UB, UBc{});
+            consume_batch(rb, (b + 1) * UB, UBc{});
+        } else if (b < nb) {
+            consume_batch(ra, b * UB, UBc{});
+        }
+        for (int i = nb * UB; i < iters; ++i) {
+            issue(ra, i, std::integral_constant<int, 1>{});
+            consume_batch(ra, i, std::integral_constant<int, 1>{});
         }
     } else {
         for (int i = 0; i < iters; ++i) {
@@ -145,22 +184,38 @@ __global__ void __launch_bounds__(256) k_pool_score(PoolScoreArgs a) {
     }
     __syncthreads();
 
-    // scores of levels 0..m for this chunk: max over the covered leaves
-    for (int l = 0; l <= a.m; ++l) {
-        const int per = a.tok / (int)a.pw[l];
-        const int span = (int)a.pw[l];
-        const int64_t j0 = t0 / span;
-        for (int idx = tid; idx < HG * per; idx += blockDim.x) {
-            int hh = idx / per, j = idx % per;
-            float mx = sc[(j * span) * HG + hh];
-            for (int u = 1; u < span; ++u) mx = fmaxf(mx, sc[(j * span + u) * HG + hh]);
-            a.lev[l][(int64_t)(blockIdx.y * HG + hh) * a.n[l] + j0 + j] = mx;
+    // scores of levels 0..m for this chunk.  Level l+1 is the max over p entries of
+    // level l (max is exact, so this equals the max over the covered leaves); the
+    // levels alternate between sc and lb, [HG][tok / p^l] each.
+    {
+        float* lb = smem + (size_t)a.tok * HG;
+        float* src = sc;
+        float* dst = lb;
+        int per = a.tok;
+        for (int l = 0; l <= a.m; ++l) {
+            const int64_t j0 = t0 / a.pw[l];
+            float* out = a.lev[l] + (int64_t)blockIdx.y * HG * a.n[l] + j0;
+            for (int idx = tid; idx < HG * per; idx += blockDim.x) {
+                const int hh = idx / per, j = idx - hh * per;
+                out[(int64_t)hh * a.n[l] + j] = src[idx];
+            }
+            if (l == a.m) break;
+            const int nper = per / a.p;
+            for (int idx = tid; idx < HG * nper; idx += blockDim.x) {
+                const float* g = src + (int64_t)idx * a.p;   // entries idx*p .. idx*p+p-1 of [HG][per]
+                float mx = g[0];
+                for (int k = 1; k < a.p; ++k) mx = fmaxf(mx, g[k]);
+                dst[idx] = mx;
+            }
+            __syncthreads();
+            float* t = src; src = dst; dst = t;
+            per = nper;
         }
     }
 
     // level-m means of q, k, v (only needed when the pyramid has levels)
     if (a.m >= 1) {
-        float* red = smem + a.tok * HG;   // [mt][HG][d]
+        float* red = smem + (size_t)a.tok * HG + (size_t)(a.tok / a.p) * HG;   // [mt][HG][d]
         const float inv = 1.0f / (float)a.tok;
         const int64_t blk = blockIdx.x;
         float* accs[3] = {aq, ak, av};
@@ -588,7 +643,9 @@ hipError_t launch_pool_score(const Plan& P, const void* q, const void* k, const 
     while (a.HG * G * mt * P.p <= 256 && mt * P.p <= P.tok) mt *= P.p;
     a.mt = mt;
     const int threads = a.HG * G * mt;
+    // leaf scores [HG][tok], the level buffer [HG][tok/p], the mean partials [mt][HG][d]
     size_t lds = sizeof(float) * (size_t)P.tok * a.HG;
+    if (P.m >= 1) lds += sizeof(float) * (size_t)(P.tok / P.p) * a.HG;
     if (P.m >= 1 && mt > 1) lds += sizeof(float) * (size_t)mt * a.HG * P.d;
     dim3 grid((unsigned)(P.N / P.tok), (unsigned)(P.H / a.HG));
     if (P.dtype == BF16) {
