@@ -25,7 +25,9 @@ COMMON = ["--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17", "-Wall",
 SOURCES = {
     "lh_stream.hip": ["-ffp-contract=off"],
     "lh_topk.hip": [],
-    "lh_attn.hip": [],
+    # MFMA accumulators in ordinary VGPRs: the softmax rescale and the split of P
+    # work on them with VALU ops, which cannot read AGPRs
+    "lh_attn.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
     "lh_prep.hip": [],
     "lh_api.cpp": ["-x", "hip"],
 }

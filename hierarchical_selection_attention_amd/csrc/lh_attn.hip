@@ -10,8 +10,9 @@
 // Scores are computed transposed (S^T = K Q^T, one query per lane column) so
 // the online-softmax statistics of a query live in the lanes that own its
 // output column (O^T = V^T P^T).  Operands whose contraction index is the
-// sequence position come from [H][d][Sp] transposed copies, so every operand
-// load is one contiguous vector.
+// sequence position come from [H][d][Sp] transposed copies whose blocks of 32
+// positions are stored in fragment order, so every operand load is one
+// contiguous 16-byte vector.
 //
 // Precision: the pooled sub-sequence is not representable in 16 bits, and
 // the backward's dS = P o (dP - D) cancels heavily on heavy-tailed inputs, so
@@ -41,12 +42,6 @@ __device__ __forceinline__ f16x8 ld_f16x8(const uint16_t* p) {
 }
 __device__ __forceinline__ bf16x8 ld_b16x8(const uint16_t* p) {
     return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p));
-}
-// elements {4g..4g+3} and {16+4g..16+4g+3} of a 32-wide block of a transposed row
-__device__ __forceinline__ u32x4 ld_split_raw(const uint16_t* p) {
-    const u32x2 lo = *reinterpret_cast<const u32x2*>(p);
-    const u32x2 hi = *reinterpret_cast<const u32x2*>(p + 16);
-    return u32x4{lo[0], lo[1], hi[0], hi[1]};
 }
 __device__ __forceinline__ f32x4 mma_h(const f16x8& a, const f16x8& b, const f32x4& c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
@@ -120,7 +115,7 @@ struct Tiles {
 };
 
 __device__ __forceinline__ int swz_row(int r, int slot, int nslot) { return slot ^ (r & (nslot - 1)); }
-__device__ __forceinline__ int swz_t(int r, int slot) { return slot ^ ((r >> 1) & 3); }
+__device__ __forceinline__ int swz_t(int r, int slot) { return slot ^ ((r >> 2) & 3); }
 
 // global [rows][D] (head base `g`, first row r0) -> registers
 template <int D>
@@ -164,12 +159,11 @@ template <int D>
 __device__ __forceinline__ u32x4 frag_row(const uint16_t* lds, int r, int c) {
     return *reinterpret_cast<const u32x4*>(lds + r * D + swz_row(r, c, Tiles<D>::NSLOT) * 8);
 }
-// fragment of transposed tile: row r, elements {4g..4g+3} and {16+4g..16+4g+3}
+// fragment of transposed tile: row r, sequence positions {4g..4g+3} and
+// {16+4g..16+4g+3} of the block, which the split stores as the 16-byte run g
+// (fragment order); one read, conflict-free over the 16 rows of a fragment
 __device__ __forceinline__ u32x4 frag_t(const uint16_t* lds, int r, int g) {
-    const uint16_t* row = lds + r * kBN;
-    const u32x2 lo = *reinterpret_cast<const u32x2*>(row + swz_t(r, g >> 1) * 8 + (g & 1) * 4);
-    const u32x2 hi = *reinterpret_cast<const u32x2*>(row + swz_t(r, 2 + (g >> 1)) * 8 + (g & 1) * 4);
-    return u32x4{lo[0], lo[1], hi[0], hi[1]};
+    return *reinterpret_cast<const u32x4*>(lds + r * kBN + swz_t(r, g) * 8);
 }
 
 // Work item -> (head, 64-row tile).  When H is a multiple of 8, the workgroups
@@ -269,30 +263,33 @@ __global__ void __launch_bounds__(256) k_attn_fwd(AttnK a) {
                     }
                 }
             }
+            // key kb + 16u + 4g + r is visible to query myq iff 16u + r <= myq - kb - 4g
+            const int vis = (int)(myq - kb) - 4 * lg;
             float mx = -INFINITY;
 #pragma unroll
             for (int u = 0; u < 2; ++u)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const int64_t key = kb + 16 * u + 4 * lg + r;
                     float x = sc[u][r] * c2;
-                    x = key > myq ? -INFINITY : x;
+                    x = 16 * u + r > vis ? -INFINITY : x;
                     sc[u][r] = x;
                     mx = fmaxf(mx, x);
                 }
-            mx = fmaxf(mx, shfl_xor_f(mx, 16));
-            mx = fmaxf(mx, shfl_xor_f(mx, 32));
+            mx = rows4_max(mx);
             const float mnew = fmaxf(m, mx);
-            const float alpha = exp2f(m - mnew);
-            m = mnew;
-            lsum *= alpha;
+            // rescale only when some row maximum grew (alpha is exactly 1 otherwise)
+            if (__ballot(mnew > m) != 0) {
+                const float alpha = fast_exp2(m - mnew);
+                lsum *= alpha;
 #pragma unroll
-            for (int v = 0; v < NV; ++v) o[v] *= alpha;
+                for (int v = 0; v < NV; ++v) o[v] *= alpha;
+            }
+            m = mnew;
 #pragma unroll
             for (int u = 0; u < 2; ++u)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const float pr = exp2f(sc[u][r] - m);
+                    const float pr = fast_exp2(sc[u][r] - m);
                     lsum += pr;
                     sc[u][r] = pr;
                 }
@@ -309,8 +306,7 @@ __global__ void __launch_bounds__(256) k_attn_fwd(AttnK a) {
         if (b + 1 < nblk) store(buf ^ 1);
         __syncthreads();
     }
-    lsum += shfl_xor_f(lsum, 16);
-    lsum += shfl_xor_f(lsum, 32);
+    lsum = rows4_sum(lsum);
     const float mul = mv / lsum;
     // o[v][r] holds O^T[16v + 4g + r][myq]
     if (a.o) {
@@ -462,9 +458,9 @@ __global__ void __launch_bounds__(256) k_attn_dkdv(AttnK a) {
                 const f32x4 d4 = *reinterpret_cast<const f32x4*>(Dv + qq);
 #pragma unroll
                 for (int r2 = 0; r2 < 4; ++r2) {
-                    const int64_t q = qq + r2;
-                    float pr = exp2f(s[r2] * cS - l4[r2]);
-                    pr = (q >= mykey && q < a.rows) ? pr : 0.f;
+                    const int q = (int)qq + r2;
+                    float pr = fast_exp2(s[r2] * cS - l4[r2]);
+                    pr = (q >= (int)mykey && q < (int)a.rows) ? pr : 0.f;
                     P[u][r2] = pr;
                     dS[u][r2] = pr * (dp[r2] * cP - d4[r2]);
                 }
@@ -633,9 +629,9 @@ __global__ void __launch_bounds__(256) k_attn_dq(AttnK a) {
                 }
 #pragma unroll
                 for (int r2 = 0; r2 < 4; ++r2) {
-                    const int64_t key = kb + 16 * u + 4 * lg + r2;
-                    float pr = exp2f(s[r2] * cS - l2);
-                    pr = key <= myq ? pr : 0.f;
+                    const int key = (int)kb + 16 * u + 4 * lg + r2;
+                    float pr = fast_exp2(s[r2] * cS - l2);
+                    pr = key <= (int)myq ? pr : 0.f;
                     dS[u][r2] = pr * (dp[r2] * cP - Dq) * down;
                 }
             }

@@ -143,4 +143,25 @@ __device__ __forceinline__ float xor_lane(float v) {
     return __int_as_float(r);
 }
 
+// Max / sum over the four 16-lane rows of a wave (lanes l, l^16, l^32, l^48),
+// with the gfx950 row-swap permutes: permlane16_swap(v, v) yields the values of
+// lanes l & ~16 and l | 16, permlane32_swap(v, v) those of l & ~32 and l | 32.
+// Every lane receives the result; the pairing is the same on all lanes.
+__device__ __forceinline__ float rows4_max(float v) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float rows4_sum(float v) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+// 2^x with the hardware instruction (no denormal rescaling: results below the
+// normal range flush to zero, which softmax weights tolerate).
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
 }  // namespace lh

@@ -49,6 +49,15 @@ __device__ __forceinline__ float down_scale(float mx) {
 // One 64x64 tile of head h: x = src * down (down = power-of-two scale of the
 // head); writes fp16 hi/lo rows, and a transposed copy as fp16 hi/lo (scaled)
 // or bf16 hi/lo (unscaled).  Rows >= `rows` are written as zeros.
+//
+// Transposed copies are [H][d][Sp] with the sequence positions of each aligned
+// block of 32 stored in MFMA-fragment order: position 16h + 4g + e (h < 2,
+// g < 4, e < 4) sits at 8g + 4h + e, so the 8 positions {4g..4g+3, 16+4g..
+// 16+4g+3} that lane group g of a 16x16x32 MFMA supplies are one 16-byte run.
+__device__ __forceinline__ int frag_order(int r) {
+    const int k = r & 31;
+    return (r & ~31) | (((k >> 2) & 3) << 3) | ((k >> 4) << 2) | (k & 3);
+}
 struct SplitArgs {
     const void* src;
     int64_t ld, hs, rows, Sp;
@@ -111,8 +120,8 @@ __global__ void __launch_bounds__(256) k_split(SplitArgs a) {
                     hb = h16(xs);
                     lb = h16(xs - f16f(hb));
                 }
-                th[cc + e][r] = hb;
-                tl[cc + e][r] = lb;
+                th[cc + e][frag_order(r)] = hb;
+                tl[cc + e][frag_order(r)] = lb;
             }
         }
     }
