@@ -154,6 +154,38 @@ __device__ __forceinline__ void store_t(uint16_t* lds, const u32x4 (&reg)[Tiles<
         *reinterpret_cast<u32x4*>(lds + c * 8) = reg[i];
     }
 }
+// Direct global -> LDS copies of the same tiles (no staging registers): thread
+// c fetches the 16-byte chunk that fetch_row / fetch_t would give it, and the
+// load writes it at wave base + 16 * lane, i.e. at chunk c of the LDS tile.
+// The data is in LDS once the issuing wave's vmcnt has drained.
+#define LH_LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
+template <int D>
+__device__ __forceinline__ void dma_row(const uint16_t* g, int64_t r0, uint16_t* lds) {
+    constexpr int NSLOT = Tiles<D>::NSLOT;
+    const int wbase = threadIdx.x & ~63;
+#pragma unroll
+    for (int i = 0; i < Tiles<D>::CH_ROW; ++i) {
+        const int c = threadIdx.x + 256 * i;
+        const int r = c / NSLOT, slot = c % NSLOT;
+        __builtin_amdgcn_global_load_lds(g + (r0 + r) * D + swz_row(r, slot, NSLOT) * 8,
+                                         LH_LDS_PTR(lds + (256 * i + wbase) * 8), 16, 0, 0);
+    }
+}
+template <int D>
+__device__ __forceinline__ void dma_t(const uint16_t* g, int64_t Sp, int64_t c0, uint16_t* lds) {
+    const int wbase = threadIdx.x & ~63;
+#pragma unroll
+    for (int i = 0; i < Tiles<D>::CH_T; ++i) {
+        const int c = threadIdx.x + 256 * i;
+        const int r = c / 4, slot = c % 4;
+        __builtin_amdgcn_global_load_lds(g + (int64_t)r * Sp + c0 + swz_t(r, slot) * 8,
+                                         LH_LDS_PTR(lds + (256 * i + wbase) * 8), 16, 0, 0);
+    }
+}
+// wait until this wave's outstanding vector-memory operations (its tile
+// copies and loads) have completed (gfx9 s_waitcnt: vmcnt 0, others unchanged)
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 // fragment of row tile: row r, global 16-byte chunk c
 template <int D>
 __device__ __forceinline__ u32x4 frag_row(const uint16_t* lds, int r, int c) {
@@ -337,9 +369,14 @@ __global__ void __launch_bounds__(256) k_attn_dkdv(AttnK a) {
     using T = Tiles<D>;
     constexpr int NS = D / 32, NV = D / 16;
     constexpr int NA = SPLIT ? 2 : 1;
-    // stage: q rows, dO rows, q^T (bf16), dO^T
-    constexpr int STAGE = NA * (2 * T::ROW + 2 * T::TR);
-    __shared__ __attribute__((aligned(16))) uint16_t sm[2 * STAGE];
+    // LDS, one buffer each: q and dO rows (read by the score phase), q^T (bf16)
+    // and dO^T (read by the gradient phase); each group is refilled as soon as
+    // every wave is past its phase: 64 KiB at d = 128 with split operands
+    constexpr int ROWS = NA * 2 * T::ROW;
+    __shared__ __attribute__((aligned(16))) uint16_t sm[ROWS + NA * 2 * T::TR];
+    // per-query lse2 and D of the block, copied with the rows: the score phase
+    // then waits on no global load issued after the transposed-tile copies
+    __shared__ __attribute__((aligned(16))) float qstat[2 * kBN];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int lq = lane & 15, lg = lane >> 4;
     const int64_t Sp = a.Sp;
@@ -373,67 +410,52 @@ __global__ void __launch_bounds__(256) k_attn_dkdv(AttnK a) {
 
     const int64_t qfirst = (int64_t)kt * 64;              // first query that can see the workgroup's keys
     const int nblk = (int)((a.rows - qfirst + kBN - 1) / kBN);
-    u32x4 rA[4][T::CH_ROW];   // q h/l, dO h/l rows
-    u32x4 rB[4][T::CH_T];     // q^T h/l (bf16), dO^T h/l
-    auto fetchA = [&](int b) {
+    // layout: [qh][ql?][doh][dol?] rows, then [qTh][qTl?][doTh][doTl?]
+    auto loadA = [&](int b) {
         const int64_t qb = qfirst + (int64_t)b * kBN;
-        fetch_row<D>(a.qh + hb, qb, rA[0]);
-        fetch_row<D>(a.doh + hb, qb, rA[2]);
+        if (wave == 0) {   // lanes 0..31: lse2, lanes 32..63: D (qb + 32 <= Sp)
+            const float* src = (lane < kBN ? lse2 : Dv) + qb + (lane & (kBN - 1));
+            __builtin_amdgcn_global_load_lds(src, LH_LDS_PTR(qstat), 4, 0, 0);
+        }
+        dma_row<D>(a.qh + hb, qb, sm);
+        dma_row<D>(a.doh + hb, qb, sm + NA * T::ROW);
         if constexpr (SPLIT) {
-            fetch_row<D>(a.ql + hb, qb, rA[1]);
-            fetch_row<D>(a.dol + hb, qb, rA[3]);
+            dma_row<D>(a.ql + hb, qb, sm + T::ROW);
+            dma_row<D>(a.dol + hb, qb, sm + 3 * T::ROW);
         }
     };
-    auto fetchB = [&](int b) {
+    auto loadB = [&](int b) {
         const int64_t qb = qfirst + (int64_t)b * kBN;
-        fetch_t<D>(a.qTbh + hb, Sp, qb, rB[0]);
-        fetch_t<D>(a.doTh + hb, Sp, qb, rB[2]);
+        uint16_t* base = sm + ROWS;
+        dma_t<D>(a.qTbh + hb, Sp, qb, base);
+        dma_t<D>(a.doTh + hb, Sp, qb, base + NA * T::TR);
         if constexpr (SPLIT) {
-            fetch_t<D>(a.qTbl + hb, Sp, qb, rB[1]);
-            fetch_t<D>(a.doTl + hb, Sp, qb, rB[3]);
-        }
-    };
-    // stage layout: [qh][ql?][doh][dol?] rows, then [qTh][qTl?][doTh][doTl?]
-    auto storeA = [&](int buf) {
-        uint16_t* base = sm + buf * STAGE;
-        store_row<D>(base, rA[0]);
-        store_row<D>(base + NA * T::ROW, rA[2]);
-        if constexpr (SPLIT) {
-            store_row<D>(base + T::ROW, rA[1]);
-            store_row<D>(base + 3 * T::ROW, rA[3]);
-        }
-    };
-    auto storeB = [&](int buf) {
-        uint16_t* base = sm + buf * STAGE + NA * 2 * T::ROW;
-        store_t<D>(base, rB[0]);
-        store_t<D>(base + NA * T::TR, rB[2]);
-        if constexpr (SPLIT) {
-            store_t<D>(base + T::TR, rB[1]);
-            store_t<D>(base + 3 * T::TR, rB[3]);
+            dma_t<D>(a.qTbl + hb, Sp, qb, base + T::TR);
+            dma_t<D>(a.doTl + hb, Sp, qb, base + 3 * T::TR);
         }
     };
     if (nblk > 0) {
-        fetchA(0);
-        fetchB(0);
-        storeA(0);
-        storeB(0);
+        loadA(0);
+        loadB(0);
     }
+    wait_vmem();
     __syncthreads();
+    const uint16_t* Qh = sm;
+    const uint16_t* Ql = sm + T::ROW;
+    const uint16_t* Oh = sm + NA * T::ROW;
+    const uint16_t* Ol = Oh + T::ROW;
+    const uint16_t* QTh = sm + ROWS;
+    const uint16_t* QTl = QTh + T::TR;
+    const uint16_t* OTh = QTh + NA * T::TR;
+    const uint16_t* OTl = OTh + T::TR;
+    // Per block: the score phase reads the rows while this block's transposed
+    // tiles may still be arriving; the barrier after it publishes them and frees
+    // the rows, which are refilled during the gradient phase; the second barrier
+    // publishes the rows and frees the transposed tiles for the next block.
     for (int b = 0; b < nblk; ++b) {
-        const int buf = b & 1;
         const bool more = b + 1 < nblk;
-        if (more) fetchA(b + 1);
         const int64_t qb = qfirst + (int64_t)b * kBN;
         const bool active = qb + kBN > k0;   // some query of the block sees some key of the wave
-        const uint16_t* base = sm + buf * STAGE;
-        const uint16_t* Qh = base;
-        const uint16_t* Ql = base + T::ROW;
-        const uint16_t* Oh = base + NA * T::ROW;
-        const uint16_t* Ol = Oh + T::ROW;
-        const uint16_t* QTh = base + NA * 2 * T::ROW;
-        const uint16_t* QTl = QTh + T::TR;
-        const uint16_t* OTh = QTh + NA * T::TR;
-        const uint16_t* OTl = OTh + T::TR;
         f32x4 P[2], dS[2];
         if (active) {
 #pragma unroll
@@ -454,8 +476,8 @@ __global__ void __launch_bounds__(256) k_attn_dkdv(AttnK a) {
                     }
                 }
                 const int64_t qq = qb + 16 * u + 4 * lg;
-                const f32x4 l4 = *reinterpret_cast<const f32x4*>(lse2 + qq);
-                const f32x4 d4 = *reinterpret_cast<const f32x4*>(Dv + qq);
+                const f32x4 l4 = *reinterpret_cast<const f32x4*>(qstat + 16 * u + 4 * lg);
+                const f32x4 d4 = *reinterpret_cast<const f32x4*>(qstat + kBN + 16 * u + 4 * lg);
 #pragma unroll
                 for (int r2 = 0; r2 < 4; ++r2) {
                     const int q = (int)qq + r2;
@@ -466,10 +488,9 @@ __global__ void __launch_bounds__(256) k_attn_dkdv(AttnK a) {
                 }
             }
         }
-        if (more) {
-            storeA(buf ^ 1);
-            fetchB(b + 1);
-        }
+        wait_vmem();
+        __syncthreads();
+        if (more) loadA(b + 1);
         if (active) {
             f16x8 ph, pl;
             split_h(P[0], P[1], ph, pl);
@@ -490,8 +511,9 @@ __global__ void __launch_bounds__(256) k_attn_dkdv(AttnK a) {
                 }
             }
         }
-        if (more) storeB(buf ^ 1);
+        wait_vmem();
         __syncthreads();
+        if (more) loadB(b + 1);
     }
     // dk[v][r], dv[v][r] hold the gradients of key mykey at d-index 16v + 4g + r
     if (mykey < a.rows) {
@@ -524,9 +546,13 @@ __global__ void __launch_bounds__(256) k_attn_dq(AttnK a) {
     using T = Tiles<D>;
     constexpr int NS = D / 32, NV = D / 16;
     constexpr int NA = SPLIT ? 2 : 1;
-    // stage: k rows, v rows, k^T
-    constexpr int STAGE = NA * (2 * T::ROW + T::TR);
-    __shared__ __attribute__((aligned(16))) uint16_t sm[2 * STAGE];
+    // LDS: one buffer of k and v rows (read by the score phase, refilled after
+    // the first barrier of a block) and two buffers of k^T (read by the dQ phase,
+    // the next block's copy written into the other one meanwhile): 64 KiB at
+    // d = 128 with split operands, two workgroups per CU
+    constexpr int ROWS = NA * 2 * T::ROW;
+    constexpr int KT = NA * T::TR;
+    __shared__ __attribute__((aligned(16))) uint16_t sm[ROWS + 2 * KT];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int lq = lane & 15, lg = lane >> 4;
     const int64_t Sp = a.Sp;
@@ -576,23 +602,22 @@ __global__ void __launch_bounds__(256) k_attn_dq(AttnK a) {
         fetch_t<D>(a.kTh + hb, Sp, kb, rB[0]);
         if constexpr (SPLIT) fetch_t<D>(a.kTl + hb, Sp, kb, rB[1]);
     };
-    auto storeA = [&](int buf) {
-        uint16_t* base = sm + buf * STAGE;
-        store_row<D>(base, rA[0]);
-        store_row<D>(base + NA * T::ROW, rA[2]);
+    auto storeA = [&]() {
+        store_row<D>(sm, rA[0]);
+        store_row<D>(sm + NA * T::ROW, rA[2]);
         if constexpr (SPLIT) {
-            store_row<D>(base + T::ROW, rA[1]);
-            store_row<D>(base + 3 * T::ROW, rA[3]);
+            store_row<D>(sm + T::ROW, rA[1]);
+            store_row<D>(sm + 3 * T::ROW, rA[3]);
         }
     };
     auto storeB = [&](int buf) {
-        uint16_t* base = sm + buf * STAGE + NA * 2 * T::ROW;
+        uint16_t* base = sm + ROWS + buf * KT;
         store_t<D>(base, rB[0]);
         if constexpr (SPLIT) store_t<D>(base + T::TR, rB[1]);
     };
     fetchA(0);
     fetchB(0);
-    storeA(0);
+    storeA();
     storeB(0);
     __syncthreads();
     for (int b = 0; b < nblk; ++b) {
@@ -601,12 +626,11 @@ __global__ void __launch_bounds__(256) k_attn_dq(AttnK a) {
         if (more) fetchA(b + 1);
         const int64_t kb = (int64_t)b * kBN;
         const bool active = kb < q0 + 16;
-        const uint16_t* base = sm + buf * STAGE;
-        const uint16_t* Kh = base;
-        const uint16_t* Kl = base + T::ROW;
-        const uint16_t* Vh = base + NA * T::ROW;
+        const uint16_t* Kh = sm;
+        const uint16_t* Kl = sm + T::ROW;
+        const uint16_t* Vh = sm + NA * T::ROW;
         const uint16_t* Vl = Vh + T::ROW;
-        const uint16_t* KTh = base + NA * 2 * T::ROW;
+        const uint16_t* KTh = sm + ROWS + buf * KT;
         const uint16_t* KTl = KTh + T::TR;
         f32x4 dS[2];
         if (active) {
@@ -636,8 +660,10 @@ __global__ void __launch_bounds__(256) k_attn_dq(AttnK a) {
                 }
             }
         }
+        // every wave is done with this block's rows: refill them
+        __syncthreads();
         if (more) {
-            storeA(buf ^ 1);
+            storeA();
             fetchB(b + 1);
         }
         if (active) {
@@ -651,6 +677,7 @@ __global__ void __launch_bounds__(256) k_attn_dq(AttnK a) {
                 if constexpr (SPLIT) dq[v] = mma_h(__builtin_bit_cast(f16x8, frag_t(KTl, 16 * v + lq, lg)), sh, dq[v]);
             }
         }
+        // k^T buffer buf ^ 1 was last read by block b - 1, before the barrier above
         if (more) storeB(buf ^ 1);
         __syncthreads();
     }
