@@ -222,8 +222,10 @@ __global__ void __launch_bounds__(256) k_attn_fwd(AttnK a) {
     using T = Tiles<D>;
     constexpr int NS = D / 32, NV = D / 16;
     constexpr int NA = SPLIT ? 2 : 1;
-    constexpr int STAGE = NA * (T::ROW + T::TR);
-    __shared__ __attribute__((aligned(16))) uint16_t sm[2 * STAGE];
+    // K rows (read by the score phase) and V^T (read by the P V phase): one LDS
+    // buffer each, refilled by direct copies while the other one is in use
+    constexpr int KR = NA * T::ROW;
+    __shared__ __attribute__((aligned(16))) uint16_t sm[KR + NA * T::TR];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int lq = lane & 15, lg = lane >> 4;
     const int64_t Sp = a.Sp;
@@ -249,38 +251,33 @@ __global__ void __launch_bounds__(256) k_attn_fwd(AttnK a) {
     float m = -INFINITY, lsum = 0.f;
 
     const int nblk = (int)(((int64_t)qt * 64 + 64) / kBN);
-    u32x4 rkh[T::CH_ROW], rkl[T::CH_ROW], rvh[T::CH_T], rvl[T::CH_T];
-    auto fetch = [&](int b) {
+    const uint16_t* Kh = sm;
+    const uint16_t* Kl = sm + T::ROW;
+    const uint16_t* Vh = sm + KR;
+    const uint16_t* Vl = Vh + T::TR;
+    auto loadK = [&](int b) {
         const int64_t kb = (int64_t)b * kBN;
-        fetch_row<D>(a.kh + hb, kb, rkh);
-        fetch_t<D>(a.vTh + hb, Sp, kb, rvh);
-        if constexpr (SPLIT) {
-            fetch_row<D>(a.kl + hb, kb, rkl);
-            fetch_t<D>(a.vTl + hb, Sp, kb, rvl);
-        }
+        dma_row<D>(a.kh + hb, kb, sm);
+        if constexpr (SPLIT) dma_row<D>(a.kl + hb, kb, sm + T::ROW);
     };
-    auto store = [&](int buf) {
-        uint16_t* base = sm + buf * STAGE;
-        store_row<D>(base, rkh);
-        store_t<D>(base + NA * T::ROW, rvh);
-        if constexpr (SPLIT) {
-            store_row<D>(base + T::ROW, rkl);
-            store_t<D>(base + NA * T::ROW + T::TR, rvl);
-        }
+    auto loadV = [&](int b) {
+        const int64_t kb = (int64_t)b * kBN;
+        dma_t<D>(a.vTh + hb, Sp, kb, sm + KR);
+        if constexpr (SPLIT) dma_t<D>(a.vTl + hb, Sp, kb, sm + KR + T::TR);
     };
-    fetch(0);
-    store(0);
+    loadK(0);
+    loadV(0);
+    wait_vmem();
     __syncthreads();
+    // Per block: scores and softmax from K while this block's V^T may still be
+    // arriving; the barrier publishes V^T and frees K, which is refilled during
+    // the P V phase; the second barrier publishes K and frees V^T.
     for (int b = 0; b < nblk; ++b) {
-        const int buf = b & 1;
-        if (b + 1 < nblk) fetch(b + 1);
+        const bool more = b + 1 < nblk;
         const int64_t kb = (int64_t)b * kBN;
-        if (kb < q0 + 16) {
-            const uint16_t* Kh = sm + buf * STAGE;
-            const uint16_t* Kl = Kh + T::ROW;
-            const uint16_t* Vh = Kh + NA * T::ROW;
-            const uint16_t* Vl = Vh + T::TR;
-            f32x4 sc[2];
+        const bool active = kb < q0 + 16;
+        f32x4 sc[2];
+        if (active) {
 #pragma unroll
             for (int u = 0; u < 2; ++u) {
                 sc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -325,6 +322,11 @@ __global__ void __launch_bounds__(256) k_attn_fwd(AttnK a) {
                     lsum += pr;
                     sc[u][r] = pr;
                 }
+        }
+        wait_vmem();
+        __syncthreads();
+        if (more) loadK(b + 1);
+        if (active) {
             f16x8 ph, pl;
             split_h(sc[0], sc[1], ph, pl);
 #pragma unroll
@@ -335,8 +337,9 @@ __global__ void __launch_bounds__(256) k_attn_fwd(AttnK a) {
                 if constexpr (SPLIT) o[v] = mma_h(__builtin_bit_cast(f16x8, frag_t(Vl, 16 * v + lq, lg)), ph, o[v]);
             }
         }
-        if (b + 1 < nblk) store(buf ^ 1);
+        wait_vmem();
         __syncthreads();
+        if (more) loadV(b + 1);
     }
     lsum = rows4_sum(lsum);
     const float mul = mv / lsum;
@@ -546,13 +549,11 @@ __global__ void __launch_bounds__(256) k_attn_dq(AttnK a) {
     using T = Tiles<D>;
     constexpr int NS = D / 32, NV = D / 16;
     constexpr int NA = SPLIT ? 2 : 1;
-    // LDS: one buffer of k and v rows (read by the score phase, refilled after
-    // the first barrier of a block) and two buffers of k^T (read by the dQ phase,
-    // the next block's copy written into the other one meanwhile): 64 KiB at
-    // d = 128 with split operands, two workgroups per CU
+    // LDS: k and v rows (read by the score phase) and k^T (read by the dQ
+    // phase), one buffer each, refilled by direct copies while the other one is
+    // in use: 48 KiB at d = 128 with split operands
     constexpr int ROWS = NA * 2 * T::ROW;
-    constexpr int KT = NA * T::TR;
-    __shared__ __attribute__((aligned(16))) uint16_t sm[ROWS + 2 * KT];
+    __shared__ __attribute__((aligned(16))) uint16_t sm[ROWS + NA * T::TR];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int lq = lane & 15, lg = lane >> 4;
     const int64_t Sp = a.Sp;
@@ -586,52 +587,37 @@ __global__ void __launch_bounds__(256) k_attn_dq(AttnK a) {
     for (int v = 0; v < NV; ++v) dq[v] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     const int nblk = (int)(((int64_t)qt * 64 + 64) / kBN);
-    u32x4 rA[4][T::CH_ROW];   // k h/l, v h/l rows
-    u32x4 rB[2][T::CH_T];     // k^T h/l
-    auto fetchA = [&](int b) {
+    auto loadA = [&](int b) {
         const int64_t kb = (int64_t)b * kBN;
-        fetch_row<D>(a.kh + hb, kb, rA[0]);
-        fetch_row<D>(a.vh + hb, kb, rA[2]);
+        dma_row<D>(a.kh + hb, kb, sm);
+        dma_row<D>(a.vh + hb, kb, sm + NA * T::ROW);
         if constexpr (SPLIT) {
-            fetch_row<D>(a.kl + hb, kb, rA[1]);
-            fetch_row<D>(a.vl + hb, kb, rA[3]);
+            dma_row<D>(a.kl + hb, kb, sm + T::ROW);
+            dma_row<D>(a.vl + hb, kb, sm + 3 * T::ROW);
         }
     };
-    auto fetchB = [&](int b) {
+    auto loadB = [&](int b) {
         const int64_t kb = (int64_t)b * kBN;
-        fetch_t<D>(a.kTh + hb, Sp, kb, rB[0]);
-        if constexpr (SPLIT) fetch_t<D>(a.kTl + hb, Sp, kb, rB[1]);
+        dma_t<D>(a.kTh + hb, Sp, kb, sm + ROWS);
+        if constexpr (SPLIT) dma_t<D>(a.kTl + hb, Sp, kb, sm + ROWS + T::TR);
     };
-    auto storeA = [&]() {
-        store_row<D>(sm, rA[0]);
-        store_row<D>(sm + NA * T::ROW, rA[2]);
-        if constexpr (SPLIT) {
-            store_row<D>(sm + T::ROW, rA[1]);
-            store_row<D>(sm + 3 * T::ROW, rA[3]);
-        }
-    };
-    auto storeB = [&](int buf) {
-        uint16_t* base = sm + ROWS + buf * KT;
-        store_t<D>(base, rB[0]);
-        if constexpr (SPLIT) store_t<D>(base + T::TR, rB[1]);
-    };
-    fetchA(0);
-    fetchB(0);
-    storeA();
-    storeB(0);
+    loadA(0);
+    loadB(0);
+    wait_vmem();
     __syncthreads();
+    const uint16_t* Kh = sm;
+    const uint16_t* Kl = sm + T::ROW;
+    const uint16_t* Vh = sm + NA * T::ROW;
+    const uint16_t* Vl = Vh + T::ROW;
+    const uint16_t* KTh = sm + ROWS;
+    const uint16_t* KTl = KTh + T::TR;
+    // Per block: scores from the rows while this block's k^T may still be
+    // arriving; the barrier publishes k^T and frees the rows, refilled during the
+    // dQ phase; the second barrier publishes the rows and frees k^T.
     for (int b = 0; b < nblk; ++b) {
-        const int buf = b & 1;
         const bool more = b + 1 < nblk;
-        if (more) fetchA(b + 1);
         const int64_t kb = (int64_t)b * kBN;
         const bool active = kb < q0 + 16;
-        const uint16_t* Kh = sm;
-        const uint16_t* Kl = sm + T::ROW;
-        const uint16_t* Vh = sm + NA * T::ROW;
-        const uint16_t* Vl = Vh + T::ROW;
-        const uint16_t* KTh = sm + ROWS + buf * KT;
-        const uint16_t* KTl = KTh + T::TR;
         f32x4 dS[2];
         if (active) {
 #pragma unroll
@@ -660,12 +646,9 @@ __global__ void __launch_bounds__(256) k_attn_dq(AttnK a) {
                 }
             }
         }
-        // every wave is done with this block's rows: refill them
+        wait_vmem();
         __syncthreads();
-        if (more) {
-            storeA();
-            fetchB(b + 1);
-        }
+        if (more) loadA(b + 1);
         if (active) {
             f16x8 sh, sl;
             split_h(dS[0], dS[1], sh, sl);
@@ -677,9 +660,9 @@ __global__ void __launch_bounds__(256) k_attn_dq(AttnK a) {
                 if constexpr (SPLIT) dq[v] = mma_h(__builtin_bit_cast(f16x8, frag_t(KTl, 16 * v + lq, lg)), sh, dq[v]);
             }
         }
-        // k^T buffer buf ^ 1 was last read by block b - 1, before the barrier above
-        if (more) storeB(buf ^ 1);
+        wait_vmem();
         __syncthreads();
+        if (more) loadB(b + 1);
     }
     if (myq < a.rows) {
         const float mul = a.scale * mk / down;
