@@ -34,6 +34,10 @@ struct PoolScoreArgs {
 #ifndef LH_POOL_U
 #define LH_POOL_U 1
 #endif
+// Tokens per load batch of the bf16 scatter adjoint (one tensor streamed).
+#ifndef LH_SCATTER_U
+#define LH_SCATTER_U 4
+#endif
 
 template <int DT, int G>
 __global__ void __launch_bounds__(256) k_pool_score(PoolScoreArgs a) {
@@ -516,7 +520,8 @@ __global__ void __launch_bounds__(256) k_scatter_bwd(ScatterBwdArgs a) {
     constexpr int d = G * 8;
     const int tid = threadIdx.x;
     const int c = tid % G;
-    const int h = blockIdx.y * a.HG + tid / G;
+    const int hl = tid / G;
+    const int h = blockIdx.y * a.HG + hl;
     const int64_t tb = (int64_t)blockIdx.x * a.tok;
     const int64_t te = tb + a.tok;
     const int32_t* st = a.start + (int64_t)h * a.S;
@@ -527,27 +532,81 @@ __global__ void __launch_bounds__(256) k_scatter_bwd(ScatterBwdArgs a) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) s[e] = 0.f;
     const int64_t H = a.H;
-    constexpr int U = 8;
-    for (int64_t t0 = tb; t0 < te; t0 += U) {
-        float x[U][8];
+    // token t's row of dO joins the running sum of its entry; an entry is
+    // flushed when the next one starts
+    auto add_token = [&](int64_t t, const float (&x)[8]) {
+        if (t >= nxt) {
+            flush_entry<DT, G, MODE>(a, h, c, slot, beg >= tb && nxt <= te, s);
 #pragma unroll
-        for (int u = 0; u < U; ++u)
-            if (t0 + u < te) load8_nt<DT>(a.dout, ((t0 + u) * H + h) * d + c * 8, x[u]);
+            for (int e = 0; e < 8; ++e) s[e] = 0.f;
+            ++slot;
+            beg = nxt;
+            nxt = slot + 1 < a.S ? st[slot + 1] : a.N;
+        }
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int64_t t = t0 + u;
-            if (t < te) {
-                if (t >= nxt) {
-                    flush_entry<DT, G, MODE>(a, h, c, slot, beg >= tb && nxt <= te, s);
+        for (int e = 0; e < 8; ++e) s[e] += x[e];
+    };
+    if constexpr (DT == 0) {
+        // bf16: buffer loads over this workgroup's chunk (a lane offset and a
+        // uniform offset per token), batches of UB tokens double-buffered: the
+        // loads of batch b+1 are in flight while batch b is summed
+        constexpr int UB = LH_SCATTER_U;
+        const int64_t base0 = (tb * H + (int64_t)blockIdx.y * a.HG) * d;
+        const uint32_t chunk_bytes = (uint32_t)((((int64_t)a.tok - 1) * H + a.HG) * d * 2);
+        const uint32_t tstride = (uint32_t)(H * d * 2);
+        const uint32_t lane_off = (uint32_t)((hl * d + c * 8) * 2);
+        const auto R = make_rsrc(reinterpret_cast<const uint16_t*>(a.dout) + base0, chunk_bytes);
+        auto issue = [&](u32x4* r, int i0, auto Uc) {
+            constexpr int U = decltype(Uc)::value;
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) s[e] = 0.f;
-                    ++slot;
-                    beg = nxt;
-                    nxt = slot + 1 < a.S ? st[slot + 1] : a.N;
-                }
+            for (int u = 0; u < U; ++u) r[u] = buf_ld16_nt(R, lane_off, (uint32_t)(i0 + u) * tstride);
+        };
+        auto consume_batch = [&](const u32x4* r, int i0, auto Uc) {
+            constexpr int U = decltype(Uc)::value;
 #pragma unroll
-                for (int e = 0; e < 8; ++e) s[e] += x[u][e];
+            for (int u = 0; u < U; ++u) {
+                float x[8];
+                unpack8(r[u], x);
+                add_token(tb + i0 + u, x);
             }
+        };
+        using UBc = std::integral_constant<int, UB>;
+        const int iters = a.tok;
+        const int nb = iters / UB;
+        u32x4 ra[UB], rb[UB];
+        // (no branch between a prefetch and the consume after it, so the waits stay exact)
+        if (nb > 0) issue(ra, 0, UBc{});
+        int b = 0;
+        for (; b + 2 < nb; b += 2) {
+            issue(rb, (b + 1) * UB, UBc{});
+            __builtin_amdgcn_sched_barrier(0);
+            consume_batch(ra, b * UB, UBc{});
+            issue(ra, (b + 2) * UB, UBc{});
+            __builtin_amdgcn_sched_barrier(0);
+            consume_batch(rb, (b + 1) * UB, UBc{});
+        }
+        if (b + 1 < nb) {
+            issue(rb, (b + 1) * UB, UBc{});
+            __builtin_amdgcn_sched_barrier(0);
+            consume_batch(ra, b * UB, UBc{});
+            consume_batch(rb, (b + 1) * UB, UBc{});
+        } else if (b < nb) {
+            consume_batch(ra, b * UB, UBc{});
+        }
+        for (int i = nb * UB; i < iters; ++i) {
+            issue(ra, i, std::integral_constant<int, 1>{});
+            consume_batch(ra, i, std::integral_constant<int, 1>{});
+        }
+    } else {
+        constexpr int U = 8;
+        for (int64_t t0 = tb; t0 < te; t0 += U) {
+            float x[U][8];
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                if (t0 + u < te) load8_nt<DT>(a.dout, ((t0 + u) * H + h) * d + c * 8, x[u]);
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                if (t0 + u < te) add_token(t0 + u, x[u]);
         }
     }
     flush_entry<DT, G, MODE>(a, h, c, slot, beg >= tb && nxt <= te, s);

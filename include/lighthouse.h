@@ -128,9 +128,9 @@ int lh_dense_attn_bwd(const void* q, const void* k, const void* v, const void* o
 /* Per-stage timing with HIP events recorded on the caller's stream around
  * each kernel of lh_forward/lh_backward.  enable != 0 starts recording (and
  * clears earlier results); lh_stage_timing_read synchronises on the recorded
- * events, adds each stage's elapsed milliseconds into ms[stage] and its
- * launch count into count[stage] for stage < n, and returns the number of
- * stages.  lh_stage_name gives a stage's kernel name. */
+ * events, adds each stage's elapsed milliseconds into ms[stage] and the
+ * number of times the stage ran into count[stage] for stage < n, and returns
+ * the number of stages.  lh_stage_name gives a stage's name. */
 int lh_stage_timing(int enable);
 int lh_stage_timing_read(double* ms, int* count, int n);
 const char* lh_stage_name(int stage);
