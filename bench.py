@@ -73,6 +73,35 @@ def measured_traffic(workload, stage):
     return rec["fetch_bytes"] + rec["write_bytes"]
 
 
+def achievable_peaks(lh, torch, stream):
+    """What plain in-repo kernels reach on this GPU (lh_peak_probe): 2 GiB read, write and
+    copy streams, and a register-only bf16 MFMA loop.  Reported beside the vendor peaks."""
+    nbytes = 2 << 30
+    src = torch.empty(nbytes // 4, dtype=torch.int32, device="cuda")
+    dst = torch.empty_like(src)
+    acc = torch.zeros(4 * max(nbytes >> 20, 1024), dtype=torch.int32, device="cuda")   # per-workgroup folds
+    src.fill_(1)
+    iters = 10000
+    mfma_flops = 4096 * iters * 4 * 32768
+    out = {}
+    for kind, name, moved in ((0, "read_GBs", nbytes), (1, "write_GBs", nbytes), (2, "copy_GBs", 2 * nbytes),
+                              (3, "mfma_bf16_TFLOPs", mfma_flops)):
+        a = src if kind in (0, 2) else None
+        b = acc if kind in (0, 3) else dst
+        n = iters if kind == 3 else nbytes
+        lh.peak_probe(kind, a, b, n, stream)            # warm-up
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev[0].record(stream)
+        for _ in range(5):
+            lh.peak_probe(kind, a, b, n, stream)
+        ev[1].record(stream)
+        torch.cuda.synchronize()
+        sec = ev[0].elapsed_time(ev[1]) / 5 / 1e3
+        out[name] = round(moved / sec / (1e12 if kind == 3 else 1e9), 1)
+    del src, dst, acc
+    return out
+
+
 def cpu_baseline(w, x, heads):
     """The oracle (fwd+bwd) on the first `heads` heads of the same inputs, scaled to all heads."""
     import numpy as np
@@ -200,6 +229,9 @@ def main():
         roof = {"bound": "mfma", "kernel": dominant, "achieved": round(ach, 2), "peak": BF16_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(ach / BF16_PEAK_TFLOPS, 4),
                 "traffic": measured_traffic(w["name"], dominant), "avg_launch_ms": round(dom_ms, 4)}
+
+    roof["achievable"] = achievable_peaks(lh, torch, stream)
+    log(f"achievable on this GPU: {roof['achievable']}")
 
     dense = None
     if not args.no_dense and w["dtype"] == "bf16" and N % 64 == 0:

@@ -6,4 +6,4 @@ fallback implementation.
 """
 from ._lib import *  # noqa: F401,F403
 from ._lib import (EXPORTS, LIB_PATH, LighthouseError, alloc_workspace, backward, dense_backward,  # noqa: F401
-                   dense_forward, dtype_code, forward, workspace_tensor)
+                   dense_forward, dtype_code, forward, peak_probe, read_selection, workspace_tensor)

@@ -21,7 +21,7 @@ VIEWS = {"scores": 0, "sel_start": 1, "sel_level": 2, "qsub": 3, "ksub": 4, "vsu
 
 EXPORTS = ("lh_subseq_len", "lh_workspace_bytes", "lh_forward", "lh_backward", "lh_workspace_view",
            "lh_dense_workspace_bytes", "lh_dense_attn_fwd", "lh_dense_attn_bwd", "lh_stage_timing",
-           "lh_stage_timing_read", "lh_stage_name", "lh_status_str")
+           "lh_stage_timing_read", "lh_stage_name", "lh_status_str", "lh_read_selection", "lh_peak_probe")
 
 
 class LighthouseError(RuntimeError):
@@ -39,6 +39,8 @@ def _load():
         "lh_forward": (i, [vp, vp, vp, vp, i, i, i, i, i, i, i, vp, sz, vp]),
         "lh_backward": (i, [vp, vp, vp, vp, i, i, i, i, i, i, i, i, vp, sz, vp]),
         "lh_workspace_view": (i, [vp, i, i, i, i, i, i, i, i, C.POINTER(vp), C.POINTER(sz)]),
+        "lh_read_selection": (i, [vp, i, i, i, i, i, i, i, vp, vp, vp]),
+        "lh_peak_probe": (i, [i, vp, vp, sz, vp]),
         "lh_dense_workspace_bytes": (sz, [i, i, i, i]),
         "lh_dense_attn_fwd": (i, [vp, vp, vp, vp, vp, i, i, i, i, vp, sz, vp]),
         "lh_dense_attn_bwd": (i, [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, vp, sz, vp]),
@@ -65,6 +67,8 @@ lh_dense_workspace_bytes = _L.lh_dense_workspace_bytes
 lh_dense_attn_fwd = _L.lh_dense_attn_fwd
 lh_dense_attn_bwd = _L.lh_dense_attn_bwd
 lh_stage_timing = _L.lh_stage_timing
+lh_read_selection = _L.lh_read_selection
+lh_peak_probe = _L.lh_peak_probe
 
 
 def lh_status_str(rc: int) -> str:
@@ -187,6 +191,27 @@ def workspace_tensor(ws, N, H, d, p, L, K, dtype, view):
     if name == "block_first":
         return raw.view(torch.int32).view(H, -1)
     raise LighthouseError(f"unknown view {view}")
+
+
+def read_selection(ws, N, H, d, p, L, K, dtype, stream=None):
+    """Copies of the kept entries' (start int32 [H][S], level uint8 [H][S])."""
+    torch = _torch()
+    S = int(lh_subseq_len(N, p, L, K))
+    if S < 0:
+        raise LighthouseError("invalid layer parameters")
+    start = torch.empty((H, S), dtype=torch.int32, device=ws.device)
+    level = torch.empty((H, S), dtype=torch.uint8, device=ws.device)
+    rc = lh_read_selection(ws.data_ptr(), N, H, d, p, L, K, dtype, start.data_ptr(), level.data_ptr(),
+                           _stream_handle(stream))
+    _check(rc, "lh_read_selection")
+    return start, level
+
+
+def peak_probe(kind, src, dst, n, stream=None):
+    """Enqueue one achievable-peak probe (see lh_peak_probe); src/dst are device tensors."""
+    rc = lh_peak_probe(kind, src.data_ptr() if src is not None else None, dst.data_ptr(), n,
+                       _stream_handle(stream))
+    _check(rc, "lh_peak_probe")
 
 
 def dense_forward(q, k, v, ws=None, out=None, lse=None, stream=None):

@@ -29,6 +29,7 @@ SOURCES = {
     # work on them with VALU ops, which cannot read AGPRs
     "lh_attn.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
     "lh_prep.hip": [],
+    "lh_probe.hip": [],
     "lh_api.cpp": ["-x", "hip"],
 }
 

@@ -331,6 +331,34 @@ int lh_workspace_view(void* ws, int N, int H, int d, int p, int L, int K, int dt
     return LH_OK;
 }
 
+int lh_read_selection(const void* ws, int N, int H, int d, int p, int L, int K, int dtype, int32_t* start,
+                      uint8_t* level, void* stream) {
+    Plan P;
+    int rc = make_plan(N, H, d, p, L, K, dtype, &P);
+    if (rc) return rc;
+    if (!ws || (!start && !level)) return LH_ERR_ARG;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    const char* w = reinterpret_cast<const char*>(ws);
+    const size_t n = (size_t)H * P.S;
+    if (start && hipMemcpyAsync(start, w + P.off_start, n * sizeof(int32_t), hipMemcpyDeviceToDevice, s) != hipSuccess)
+        return LH_ERR_HIP;
+    if (level && hipMemcpyAsync(level, w + P.off_level, n, hipMemcpyDeviceToDevice, s) != hipSuccess)
+        return LH_ERR_HIP;
+    return LH_OK;
+}
+
+int lh_peak_probe(int kind, const void* src, void* dst, size_t n, void* stream) {
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    if (!dst || n == 0) return LH_ERR_ARG;
+    if (kind >= 0 && kind <= 2) {
+        if (n % 16 != 0 || (kind != 1 && !src)) return LH_ERR_ARG;
+        if ((reinterpret_cast<uintptr_t>(dst) | reinterpret_cast<uintptr_t>(src)) % 16 != 0) return LH_ERR_ARG;
+    } else if (kind != 3 || n > (1u << 30)) {
+        return LH_ERR_ARG;
+    }
+    return launch_peak_probe(kind, src, dst, n, s) == hipSuccess ? LH_OK : LH_ERR_HIP;
+}
+
 // ------------------------------------------------------------ dense path
 static int dense_check(int N, int H, int d, int dtype) {
     if (dtype != BF16) return LH_ERR_DTYPE;

@@ -278,19 +278,37 @@ __global__ void __launch_bounds__(256) k_attn_fwd(AttnK a) {
         const bool active = kb < q0 + 16;
         f32x4 sc[2];
         if (active) {
+            // one accumulator per (key tile u, d step st), so consecutive MFMAs are
+            // independent (a 16x16x32 MFMA chain needs many in flight); the partial
+            // sums are added at the end
+            f32x4 part[2][NS];
+            f16x8 kfr[2][NS], klr[2][NS];
+#pragma unroll
+            for (int st = 0; st < NS; ++st)
+#pragma unroll
+                for (int u = 0; u < 2; ++u) {
+                    kfr[u][st] = __builtin_bit_cast(f16x8, frag_row<D>(Kh, 16 * u + lq, 4 * st + lg));
+                    if constexpr (SPLIT) klr[u][st] = __builtin_bit_cast(f16x8, frag_row<D>(Kl, 16 * u + lq, 4 * st + lg));
+                }
+#pragma unroll
+            for (int st = 0; st < NS; ++st)
+#pragma unroll
+                for (int u = 0; u < 2; ++u) part[u][st] = mma_h(kfr[u][st], qfh[st], f32x4{0.f, 0.f, 0.f, 0.f});
+            if constexpr (SPLIT) {
+#pragma unroll
+                for (int st = 0; st < NS; ++st)
+#pragma unroll
+                    for (int u = 0; u < 2; ++u) part[u][st] = mma_h(kfr[u][st], qfl[st], part[u][st]);
+#pragma unroll
+                for (int st = 0; st < NS; ++st)
+#pragma unroll
+                    for (int u = 0; u < 2; ++u) part[u][st] = mma_h(klr[u][st], qfh[st], part[u][st]);
+            }
 #pragma unroll
             for (int u = 0; u < 2; ++u) {
-                sc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
-                const int r = 16 * u + lq;
+                sc[u] = part[u][0];
 #pragma unroll
-                for (int st = 0; st < NS; ++st) {
-                    const f16x8 kh = __builtin_bit_cast(f16x8, frag_row<D>(Kh, r, 4 * st + lg));
-                    sc[u] = mma_h(kh, qfh[st], sc[u]);
-                    if constexpr (SPLIT) {
-                        sc[u] = mma_h(kh, qfl[st], sc[u]);
-                        sc[u] = mma_h(__builtin_bit_cast(f16x8, frag_row<D>(Kl, r, 4 * st + lg)), qfh[st], sc[u]);
-                    }
-                }
+                for (int st = 1; st < NS; ++st) sc[u] += part[u][st];
             }
             // key kb + 16u + 4g + r is visible to query myq iff 16u + r <= myq - kb - 4g
             const int vis = (int)(myq - kb) - 4 * lg;

@@ -122,4 +122,7 @@ hipError_t launch_split(const SplitSpec& sp, hipStream_t s);
 hipError_t launch_clear_slot(unsigned int* hmax, int H, int slot, hipStream_t s);
 hipError_t launch_row_prep(const RowPrepSpec& sp, hipStream_t s);
 
+// Achievable-peak probes (kind 0 read, 1 write, 2 copy, 3 bf16 MFMA loop).
+hipError_t launch_peak_probe(int kind, const void* src, void* dst, size_t n, hipStream_t s);
+
 }  // namespace lh

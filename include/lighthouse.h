@@ -112,6 +112,29 @@ typedef enum {
 int lh_workspace_view(void* ws, int N, int H, int d, int p, int L, int K, int dtype,
                       int view, void** ptr, size_t* bytes);
 
+/* Copy the kept entries' descriptors out of a workspace that lh_forward
+ * filled: start (int32 [H][S], first token of each entry of the causal
+ * sub-sequence, strictly increasing per head) and level (uint8 [H][S],
+ * pyramid level; the entry covers p^level tokens) -- the partition of
+ * [0, N) selected in stage (ii) and ordered in stage (iii) (Sec. 3, Fig. 2).
+ * start and level are device pointers owned by the caller (either may be
+ * NULL, not both); the copies are enqueued on `stream`.  Parameters must be
+ * those of the forward call.  Returns LH_OK, LH_ERR_ARG/SHAPE/DTYPE for bad
+ * arguments (nothing enqueued), or LH_ERR_HIP. */
+int lh_read_selection(const void* ws, int N, int H, int d, int p, int L, int K, int dtype,
+                      int32_t* start, uint8_t* level, void* stream);
+
+/* Achievable-peak probes (not part of the layer), reported beside the vendor
+ * peaks.  kind 0 reads n bytes at src in 1 MiB chunks and stores the XOR fold
+ * of each chunk's 16-byte words to dst[16c .. 16c+15] (dst: ceil(n / 2^20) * 16
+ * bytes); kind 1 writes n bytes at dst; kind 2 copies n bytes from src to dst
+ * (these three use 16-byte non-temporal accesses; n a multiple of 16, pointers
+ * 16-byte aligned); kind 3 runs n rounds (n <= 2^30) of 4 independent bf16
+ * 32x32x16 MFMAs in each of 4096 wavefronts (4096 * n * 4 * 32768 flops) and
+ * stores a checksum per workgroup of 4 wavefronts (dst: 1024 * 16 bytes).  Device
+ * pointers; enqueued on `stream`.  Returns LH_OK, LH_ERR_ARG, or LH_ERR_HIP. */
+int lh_peak_probe(int kind, const void* src, void* dst, size_t n, void* stream);
+
 /* Dense causal attention over all N tokens with the same attention kernels
  * (the comparison path of the benchmark).  lse is fp32 [H][N] (natural log);
  * N must be a multiple of 64; bf16 only.  Workspace: lh_dense_workspace_bytes.

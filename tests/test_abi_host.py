@@ -75,6 +75,16 @@ def test_entry_points_validate_before_launching():
     assert lh.lh_dense_workspace_bytes(1024, 2, 64, 1) == 0          # dense path is bf16
     assert lh.lh_dense_attn_fwd(fake, fake, fake, fake, fake, 1000, 2, 64, 0, aligned_ws, 1 << 30, None) \
         == lh.LH_ERR_SHAPE
+    assert lh.lh_read_selection(None, N, H, d, p, L, K, 1, fake, fake, None) == lh.LH_ERR_ARG
+    assert lh.lh_read_selection(aligned_ws, N, H, d, p, L, K, 1, None, None, None) == lh.LH_ERR_ARG
+    assert lh.lh_read_selection(aligned_ws, 2047, H, d, p, L, K, 1, fake, fake, None) == lh.LH_ERR_SHAPE
+    assert lh.lh_read_selection(aligned_ws, N, H, d, p, L, K, 7, fake, fake, None) == lh.LH_ERR_DTYPE
+    assert lh.lh_peak_probe(4, fake, fake, 1 << 20, None) == lh.LH_ERR_ARG        # unknown kind
+    assert lh.lh_peak_probe(0, fake, fake, 17, None) == lh.LH_ERR_ARG             # not a multiple of 16
+    assert lh.lh_peak_probe(0, None, fake, 1 << 20, None) == lh.LH_ERR_ARG        # read needs a source
+    assert lh.lh_peak_probe(2, fake + 4, fake, 1 << 20, None) == lh.LH_ERR_ARG    # misaligned
+    assert lh.lh_peak_probe(1, None, None, 1 << 20, None) == lh.LH_ERR_ARG
+    assert lh.lh_peak_probe(3, None, fake, (1 << 30) + 1, None) == lh.LH_ERR_ARG
 
 
 def test_workspace_views_are_inside_the_workspace():
