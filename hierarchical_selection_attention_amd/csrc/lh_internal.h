@@ -10,7 +10,7 @@
 namespace lh {
 
 constexpr int kMaxLevels = 24;
-constexpr int kMaxK = 2048;        // largest K the top-K network sorts (when K < #candidates)
+constexpr int kMaxK = 2048;        // largest K accepted when K < #candidates (a validation limit)
 constexpr int kRowPad = 64;        // sub-sequence rows are padded to a multiple of this
 constexpr int kChunkTokMax = 256;  // tokens per workgroup in the pooling/scoring pass
 constexpr int kChunkScoreMax = 8192;  // tokens*heads of leaf scores kept in LDS per workgroup

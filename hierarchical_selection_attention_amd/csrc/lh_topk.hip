@@ -4,21 +4,19 @@
 // From the top level down, the candidates of a level are scored by 64-bit
 // keys (fp32 score bits << 32 | ~index): scores are >= +0 so the bit pattern
 // orders them, and the complemented index makes equal scores rank the lower
-// index first; keys are unique, so the selected set does not depend on how the
-// network orders ties.  The K largest keys are found with a chunked bitonic
-// network in LDS: each chunk of up to 2048 keys is sorted descending, merged
-// into the running top-K list (elementwise max against the reversed chunk
-// head, then a bitonic merge).  Selected entries are replaced by their p
-// children, the others are kept; finally every kept entry gets its slot in
-// the position-ordered sub-sequence from entry counts (bottom-up) and prefix
-// offsets (top-down).
+// index first; keys are unique, so the K selected candidates are exactly those
+// whose key is at least the K-th largest key.  That key is found by an
+// MSB-first radix selection (eight 8-bit digits, a 256-bin LDS histogram per
+// digit) -- the set an argsort would select, without sorting.  Selected
+// entries are replaced by their p children, the others are kept; finally
+// every kept entry gets its slot in the position-ordered sub-sequence from
+// entry counts (bottom-up) and prefix offsets (top-down).
 #include "lh_device.h"
 #include "lh_internal.h"
 
 namespace lh {
 
 constexpr int kTopkThreads = 1024;
-constexpr int kChunk = 2048;
 
 struct TopkArgs {
     const float* lev[kMaxLevels];   // scores of level l: [H][n_l]
@@ -37,39 +35,73 @@ __device__ __forceinline__ uint64_t make_key(float s, int32_t idx) {
     return ((uint64_t)__float_as_uint(s) << 32) | (uint64_t)(uint32_t)(~idx);
 }
 
-// Sort n (power of two) keys in LDS descending.
-__device__ void bitonic_sort_desc(uint64_t* b, int n) {
-    for (int k = 2; k <= n; k <<= 1) {
-        for (int j = k >> 1; j > 0; j >>= 1) {
-            for (int i = threadIdx.x; i < n / 2; i += blockDim.x) {
-                const int lo = 2 * i - (i & (j - 1));
-                const int hi = lo + j;
-                const bool desc = (lo & k) == 0;
-                const uint64_t x = b[lo], y = b[hi];
-                if (desc ? (x < y) : (x > y)) {
-                    b[lo] = y;
-                    b[hi] = x;
-                }
-            }
-            __syncthreads();
+// The k-th largest (1 <= k <= nc) of the unique keys of candidates idx[0..nc)
+// of level scores sc.  Each pass fixes one 8-bit digit, from the most
+// significant: among the keys that match the digits fixed so far, a histogram
+// of the next digit is counted, and wavefront 0 walks it from the top to the
+// bin that holds the k-th largest, which becomes the next digit of the answer.
+// When that bin holds a single key, one more pass reads the key itself.
+__device__ uint64_t kth_largest_key(const float* sc, const int32_t* idx, int64_t nc, int64_t k, int32_t* hist,
+                                    int64_t* bcast) {
+    const int tid = threadIdx.x, lane = tid & 63;
+    uint64_t pre = 0, mask = 0;
+    int64_t krem = k;   // rank of the answer among the keys that match `pre`
+    for (int shift = 56; shift >= 0; shift -= 8) {
+        for (int i = tid; i < 256; i += blockDim.x) hist[i] = 0;
+        __syncthreads();
+        for (int64_t i = tid; i < nc; i += blockDim.x) {
+            const int32_t j = idx[i];
+            const uint64_t key = make_key(sc[j], j);
+            if ((key & mask) == pre) atomicAdd(&hist[(key >> shift) & 0xFF], 1);
         }
-    }
-}
-
-// Sort a bitonic sequence of n (power of two) keys descending.
-__device__ void bitonic_merge_desc(uint64_t* b, int n) {
-    for (int j = n >> 1; j > 0; j >>= 1) {
-        for (int i = threadIdx.x; i < n / 2; i += blockDim.x) {
-            const int lo = 2 * i - (i & (j - 1));
-            const int hi = lo + j;
-            const uint64_t x = b[lo], y = b[hi];
-            if (x < y) {
-                b[lo] = y;
-                b[hi] = x;
+        __syncthreads();
+        if (tid < 64) {
+            // lane l holds bins 255-4l .. 252-4l (descending); x = keys in bins >= its lowest
+            int c[4], sum = 0;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                c[q] = hist[255 - 4 * lane - q];
+                sum += c[q];
+            }
+            int x = sum;
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1) {
+                const int y = __shfl_up(x, off, 64);
+                if (lane >= off) x += y;
+            }
+            int64_t acc = x - sum;   // keys in bins above this lane's
+            if (acc < krem && x >= krem) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    if (acc + c[q] >= krem) {
+                        bcast[0] = 255 - 4 * lane - q;
+                        bcast[1] = krem - acc;
+                        bcast[2] = c[q];
+                        break;
+                    }
+                    acc += c[q];
+                }
             }
         }
         __syncthreads();
+        pre |= (uint64_t)bcast[0] << shift;
+        mask |= (uint64_t)0xFF << shift;
+        krem = bcast[1];
+        const bool unique = bcast[2] == 1;   // one key left with this prefix: it is the answer
+        __syncthreads();                     // bcast is rewritten below
+        if (unique) {
+            for (int64_t i = tid; i < nc; i += blockDim.x) {
+                const int32_t j = idx[i];
+                const uint64_t key = make_key(sc[j], j);
+                if ((key & mask) == pre) bcast[3] = (int64_t)key;
+            }
+            __syncthreads();
+            const uint64_t key = (uint64_t)bcast[3];
+            __syncthreads();
+            return key;
+        }
     }
+    return pre;
 }
 
 // Exclusive prefix sum of in[0..n) into out[0..n); returns the total.
@@ -105,8 +137,8 @@ __device__ int64_t block_scan_excl(const int32_t* in, int32_t* out, int64_t n, i
 }
 
 __global__ void __launch_bounds__(kTopkThreads) k_topk(TopkArgs a) {
-    __shared__ uint64_t chunk[kChunk];
-    __shared__ uint64_t top[kMaxK];
+    __shared__ int32_t hist[256];
+    __shared__ int64_t bcast[4];
     __shared__ int32_t wsum[kTopkThreads / 64 + 1];
     const int h = blockIdx.x;
     const int tid = threadIdx.x;
@@ -130,33 +162,7 @@ __global__ void __launch_bounds__(kTopkThreads) k_topk(TopkArgs a) {
             const int32_t all = nc <= K ? 1 : 0;
             for (int64_t i = tid; i < nc; i += blockDim.x) flag[i] = all;
         } else {
-            int KP = 1;
-            while (KP < K) KP <<= 1;
-            for (int i = tid; i < KP; i += blockDim.x) top[i] = 0;
-            __syncthreads();
-            for (int64_t c0 = 0; c0 < nc; c0 += kChunk) {
-                const int cnt = (int)((nc - c0) < kChunk ? (nc - c0) : kChunk);
-                int NP = 1;
-                while (NP < cnt) NP <<= 1;
-                if (NP < KP) NP = KP;
-                for (int i = tid; i < NP; i += blockDim.x) {
-                    uint64_t key = 0;
-                    if (i < cnt) {
-                        const int32_t j = idx[c0 + i];
-                        key = make_key(sc[j], j);
-                    }
-                    chunk[i] = key;
-                }
-                __syncthreads();
-                bitonic_sort_desc(chunk, NP);
-                for (int i = tid; i < KP; i += blockDim.x) {
-                    const uint64_t x = top[i], y = chunk[KP - 1 - i];
-                    top[i] = x > y ? x : y;
-                }
-                __syncthreads();
-                bitonic_merge_desc(top, KP);
-            }
-            const uint64_t tau = top[K - 1];
+            const uint64_t tau = kth_largest_key(sc, idx, nc, K, hist, bcast);
             for (int64_t i = tid; i < nc; i += blockDim.x) {
                 const int32_t j = idx[i];
                 flag[i] = make_key(sc[j], j) >= tau ? 1 : 0;
