@@ -101,8 +101,8 @@ struct AttnK {
 // Streamed operands move through double-buffered LDS in blocks of kBN
 // sequence positions, shared by the 4 wavefronts of a workgroup.  Row tiles
 // hold kBN rows of d elements; transposed tiles hold d rows of kBN elements.
-// 16-byte slots are XOR-swizzled by row so the 16 rows a fragment read
-// touches fall into different banks.
+// 16-byte slots are XOR-swizzled by row so a fragment read is free of LDS
+// bank conflicts.
 constexpr int kBN = 32;
 
 template <int D>
@@ -115,7 +115,11 @@ struct Tiles {
 };
 
 __device__ __forceinline__ int swz_row(int r, int slot, int nslot) { return slot ^ (r & (nslot - 1)); }
-__device__ __forceinline__ int swz_t(int r, int slot) { return slot ^ ((r >> 2) & 3); }
+// Transposed tiles have 64-byte rows (4 slots).  A ds_read_b128 of rows
+// r0..r0+15 (r0 a multiple of 16) at one slot per 16-lane group runs at the
+// full 256 B/clk on gfx950 with this XOR (measured; (r >> 2) & 3 and no
+// swizzle both run at half rate).
+__device__ __forceinline__ int swz_t(int r, int slot) { return slot ^ ((r >> 1) & 3); }
 
 // global [rows][D] (head base `g`, first row r0) -> registers
 template <int D>
