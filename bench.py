@@ -44,9 +44,9 @@ def stage_bytes(w, S):
     sub32 = S * H * d * 4
     return {
         "pool_score": 3 * row + nscore + pool_m,      # read q, k, v; write scores and level-m means
-        "scatter_fwd": row + sub32,                   # write o; read O~ once
+        "scatter_fwd": row + S * H * d * e,           # write o; read the rows of O~ once
         "scatter_bwd": row + sub32,                   # read dO; write dO~ once
-        "pool_bwd": 3 * row + 3 * sub32,              # write dq, dk, dv; read dQ~, dK~, dV~ once
+        "pool_bwd": 3 * row + 3 * S * H * d * e,      # write dq, dk, dv; read their sub-sequence rows once
     }
 
 

@@ -106,6 +106,9 @@ int make_plan(int N, int H, int d, int p, int L, int K, int dtype, Plan* P) {
     pl.off_dq = take(sizeof(float) * HSd);
     pl.off_dk = take(sizeof(float) * HSd);
     pl.off_dv = take(sizeof(float) * HSd);
+    pl.rowcopy = dtype == BF16;
+    pl.off_otab = take(pl.rowcopy ? 2 * HSd : 0);
+    pl.off_gtab = take(pl.rowcopy ? 3 * 2 * HSd : 0);
     pl.total = off;
     return LH_OK;
 }
@@ -255,8 +258,19 @@ int lh_forward(const void* q, const void* k, const void* v, void* o, int N, int 
         return e;
     }));
     AttnArgs a = sub_attn_args(P, w);
+    if (P.rowcopy) {
+        // O~ also leaves the attention as bf16 rows, rounded as the scatter rounds them
+        a.o_bf16 = u16m(w, P.off_otab);
+        a.ld_o = d;
+        a.hs_o = P.Sp * d;
+    }
     LH_TRY(stage(ST_ATTN_FWD, s, [&] { return launch_attn_fwd(a, s); }));
-    LH_TRY(stage(ST_SCATTER_FWD, s, [&] { return launch_scatter_fwd(P, w, o, s); }));
+    LH_TRY(stage(ST_SCATTER_FWD, s, [&] {
+        if (!P.rowcopy) return launch_scatter_fwd(P, w, o, s);
+        const uint16_t* tab[1] = {u16(w, P.off_otab)};
+        void* out[1] = {o};
+        return launch_row_copy(P, w, tab, out, 1, s);
+    }));
     return LH_OK;
 }
 
@@ -289,9 +303,23 @@ int lh_backward(const void* dout, void* dq, void* dk, void* dv, int N, int H, in
         return e;
     }));
     AttnArgs a = sub_attn_args(P, w);
+    const size_t HSd2 = 2 * HSd;
+    if (P.rowcopy) {
+        // the gradients also leave the attention as the pool adjoint's bf16 rows
+        a.tq = u16m(w, P.off_gtab);
+        a.tk = u16m(w, P.off_gtab + HSd2);
+        a.tv = u16m(w, P.off_gtab + 2 * HSd2);
+        a.level = reinterpret_cast<const uint8_t*>(w + P.off_level);
+        a.p = p;
+    }
     LH_TRY(stage(ST_ATTN_BWD_DKDV, s, [&] { return launch_attn_bwd(a, s, 0); }));
     if (dtype == BF16) LH_TRY(stage(ST_ATTN_BWD_DQ, s, [&] { return launch_attn_bwd(a, s, 1); }));
-    LH_TRY(stage(ST_POOL_BWD, s, [&] { return launch_pool_bwd(P, w, dq, dk, dv, s); }));
+    LH_TRY(stage(ST_POOL_BWD, s, [&] {
+        if (!P.rowcopy) return launch_pool_bwd(P, w, dq, dk, dv, s);
+        const uint16_t* tab[3] = {u16(w, P.off_gtab), u16(w, P.off_gtab + HSd2), u16(w, P.off_gtab + 2 * HSd2)};
+        void* out[3] = {dq, dk, dv};
+        return launch_row_copy(P, w, tab, out, 3, s);
+    }));
     return LH_OK;
 }
 

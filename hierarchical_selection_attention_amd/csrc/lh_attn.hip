@@ -91,6 +91,9 @@ struct AttnK {
     const float* rowdown;   // [H][Sp]: power-of-two down-scale of dS rows (dq kernel)
     float *dq, *dk, *dv;    // fp32 [H][Sp][d] gradients, or
     uint16_t *dq_b, *dk_b, *dv_b;   // bf16 gradients with strides ld_o/hs_o
+    uint16_t *tq, *tk, *tv;         // or null: bf16 [H][Sp][d] copies of the fp32 gradients / p^level
+    const uint8_t* level;           // [H][rows]
+    int p;
     int64_t rows, Sp, ld_o, hs_o;
     float scale;            // 1/sqrt(d)
     // fp32 path (double arithmetic)
@@ -200,6 +203,19 @@ __device__ __forceinline__ u32x4 frag_row(const uint16_t* lds, int r, int c) {
 // (fragment order); one read, conflict-free over the 16 rows of a fragment
 __device__ __forceinline__ u32x4 frag_t(const uint16_t* lds, int r, int g) {
     return *reinterpret_cast<const u32x4*>(lds + r * kBN + swz_t(r, g) * 8);
+}
+
+// p^level of row `row` of head h as a float (exact for every level that fits
+// the sub-sequence's rows), for the pool adjoint's division
+__device__ __forceinline__ float level_den(const AttnK& a, int h, int64_t row) {
+    const int lv = a.level[(int64_t)h * a.rows + row];
+    float den = 1.0f;
+    for (int z = 0; z < lv; ++z) den *= (float)a.p;
+    return den;
+}
+// 4 fp32 values / den, rounded to bf16 (round to nearest even)
+__device__ __forceinline__ u32x2 bf16x4_div(const f32x4& x, float den) {
+    return u32x2{pack_bf16x2(x[0] / den, x[1] / den), pack_bf16x2(x[2] / den, x[3] / den)};
 }
 
 // Work item -> (head, 64-row tile).  When H is a multiple of 8, the workgroups
@@ -557,6 +573,14 @@ __global__ void __launch_bounds__(256) k_attn_dkdv(AttnK a) {
                 *reinterpret_cast<f32x4*>(a.dk + base + 16 * v) = dk[v] * a.scale;
                 *reinterpret_cast<f32x4*>(a.dv + base + 16 * v) = dv[v] * mdo;
             }
+            if (a.tk) {
+                const float den = level_den(a, h, mykey);
+#pragma unroll
+                for (int v = 0; v < NV; ++v) {
+                    *reinterpret_cast<u32x2*>(a.tk + base + 16 * v) = bf16x4_div(dk[v] * a.scale, den);
+                    *reinterpret_cast<u32x2*>(a.tv + base + 16 * v) = bf16x4_div(dv[v] * mdo, den);
+                }
+            }
         }
     }
 }
@@ -699,6 +723,12 @@ __global__ void __launch_bounds__(256) k_attn_dq(AttnK a) {
             const int64_t base = hb + myq * D + 4 * lg;
 #pragma unroll
             for (int v = 0; v < NV; ++v) *reinterpret_cast<f32x4*>(a.dq + base + 16 * v) = dq[v] * mul;
+            if (a.tq) {
+                const float den = level_den(a, h, myq);
+#pragma unroll
+                for (int v = 0; v < NV; ++v)
+                    *reinterpret_cast<u32x2*>(a.tq + base + 16 * v) = bf16x4_div(dq[v] * mul, den);
+            }
         }
     }
 }
@@ -818,6 +848,7 @@ static AttnK to_k(const AttnArgs& x) {
     a.lse = x.lse; a.lse2 = x.lse2; a.D = x.D; a.rowdown = x.rowdown;
     a.dq = x.dq; a.dk = x.dk; a.dv = x.dv;
     a.dq_b = x.dq_b; a.dk_b = x.dk_b; a.dv_b = x.dv_b;
+    a.tq = x.tq; a.tk = x.tk; a.tv = x.tv; a.level = x.level; a.p = x.p;
     a.rows = x.rows; a.Sp = x.Sp; a.ld_o = x.ld_o; a.hs_o = x.hs_o;
     a.scale = x.scale;
     a.qf = x.qf; a.kf = x.kf; a.vf = x.vf; a.dof = x.dof;

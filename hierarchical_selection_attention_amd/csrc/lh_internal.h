@@ -28,6 +28,7 @@ struct Plan {
     int N, H, d, p, L, K, dtype, esz;
     int64_t S, Sp;
     int m;                  // pyramid level produced per workgroup by the pooling pass
+    int rowcopy;            // bf16: back-scatter and pool adjoint copy bf16 rows the attention leaves
     int64_t tok;            // p^m tokens per pooling workgroup
     int64_t ntop;           // N / p^(L-1)
     int64_t n[kMaxLevels];  // entries at level l
@@ -53,6 +54,10 @@ struct Plan {
     size_t off_doh, off_dol, off_doTh, off_doTl;   // fp16 copies of dO~
     size_t off_D, off_rowdown;    // fp32 [H][Sp]
     size_t off_dq, off_dk, off_dv;   // fp32 [H][Sp][d]
+    // bf16 path: the rows the back-scatter and the pool adjoint copy out,
+    // already rounded to bf16
+    size_t off_otab;              // bf16 [H][Sp][d]: O~
+    size_t off_gtab;              // bf16 [3][H][Sp][d]: dQ~, dK~, dV~ divided by p^level
     size_t total;
 };
 
@@ -74,6 +79,10 @@ hipError_t launch_scatter_fwd(const Plan& P, char* ws, void* o, hipStream_t s);
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
 hipError_t launch_scatter_bwd(const Plan& P, const void* dout, int mode, char* ws, hipStream_t s);
 hipError_t launch_pool_bwd(const Plan& P, char* ws, void* dq, void* dk, void* dv, hipStream_t s);
+// bf16 path: out[z][t][h] = tab[z][h][slot_h(t)], the back-scatter (Z = 1) and
+// the pool adjoint (Z = 3) from bf16 rows the attention kernels leave
+hipError_t launch_row_copy(const Plan& P, const char* ws, const uint16_t* const* tab, void* const* out, int Z,
+                           hipStream_t s);
 
 // Attention operands: 16-bit copies laid out [H][Sp][d] (rows) and
 // [H][d][Sp] (transposed); lo parts are used when `split`.
@@ -87,6 +96,11 @@ struct AttnArgs {
     const float *D, *rowdown;
     float *dq, *dk, *dv;       // fp32 [H][Sp][d] or null
     uint16_t *dq_b, *dk_b, *dv_b;   // bf16 rows (ld_o, hs_o) or null
+    // with fp32 gradients: bf16 copies [H][Sp][d] of dQ, dK, dV divided by
+    // p^level[h][row] (the pool adjoint's rows), or null
+    uint16_t *tq, *tk, *tv;
+    const uint8_t* level;
+    int p;
     int64_t rows, Sp, ld_o, hs_o;
     int H, d;
     bool split, fp32_path;
