@@ -5,6 +5,7 @@ Usage: python hierarchical_selection_attention_amd/build.py [-v]
 """
 from __future__ import annotations
 
+import ctypes
 import os
 import subprocess
 import sys
@@ -60,6 +61,9 @@ def build(verbose: bool = False) -> str:
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
+    # every symbol must resolve (a kernel whose host stub was not emitted only
+    # shows up here, as an undefined __device_stub__)
+    ctypes.CDLL(tmp, mode=os.RTLD_NOW)
     os.replace(tmp, LIB)
     return LIB
 

@@ -34,6 +34,9 @@ namespace lh {
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+// forward: the softmax reference maximum lags the row maximum by up to this
+// much (log2 units); P then lies in [0, 2^8], still split exactly into fp16 hi/lo
+constexpr float kLazyMax = 8.0f;
 
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 
@@ -189,6 +192,50 @@ __device__ __forceinline__ void dma_t(const uint16_t* g, int64_t Sp, int64_t c0,
                                          LH_LDS_PTR(lds + (256 * i + wbase) * 8), 16, 0, 0);
     }
 }
+// The same copies through a buffer resource over one head's operand: the
+// per-lane byte offsets are computed once (row_voff / t_voff), the block's
+// offset is a scalar, and `wofs` (the wave's byte offset inside a tile,
+// wave * 1024) is uniform.
+template <int D>
+__device__ __forceinline__ void row_voff(uint32_t (&voff)[Tiles<D>::CH_ROW]) {
+    constexpr int NSLOT = Tiles<D>::NSLOT;
+#pragma unroll
+    for (int i = 0; i < Tiles<D>::CH_ROW; ++i) {
+        const int c = threadIdx.x + 256 * i;
+        const int r = c / NSLOT, slot = c % NSLOT;
+        voff[i] = (uint32_t)(r * D + swz_row(r, slot, NSLOT) * 8) * 2u;
+    }
+}
+template <int D>
+__device__ __forceinline__ void t_voff(uint32_t (&voff)[Tiles<D>::CH_T], int64_t Sp) {
+#pragma unroll
+    for (int i = 0; i < Tiles<D>::CH_T; ++i) {
+        const int c = threadIdx.x + 256 * i;
+        const int r = c / 4, slot = c % 4;
+        voff[i] = (uint32_t)((int64_t)r * Sp + swz_t(r, slot) * 8) * 2u;
+    }
+}
+// rows r0 .. r0 + kBN - 1 of a head's [rows][D] operand -> LDS row tile
+template <int D>
+__device__ __forceinline__ void bdma_row(const uint16_t* head, uint32_t bytes, const uint32_t* voff,
+                                         int64_t r0, uint16_t* tile, uint32_t wofs) {
+    const auto rs = make_rsrc(head, bytes);
+#pragma unroll
+    for (int i = 0; i < Tiles<D>::CH_ROW; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, LH_LDS_PTR(reinterpret_cast<char*>(tile) + 4096 * i + wofs), 16,
+                                                 voff[i], (uint32_t)(r0 * D * 2), 0, 0);
+}
+// columns c0 .. c0 + kBN - 1 of a head's [D][Sp] operand -> LDS transposed tile
+template <int D>
+__device__ __forceinline__ void bdma_t(const uint16_t* head, uint32_t bytes, const uint32_t* voff,
+                                       int64_t c0, uint16_t* tile, uint32_t wofs) {
+    const auto rs = make_rsrc(head, bytes);
+#pragma unroll
+    for (int i = 0; i < Tiles<D>::CH_T; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, LH_LDS_PTR(reinterpret_cast<char*>(tile) + 4096 * i + wofs), 16,
+                                                 voff[i], (uint32_t)(c0 * 2), 0, 0);
+}
+
 // wait until this wave's outstanding vector-memory operations (its tile
 // copies and loads) have completed (gfx9 s_waitcnt: vmcnt 0, others unchanged)
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
@@ -275,15 +322,18 @@ __global__ void __launch_bounds__(256) k_attn_fwd(AttnK a) {
     const uint16_t* Kl = sm + T::ROW;
     const uint16_t* Vh = sm + KR;
     const uint16_t* Vl = Vh + T::TR;
+    const uint32_t wofs = __builtin_amdgcn_readfirstlane((uint32_t)wave * 1024u);
+    const uint32_t hbytes = (uint32_t)(Sp * D * 2);
+    uint32_t rvo[T::CH_ROW], tvo[T::CH_T];
+    row_voff<D>(rvo);
+    t_voff<D>(tvo, Sp);
     auto loadK = [&](int b) {
-        const int64_t kb = (int64_t)b * kBN;
-        dma_row<D>(a.kh + hb, kb, sm);
-        if constexpr (SPLIT) dma_row<D>(a.kl + hb, kb, sm + T::ROW);
+        bdma_row<D>(a.kh + hb, hbytes, rvo, (int64_t)b * kBN, sm, wofs);
+        if constexpr (SPLIT) bdma_row<D>(a.kl + hb, hbytes, rvo, (int64_t)b * kBN, sm + T::ROW, wofs);
     };
     auto loadV = [&](int b) {
-        const int64_t kb = (int64_t)b * kBN;
-        dma_t<D>(a.vTh + hb, Sp, kb, sm + KR);
-        if constexpr (SPLIT) dma_t<D>(a.vTl + hb, Sp, kb, sm + KR + T::TR);
+        bdma_t<D>(a.vTh + hb, hbytes, tvo, (int64_t)b * kBN, sm + KR, wofs);
+        if constexpr (SPLIT) bdma_t<D>(a.vTl + hb, hbytes, tvo, (int64_t)b * kBN, sm + KR + T::TR, wofs);
     };
     loadK(0);
     loadV(0);
@@ -330,33 +380,44 @@ __global__ void __launch_bounds__(256) k_attn_fwd(AttnK a) {
 #pragma unroll
                 for (int st = 1; st < NS; ++st) sc[u] += part[u][st];
             }
-            // key kb + 16u + 4g + r is visible to query myq iff 16u + r <= myq - kb - 4g
-            const int vis = (int)(myq - kb) - 4 * lg;
+            // row maximum of the unscaled scores (c2 > 0); only the block that meets
+            // the diagonal needs the causal mask: key kb + 16u + 4g + r is visible to
+            // query myq iff 16u + r <= myq - kb - 4g
             float mx = -INFINITY;
+            if (kb + kBN - 1 > q0) {
+                const int vis = (int)(myq - kb) - 4 * lg;
 #pragma unroll
-            for (int u = 0; u < 2; ++u)
+                for (int u = 0; u < 2; ++u)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    float x = sc[u][r] * c2;
-                    x = 16 * u + r > vis ? -INFINITY : x;
-                    sc[u][r] = x;
-                    mx = fmaxf(mx, x);
-                }
-            mx = rows4_max(mx);
-            const float mnew = fmaxf(m, mx);
-            // rescale only when some row maximum grew (alpha is exactly 1 otherwise)
-            if (__ballot(mnew > m) != 0) {
-                const float alpha = fast_exp2(m - mnew);
+                    for (int r = 0; r < 4; ++r) {
+                        const float x = 16 * u + r > vis ? -INFINITY : sc[u][r];
+                        sc[u][r] = x;
+                        mx = fmaxf(mx, x);
+                    }
+            } else {
+#pragma unroll
+                for (int u = 0; u < 2; ++u)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) mx = fmaxf(mx, sc[u][r]);
+            }
+            mx = rows4_max(mx) * c2;
+            // The reference maximum m moves only when a row maximum exceeds it by
+            // more than kLazyMax (log2 units), so P stays in [0, 2^kLazyMax] and
+            // the rescale of O is rare; alpha is exactly 1 for rows that keep m.
+            const bool grow = mx > m + kLazyMax;
+            if (__ballot(grow) != 0) {
+                const float mnew = grow ? mx : m;
+                const float alpha = grow ? fast_exp2(m - mnew) : 1.0f;
                 lsum *= alpha;
 #pragma unroll
                 for (int v = 0; v < NV; ++v) o[v] *= alpha;
+                m = mnew;
             }
-            m = mnew;
 #pragma unroll
             for (int u = 0; u < 2; ++u)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const float pr = fast_exp2(sc[u][r] - m);
+                    const float pr = fast_exp2(fmaf(sc[u][r], c2, -m));
                     lsum += pr;
                     sc[u][r] = pr;
                 }
