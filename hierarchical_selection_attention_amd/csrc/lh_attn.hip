@@ -360,6 +360,7 @@ __global__ void __launch_bounds__(256) k_attn_fwd(AttnK a) {
                     kfr[u][st] = __builtin_bit_cast(f16x8, frag_row<D>(Kh, 16 * u + lq, 4 * st + lg));
                     if constexpr (SPLIT) klr[u][st] = __builtin_bit_cast(f16x8, frag_row<D>(Kl, 16 * u + lq, 4 * st + lg));
                 }
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int st = 0; st < NS; ++st)
 #pragma unroll
@@ -428,12 +429,22 @@ __global__ void __launch_bounds__(256) k_attn_fwd(AttnK a) {
         if (active) {
             f16x8 ph, pl;
             split_h(sc[0], sc[1], ph, pl);
+            // all V^T fragments first, then the products in passes over v, so the
+            // three MFMAs into one accumulator are NV issues apart
+            f16x8 vfh[NV], vfl[NV];
 #pragma unroll
             for (int v = 0; v < NV; ++v) {
-                const f16x8 vh = __builtin_bit_cast(f16x8, frag_t(Vh, 16 * v + lq, lg));
-                o[v] = mma_h(vh, ph, o[v]);
-                o[v] = mma_h(vh, pl, o[v]);
-                if constexpr (SPLIT) o[v] = mma_h(__builtin_bit_cast(f16x8, frag_t(Vl, 16 * v + lq, lg)), ph, o[v]);
+                vfh[v] = __builtin_bit_cast(f16x8, frag_t(Vh, 16 * v + lq, lg));
+                if constexpr (SPLIT) vfl[v] = __builtin_bit_cast(f16x8, frag_t(Vl, 16 * v + lq, lg));
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int v = 0; v < NV; ++v) o[v] = mma_h(vfh[v], ph, o[v]);
+#pragma unroll
+            for (int v = 0; v < NV; ++v) o[v] = mma_h(vfh[v], pl, o[v]);
+            if constexpr (SPLIT) {
+#pragma unroll
+                for (int v = 0; v < NV; ++v) o[v] = mma_h(vfl[v], ph, o[v]);
             }
         }
         wait_vmem();
