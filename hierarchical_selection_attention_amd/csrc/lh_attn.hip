@@ -740,21 +740,41 @@ __global__ void __launch_bounds__(256) k_attn_dq(AttnK a) {
         if (active) {
 #pragma unroll
             for (int u = 0; u < 2; ++u) {
-                f32x4 s = {0.f, 0.f, 0.f, 0.f}, dp = {0.f, 0.f, 0.f, 0.f};
+                // the key tile's fragments first, then its products in four
+                // independent chains (s and dp, by parity of the d step)
                 const int r = 16 * u + lq;
+                f16x8 kh[NS], kl[NS], vh[NS], vl[NS];
 #pragma unroll
                 for (int st = 0; st < NS; ++st) {
-                    const f16x8 kh = __builtin_bit_cast(f16x8, frag_row<D>(Kh, r, 4 * st + lg));
-                    const f16x8 vh = __builtin_bit_cast(f16x8, frag_row<D>(Vh, r, 4 * st + lg));
-                    s = mma_h(kh, qfh[st], s);
-                    dp = mma_h(vh, dfh[st], dp);
+                    kh[st] = __builtin_bit_cast(f16x8, frag_row<D>(Kh, r, 4 * st + lg));
+                    vh[st] = __builtin_bit_cast(f16x8, frag_row<D>(Vh, r, 4 * st + lg));
                     if constexpr (SPLIT) {
-                        s = mma_h(kh, qfl[st], s);
-                        s = mma_h(__builtin_bit_cast(f16x8, frag_row<D>(Kl, r, 4 * st + lg)), qfh[st], s);
-                        dp = mma_h(vh, dfl[st], dp);
-                        dp = mma_h(__builtin_bit_cast(f16x8, frag_row<D>(Vl, r, 4 * st + lg)), dfh[st], dp);
+                        kl[st] = __builtin_bit_cast(f16x8, frag_row<D>(Kl, r, 4 * st + lg));
+                        vl[st] = __builtin_bit_cast(f16x8, frag_row<D>(Vl, r, 4 * st + lg));
                     }
                 }
+                __builtin_amdgcn_sched_barrier(0);
+                f32x4 s2[2], dp2[2];
+#pragma unroll
+                for (int e = 0; e < 2; ++e) s2[e] = dp2[e] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int st = 0; st < NS; ++st) {
+                    s2[st & 1] = mma_h(kh[st], qfh[st], s2[st & 1]);
+                    dp2[st & 1] = mma_h(vh[st], dfh[st], dp2[st & 1]);
+                }
+                if constexpr (SPLIT) {
+#pragma unroll
+                    for (int st = 0; st < NS; ++st) {
+                        s2[st & 1] = mma_h(kh[st], qfl[st], s2[st & 1]);
+                        dp2[st & 1] = mma_h(vh[st], dfl[st], dp2[st & 1]);
+                    }
+#pragma unroll
+                    for (int st = 0; st < NS; ++st) {
+                        s2[st & 1] = mma_h(kl[st], qfh[st], s2[st & 1]);
+                        dp2[st & 1] = mma_h(vl[st], dfh[st], dp2[st & 1]);
+                    }
+                }
+                const f32x4 s = s2[0] + s2[1], dp = dp2[0] + dp2[1];
 #pragma unroll
                 for (int r2 = 0; r2 < 4; ++r2) {
                     const int key = (int)kb + 16 * u + 4 * lg + r2;
@@ -770,12 +790,22 @@ __global__ void __launch_bounds__(256) k_attn_dq(AttnK a) {
         if (active) {
             f16x8 sh, sl;
             split_h(dS[0], dS[1], sh, sl);
+            // all k^T fragments first, then the products in passes over v, so the
+            // three MFMAs into one accumulator are NV issues apart
+            f16x8 kth[NV], ktl[NV];
 #pragma unroll
             for (int v = 0; v < NV; ++v) {
-                const f16x8 kth = __builtin_bit_cast(f16x8, frag_t(KTh, 16 * v + lq, lg));
-                dq[v] = mma_h(kth, sh, dq[v]);
-                dq[v] = mma_h(kth, sl, dq[v]);
-                if constexpr (SPLIT) dq[v] = mma_h(__builtin_bit_cast(f16x8, frag_t(KTl, 16 * v + lq, lg)), sh, dq[v]);
+                kth[v] = __builtin_bit_cast(f16x8, frag_t(KTh, 16 * v + lq, lg));
+                if constexpr (SPLIT) ktl[v] = __builtin_bit_cast(f16x8, frag_t(KTl, 16 * v + lq, lg));
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int v = 0; v < NV; ++v) dq[v] = mma_h(kth[v], sh, dq[v]);
+#pragma unroll
+            for (int v = 0; v < NV; ++v) dq[v] = mma_h(kth[v], sl, dq[v]);
+            if constexpr (SPLIT) {
+#pragma unroll
+                for (int v = 0; v < NV; ++v) dq[v] = mma_h(ktl[v], sh, dq[v]);
             }
         }
         wait_vmem();
