@@ -118,6 +118,13 @@ __device__ __forceinline__ void store8f(float* base, int64_t elem, const float (
     p[1] = f32x4{x[4], x[5], x[6], x[7]};
 }
 
+// 8 fp32 values with non-temporal stores
+__device__ __forceinline__ void store8f_nt(float* base, int64_t elem, const float (&x)[8]) {
+    f32x4* p = reinterpret_cast<f32x4*>(base + elem);
+    __builtin_nontemporal_store(f32x4{x[0], x[1], x[2], x[3]}, p);
+    __builtin_nontemporal_store(f32x4{x[4], x[5], x[6], x[7]}, p + 1);
+}
+
 // 8 bf16 values packed in 4 dwords -> fp32, exact.
 __device__ __forceinline__ void unpack8(const u32x4& w, float (&x)[8]) {
 #pragma unroll

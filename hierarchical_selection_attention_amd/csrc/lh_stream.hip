@@ -199,9 +199,20 @@ __global__ void __launch_bounds__(256) k_pool_score(PoolScoreArgs a) {
         for (int l = 0; l <= a.m; ++l) {
             const int64_t j0 = t0 / a.pw[l];
             float* out = a.lev[l] + (int64_t)blockIdx.y * HG * a.n[l] + j0;
-            for (int idx = tid; idx < HG * per; idx += blockDim.x) {
-                const int hh = idx / per, j = idx - hh * per;
-                out[(int64_t)hh * a.n[l] + j] = src[idx];
+            // non-temporal stores: nothing reads the scores until the selection,
+            // and cached lines written inside this read stream cost more (16-byte
+            // stores when every head's run is 16-byte aligned)
+            if ((per & 3) == 0 && (a.n[l] & 3) == 0 && (reinterpret_cast<uintptr_t>(out) & 15) == 0) {
+                for (int idx = tid; idx < HG * per / 4; idx += blockDim.x) {
+                    const int i4 = idx * 4, hh = i4 / per, j = i4 - hh * per;
+                    const f32x4 x = *reinterpret_cast<const f32x4*>(src + i4);
+                    __builtin_nontemporal_store(x, reinterpret_cast<f32x4*>(out + (int64_t)hh * a.n[l] + j));
+                }
+            } else {
+                for (int idx = tid; idx < HG * per; idx += blockDim.x) {
+                    const int hh = idx / per, j = idx - hh * per;
+                    __builtin_nontemporal_store(src[idx], out + (int64_t)hh * a.n[l] + j);
+                }
             }
             if (l == a.m) break;
             const int nper = per / a.p;
@@ -231,7 +242,7 @@ __global__ void __launch_bounds__(256) k_pool_score(PoolScoreArgs a) {
                 float o[8];
 #pragma unroll
                 for (int e = 0; e < 8; ++e) o[e] = acc[e] * inv;
-                store8f(dst, (int64_t)h * d + c * 8, o);
+                store8f_nt(dst, (int64_t)h * d + c * 8, o);
             } else {
                 __syncthreads();
 #pragma unroll
@@ -245,7 +256,7 @@ __global__ void __launch_bounds__(256) k_pool_score(PoolScoreArgs a) {
                         for (int z = 0; z < a.mt; ++z) s += red[(z * HG + hl) * d + c * 8 + e];
                         o[e] = s * inv;
                     }
-                    store8f(dst, (int64_t)h * d + c * 8, o);
+                    store8f_nt(dst, (int64_t)h * d + c * 8, o);
                 }
             }
         }
