@@ -457,7 +457,7 @@ __global__ void __launch_bounds__(256) k_attn_fwd(AttnK a) {
     if (a.o) {
         float* O = a.o + hb + myq * D;
 #pragma unroll
-        for (int v = 0; v < NV; ++v) *reinterpret_cast<f32x4*>(O + 16 * v + 4 * lg) = o[v] * mul;
+        for (int v = 0; v < NV; ++v) __builtin_nontemporal_store(o[v] * mul, reinterpret_cast<f32x4*>(O + 16 * v + 4 * lg));
     }
     if (a.o_bf16 && myq < a.rows) {
         uint16_t* O = a.o_bf16 + h * a.hs_o + myq * a.ld_o;
@@ -642,8 +642,8 @@ __global__ void __launch_bounds__(256) k_attn_dkdv(AttnK a) {
             const int64_t base = hb + mykey * D + 4 * lg;
 #pragma unroll
             for (int v = 0; v < NV; ++v) {
-                *reinterpret_cast<f32x4*>(a.dk + base + 16 * v) = dk[v] * a.scale;
-                *reinterpret_cast<f32x4*>(a.dv + base + 16 * v) = dv[v] * mdo;
+                __builtin_nontemporal_store(dk[v] * a.scale, reinterpret_cast<f32x4*>(a.dk + base + 16 * v));
+                __builtin_nontemporal_store(dv[v] * mdo, reinterpret_cast<f32x4*>(a.dv + base + 16 * v));
             }
             if (a.tk) {
                 const float den = level_den(a, h, mykey);
@@ -824,7 +824,7 @@ __global__ void __launch_bounds__(256) k_attn_dq(AttnK a) {
         } else {
             const int64_t base = hb + myq * D + 4 * lg;
 #pragma unroll
-            for (int v = 0; v < NV; ++v) *reinterpret_cast<f32x4*>(a.dq + base + 16 * v) = dq[v] * mul;
+            for (int v = 0; v < NV; ++v) __builtin_nontemporal_store(dq[v] * mul, reinterpret_cast<f32x4*>(a.dq + base + 16 * v));
             if (a.tq) {
                 const float den = level_den(a, h, myq);
 #pragma unroll
