@@ -220,15 +220,15 @@ static AttnArgs sub_attn_args(const Plan& P, char* w) {
 }
 
 // fp16 hi/lo copy of one [H][Sp][d] fp32 tensor (rows and optionally a transposed copy)
-static hipError_t split_sub(const Plan& P, char* w, size_t src, unsigned int* hmax, int slot, size_t rh, size_t rl,
-                            size_t th, size_t tl, int t_bf16, hipStream_t s) {
+static SplitSpec split_spec(const Plan& P, char* w, size_t src, unsigned int* hmax, int slot, size_t rh, size_t rl,
+                            size_t th, size_t tl, int t_bf16) {
     SplitSpec sp{};
     sp.src = w + src; sp.ld = P.d; sp.hs = P.Sp * P.d; sp.rows = P.Sp; sp.Sp = P.Sp;
     sp.d = P.d; sp.H = P.H; sp.src_bf16 = 0;
     sp.hmax = hmax; sp.hscale = f32(w, P.off_hscale); sp.slot = slot;
     sp.rh = u16m(w, rh); sp.rl = u16m(w, rl); sp.th = u16m(w, th); sp.tl = u16m(w, tl);
     sp.t_bf16 = t_bf16;
-    return launch_split(sp, s);
+    return sp;
 }
 
 int lh_forward(const void* q, const void* k, const void* v, void* o, int N, int H, int d, int p, int L,
@@ -249,12 +249,14 @@ int lh_forward(const void* q, const void* k, const void* v, void* o, int N, int 
     LH_TRY(stage(ST_SUB_PREP, s, [&] {
         hipError_t e = launch_fill_zero(hmax, sizeof(uint32_t) * 8 * (size_t)H, s);
         if (e != hipSuccess || dtype != BF16) return e;
-        const size_t src[3] = {P.off_qs, P.off_ks, P.off_vs};
-        for (int t = 0; t < 3 && e == hipSuccess; ++t)
-            e = launch_maxabs(w + src[t], false, P.d, P.Sp * P.d, P.Sp, P.d, H, hmax + t, s);
-        if (e == hipSuccess) e = split_sub(P, w, P.off_qs, hmax, 0, P.off_qh, P.off_ql, P.off_qTbh, P.off_qTbl, 1, s);
-        if (e == hipSuccess) e = split_sub(P, w, P.off_ks, hmax, 1, P.off_kh, P.off_kl, P.off_kTh, P.off_kTl, 0, s);
-        if (e == hipSuccess) e = split_sub(P, w, P.off_vs, hmax, 2, P.off_vh, P.off_vl, P.off_vTh, P.off_vTl, 0, s);
+        const void* src[3] = {w + P.off_qs, w + P.off_ks, w + P.off_vs};
+        unsigned int* out[3] = {hmax, hmax + 1, hmax + 2};
+        e = launch_maxabs(src, out, 3, false, P.d, P.Sp * P.d, P.Sp, P.d, H, s);
+        const SplitSpec sp[3] = {
+            split_spec(P, w, P.off_qs, hmax, 0, P.off_qh, P.off_ql, P.off_qTbh, P.off_qTbl, 1),
+            split_spec(P, w, P.off_ks, hmax, 1, P.off_kh, P.off_kl, P.off_kTh, P.off_kTl, 0),
+            split_spec(P, w, P.off_vs, hmax, 2, P.off_vh, P.off_vl, P.off_vTh, P.off_vTl, 0)};
+        if (e == hipSuccess) e = launch_split(sp, 3, s);
         return e;
     }));
     AttnArgs a = sub_attn_args(P, w);
@@ -298,8 +300,11 @@ int lh_backward(const void* dout, void* dq, void* dk, void* dv, int N, int H, in
         hipError_t e = launch_row_prep(rp, s);
         if (e != hipSuccess || dtype != BF16) return e;
         e = launch_fill_zero(hmax_b, sizeof(uint32_t) * 4 * (size_t)H, s);
-        if (e == hipSuccess) e = launch_maxabs(w + P.off_dos, false, P.d, P.Sp * P.d, P.Sp, P.d, H, hmax_b + 3, s);
-        if (e == hipSuccess) e = split_sub(P, w, P.off_dos, hmax_b, 3, P.off_doh, P.off_dol, P.off_doTh, P.off_doTl, 0, s);
+        const void* src[1] = {w + P.off_dos};
+        unsigned int* out[1] = {hmax_b + 3};
+        if (e == hipSuccess) e = launch_maxabs(src, out, 1, false, P.d, P.Sp * P.d, P.Sp, P.d, H, s);
+        const SplitSpec sp = split_spec(P, w, P.off_dos, hmax_b, 3, P.off_doh, P.off_dol, P.off_doTh, P.off_doTl, 0);
+        if (e == hipSuccess) e = launch_split(&sp, 1, s);
         return e;
     }));
     AttnArgs a = sub_attn_args(P, w);
@@ -436,7 +441,7 @@ static hipError_t dense_split(const void* src, int N, int H, int d, char* w, con
     sp.rh = rh == SIZE_MAX ? nullptr : u16m(w, rh);
     sp.th = th == SIZE_MAX ? nullptr : u16m(w, th);
     sp.t_bf16 = t_bf16;
-    return launch_split(sp, s);
+    return launch_split(&sp, 1, s);
 }
 
 static AttnArgs dense_args(int N, int H, int d, char* w, const DenseLayout& DL) {
@@ -460,7 +465,10 @@ static hipError_t dense_maxabs(const void* const* src, int n, int N, int H, int 
     if (first == 0) e = launch_fill_zero(hmax, sizeof(uint32_t) * 4 * (size_t)H, s);
     else e = launch_clear_slot(hmax, H, first, s);
     for (int t = first; t < n && e == hipSuccess; ++t)
-        if (src[t]) e = launch_maxabs(src[t], true, (int64_t)H * d, d, N, d, H, hmax + t, s);
+        if (src[t]) {
+            unsigned int* out = hmax + t;
+            e = launch_maxabs(&src[t], &out, 1, true, (int64_t)H * d, d, N, d, H, s);
+        }
     return e;
 }
 

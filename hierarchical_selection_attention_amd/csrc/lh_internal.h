@@ -130,9 +130,11 @@ struct RowPrepSpec {
     int64_t S, Sp;
     int H, d, mode, dense;
 };
-hipError_t launch_maxabs(const void* src, bool src_bf16, int64_t ld, int64_t hs, int64_t rows, int d, int H,
-                         unsigned int* out, hipStream_t s);
-hipError_t launch_split(const SplitSpec& sp, hipStream_t s);
+// max |x| per head of T <= 3 tensors of one layout (out[t]: the tensor's [H][4] slot word)
+hipError_t launch_maxabs(const void* const* src, unsigned int* const* out, int T, bool src_bf16, int64_t ld,
+                         int64_t hs, int64_t rows, int d, int H, hipStream_t s);
+// splits of T <= 3 tensors of one layout (same strides, rows, hmax and hscale) in one launch
+hipError_t launch_split(const SplitSpec* sp, int T, hipStream_t s);
 hipError_t launch_clear_slot(unsigned int* hmax, int H, int slot, hipStream_t s);
 hipError_t launch_row_prep(const RowPrepSpec& sp, hipStream_t s);
 

@@ -8,19 +8,26 @@ namespace lh {
 
 // ---------------------------------------------------------------- max |x|
 // Per-head maximum of |x| over [rows][d] (fp32 [H][Sp][d] or bf16 rows with
-// strides), accumulated as float bits with atomicMax (values are >= 0).
+// strides), accumulated as float bits with atomicMax (values are >= 0), for up
+// to three tensors of the same layout (tensor blockIdx.z).
+struct MaxAbsArgs {
+    const void* src[3];
+    unsigned int* out[3];   // [H][4] word of the tensor's slot
+    int64_t ld, hs, rows;
+    int d;
+};
 template <int SRC_BF16>
-__global__ void __launch_bounds__(256) k_maxabs(const void* src, int64_t ld, int64_t hs, int64_t rows, int d,
-                                                unsigned int* out) {
-    const int h = blockIdx.y;
+__global__ void __launch_bounds__(256) k_maxabs(MaxAbsArgs a) {
+    const int h = blockIdx.y, t = blockIdx.z;
+    const void* src = a.src[t];
     const int64_t r0 = (int64_t)blockIdx.x * 64;
-    const int G = d / 8;
+    const int G = a.d / 8;
     float mx = 0.f;
     for (int idx = threadIdx.x; idx < 64 * G; idx += 256) {
         const int64_t r = r0 + idx / G;
-        if (r >= rows) break;
+        if (r >= a.rows) break;
         float x[8];
-        const int64_t el = h * hs + r * ld + (idx % G) * 8;
+        const int64_t el = h * a.hs + r * a.ld + (idx % G) * 8;
         if constexpr (SRC_BF16) load8<0>(src, el, x);
         else load8f(reinterpret_cast<const float*>(src), el, x);
 #pragma unroll
@@ -33,7 +40,7 @@ __global__ void __launch_bounds__(256) k_maxabs(const void* src, int64_t ld, int
     __syncthreads();
     if (threadIdx.x == 0) {
         const float m = fmaxf(fmaxf(wm[0], wm[1]), fmaxf(wm[2], wm[3]));
-        atomicMax(out + h * 4, __float_as_uint(m));
+        atomicMax(a.out[t] + h * 4, __float_as_uint(m));
     }
 }
 
@@ -58,16 +65,17 @@ __device__ __forceinline__ int frag_order(int r) {
     const int k = r & 31;
     return (r & ~31) | (((k >> 2) & 3) << 3) | ((k >> 4) << 2) | (k & 3);
 }
+// Up to three tensors of the same layout per launch: blockIdx.z = tensor * H + head.
 struct SplitArgs {
-    const void* src;
+    const void* src[3];
     int64_t ld, hs, rows, Sp;
-    int d, src_bf16;
+    int d, H, src_bf16;
     const unsigned int* hmax;   // [H][4], slot `slot`
     float* hscale;              // [H][4]: stored * hscale = true value
-    int slot;
-    uint16_t *rh, *rl;          // fp16 [H][Sp][d] (scaled) or null
-    uint16_t *th, *tl;          // [H][d][Sp] or null
-    int t_bf16;                 // transposed copy in bf16, unscaled
+    int slot[3];
+    uint16_t *rh[3], *rl[3];    // fp16 [H][Sp][d] (scaled) or null
+    uint16_t *th[3], *tl[3];    // [H][d][Sp] or null
+    int t_bf16[3];              // transposed copy in bf16, unscaled
 };
 
 __device__ __forceinline__ uint16_t h16(float x) { return __builtin_bit_cast(uint16_t, (_Float16)x); }
@@ -76,26 +84,29 @@ __device__ __forceinline__ float f16f(uint16_t b) { return (float)__builtin_bit_
 __global__ void __launch_bounds__(256) k_split(SplitArgs a) {
     __shared__ uint16_t th[64][64 + 2];
     __shared__ uint16_t tl[64][64 + 2];
-    const int h = blockIdx.z;
+    const int t = blockIdx.z / a.H, h = blockIdx.z % a.H;
+    const void* src = a.src[t];
+    uint16_t *rh = a.rh[t], *rl = a.rl[t], *tth = a.th[t], *ttl = a.tl[t];
+    const int tb16 = a.t_bf16[t];
     const int64_t r0 = (int64_t)blockIdx.x * 64;
     const int c0 = blockIdx.y * 64;
-    const float mx = __uint_as_float(a.hmax[h * 4 + a.slot]);
+    const float mx = __uint_as_float(a.hmax[h * 4 + a.slot[t]]);
     const float down = down_scale(mx);
-    if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) a.hscale[h * 4 + a.slot] = 1.0f / down;
-    const float tdown = a.t_bf16 ? 1.0f : down;
+    if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) a.hscale[h * 4 + a.slot[t]] = 1.0f / down;
+    const float tdown = tb16 ? 1.0f : down;
     // each thread: 2 (row, 8-column chunk) items of the 64x64 tile
     for (int it = threadIdx.x; it < 64 * 8; it += 256) {
         const int r = it / 8, cc = (it % 8) * 8;
         float x[8];
         if (r0 + r < a.rows) {
             const int64_t el = h * a.hs + (r0 + r) * a.ld + c0 + cc;
-            if (a.src_bf16) load8<0>(a.src, el, x);
-            else load8f(reinterpret_cast<const float*>(a.src), el, x);
+            if (a.src_bf16) load8<0>(src, el, x);
+            else load8f(reinterpret_cast<const float*>(src), el, x);
         } else {
 #pragma unroll
             for (int e = 0; e < 8; ++e) x[e] = 0.f;
         }
-        if (a.rh) {
+        if (rh) {
             u32x4 wh, wl;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -105,15 +116,15 @@ __global__ void __launch_bounds__(256) k_split(SplitArgs a) {
                 wl[e] = (uint32_t)h16(x0 - f16f(h0)) | ((uint32_t)h16(x1 - f16f(h1)) << 16);
             }
             const int64_t o = ((int64_t)h * a.Sp + r0 + r) * a.d + c0 + cc;
-            *reinterpret_cast<u32x4*>(a.rh + o) = wh;
-            if (a.rl) *reinterpret_cast<u32x4*>(a.rl + o) = wl;
+            *reinterpret_cast<u32x4*>(rh + o) = wh;
+            if (rl) *reinterpret_cast<u32x4*>(rl + o) = wl;
         }
-        if (a.th) {
+        if (tth) {
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const float xs = x[e] * tdown;
                 uint16_t hb, lb;
-                if (a.t_bf16) {
+                if (tb16) {
                     hb = (uint16_t)f32_to_bf16_bits(xs);
                     lb = (uint16_t)f32_to_bf16_bits(xs - bf16_lo(hb));
                 } else {
@@ -125,7 +136,7 @@ __global__ void __launch_bounds__(256) k_split(SplitArgs a) {
             }
         }
     }
-    if (!a.th) return;
+    if (!tth) return;
     __syncthreads();
     for (int it = threadIdx.x; it < 64 * 8; it += 256) {
         const int col = it / 8, rr = (it % 8) * 8;
@@ -136,8 +147,8 @@ __global__ void __launch_bounds__(256) k_split(SplitArgs a) {
             wl[e] = (uint32_t)tl[col][rr + 2 * e] | ((uint32_t)tl[col][rr + 2 * e + 1] << 16);
         }
         const int64_t o = ((int64_t)h * a.d + c0 + col) * a.Sp + r0 + rr;
-        *reinterpret_cast<u32x4*>(a.th + o) = wh;
-        if (a.tl) *reinterpret_cast<u32x4*>(a.tl + o) = wl;
+        *reinterpret_cast<u32x4*>(tth + o) = wh;
+        if (ttl) *reinterpret_cast<u32x4*>(ttl + o) = wl;
     }
 }
 
@@ -224,20 +235,36 @@ hipError_t launch_clear_slot(unsigned int* hmax, int H, int slot, hipStream_t s)
     return hipGetLastError();
 }
 
-hipError_t launch_maxabs(const void* src, bool src_bf16, int64_t ld, int64_t hs, int64_t rows, int d, int H,
-                         unsigned int* out, hipStream_t s) {
-    dim3 grid((unsigned)((rows + 63) / 64), (unsigned)H);
-    if (src_bf16) hipLaunchKernelGGL(k_maxabs<1>, grid, dim3(256), 0, s, src, ld, hs, rows, d, out);
-    else hipLaunchKernelGGL(k_maxabs<0>, grid, dim3(256), 0, s, src, ld, hs, rows, d, out);
+hipError_t launch_maxabs(const void* const* src, unsigned int* const* out, int T, bool src_bf16, int64_t ld,
+                         int64_t hs, int64_t rows, int d, int H, hipStream_t s) {
+    if (T < 1 || T > 3) return hipErrorInvalidValue;
+    MaxAbsArgs a{};
+    for (int t = 0; t < T; ++t) {
+        a.src[t] = src[t];
+        a.out[t] = out[t];
+    }
+    a.ld = ld; a.hs = hs; a.rows = rows; a.d = d;
+    dim3 grid((unsigned)((rows + 63) / 64), (unsigned)H, (unsigned)T);
+    if (src_bf16) hipLaunchKernelGGL(k_maxabs<1>, grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL(k_maxabs<0>, grid, dim3(256), 0, s, a);
     return hipGetLastError();
 }
 
-hipError_t launch_split(const SplitSpec& sp, hipStream_t s) {
+hipError_t launch_split(const SplitSpec* sp, int T, hipStream_t s) {
+    if (T < 1 || T > 3) return hipErrorInvalidValue;
     SplitArgs a{};
-    a.src = sp.src; a.ld = sp.ld; a.hs = sp.hs; a.rows = sp.rows; a.Sp = sp.Sp;
-    a.d = sp.d; a.src_bf16 = sp.src_bf16; a.hmax = sp.hmax; a.hscale = sp.hscale; a.slot = sp.slot;
-    a.rh = sp.rh; a.rl = sp.rl; a.th = sp.th; a.tl = sp.tl; a.t_bf16 = sp.t_bf16;
-    dim3 grid((unsigned)(sp.Sp / 64), (unsigned)(sp.d / 64), (unsigned)sp.H);
+    const SplitSpec& s0 = sp[0];
+    a.ld = s0.ld; a.hs = s0.hs; a.rows = s0.rows; a.Sp = s0.Sp;
+    a.d = s0.d; a.H = s0.H; a.src_bf16 = s0.src_bf16; a.hmax = s0.hmax; a.hscale = s0.hscale;
+    for (int t = 0; t < T; ++t) {
+        const SplitSpec& x = sp[t];
+        if (x.ld != s0.ld || x.hs != s0.hs || x.rows != s0.rows || x.Sp != s0.Sp || x.d != s0.d || x.H != s0.H ||
+            x.src_bf16 != s0.src_bf16 || x.hmax != s0.hmax || x.hscale != s0.hscale)
+            return hipErrorInvalidValue;
+        a.src[t] = x.src; a.slot[t] = x.slot;
+        a.rh[t] = x.rh; a.rl[t] = x.rl; a.th[t] = x.th; a.tl[t] = x.tl; a.t_bf16[t] = x.t_bf16;
+    }
+    dim3 grid((unsigned)(s0.Sp / 64), (unsigned)(s0.d / 64), (unsigned)(s0.H * T));
     hipLaunchKernelGGL(k_split, grid, dim3(256), 0, s, a);
     return hipGetLastError();
 }

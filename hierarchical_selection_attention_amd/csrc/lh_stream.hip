@@ -307,6 +307,9 @@ __global__ void __launch_bounds__(256) k_pool_up(PoolUpArgs a) {
 // the pyramid entry (start_i, level_i).  One wavefront per row; the entry is
 // read from the stored top level, from the stored level m (p^(l-m) rows), or
 // from the input tokens (p^l rows).  Rows i in [S, Sp) are written as zeros.
+// Rows differ in cost by up to p^(m-1) input rows, so each row is a workgroup
+// of its own: a workgroup of several rows would hold its slot until its
+// slowest row finished.
 struct GatherArgs {
     const void *q, *k, *v;
     const float* pool_m;
@@ -320,13 +323,13 @@ struct GatherArgs {
 };
 
 template <int DT, int G>
-__global__ void __launch_bounds__(256) k_gather(GatherArgs a) {
+__global__ void __launch_bounds__(64) k_gather(GatherArgs a) {
     constexpr int d = G * 8;
     constexpr int NR = 64 / G;   // rows read per wavefront instruction
     const int lane = threadIdx.x & 63;
     const int c = lane % G, rs = lane / G;
     const int h = blockIdx.y;
-    const int64_t i = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int64_t i = (int64_t)blockIdx.x;
     if (i >= a.Sp) return;
     const int64_t orow = ((int64_t)h * a.Sp + i) * d + c * 8;
     if (i >= a.S) {
@@ -370,7 +373,7 @@ __global__ void __launch_bounds__(256) k_gather(GatherArgs a) {
     } else {
         R = a.pw[l];
         const void* src[3] = {a.q, a.k, a.v};
-        constexpr int U = 4;
+        constexpr int U = 2;
         for (int64_t r0 = rs; r0 < R; r0 += NR * U) {
             float x[U][3][8];
 #pragma unroll
@@ -798,14 +801,14 @@ hipError_t launch_gather(const Plan& P, const void* q, const void* k, const void
     a.S = P.S; a.Sp = P.Sp; a.n_m = P.n[P.m]; a.ntop = P.ntop;
     for (int l = 0; l < P.L; ++l) a.pw[l] = P.pw[l];
     a.H = P.H; a.m = P.m; a.L = P.L;
-    dim3 grid((unsigned)((P.Sp + 3) / 4), (unsigned)P.H);
+    dim3 grid((unsigned)P.Sp, (unsigned)P.H);
     const int G = P.d / 8;
     if (P.dtype == BF16) {
-        if (G == 16) hipLaunchKernelGGL((k_gather<0, 16>), grid, dim3(256), 0, s, a);
-        else hipLaunchKernelGGL((k_gather<0, 8>), grid, dim3(256), 0, s, a);
+        if (G == 16) hipLaunchKernelGGL((k_gather<0, 16>), grid, dim3(64), 0, s, a);
+        else hipLaunchKernelGGL((k_gather<0, 8>), grid, dim3(64), 0, s, a);
     } else {
-        if (G == 16) hipLaunchKernelGGL((k_gather<1, 16>), grid, dim3(256), 0, s, a);
-        else hipLaunchKernelGGL((k_gather<1, 8>), grid, dim3(256), 0, s, a);
+        if (G == 16) hipLaunchKernelGGL((k_gather<1, 16>), grid, dim3(64), 0, s, a);
+        else hipLaunchKernelGGL((k_gather<1, 8>), grid, dim3(64), 0, s, a);
     }
     return hipGetLastError();
 }
