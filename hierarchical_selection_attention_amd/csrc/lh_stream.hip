@@ -36,7 +36,7 @@ struct PoolScoreArgs {
 #endif
 // Tokens per load batch of the bf16 scatter adjoint (one tensor streamed).
 #ifndef LH_SCATTER_U
-#define LH_SCATTER_U 4
+#define LH_SCATTER_U 3
 #endif
 
 template <int DT, int G>
