@@ -10,6 +10,11 @@ Prints one JSON line with the metric, per-stage times (HIP events on the
 launch stream), the roofline position of the dominant kernel, the CPU oracle
 timed on a bounded sample, and the dense causal attention comparison at the
 same N.  Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+With --block it instead times the attention block around the layer at the
+530M model's shape (x W_QKV projections, the layer, the W_O projection,
+forward and backward; N=98304, d_model=2048, H=16, d=128, p=4, L=4, K=128) and
+prints that measurement's own JSON line.
 """
 import argparse
 import json
@@ -119,6 +124,146 @@ def cpu_baseline(w, x, heads):
                       f"scaled by {w['H']}/{heads} heads (heads are independent)"}
 
 
+BLOCK_METRIC = ("Lighthouse attention block (QKV projections + layer + output projection) "
+                "fwd+bwd tokens/s at 98K, 530M-model shape")
+
+
+def block_gemm_flops(N, dm, hd):
+    """Flops of one launch of each projection GEMM of the block."""
+    one = 2 * N * dm * hd
+    return {"proj_qkv": one, "proj_out": one, "proj_out_dx": one, "proj_out_dw": one,
+            "proj_qkv_dx": 3 * one, "proj_qkv_dw": 3 * one}
+
+
+def bench_block(args, lh, torch, np, si):
+    w = si.BLOCK_WORKLOAD
+    N, dm, H, d, p, L, K = w["N"], w["dm"], w["H"], w["d"], w["p"], w["L"], w["K"]
+    hd = H * d
+    S = int(lh.lh_subseq_len(N, p, L, K))
+    log(f"block workload {w['name']}: N={N} dm={dm} H={H} d={d} p={p} L={L} K={K} S={S}")
+    t0 = time.perf_counter()
+    b = si.block_inputs(with_dy=True, threads=16)
+    log(f"inputs generated in {time.perf_counter() - t0:.1f} s")
+
+    def dev(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+
+    x, wqkv, wo, dy = dev(b["x"]), dev(b["w_qkv"]), dev(b["w_o"]), dev(b["dy"])
+    ws = lh.block_workspace(N, H, d, dm, p, L, K)
+    o = torch.empty((N, H, d), dtype=torch.bfloat16, device="cuda")
+    y = torch.empty_like(x)
+    grads = (torch.empty_like(x), torch.empty((dm, 3 * hd), dtype=torch.float32, device="cuda"),
+             torch.empty((hd, dm), dtype=torch.float32, device="cuda"))
+    stream = torch.cuda.current_stream()
+
+    def step():
+        lh.block_forward(x, wqkv, wo, H, d, p, L, K, ws=ws, o=o, y=y, stream=stream)
+        lh.block_backward(x, wqkv, wo, o, dy, H, d, p, L, K, ws, mode=args.mode, grads=grads, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log("warmup done")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    log(f"timed {args.steps} steps: {ms_per_step:.3f} ms/step")
+
+    lh.lh_stage_timing(1)
+    torch.cuda.synchronize()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    stages = lh.lh_stage_timing_read(32)
+    lh.lh_stage_timing(0)
+    fl = block_gemm_flops(N, dm, hd)
+    stage_rep = {}
+    for name, (ms, cnt) in stages.items():
+        avg = ms / cnt
+        rec = {"ms": round(avg, 4), "launches": cnt}
+        if name in fl:
+            rec["TFLOP/s"] = round(fl[name] / (avg / 1e3) / 1e12, 1)
+            rec["frac_mfma_bf16"] = round(rec["TFLOP/s"] / BF16_PEAK_TFLOPS, 4)
+        stage_rep[name] = rec
+    gemm_ms = sum(stages[s][0] for s in stages if s in fl) / args.steps
+    gemm_flops = sum(fl[s] * stages[s][1] for s in stages if s in fl) / args.steps
+    layer_ms = sum(stages[s][0] for s in stages if s not in fl) / args.steps
+    dominant = max((s for s in stages if s in fl), key=lambda s: stages[s][0])
+    dom_ms = stages[dominant][0] / stages[dominant][1]
+    ach = fl[dominant] / (dom_ms / 1e3) / 1e12
+    roof = {"bound": "mfma", "kernel": dominant, "achieved": round(ach, 1), "peak": BF16_PEAK_TFLOPS,
+            "unit": "TFLOP/s", "frac": round(ach / BF16_PEAK_TFLOPS, 4),
+            "traffic": measured_traffic(w["name"], dominant),
+            "algorithmic_flops_per_launch": fl[dominant], "avg_launch_ms": round(dom_ms, 4),
+            "all_gemms": {"ms_per_step": round(gemm_ms, 3), "TFLOP/s": round(gemm_flops / (gemm_ms / 1e3) / 1e12, 1)}}
+
+    dense = None
+    if not args.no_dense:
+        log("dense causal attention at the same N ...")
+        q = torch.empty((N, H, d), dtype=torch.bfloat16, device="cuda").normal_()
+        kk, vv, do = torch.randn_like(q), torch.randn_like(q), torch.randn_like(q)
+        dws = torch.empty(lh.lh_dense_workspace_bytes(N, H, d, 0), dtype=torch.uint8, device="cuda")
+        od = torch.empty_like(q)
+        lse = torch.empty((H, N), dtype=torch.float32, device="cuda")
+        dg = tuple(torch.empty_like(q) for _ in range(3))
+        lh.dense_forward(q, kk, vv, ws=dws, out=od, lse=lse, stream=stream)
+        lh.dense_backward(q, kk, vv, od, lse, do, dws, grads=dg, stream=stream)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        reps = 3
+        ev[0].record(stream)
+        for _ in range(reps):
+            lh.dense_forward(q, kk, vv, ws=dws, out=od, lse=lse, stream=stream)
+            lh.dense_backward(q, kk, vv, od, lse, do, dws, grads=dg, stream=stream)
+        ev[1].record(stream)
+        torch.cuda.synchronize()
+        dense_ms = ev[0].elapsed_time(ev[1]) / reps
+        dense = {"dense_attention_fwd_bwd_ms": round(dense_ms, 2), "reps": reps,
+                 "block_with_dense_attention_ms_derived": round(gemm_ms + dense_ms, 2),
+                 "speedup_block_derived": round((gemm_ms + dense_ms) / ms_per_step, 2),
+                 "note": "derived: the block's measured GEMM time plus dense causal attention fwd+bwd "
+                         "(same MFMA kernels) at the same N, against the measured Lighthouse block step"}
+        del dws, od, lse, dg, q, kk, vv, do
+        log(f"dense attention fwd+bwd {dense_ms:.1f} ms")
+
+    cpu = None
+    if not args.no_cpu:
+        import oracle
+        threads = max(1, min(16, os.cpu_count() or 1))
+        log(f"CPU oracle block fwd+bwd on {threads} threads ...")
+        t0 = time.perf_counter()
+        f = oracle.block_forward(b["x"], b["w_qkv"], b["w_o"], H, d, p, L, K, nthreads=threads)
+        oracle.block_backward(f, b["x"], b["w_qkv"], b["w_o"], b["dy"], H, d, p, L, K, nthreads=threads)
+        t = time.perf_counter() - t0
+        cpu = {"value": N / t, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+               "sample": f"the whole block fwd+bwd ({N} tokens), {t:.1f} s (fp64 numpy GEMMs and the layer oracle)"}
+
+    out = {
+        "metric": BLOCK_METRIC,
+        "value": round(N / (ms_per_step / 1e3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded, inputs resident in HBM)",
+        "config": {"workload": w["name"], "N": N, "d_model": dm, "H": H, "d": d, "p": p, "L": L, "K": K, "S": S,
+                   "scatter_mode": "int_atomic" if args.mode else "fp_atomic"},
+        "layer_ms_per_step": round(layer_ms, 3),
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "dense_comparison": dense,
+        "stages": stage_rep,
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -129,6 +274,8 @@ def main():
     ap.add_argument("--no-dense", action="store_true", help="skip the dense attention comparison")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-heads", type=int, default=8)
+    ap.add_argument("--block", action="store_true",
+                    help="time the attention block (projections + layer) at the 530M shape instead")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB three times (HBM counter calibration)")
     args = ap.parse_args()
@@ -151,6 +298,9 @@ def main():
         return
     import hierarchical_selection_attention_amd as lh
     import synth_inputs as si
+    if args.block:
+        bench_block(args, lh, torch, np, si)
+        return
 
     w = si.WORKLOADS[args.workload]
     N, H, d, p, L, K = w["N"], w["H"], w["d"], w["p"], w["L"], w["K"]
@@ -198,7 +348,7 @@ def main():
     for _ in range(args.steps):
         step()
     torch.cuda.synchronize()
-    stages = lh.lh_stage_timing_read(16)
+    stages = lh.lh_stage_timing_read(32)
     lh.lh_stage_timing(0)
 
     sb = stage_bytes(w, S)

@@ -5,5 +5,6 @@ Import fails loudly when liblighthouse.so has not been built
 fallback implementation.
 """
 from ._lib import *  # noqa: F401,F403
-from ._lib import (EXPORTS, LIB_PATH, LighthouseError, alloc_workspace, backward, dense_backward,  # noqa: F401
-                   dense_forward, dtype_code, forward, peak_probe, read_selection, workspace_tensor)
+from ._lib import (EXPORTS, LIB_PATH, LighthouseError, alloc_workspace, backward, block_backward,  # noqa: F401
+                   block_forward, block_workspace, dense_backward, dense_forward, dtype_code, forward, peak_probe,
+                   read_selection, workspace_tensor)

@@ -13,7 +13,7 @@ import os
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "liblighthouse.so")
 
-LH_OK, LH_ERR_ARG, LH_ERR_SHAPE, LH_ERR_DTYPE, LH_ERR_WORKSPACE, LH_ERR_HIP = 0, -1, -2, -3, -4, -5
+LH_OK, LH_ERR_ARG, LH_ERR_SHAPE, LH_ERR_DTYPE, LH_ERR_WORKSPACE, LH_ERR_HIP, LH_ERR_GEMM = 0, -1, -2, -3, -4, -5, -6
 LH_BF16, LH_FP32 = 0, 1
 LH_SCATTER_FP_ATOMIC, LH_SCATTER_INT_ATOMIC = 0, 1
 VIEWS = {"scores": 0, "sel_start": 1, "sel_level": 2, "qsub": 3, "ksub": 4, "vsub": 5, "osub": 6,
@@ -21,7 +21,8 @@ VIEWS = {"scores": 0, "sel_start": 1, "sel_level": 2, "qsub": 3, "ksub": 4, "vsu
 
 EXPORTS = ("lh_subseq_len", "lh_workspace_bytes", "lh_forward", "lh_backward", "lh_workspace_view",
            "lh_dense_workspace_bytes", "lh_dense_attn_fwd", "lh_dense_attn_bwd", "lh_stage_timing",
-           "lh_stage_timing_read", "lh_stage_name", "lh_status_str", "lh_read_selection", "lh_peak_probe")
+           "lh_stage_timing_read", "lh_stage_name", "lh_status_str", "lh_read_selection", "lh_peak_probe",
+           "lh_block_workspace_bytes", "lh_block_forward", "lh_block_backward")
 
 
 class LighthouseError(RuntimeError):
@@ -44,6 +45,9 @@ def _load():
         "lh_dense_workspace_bytes": (sz, [i, i, i, i]),
         "lh_dense_attn_fwd": (i, [vp, vp, vp, vp, vp, i, i, i, i, vp, sz, vp]),
         "lh_dense_attn_bwd": (i, [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, vp, sz, vp]),
+        "lh_block_workspace_bytes": (sz, [i, i, i, i, i, i, i]),
+        "lh_block_forward": (i, [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, vp, sz, vp]),
+        "lh_block_backward": (i, [vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, vp, sz, vp]),
         "lh_stage_timing": (i, [i]),
         "lh_stage_timing_read": (i, [C.POINTER(C.c_double), C.POINTER(C.c_int), i]),
         "lh_stage_name": (C.c_char_p, [i]),
@@ -69,6 +73,9 @@ lh_dense_attn_bwd = _L.lh_dense_attn_bwd
 lh_stage_timing = _L.lh_stage_timing
 lh_read_selection = _L.lh_read_selection
 lh_peak_probe = _L.lh_peak_probe
+lh_block_workspace_bytes = _L.lh_block_workspace_bytes
+lh_block_forward = _L.lh_block_forward
+lh_block_backward = _L.lh_block_backward
 
 
 def lh_status_str(rc: int) -> str:
@@ -86,7 +93,7 @@ def lh_workspace_view(ws_ptr, N, H, d, p, L, K, dtype, view):
     return ptr.value, nbytes.value
 
 
-def lh_stage_timing_read(n: int = 16):
+def lh_stage_timing_read(n: int = 32):
     ms = (C.c_double * n)()
     cnt = (C.c_int * n)()
     rc = _L.lh_stage_timing_read(ms, cnt, n)
@@ -205,6 +212,53 @@ def read_selection(ws, N, H, d, p, L, K, dtype, stream=None):
                            _stream_handle(stream))
     _check(rc, "lh_read_selection")
     return start, level
+
+
+def block_workspace(N, H, d, dm, p, L, K, device="cuda"):
+    torch = _torch()
+    nbytes = lh_block_workspace_bytes(N, H, d, dm, p, L, K)
+    if nbytes == 0:
+        raise LighthouseError("invalid block parameters")
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+def block_forward(x, w_qkv, w_o, H, d, p, L, K, ws=None, o=None, y=None, stream=None):
+    """y = Lighthouse(x W_Q, x W_K, x W_V) W_O for bf16 x [N, dm], w_qkv [dm, 3Hd], w_o [Hd, dm].
+
+    Returns (y, o, ws); o [N, H, d] and ws are needed by block_backward."""
+    torch = _torch()
+    _dev_tensor_check(x, w_qkv, w_o)
+    N, dm = x.shape
+    if x.dtype != torch.bfloat16 or w_qkv.dtype != torch.bfloat16 or w_o.dtype != torch.bfloat16:
+        raise LighthouseError("the block takes bf16 tensors")
+    if tuple(w_qkv.shape) != (dm, 3 * H * d) or tuple(w_o.shape) != (H * d, dm):
+        raise LighthouseError("weight shapes do not match x, H and d")
+    if ws is None:
+        ws = block_workspace(N, H, d, dm, p, L, K, x.device)
+    if o is None:
+        o = torch.empty((N, H, d), dtype=torch.bfloat16, device=x.device)
+    if y is None:
+        y = torch.empty((N, dm), dtype=torch.bfloat16, device=x.device)
+    rc = lh_block_forward(x.data_ptr(), w_qkv.data_ptr(), w_o.data_ptr(), o.data_ptr(), y.data_ptr(), N, H, d, dm,
+                          p, L, K, ws.data_ptr(), ws.numel(), _stream_handle(stream))
+    _check(rc, "lh_block_forward")
+    return y, o, ws
+
+
+def block_backward(x, w_qkv, w_o, o, dy, H, d, p, L, K, ws, mode=LH_SCATTER_FP_ATOMIC, grads=None, stream=None):
+    """(dx bf16 [N, dm], dw_qkv fp32 [dm, 3Hd], dw_o fp32 [Hd, dm]) of the block."""
+    torch = _torch()
+    _dev_tensor_check(x, w_qkv, w_o, o, dy)
+    N, dm = x.shape
+    if grads is None:
+        grads = (torch.empty_like(x), torch.empty(w_qkv.shape, dtype=torch.float32, device=x.device),
+                 torch.empty(w_o.shape, dtype=torch.float32, device=x.device))
+    dx, dwqkv, dwo = grads
+    rc = lh_block_backward(x.data_ptr(), w_qkv.data_ptr(), w_o.data_ptr(), o.data_ptr(), dy.data_ptr(),
+                           dx.data_ptr(), dwqkv.data_ptr(), dwo.data_ptr(), N, H, d, dm, p, L, K, mode,
+                           ws.data_ptr(), ws.numel(), _stream_handle(stream))
+    _check(rc, "lh_block_backward")
+    return dx, dwqkv, dwo
 
 
 def peak_probe(kind, src, dst, n, stream=None):

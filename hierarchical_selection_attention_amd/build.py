@@ -32,7 +32,10 @@ SOURCES = {
     "lh_prep.hip": [],
     "lh_probe.hip": [],
     "lh_api.cpp": ["-x", "hip"],
+    # the projections around the layer (hipBLASLt GEMMs)
+    "lh_block.cpp": ["-x", "hip"],
 }
+ROCM_LIB = "/opt/rocm/lib"
 
 
 def build(verbose: bool = False) -> str:
@@ -57,7 +60,8 @@ def build(verbose: bool = False) -> str:
     if failed:
         raise RuntimeError(f"hipcc failed for {failed}")
     tmp = LIB + ".tmp"
-    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs]
+    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs,
+           "-L", ROCM_LIB, "-lhipblaslt", f"-Wl,-rpath,{ROCM_LIB}"]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)

@@ -137,29 +137,29 @@ hipEvent_t take_event() {
 
 const char* kStageNames[ST_COUNT] = {
     "pool_score", "pool_up", "topk", "gather", "sub_prep", "attn_fwd", "scatter_fwd",
-    "zero_acc", "scatter_bwd", "bwd_prep", "attn_bwd_dkdv", "attn_bwd_dq", "pool_bwd"};
+    "zero_acc", "scatter_bwd", "bwd_prep", "attn_bwd_dkdv", "attn_bwd_dq", "pool_bwd",
+    "proj_qkv", "proj_out", "proj_out_dx", "proj_out_dw", "proj_qkv_dx", "proj_qkv_dw"};
 
-// Runs `fn` (which enqueues one stage) between two timing events when enabled.
-template <class F>
-hipError_t stage(int id, hipStream_t s, F&& fn) {
-    hipEvent_t a = nullptr, b = nullptr;
+}  // namespace
+
+StageMark stage_open(hipStream_t s) {
+    StageMark m;
     {
         std::lock_guard<std::mutex> g(g_mu);
-        if (g_timing) {
-            a = take_event();
-            b = take_event();
-        }
+        if (!g_timing) return m;
+        m.a = take_event();
+        m.b = take_event();
     }
-    if (a && b) (void)hipEventRecord(a, s);
-    hipError_t e = fn();
-    if (a && b) {
-        (void)hipEventRecord(b, s);
-        std::lock_guard<std::mutex> g(g_mu);
-        g_recs.push_back({id, a, b});
-    }
-    return e;
+    if (m.a && m.b) (void)hipEventRecord(m.a, s);
+    return m;
 }
-}  // namespace
+
+void stage_close(int id, hipStream_t s, const StageMark& m) {
+    if (!m.a || !m.b) return;
+    (void)hipEventRecord(m.b, s);
+    std::lock_guard<std::mutex> g(g_mu);
+    g_recs.push_back({id, m.a, m.b});
+}
 
 }  // namespace lh
 
@@ -271,17 +271,21 @@ int lh_forward(const void* q, const void* k, const void* v, void* o, int N, int 
         if (!P.rowcopy) return launch_scatter_fwd(P, w, o, s);
         const uint16_t* tab[1] = {u16(w, P.off_otab)};
         void* out[1] = {o};
-        return launch_row_copy(P, w, tab, out, 1, s);
+        return launch_row_copy(P, w, tab, out, 1, (int64_t)H * d, s);
     }));
     return LH_OK;
 }
 
-int lh_backward(const void* dout, void* dq, void* dk, void* dv, int N, int H, int d, int p, int L, int K,
-                int dtype, int scatter_mode, void* ws, size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+namespace lh {
+int backward_strided(const void* dout, void* dq, void* dk, void* dv, int N, int H, int d, int p, int L, int K,
+                         int dtype, int scatter_mode, void* ws, size_t ws_bytes, void* stream, int64_t grad_ld) {
     Plan P;
     int rc = make_plan(N, H, d, p, L, K, dtype, &P);
     if (rc) return rc;
     if (scatter_mode != LH_SCATTER_FP_ATOMIC && scatter_mode != LH_SCATTER_INT_ATOMIC) return LH_ERR_DTYPE;
+    if (grad_ld != (int64_t)H * d && (!P.rowcopy || grad_ld < (int64_t)H * d || grad_ld % 8 != 0)) return LH_ERR_ARG;
     if (!dout || !dq || !dk || !dv) return LH_ERR_ARG;
     if (!aligned16(dout) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv)) return LH_ERR_ARG;
     if ((rc = check_ws(P, ws, ws_bytes))) return rc;
@@ -323,9 +327,18 @@ int lh_backward(const void* dout, void* dq, void* dk, void* dv, int N, int H, in
         if (!P.rowcopy) return launch_pool_bwd(P, w, dq, dk, dv, s);
         const uint16_t* tab[3] = {u16(w, P.off_gtab), u16(w, P.off_gtab + HSd2), u16(w, P.off_gtab + 2 * HSd2)};
         void* out[3] = {dq, dk, dv};
-        return launch_row_copy(P, w, tab, out, 3, s);
+        return launch_row_copy(P, w, tab, out, 3, grad_ld, s);
     }));
     return LH_OK;
+}
+}  // namespace lh
+
+extern "C" {
+
+int lh_backward(const void* dout, void* dq, void* dk, void* dv, int N, int H, int d, int p, int L, int K,
+                int dtype, int scatter_mode, void* ws, size_t ws_bytes, void* stream) {
+    return backward_strided(dout, dq, dk, dv, N, H, d, p, L, K, dtype, scatter_mode, ws, ws_bytes, stream,
+                         (int64_t)H * d);
 }
 
 int lh_workspace_view(void* ws, int N, int H, int d, int p, int L, int K, int dtype, int view, void** ptr,
@@ -578,6 +591,7 @@ const char* lh_status_str(int status) {
         case LH_ERR_DTYPE: return "unknown dtype or mode";
         case LH_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
         case LH_ERR_HIP: return "HIP launch or runtime error";
+        case LH_ERR_GEMM: return "GEMM library error or no algorithm for the shape";
         default: return "unknown status";
     }
 }

@@ -523,9 +523,12 @@ __global__ void __launch_bounds__(256) k_attn_dkdv(AttnK a) {
 
     const int64_t qfirst = (int64_t)kt * 64;              // first query that can see the workgroup's keys
     const int nblk = (int)((a.rows - qfirst + kBN - 1) / kBN);
+    // query blocks run from the last one down, so the workgroups of a head read
+    // the same block at about the same time (one L2 working set per head)
+    auto qblock = [&](int b) { return qfirst + (int64_t)(nblk - 1 - b) * kBN; };
     // layout: [qh][ql?][doh][dol?] rows, then [qTh][qTl?][doTh][doTl?]
     auto loadA = [&](int b) {
-        const int64_t qb = qfirst + (int64_t)b * kBN;
+        const int64_t qb = qblock(b);
         if (wave == 0) {   // lanes 0..31: lse2, lanes 32..63: D (qb + 32 <= Sp)
             const float* src = (lane < kBN ? lse2 : Dv) + qb + (lane & (kBN - 1));
             __builtin_amdgcn_global_load_lds(src, LH_LDS_PTR(qstat), 4, 0, 0);
@@ -538,7 +541,7 @@ __global__ void __launch_bounds__(256) k_attn_dkdv(AttnK a) {
         }
     };
     auto loadB = [&](int b) {
-        const int64_t qb = qfirst + (int64_t)b * kBN;
+        const int64_t qb = qblock(b);
         uint16_t* base = sm + ROWS;
         dma_t<D>(a.qTbh + hb, Sp, qb, base);
         dma_t<D>(a.doTh + hb, Sp, qb, base + NA * T::TR);
@@ -567,7 +570,7 @@ __global__ void __launch_bounds__(256) k_attn_dkdv(AttnK a) {
     // publishes the rows and frees the transposed tiles for the next block.
     for (int b = 0; b < nblk; ++b) {
         const bool more = b + 1 < nblk;
-        const int64_t qb = qfirst + (int64_t)b * kBN;
+        const int64_t qb = qblock(b);
         const bool active = qb + kBN > k0;   // some query of the block sees some key of the wave
         f32x4 P[2], dS[2];
         if (active) {

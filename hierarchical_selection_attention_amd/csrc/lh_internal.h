@@ -21,8 +21,30 @@ enum Dtype { BF16 = 0, FP32 = 1 };
 enum Stage {
     ST_POOL_SCORE = 0, ST_POOL_UP, ST_TOPK, ST_GATHER, ST_SUB_PREP, ST_ATTN_FWD,
     ST_SCATTER_FWD, ST_ZERO_ACC, ST_SCATTER_BWD, ST_BWD_PREP, ST_ATTN_BWD_DKDV,
-    ST_ATTN_BWD_DQ, ST_POOL_BWD, ST_COUNT
+    ST_ATTN_BWD_DQ, ST_POOL_BWD,
+    // projections around the layer (lh_block_*)
+    ST_PROJ_QKV, ST_PROJ_OUT, ST_PROJ_OUT_DX, ST_PROJ_OUT_DW, ST_PROJ_QKV_DX, ST_PROJ_QKV_DW, ST_COUNT
 };
+
+// Event pair around one stage when stage timing is on (lh_stage_timing).
+struct StageMark {
+    hipEvent_t a = nullptr, b = nullptr;
+};
+StageMark stage_open(hipStream_t s);
+void stage_close(int id, hipStream_t s, const StageMark& m);
+// Runs `fn`, which enqueues one stage, between the two events.
+template <class F>
+hipError_t stage(int id, hipStream_t s, F&& fn) {
+    const StageMark m = stage_open(s);
+    const hipError_t e = fn();
+    stage_close(id, s, m);
+    return e;
+}
+
+// lh_backward with dq, dk, dv rows grad_ld elements apart (grad_ld = H*d for
+// [N][H][d] tensors; larger strides need the bf16 path, grad_ld % 8 == 0)
+int backward_strided(const void* dout, void* dq, void* dk, void* dv, int N, int H, int d, int p, int L, int K,
+                     int dtype, int scatter_mode, void* ws, size_t ws_bytes, void* stream, int64_t grad_ld);
 
 struct Plan {
     int N, H, d, p, L, K, dtype, esz;
@@ -80,9 +102,10 @@ hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
 hipError_t launch_scatter_bwd(const Plan& P, const void* dout, int mode, char* ws, hipStream_t s);
 hipError_t launch_pool_bwd(const Plan& P, char* ws, void* dq, void* dk, void* dv, hipStream_t s);
 // bf16 path: out[z][t][h] = tab[z][h][slot_h(t)], the back-scatter (Z = 1) and
-// the pool adjoint (Z = 3) from bf16 rows the attention kernels leave
+// the pool adjoint (Z = 3) from bf16 rows the attention kernels leave; token t's
+// row of out[z] starts t * out_ld elements in (out_ld >= H*d, a multiple of 8)
 hipError_t launch_row_copy(const Plan& P, const char* ws, const uint16_t* const* tab, void* const* out, int Z,
-                           hipStream_t s);
+                           int64_t out_ld, hipStream_t s);
 
 // Attention operands: 16-bit copies laid out [H][Sp][d] (rows) and
 // [H][d][Sp] (transposed); lo parts are used when `split`.

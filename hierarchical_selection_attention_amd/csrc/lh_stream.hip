@@ -688,8 +688,8 @@ __global__ void __launch_bounds__(256) k_pool_bwd(PoolBwdArgs a) {
 struct RowCopyArgs {
     const int32_t* start;     // [H][S]
     const u32x4* tab[3];      // [H][Sp][G] words
-    u32x4* out[3];            // [N][H][G] words
-    int64_t N, S, Sp;
+    u32x4* out[3];            // token t, head h at word t * ld + h * G
+    int64_t N, S, Sp, ld;
     int H, HG, mt;
 };
 
@@ -703,7 +703,7 @@ __global__ void __launch_bounds__(256) k_row_copy(RowCopyArgs a) {
     int64_t nxt = slot + 1 < a.S ? st[slot + 1] : a.N;
     const u32x4* tb = a.tab[z] + (int64_t)tm.h * a.Sp * G + tm.c;
     u32x4* ob = a.out[z] + (int64_t)tm.h * G + tm.c;
-    const int64_t ld = (int64_t)a.H * G;
+    const int64_t ld = a.ld;
     u32x4 x = tb[slot * G];
     for (int64_t t = tm.tb; t < tm.te; ++t) {
         if (t >= nxt) {
@@ -895,8 +895,9 @@ hipError_t launch_pool_bwd(const Plan& P, char* ws, void* dq, void* dk, void* dv
 }
 
 hipError_t launch_row_copy(const Plan& P, const char* ws, const uint16_t* const* tab, void* const* out, int Z,
-                           hipStream_t s) {
+                           int64_t out_ld, hipStream_t s) {
     if (Z < 1 || Z > 3 || P.dtype != BF16) return hipErrorInvalidValue;
+    if (out_ld < (int64_t)P.H * P.d || out_ld % 8 != 0) return hipErrorInvalidValue;
     const int G = P.d / 8;
     RowCopyArgs a{};
     a.start = reinterpret_cast<const int32_t*>(ws + P.off_start);
@@ -905,6 +906,7 @@ hipError_t launch_row_copy(const Plan& P, const char* ws, const uint16_t* const*
         a.out[z] = reinterpret_cast<u32x4*>(out[z]);
     }
     a.N = P.N; a.S = P.S; a.Sp = P.Sp; a.H = P.H;
+    a.ld = out_ld / 8;
     const int threads = scatter_threads(P, &a.HG, &a.mt);
     dim3 grid((unsigned)((P.N + kTileTok - 1) / kTileTok), (unsigned)(P.H / a.HG), (unsigned)Z);
     if (G == 16) hipLaunchKernelGGL((k_row_copy<16, true>), grid, dim3(threads), 0, s, a);

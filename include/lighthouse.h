@@ -56,7 +56,8 @@ typedef enum {
     LH_ERR_SHAPE = -2,      /* shape not supported (d, H, N divisibility, sizes)  */
     LH_ERR_DTYPE = -3,      /* unknown dtype or scatter mode                      */
     LH_ERR_WORKSPACE = -4,  /* workspace missing, misaligned or too small         */
-    LH_ERR_HIP = -5         /* a HIP launch or runtime call failed                */
+    LH_ERR_HIP = -5,        /* a HIP launch or runtime call failed                */
+    LH_ERR_GEMM = -6        /* the GEMM library (hipBLASLt) failed or has no algorithm */
 } lh_status;
 
 typedef enum { LH_BF16 = 0, LH_FP32 = 1 } lh_dtype;
@@ -148,8 +149,46 @@ int lh_dense_attn_bwd(const void* q, const void* k, const void* v, const void* o
                       const float* lse, const void* dout, void* dq, void* dk, void* dv,
                       int N, int H, int d, int dtype, void* ws, size_t ws_bytes, void* stream);
 
+/* The attention block around the layer (Sec. 3.1 Eq. (1) and Fig. 1: the
+ * projections W_Q, W_K, W_V from the block input feed the pyramid pool; the
+ * layer output leaves through an output projection W_O, as in the Llama-style
+ * models of Sec. 4).  bf16 only.  With dm the model width and Hd = H*d, all
+ * row-major device tensors, 16-byte aligned:
+ *   x      [N][dm]      block input
+ *   w_qkv  [dm][3*Hd]   columns [0, Hd) give q = x W_Q, read as [N][H][d];
+ *                       [Hd, 2Hd) give k and [2Hd, 3Hd) give v
+ *   w_o    [Hd][dm]
+ *   o      [N][H][d]    the layer output: written by lh_block_forward and
+ *                       read by lh_block_backward (the caller keeps it)
+ *   y      [N][dm]      y = o W_O
+ * lh_block_backward takes dy [N][dm] and writes dx [N][dm] (bf16) and the
+ * weight gradients dw_qkv [dm][3*Hd] and dw_o [Hd][dm] in fp32; all three
+ * are overwritten, not accumulated.  x, w_qkv, w_o and o must be those of the
+ * matching forward.  Products accumulate in fp32; q, k, v and dO = dy W_O^T
+ * are rounded to bf16 (round to nearest even), the layer's I/O type.  The six
+ * weight products run in hipBLASLt; the first call on a device creates its
+ * handle and each new GEMM shape chooses an algorithm once (host state kept
+ * until the process ends).  Workspace: lh_block_workspace_bytes (256-byte
+ * aligned); it begins with the layer's workspace, so lh_read_selection and
+ * lh_workspace_view (dtype LH_BF16) read it directly.  At the next 256-byte
+ * boundary after it the forward leaves q, k, v ([3][N][H][d] bf16), which the
+ * backward overwrites with the gradients ([N][3][H][d]: dq, dk, dv of a token
+ * side by side); at the next 256-byte boundary after those the backward
+ * leaves dO = dy W_O^T ([N][H][d] bf16).  The workspace must stay untouched
+ * between the forward and the backward.  dm must be a multiple of
+ * 8; the other shape limits are the layer's.  Returns LH_OK, a negative
+ * lh_status for bad arguments (nothing enqueued), LH_ERR_HIP or LH_ERR_GEMM. */
+size_t lh_block_workspace_bytes(int N, int H, int d, int dm, int p, int L, int K);
+int lh_block_forward(const void* x, const void* w_qkv, const void* w_o, void* o, void* y,
+                     int N, int H, int d, int dm, int p, int L, int K,
+                     void* ws, size_t ws_bytes, void* stream);
+int lh_block_backward(const void* x, const void* w_qkv, const void* w_o, const void* o,
+                      const void* dy, void* dx, float* dw_qkv, float* dw_o,
+                      int N, int H, int d, int dm, int p, int L, int K, int scatter_mode,
+                      void* ws, size_t ws_bytes, void* stream);
+
 /* Per-stage timing with HIP events recorded on the caller's stream around
- * each kernel of lh_forward/lh_backward.  enable != 0 starts recording (and
+ * each kernel of lh_forward/lh_backward and each GEMM of lh_block_*.  enable != 0 starts recording (and
  * clears earlier results); lh_stage_timing_read synchronises on the recorded
  * events, adds each stage's elapsed milliseconds into ms[stage] and the
  * number of times the stage ran into count[stage] for stage < n, and returns

@@ -189,3 +189,97 @@ def backward(q, k, v, dout, p, L, K, selection, dtype="bf16", want=("sub",), nth
     if cond is not None:
         res.update(cO=cond[0], cdQ=cond[1], cdK=cond[2], cdV=cond[3])
     return res
+
+
+# ------------------------------------------------------------------ the block
+# The attention block around the layer: Sec. 3.1 Eq. (1) of the Lighthouse
+# paper gives q = x W_Q, k = x W_K, v = x W_V for the layer's input, and Fig. 1
+# shows the projections feeding the pyramid pool; the block output is the
+# layer output times the output projection W_O (the Llama-style models of
+# Sec. 4).  Everything is fp64 except at the layer's boundary: the layer's
+# I/O type is bf16, so every tensor that crosses it (q, k, v and dO = dy W_O^T
+# in; o, dq, dk, dv out) is rounded to bf16, to nearest with ties to even.  The
+# rounding of q and k decides the selection, so it must be taken in the same
+# precision as on the GPU.  With round_io=False nothing is rounded to bf16 (the
+# layer's oracle then reads fp32 values), which makes the block a smooth
+# function of its inputs away from selection changes (used by the gradient
+# pins).
+
+def _bf16_f64(bits):
+    return (np.ascontiguousarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(
+        np.float32).astype(np.float64)
+
+
+def _round_bf16(x64):
+    """fp64 -> nearest bf16 value (ties to even) via fp32; exact when x64 is an fp32 value."""
+    b = np.ascontiguousarray(x64, dtype=np.float32).view(np.uint32)
+    r = (b + np.uint32(0x7FFF) + ((b >> np.uint32(16)) & np.uint32(1))) & np.uint32(0xFFFF0000)
+    return r.view(np.float32)
+
+
+def block_forward(x, w_qkv, w_o, H, d, p, L, K, rows=None, round_io=True, cond=False, nthreads=0):
+    """y = Lighthouse(x W_Q, x W_K, x W_V) W_O for bf16 bit arrays x [N, dm],
+    w_qkv [dm, 3Hd] (columns: W_Q | W_K | W_V), w_o [Hd, dm].
+
+    Returns {"qkv": [3, N, H, d] fp32 layer inputs, "O": [N, H, d] the layer
+    output (bf16 values unless round_io=False), "y": [N or len(rows), dm] fp64,
+    "start", "level", "near_ties", "round_io"}; with cond=True also "cy" =
+    |O| |W_O|, the sums of absolute terms of y (only used to size comparison
+    tolerances: one bf16 ulp of every element of O moves y by up to 2^-8 cy).
+    """
+    X = _bf16_f64(x) if x.dtype == np.uint16 else np.asarray(x, np.float64)
+    Wq = _bf16_f64(w_qkv) if w_qkv.dtype == np.uint16 else np.asarray(w_qkv, np.float64)
+    Wo = _bf16_f64(w_o) if w_o.dtype == np.uint16 else np.asarray(w_o, np.float64)
+    N, hd = X.shape[0], H * d
+    proj = X @ Wq                                   # [N, 3Hd]
+    qkv = np.empty((3, N, H, d), np.float32)
+    for j in range(3):
+        part = proj[:, j * hd:(j + 1) * hd]
+        qkv[j] = (_round_bf16(part) if round_io else part.astype(np.float32)).reshape(N, H, d)
+    r = forward(qkv[0], qkv[1], qkv[2], p, L, K, "fp32", want=("sel", "o"), nthreads=nthreads)
+    O = _round_bf16(r["O"]).astype(np.float64) if round_io else r["O"]
+    Of = O.reshape(N, hd)
+    Or = Of if rows is None else Of[rows]
+    res = {"qkv": qkv, "O": O, "y": Or @ Wo, "start": r["start"], "level": r["level"], "near_ties": r["near_ties"],
+           "round_io": round_io}
+    if cond:
+        res["cy"] = np.abs(Or) @ np.abs(Wo)
+    return res
+
+
+def block_backward(fwd, x, w_qkv, w_o, dy, H, d, p, L, K, rows=None, cols_qkv=None, cols_o=None, cond=False,
+                   nthreads=0):
+    """Gradients of the block for upstream gradient dy [N, dm] (bf16 bits or float).
+
+    fwd is block_forward's result for the same inputs.  dO = dy W_O^T enters the
+    layer's backward (Sec. 3: through the scatter, the attention, the gather and
+    the pool; the selection carries no gradient), then
+    dx = [dq dk dv] W_QKV^T, dW_QKV = x^T [dq dk dv], dW_O = O^T dy.
+    rows / cols_qkv / cols_o select the rows of dx and the columns of the weight
+    gradients to return (None = all).  cond=True adds the sums of absolute
+    terms "cdx", "cdw_qkv", "cdw_o" of the same elements (tolerance sizing only).
+    """
+    X = _bf16_f64(x) if x.dtype == np.uint16 else np.asarray(x, np.float64)
+    Wq = _bf16_f64(w_qkv) if w_qkv.dtype == np.uint16 else np.asarray(w_qkv, np.float64)
+    Wo = _bf16_f64(w_o) if w_o.dtype == np.uint16 else np.asarray(w_o, np.float64)
+    dY = _bf16_f64(dy) if dy.dtype == np.uint16 else np.asarray(dy, np.float64)
+    N, hd = X.shape[0], H * d
+    rnd = fwd["round_io"]
+    dO = dY @ Wo.T
+    dO = (_round_bf16(dO) if rnd else dO.astype(np.float32)).reshape(N, H, d)
+    qkv = fwd["qkv"]
+    g = backward(qkv[0], qkv[1], qkv[2], dO, p, L, K, (fwd["start"], fwd["level"]), "fp32", want=("full",),
+                 nthreads=nthreads)
+    G = np.concatenate([g["dq"].reshape(N, hd), g["dk"].reshape(N, hd), g["dv"].reshape(N, hd)], axis=1)
+    if rnd:
+        G = _round_bf16(G).astype(np.float64)
+    Of = fwd["O"].reshape(N, hd)
+    Gr = G if rows is None else G[rows]
+    Gc = G if cols_qkv is None else G[:, cols_qkv]
+    dYc = dY if cols_o is None else dY[:, cols_o]
+    res = {"dx": Gr @ Wq.T, "dw_qkv": X.T @ Gc, "dw_o": Of.T @ dYc, "dO": dO, "G": G}
+    if cond:
+        res["cdx"] = np.abs(Gr) @ np.abs(Wq.T)
+        res["cdw_qkv"] = np.abs(X.T) @ np.abs(Gc)
+        res["cdw_o"] = np.abs(Of.T) @ np.abs(dYc)
+    return res

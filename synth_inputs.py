@@ -135,6 +135,73 @@ def make_inputs(N: int, H: int, d: int, dtype: str = "bf16", seed: int = 0,
     return out
 
 
+# The attention block around the layer at the 530M model's shape (d_model 2048,
+# 16 heads of 128, 98,304 tokens; the layer's settings of workload 3).
+BLOCK_WORKLOAD = dict(name="llama530m_block_n98304", N=98304, dm=2048, H=16, d=128, p=4, L=4, K=128,
+                      planted=0.01)
+
+X_GRID, GRID_MAX = 16, 256   # x and dy on the grid a / 16 with |a| <= 256
+
+
+def w_grid(fan_in: int) -> int:
+    """Grid 1/G of a weight drawn as N(0, 1/fan_in): G = 2^ceil(log2(16 sqrt(fan_in))), so the
+    grid integers have a standard deviation of 16 to 23 and |b| <= 256 clips nothing below 11 sigma."""
+    return 1 << int(np.ceil(np.log2(16.0 * np.sqrt(fan_in))))
+
+
+def _on_grid(z: np.ndarray, grid: float) -> np.ndarray:
+    return np.clip(np.rint(z * np.float32(grid)), -GRID_MAX, GRID_MAX).astype(np.float32)
+
+
+def _exact_fp32_sums(a: np.ndarray, b: np.ndarray) -> bool:
+    """Every partial sum of a @ b (integer grids) is below 2^24 in magnitude, by Cauchy-Schwarz:
+    max_t |a_t| * max_j |b_j| bounds sum_i |a_ti b_ij|."""
+    return float(np.sqrt(np.square(a, dtype=np.float64).sum(axis=1).max())
+                 * np.sqrt(np.square(b, dtype=np.float64).sum(axis=0).max())) < 2.0 ** 24
+
+
+def make_block_inputs(N: int, dm: int, H: int, d: int, seed: int = 0, planted: float = 0.0,
+                      with_dy: bool = False, threads: int | None = None) -> dict:
+    """Inputs of the attention block, all bf16 bit patterns (uint16).
+
+    x [N, dm] = c_t z with z ~ N(0, 1) and the per-token LogNormal(0, 0.5) scale
+    of the layer's workloads (optionally a fraction of tokens scaled x4), and
+    dy [N, dm] ~ N(0, 1), both on the grid a / 16 with |a| <= 256; w_qkv
+    [dm, 3*H*d] ~ N(0, 1/dm) and w_o [H*d, dm] ~ N(0, 1/(H*d)) on the grids
+    b / w_grid(fan_in) with |b| <= 256.  On these grids the products x w_qkv
+    and dy w_o^T are exact in fp32 whatever the order of summation (checked,
+    see _exact_fp32_sums), so both sides round the same values to bf16 where
+    they enter the layer.
+    """
+    threads = threads or _threads()
+    hd = H * d
+    ss_x, ss_w, ss_o, ss_dy, ss_c = np.random.SeedSequence(seed).spawn(5)
+    gc = np.random.Generator(np.random.PCG64(ss_c))
+    c = gc.lognormal(0.0, 0.5, size=N).astype(np.float32)
+    if planted > 0.0:
+        idx = gc.choice(N, size=int(round(planted * N)), replace=False)
+        c[idx] *= np.float32(4.0)
+    a = _on_grid(_fill_normal((N, 1, dm), ss_x, c, "fp32", threads).reshape(N, dm), X_GRID)
+    gq, go = w_grid(dm), w_grid(hd)
+    b = _on_grid(_fill_normal((dm, 1, 3 * hd), ss_w, None, "fp32", threads).reshape(dm, 3 * hd) / np.sqrt(dm), gq)
+    bo = _on_grid(_fill_normal((hd, 1, dm), ss_o, None, "fp32", threads).reshape(hd, dm) / np.sqrt(hd), go)
+    if not _exact_fp32_sums(a, b):
+        raise ValueError("block inputs too large for exact fp32 sums")
+    out = {"x": bf16_bits(a / np.float32(X_GRID)), "w_qkv": bf16_bits(b / np.float32(gq)),
+           "w_o": bf16_bits(bo / np.float32(go)), "token_scale": c}
+    if with_dy:
+        ady = _on_grid(_fill_normal((N, 1, dm), ss_dy, None, "fp32", threads).reshape(N, dm), X_GRID)
+        if not _exact_fp32_sums(ady, bo.T):
+            raise ValueError("block inputs too large for exact fp32 sums")
+        out["dy"] = bf16_bits(ady / np.float32(X_GRID))
+    return out
+
+
+def block_inputs(with_dy: bool = True, threads: int | None = None) -> dict:
+    w = BLOCK_WORKLOAD
+    return make_block_inputs(w["N"], w["dm"], w["H"], w["d"], workload_seed(6), w["planted"], with_dy, threads)
+
+
 def workload_inputs(index: int, with_dout: bool | None = None, threads: int | None = None) -> dict:
     w = WORKLOADS[index]
     wd = w["backward"] if with_dout is None else with_dout

@@ -51,7 +51,7 @@ def to_f64(t: torch.Tensor) -> np.ndarray:
 U32 = 2.0 ** -24
 
 
-def compare(got, ref, dtype, what="", cond=None, d=128):
+def compare(got, ref, dtype, what="", cond=None, d=128, cond_unit=None):
     got = np.asarray(got, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)
     assert got.shape == ref.shape, (what, got.shape, ref.shape)
@@ -65,7 +65,7 @@ def compare(got, ref, dtype, what="", cond=None, d=128):
     over = scaled_all > t["max_scaled"]
     n_cond = 0
     if cond is not None and over.any():
-        allow = 2.0 * d * U32 * np.asarray(cond, dtype=np.float64)
+        allow = (2.0 * d * U32 if cond_unit is None else cond_unit) * np.asarray(cond, dtype=np.float64)
         bad = over & (err > allow)
         n_cond = int(over.sum() - bad.sum())
         worst = float((err / np.maximum(t["max_scaled"] * np.maximum(1.0, np.abs(ref)), allow))[over].max())
@@ -73,7 +73,7 @@ def compare(got, ref, dtype, what="", cond=None, d=128):
         bad = over
         worst = scaled / t["max_scaled"]
     say(f"    {what}: max_scaled={scaled:.3e} mean_rel={mean_rel:.3e}"
-        + (f" (elements within the fp32 cancellation bound only: {n_cond}, worst/allowed={worst:.2f})"
+        + (f" (elements within the cancellation bound only: {n_cond}, worst/allowed={worst:.2f})"
            if n_cond else ""))
     if bad.any():
         i = np.unravel_index(int(np.argmax(np.where(bad, scaled_all, -1))), err.shape)

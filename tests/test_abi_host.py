@@ -106,3 +106,26 @@ def test_status_strings_and_stage_names():
         assert lh.lh_status_str(rc) and lh.lh_status_str(rc) != "unknown status"
     assert lh.lh_stage_name(0) == "pool_score"
     assert lh.lh_stage_name(99) == "unknown"
+
+
+def test_block_entry_points_validate_before_launching():
+    """The block's host checks return their status without touching the GPU."""
+    lh = _lh()
+    N, H, d, dm, p, L, K = 2048, 2, 64, 128, 4, 3, 16
+    nb = lh.lh_block_workspace_bytes(N, H, d, dm, p, L, K)
+    assert nb > lh.lh_workspace_bytes(N, H, d, p, L, K, 0)
+    assert lh.lh_block_workspace_bytes(N, H, d, 100, p, L, K) == 0       # dm not a multiple of 8
+    assert lh.lh_block_workspace_bytes(N, H, 96, dm, p, L, K) == 0       # d not in {64, 128}
+    assert lh.lh_block_workspace_bytes(2047, H, d, dm, p, L, K) == 0     # p^(L-1) does not divide N
+    fake = 1 << 20                                                       # never dereferenced
+    args = (fake, fake, fake, fake, fake)
+    assert lh.lh_block_forward(*args, N, H, d, 100, p, L, K, fake * 256, nb, None) == lh.LH_ERR_SHAPE
+    assert lh.lh_block_forward(None, fake, fake, fake, fake, N, H, d, dm, p, L, K, fake * 256, nb,
+                               None) == lh.LH_ERR_ARG
+    assert lh.lh_block_forward(*args, N, H, d, dm, p, L, K, fake * 256, nb - 1, None) == lh.LH_ERR_WORKSPACE
+    assert lh.lh_block_forward(fake + 8, fake, fake, fake, fake, N, H, d, dm, p, L, K, fake * 256, nb,
+                               None) == lh.LH_ERR_ARG                    # misaligned x
+    bargs = (fake,) * 8
+    assert lh.lh_block_backward(*bargs, N, H, d, dm, p, L, K, 5, fake * 256, nb, None) == lh.LH_ERR_DTYPE
+    assert lh.lh_block_backward(*bargs, N, H, d, dm, p, L, K, 0, fake * 256, nb - 1, None) == lh.LH_ERR_WORKSPACE
+    assert lh.lh_status_str(lh.LH_ERR_GEMM).startswith("GEMM")
