@@ -16,13 +16,14 @@ LIB_PATH = os.path.join(_HERE, "liblighthouse.so")
 LH_OK, LH_ERR_ARG, LH_ERR_SHAPE, LH_ERR_DTYPE, LH_ERR_WORKSPACE, LH_ERR_HIP, LH_ERR_GEMM = 0, -1, -2, -3, -4, -5, -6
 LH_BF16, LH_FP32 = 0, 1
 LH_SCATTER_FP_ATOMIC, LH_SCATTER_INT_ATOMIC = 0, 1
+LH_SCORE_QK, LH_SCORE_K, LH_SCORE_Q, LH_SCORE_QK_PRODUCT = 0, 1, 2, 3
 VIEWS = {"scores": 0, "sel_start": 1, "sel_level": 2, "qsub": 3, "ksub": 4, "vsub": 5, "osub": 6,
          "lse": 7, "dosub": 8, "dqsub": 9, "dksub": 10, "dvsub": 11, "block_first": 12}
 
 EXPORTS = ("lh_subseq_len", "lh_workspace_bytes", "lh_forward", "lh_backward", "lh_workspace_view",
            "lh_dense_workspace_bytes", "lh_dense_attn_fwd", "lh_dense_attn_bwd", "lh_stage_timing",
            "lh_stage_timing_read", "lh_stage_name", "lh_status_str", "lh_read_selection", "lh_peak_probe",
-           "lh_block_workspace_bytes", "lh_block_forward", "lh_block_backward")
+           "lh_block_workspace_bytes", "lh_block_forward", "lh_block_backward", "lh_forward_scored")
 
 
 class LighthouseError(RuntimeError):
@@ -38,6 +39,7 @@ def _load():
         "lh_subseq_len": (i64, [i, i, i, i]),
         "lh_workspace_bytes": (sz, [i, i, i, i, i, i, i]),
         "lh_forward": (i, [vp, vp, vp, vp, i, i, i, i, i, i, i, vp, sz, vp]),
+        "lh_forward_scored": (i, [vp, vp, vp, vp, i, i, i, i, i, i, i, i, vp, sz, vp]),
         "lh_backward": (i, [vp, vp, vp, vp, i, i, i, i, i, i, i, i, vp, sz, vp]),
         "lh_workspace_view": (i, [vp, i, i, i, i, i, i, i, i, C.POINTER(vp), C.POINTER(sz)]),
         "lh_read_selection": (i, [vp, i, i, i, i, i, i, i, vp, vp, vp]),
@@ -66,6 +68,7 @@ _L = _load()
 lh_subseq_len = _L.lh_subseq_len
 lh_workspace_bytes = _L.lh_workspace_bytes
 lh_forward = _L.lh_forward
+lh_forward_scored = _L.lh_forward_scored
 lh_backward = _L.lh_backward
 lh_dense_workspace_bytes = _L.lh_dense_workspace_bytes
 lh_dense_attn_fwd = _L.lh_dense_attn_fwd
@@ -142,8 +145,10 @@ def alloc_workspace(N, H, d, p, L, K, dtype, device="cuda"):
     return torch.empty(nbytes, dtype=torch.uint8, device=device)
 
 
-def forward(q, k, v, p, L, K, ws=None, out=None, stream=None):
-    """o = Lighthouse layer(q, k, v) for [N, H, d] tensors.  Returns (o, ws)."""
+def forward(q, k, v, p, L, K, ws=None, out=None, stream=None, score_mode=LH_SCORE_QK):
+    """o = Lighthouse layer(q, k, v) for [N, H, d] tensors.  Returns (o, ws).
+
+    score_mode other than LH_SCORE_QK selects with an alternative score (lh_forward_scored)."""
     torch = _torch()
     _dev_tensor_check(q, k, v)
     N, H, d = q.shape
@@ -152,8 +157,12 @@ def forward(q, k, v, p, L, K, ws=None, out=None, stream=None):
         ws = alloc_workspace(N, H, d, p, L, K, dt, q.device)
     if out is None:
         out = torch.empty_like(q)
-    rc = lh_forward(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), N, H, d, p, L, K, dt,
-                    ws.data_ptr(), ws.numel(), _stream_handle(stream))
+    if score_mode == LH_SCORE_QK:
+        rc = lh_forward(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), N, H, d, p, L, K, dt,
+                        ws.data_ptr(), ws.numel(), _stream_handle(stream))
+    else:
+        rc = lh_forward_scored(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), N, H, d, p, L, K, dt,
+                               score_mode, ws.data_ptr(), ws.numel(), _stream_handle(stream))
     _check(rc, "lh_forward")
     return out, ws
 

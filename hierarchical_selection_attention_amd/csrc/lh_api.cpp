@@ -233,9 +233,16 @@ static SplitSpec split_spec(const Plan& P, char* w, size_t src, unsigned int* hm
 
 int lh_forward(const void* q, const void* k, const void* v, void* o, int N, int H, int d, int p, int L,
                int K, int dtype, void* ws, size_t ws_bytes, void* stream) {
+    return lh_forward_scored(q, k, v, o, N, H, d, p, L, K, dtype, LH_SCORE_QK, ws, ws_bytes, stream);
+}
+
+int lh_forward_scored(const void* q, const void* k, const void* v, void* o, int N, int H, int d, int p, int L,
+                      int K, int dtype, int score_mode, void* ws, size_t ws_bytes, void* stream) {
     Plan P;
     int rc = make_plan(N, H, d, p, L, K, dtype, &P);
     if (rc) return rc;
+    if (score_mode < LH_SCORE_QK || score_mode > LH_SCORE_QK_PRODUCT) return LH_ERR_DTYPE;
+    P.score_mode = score_mode;
     if (!q || !k || !v || !o) return LH_ERR_ARG;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return LH_ERR_ARG;
     if ((rc = check_ws(P, ws, ws_bytes))) return rc;

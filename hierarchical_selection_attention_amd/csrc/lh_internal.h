@@ -48,6 +48,7 @@ int backward_strided(const void* dout, void* dq, void* dk, void* dv, int N, int 
 
 struct Plan {
     int N, H, d, p, L, K, dtype, esz;
+    int score_mode;         // leaf score: 0 |q|^2+|k|^2, 1 |k|^2, 2 |q|^2, 3 |q|^2*|k|^2
     int64_t S, Sp;
     int m;                  // pyramid level produced per workgroup by the pooling pass
     int rowcopy;            // bf16: back-scatter and pool adjoint copy bf16 rows the attention leaves

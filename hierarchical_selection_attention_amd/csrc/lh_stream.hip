@@ -18,15 +18,22 @@ namespace lh {
 // and their max-pool for levels 0..m, and the level-m means of q, k, v (fp32).
 // The leaf score is ||q||^2 + ||k||^2 in fp32 in a fixed order: fma over the 8
 // elements of a lane from +0, then a xor butterfly over the G lanes of the row,
-// then one add of the q and k parts.
+// then one add of the q and k parts.  The other readings of what the norm is
+// taken of are score modes: ||k||^2, ||q||^2, or ||q||^2 * ||k||^2 (one fp32
+// multiply, ranking as ||q|| ||k||).
 struct PoolScoreArgs {
     const void *q, *k, *v;
     float* lev[kMaxLevels];   // level l scores, [H][n_l]
     float* pool_m;            // fp32 [3][n_m][H][d]
     int64_t n[kMaxLevels];
     int N, H, HG, p, m, tok, mt;
+    int score_mode;
     int64_t pw[kMaxLevels];
 };
+
+__device__ __forceinline__ float leaf_score(float sq, float sk, int mode) {
+    return mode == 1 ? sk : mode == 2 ? sq : mode == 3 ? sq * sk : sq + sk;
+}
 
 // Tokens per load batch of the bf16 pooling pass (two batches in flight per wave).
 // One is fastest on MI355X at d = 128: 90 VGPRs, five waves per SIMD; the read
@@ -72,7 +79,7 @@ __global__ void __launch_bounds__(256) k_pool_score(PoolScoreArgs a) {
             sq = sq + shfl_xor_f(sq, off);
             sk = sk + shfl_xor_f(sk, off);
         }
-        if (c == 0) sc[hl * a.tok + tl] = sq + sk;
+        if (c == 0) sc[hl * a.tok + tl] = leaf_score(sq, sk, a.score_mode);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             aq[e] += xq[e];
@@ -143,7 +150,8 @@ __global__ void __launch_bounds__(256) k_pool_score(PoolScoreArgs a) {
 #undef LH_BFLY
             if (c == 0) {
 #pragma unroll
-                for (int u = 0; u < U; ++u) sc[hl * a.tok + ts + a.mt * (i0 + u)] = sq[u] + sk[u];
+                for (int u = 0; u < U; ++u)
+                    sc[hl * a.tok + ts + a.mt * (i0 + u)] = leaf_score(sq[u], sk[u], a.score_mode);
             }
         };
         // full batches of UB tokens, double-buffered: the loads of batch b+1 are
@@ -750,6 +758,7 @@ hipError_t launch_pool_score(const Plan& P, const void* q, const void* k, const 
     }
     a.pool_m = reinterpret_cast<float*>(ws + P.off_pool_m);
     a.N = P.N; a.H = P.H; a.p = P.p; a.m = P.m; a.tok = (int)P.tok;
+    a.score_mode = P.score_mode;
     const int G = P.d / 8;
     a.HG = head_group(P.H, G);
     // token lanes must divide tok (a power of p): use powers of p

@@ -84,6 +84,28 @@ int lh_forward(const void* q, const void* k, const void* v, void* o,
                int N, int H, int d, int p, int L, int K, int dtype,
                void* ws, size_t ws_bytes, void* stream);
 
+/* What the parameter-free score is taken of.  The pages call the scoring
+ * bidirectional (Sec. 1) and label Fig. 2's scores "qk" / "kq" without fixing
+ * the formula.  LH_SCORE_QK, the reading lh_forward uses, scores a leaf by
+ * ||q||^2 + ||k||^2; the alternatives score it by ||k||^2, by ||q||^2, or by
+ * ||q||^2 * ||k||^2 (ranks as ||q|| ||k||).  Each squared norm is summed in
+ * fp32 in the fixed order of the default score (fma over 8 consecutive
+ * elements from +0, then a xor butterfly over the d/8 groups); the product
+ * is one fp32 multiply.  Coarser levels take the max of their p children in
+ * every mode. */
+typedef enum {
+    LH_SCORE_QK = 0,
+    LH_SCORE_K = 1,
+    LH_SCORE_Q = 2,
+    LH_SCORE_QK_PRODUCT = 3
+} lh_score_mode;
+
+/* lh_forward with the score of `score_mode` (lh_score_mode; LH_ERR_DTYPE for
+ * an unknown mode).  Everything else, lh_backward included, is unchanged. */
+int lh_forward_scored(const void* q, const void* k, const void* v, void* o,
+                      int N, int H, int d, int p, int L, int K, int dtype, int score_mode,
+                      void* ws, size_t ws_bytes, void* stream);
+
 /* Backward pass through the scatter, the attention, the gather and the pool
  * (Fig. 1 gradient path).  q, k, v are not needed: everything is read from
  * the workspace of the matching lh_forward.  Writes dq, dk, dv [N][H][d]. */

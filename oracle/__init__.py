@@ -44,9 +44,9 @@ def lib():
         L.lho_pyramid.restype = i32
         L.lho_pyramid.argtypes = [vp, i32, i32, i32, i32, i32, i32, vp]
         L.lho_leaf_scores.restype = i32
-        L.lho_leaf_scores.argtypes = [vp, vp, i32, i32, i32, i32, vp]
+        L.lho_leaf_scores.argtypes = [vp, vp, i32, i32, i32, i32, i32, vp]
         L.lho_forward.restype = i32
-        L.lho_forward.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32,
+        L.lho_forward.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32, i32,
                                   vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32]
         L.lho_backward.restype = i32
         L.lho_backward.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, vp, vp,
@@ -92,21 +92,26 @@ def pyramid(x, p, L, dtype="bf16"):
     return res
 
 
-def leaf_scores(q, k, dtype="bf16"):
-    """fp32 leaf scores [H, N] in the fixed reduction order."""
+SCORE_MODES = {"qk": 0, "k": 1, "q": 2, "qk_product": 3}
+
+
+def leaf_scores(q, k, dtype="bf16", score_mode=0):
+    """fp32 leaf scores [H, N] in the fixed reduction order (score_mode: see SCORE_MODES)."""
     q = _in(q, dtype)
     k = _in(k, dtype)
     N, H, d = q.shape
     out = np.zeros((H, N), np.float32)
-    rc = lib().lho_leaf_scores(_ptr(q), _ptr(k), N, H, d, DTYPES[dtype], _ptr(out))
+    rc = lib().lho_leaf_scores(_ptr(q), _ptr(k), N, H, d, DTYPES[dtype], int(score_mode), _ptr(out))
     if rc:
         raise ValueError(f"lho_leaf_scores failed ({rc})")
     return out
 
 
-def forward(q, k, v, p, L, K, dtype="bf16", want=("sel",), selection=None, nthreads=0):
+def forward(q, k, v, p, L, K, dtype="bf16", want=("sel",), selection=None, nthreads=0, score_mode=0):
     """Run the oracle forward pass.
 
+    score_mode: 0 = |q|^2 + |k|^2 (the default reading), 1 = |k|^2, 2 = |q|^2,
+    3 = |q|^2 * |k|^2 (see SCORE_MODES).
     want: any of "levels", "sel", "sub" (Qt, Kt, Vt), "ot" (Ot, lse), "o" (full O).
     selection: optional (start, level) arrays [H, S] to freeze the selection.
     Returns a dict.
@@ -137,7 +142,7 @@ def forward(q, k, v, p, L, K, dtype="bf16", want=("sel",), selection=None, nthre
     lse = np.zeros((H, S)) if ot else None
     O = np.zeros((N, H, d)) if "o" in want else None
     ties = np.zeros(H, np.int32)
-    rc = lib().lho_forward(_ptr(q), _ptr(k), _ptr(v), N, H, d, DTYPES[dtype], p, L, K, given,
+    rc = lib().lho_forward(_ptr(q), _ptr(k), _ptr(v), N, H, d, DTYPES[dtype], p, L, K, int(score_mode), given,
                            _ptr(levels), _ptr(st), _ptr(lv), _ptr(Qt), _ptr(Kt), _ptr(Vt), _ptr(Ot),
                            _ptr(lse), _ptr(O), _ptr(ties), nthreads)
     if rc:

@@ -19,7 +19,10 @@
  * its reason in the design notes that ship with the repository):
  *   R1 score of an entry = ||q||^2 + ||k||^2 of its leaves (no sqrt: monotone),
  *      coarser levels take the max over their p children (Fig. 2 "l2 norm +
- *      max-pool");
+ *      max-pool").  The other readings of what the norm is taken of (Sec. 1
+ *      "bidirectional"; Fig. 2 "qk scores kq") are score modes: 1 = ||k||^2,
+ *      2 = ||q||^2, 3 = ||q||^2 * ||k||^2 (ranks as ||q|| ||k||; one fp32
+ *      multiply of the two fixed-order sums);
  *   R2 selection is top-down: K entries per level and per head, ordered by
  *      (score descending, index ascending); a selected entry is replaced by
  *      its p children, an unselected candidate is kept as it is, so the kept
@@ -155,7 +158,18 @@ static float ssq_fixed_order(const float* x, int d) {
     return a[0];
 }
 
-static void head_leaf_scores(const void* q, const void* k, int N, int H, int d, int dtype, int h, float* s0) {
+/* Leaf score from the two fixed-order sums of squares, by score mode (R1). */
+static float leaf_score(float sq, float sk, int mode) {
+    switch (mode) {
+        case 1: return sk;
+        case 2: return sq;
+        case 3: return sq * sk;
+        default: return sq + sk;
+    }
+}
+
+static void head_leaf_scores(const void* q, const void* k, int N, int H, int d, int dtype, int mode, int h,
+                             float* s0) {
     float xq[512], xk[512];
     for (int64_t t = 0; t < N; ++t) {
         int64_t base = (t * H + h) * (int64_t)d;
@@ -163,29 +177,31 @@ static void head_leaf_scores(const void* q, const void* k, int N, int H, int d, 
             xq[e] = load_f32(q, dtype, base + e);
             xk[e] = load_f32(k, dtype, base + e);
         }
-        s0[t] = ssq_fixed_order(xq, d) + ssq_fixed_order(xk, d);
+        s0[t] = leaf_score(ssq_fixed_order(xq, d), ssq_fixed_order(xk, d), mode);
     }
 }
 
-/* Same quantity in fp64 with a plain sum, for the near-tie report only. */
-static void head_leaf_scores64(const void* q, const void* k, int N, int H, int d, int dtype, int h, double* s0) {
+/* Same quantity in fp64 with plain sums, for the near-tie report only. */
+static void head_leaf_scores64(const void* q, const void* k, int N, int H, int d, int dtype, int mode, int h,
+                               double* s0) {
     for (int64_t t = 0; t < N; ++t) {
         int64_t base = (t * H + h) * (int64_t)d;
-        double acc = 0.0;
+        double aq = 0.0, ak = 0.0;
         for (int e = 0; e < d; ++e) {
             double a = load_f32(q, dtype, base + e), b = load_f32(k, dtype, base + e);
-            acc += a * a + b * b;
+            aq += a * a;
+            ak += b * b;
         }
-        s0[t] = acc;
+        s0[t] = mode == 1 ? ak : mode == 2 ? aq : mode == 3 ? aq * ak : aq + ak;
     }
 }
 
 /* Leaf scores for every head: s0 is [H][N]. */
-int lho_leaf_scores(const void* q, const void* k, int N, int H, int d, int dtype, float* s0) {
+int lho_leaf_scores(const void* q, const void* k, int N, int H, int d, int dtype, int mode, float* s0) {
     int rc = check_shape(N, H, d, dtype, 2, 1, 0);
     if (rc) return rc;
-    if (d > 512) return LHO_ERR_ARG;
-    for (int h = 0; h < H; ++h) head_leaf_scores(q, k, N, H, d, dtype, h, s0 + (int64_t)h * N);
+    if (d > 512 || mode < 0 || mode > 3) return LHO_ERR_ARG;
+    for (int h = 0; h < H; ++h) head_leaf_scores(q, k, N, H, d, dtype, mode, h, s0 + (int64_t)h * N);
     return LHO_OK;
 }
 
@@ -409,6 +425,7 @@ typedef struct {
     const void *q, *k, *v, *dout;
     int N, H, d, dtype, p, L, K;
     int64_t S;
+    int score_mode;   /* R1 and its alternatives, see leaf_score */
 } ctx_t;
 
 /* Scores, levels and the selection for head h.  Returns 0 or an error. */
@@ -427,10 +444,10 @@ static int head_scores_select(const ctx_t* c, int h, float* levels_out, int32_t*
             if (!lev64[l]) { rc = LHO_ERR_MEM; goto done; }
         }
     }
-    head_leaf_scores(c->q, c->k, c->N, c->H, c->d, c->dtype, h, lev[0]);
+    head_leaf_scores(c->q, c->k, c->N, c->H, c->d, c->dtype, c->score_mode, h, lev[0]);
     max_pool_levels_f32(lev, c->N, c->p, L);
     if (lev64) {
-        head_leaf_scores64(c->q, c->k, c->N, c->H, c->d, c->dtype, h, lev64[0]);
+        head_leaf_scores64(c->q, c->k, c->N, c->H, c->d, c->dtype, c->score_mode, h, lev64[0]);
         max_pool_levels_f64(lev64, c->N, c->p, L);
     }
     if (levels_out) {
@@ -469,6 +486,8 @@ static void head_gather(const ctx_t* c, const void* x, int h, const int32_t* st,
 
 /*
  * Forward pass (Fig. 1 forward path).  Output pointers may be NULL.
+ *   score_mode: 0 = ||q||^2 + ||k||^2 (R1), 1 = ||k||^2, 2 = ||q||^2,
+ *       3 = ||q||^2 * ||k||^2
  *   score_levels [sum_l H*N/p^l] fp32, level-major then [H][n_l]
  *   sel_start, sel_level [H][S]: written unless given_sel != 0, in which case
  *       they are read (the selection is frozen; used for finite differences)
@@ -478,13 +497,14 @@ static void head_gather(const ctx_t* c, const void* x, int h, const int32_t* st,
  *       1e-6 relative (reported, not an error)
  */
 int lho_forward(const void* q, const void* k, const void* v, int N, int H, int d, int dtype,
-                int p, int L, int K, int given_sel, float* score_levels,
+                int p, int L, int K, int score_mode, int given_sel, float* score_levels,
                 int32_t* sel_start, int8_t* sel_level, double* Qt, double* Kt, double* Vt,
                 double* Ot, double* lse, double* O, int* near_ties, int nthreads) {
     int rc = check_shape(N, H, d, dtype, p, L, K);
     if (rc) return rc;
     if (d > 512 || !sel_start || !sel_level) return LHO_ERR_ARG;
-    ctx_t c = {q, k, v, NULL, N, H, d, dtype, p, L, K, lho_subseq_len(N, p, L, K)};
+    if (score_mode < 0 || score_mode > 3) return LHO_ERR_ARG;
+    ctx_t c = {q, k, v, NULL, N, H, d, dtype, p, L, K, lho_subseq_len(N, p, L, K), score_mode};
     int64_t S = c.S;
     int err = 0;
 #ifdef _OPENMP
@@ -557,7 +577,7 @@ int lho_backward(const void* q, const void* k, const void* v, const void* dout, 
     int rc = check_shape(N, H, d, dtype, p, L, K);
     if (rc) return rc;
     if (d > 512 || !sel_start || !sel_level || !dout) return LHO_ERR_ARG;
-    ctx_t c = {q, k, v, dout, N, H, d, dtype, p, L, K, lho_subseq_len(N, p, L, K)};
+    ctx_t c = {q, k, v, dout, N, H, d, dtype, p, L, K, lho_subseq_len(N, p, L, K), 0};
     int64_t S = c.S;
     int err = 0;
 #ifdef _OPENMP

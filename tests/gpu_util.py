@@ -86,7 +86,7 @@ def compare(got, ref, dtype, what="", cond=None, d=128, cond_unit=None):
 class Run:
     """One forward (+ optional backward) of the HIP path with its workspace kept."""
 
-    def __init__(self, x, dtype, p, L, K, backward=False, mode=0, label=""):
+    def __init__(self, x, dtype, p, L, K, backward=False, mode=0, label="", score_mode=0):
         lh = lib()
         self.dtype, self.p, self.L, self.K = dtype, p, L, K
         self.N, self.H, self.d = x["q"].shape
@@ -94,9 +94,9 @@ class Run:
         self.S = int(lh.lh_subseq_len(self.N, p, L, K))
         self.Sp = (self.S + 63) // 64 * 64
         say(f"  GPU run {label}: N={self.N} H={self.H} d={self.d} {dtype} p={p} L={L} K={K} "
-            f"S={self.S} backward={backward} mode={mode}")
+            f"S={self.S} backward={backward} mode={mode} score_mode={score_mode}")
         self.q, self.k, self.v = (to_dev(x[n], dtype) for n in ("q", "k", "v"))
-        self.o, self.ws = lh.forward(self.q, self.k, self.v, p, L, K)
+        self.o, self.ws = lh.forward(self.q, self.k, self.v, p, L, K, score_mode=score_mode)
         if backward:
             self.dout = to_dev(x["dout"], dtype)
             self.grads = lh.backward(self.dout, p, L, K, self.ws, mode=mode)

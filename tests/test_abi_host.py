@@ -129,3 +129,13 @@ def test_block_entry_points_validate_before_launching():
     assert lh.lh_block_backward(*bargs, N, H, d, dm, p, L, K, 5, fake * 256, nb, None) == lh.LH_ERR_DTYPE
     assert lh.lh_block_backward(*bargs, N, H, d, dm, p, L, K, 0, fake * 256, nb - 1, None) == lh.LH_ERR_WORKSPACE
     assert lh.lh_status_str(lh.LH_ERR_GEMM).startswith("GEMM")
+
+
+def test_scored_forward_rejects_unknown_score_mode():
+    lh = _lh()
+    fake = 1 << 20                                                       # never dereferenced
+    nb = lh.lh_workspace_bytes(2048, 2, 64, 4, 3, 16, 1)
+    assert lh.lh_forward_scored(fake, fake, fake, fake, 2048, 2, 64, 4, 3, 16, 1, 7, fake * 256, nb,
+                                None) == lh.LH_ERR_DTYPE
+    assert lh.lh_forward_scored(fake, fake, fake, fake, 2048, 2, 64, 4, 3, 16, 1, -1, fake * 256, nb,
+                                None) == lh.LH_ERR_DTYPE
