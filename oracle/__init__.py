@@ -41,15 +41,17 @@ def lib():
         vp, i32, i64, dp, fp = C.c_void_p, C.c_int, C.c_int64, C.POINTER(C.c_double), C.c_void_p
         L.lho_subseq_len.restype = i64
         L.lho_subseq_len.argtypes = [i32, i32, i32, i32]
+        L.lho_subseq_len_sel.restype = i64
+        L.lho_subseq_len_sel.argtypes = [i32, i32, i32, i32, i32]
         L.lho_pyramid.restype = i32
         L.lho_pyramid.argtypes = [vp, i32, i32, i32, i32, i32, i32, vp]
         L.lho_leaf_scores.restype = i32
         L.lho_leaf_scores.argtypes = [vp, vp, i32, i32, i32, i32, i32, vp]
         L.lho_forward.restype = i32
-        L.lho_forward.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32, i32,
+        L.lho_forward.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32, i32, i32,
                                   vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32]
         L.lho_backward.restype = i32
-        L.lho_backward.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, vp, vp,
+        L.lho_backward.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32, vp, vp,
                                    vp, vp, vp, vp, vp, vp, vp, vp, i32]
         _lib = L
         del dp, fp
@@ -68,8 +70,11 @@ def _in(x, dtype):
     return x
 
 
-def subseq_len(N, p, L, K) -> int:
-    return int(lib().lho_subseq_len(N, p, L, K))
+SELECT_MODES = {"partition": 0, "parent_kept": 1}
+
+
+def subseq_len(N, p, L, K, select_mode=0) -> int:
+    return int(lib().lho_subseq_len_sel(N, p, L, K, int(select_mode)))
 
 
 def score_level_sizes(N, p, L):
@@ -107,8 +112,13 @@ def leaf_scores(q, k, dtype="bf16", score_mode=0):
     return out
 
 
-def forward(q, k, v, p, L, K, dtype="bf16", want=("sel",), selection=None, nthreads=0, score_mode=0):
+def forward(q, k, v, p, L, K, dtype="bf16", want=("sel",), selection=None, nthreads=0, score_mode=0,
+            select_mode=0):
     """Run the oracle forward pass.
+
+    select_mode: 0 = the kept entries partition [0, N) (default reading), 1 = a
+    selected parent stays beside its children and outputs of overlapping
+    entries are summed (see SELECT_MODES).
 
     score_mode: 0 = |q|^2 + |k|^2 (the default reading), 1 = |k|^2, 2 = |q|^2,
     3 = |q|^2 * |k|^2 (see SCORE_MODES).
@@ -118,7 +128,7 @@ def forward(q, k, v, p, L, K, dtype="bf16", want=("sel",), selection=None, nthre
     """
     q, k, v = _in(q, dtype), _in(k, dtype), _in(v, dtype)
     N, H, d = q.shape
-    S = subseq_len(N, p, L, K)
+    S = subseq_len(N, p, L, K, select_mode)
     if S < 0:
         raise ValueError("invalid (N, p, L, K)")
     res = {"S": S}
@@ -142,7 +152,8 @@ def forward(q, k, v, p, L, K, dtype="bf16", want=("sel",), selection=None, nthre
     lse = np.zeros((H, S)) if ot else None
     O = np.zeros((N, H, d)) if "o" in want else None
     ties = np.zeros(H, np.int32)
-    rc = lib().lho_forward(_ptr(q), _ptr(k), _ptr(v), N, H, d, DTYPES[dtype], p, L, K, int(score_mode), given,
+    rc = lib().lho_forward(_ptr(q), _ptr(k), _ptr(v), N, H, d, DTYPES[dtype], p, L, K, int(score_mode),
+                           int(select_mode), given,
                            _ptr(levels), _ptr(st), _ptr(lv), _ptr(Qt), _ptr(Kt), _ptr(Vt), _ptr(Ot),
                            _ptr(lse), _ptr(O), _ptr(ties), nthreads)
     if rc:
@@ -164,7 +175,7 @@ def forward(q, k, v, p, L, K, dtype="bf16", want=("sel",), selection=None, nthre
     return res
 
 
-def backward(q, k, v, dout, p, L, K, selection, dtype="bf16", want=("sub",), nthreads=0):
+def backward(q, k, v, dout, p, L, K, selection, dtype="bf16", want=("sub",), nthreads=0, select_mode=0):
     """Oracle backward with a given selection.
 
     want: "sub" (dOt, dQt, dKt, dVt), "full" (dq, dk, dv), "cond" (absolute term sums
@@ -173,7 +184,7 @@ def backward(q, k, v, dout, p, L, K, selection, dtype="bf16", want=("sub",), nth
     """
     q, k, v, dout = _in(q, dtype), _in(k, dtype), _in(v, dtype), _in(dout, dtype)
     N, H, d = q.shape
-    S = subseq_len(N, p, L, K)
+    S = subseq_len(N, p, L, K, select_mode)
     st = np.ascontiguousarray(selection[0], dtype=np.int32).reshape(H, S)
     lv = np.ascontiguousarray(selection[1], dtype=np.int8).reshape(H, S)
     sub = "sub" in want
@@ -182,7 +193,7 @@ def backward(q, k, v, dout, p, L, K, selection, dtype="bf16", want=("sub",), nth
     dq, dk, dv = ((np.zeros((N, H, d)) if full else None) for _ in range(3))
     cond = np.zeros((4, H, S, d)) if "cond" in want else None
     rc = lib().lho_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), N, H, d, DTYPES[dtype], p, L, K,
-                            _ptr(st), _ptr(lv), _ptr(dOt), _ptr(dQt), _ptr(dKt), _ptr(dVt),
+                            int(select_mode), _ptr(st), _ptr(lv), _ptr(dOt), _ptr(dQt), _ptr(dKt), _ptr(dVt),
                             _ptr(dq), _ptr(dk), _ptr(dv), _ptr(cond), nthreads)
     if rc:
         raise RuntimeError(f"lho_backward failed ({rc})")

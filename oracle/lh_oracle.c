@@ -33,6 +33,12 @@
  *      ordinary lower-triangular mask;
  *   R5 scatter copies each output to the p^l tokens its entry covers
  *      (Sec. 3 stage (iv)); the gradient of the mean-pool divides by p^l.
+ *   R2' the other reading of "parent kept" (select mode 1): a selected entry
+ *      stays in the sequence next to its p children, so every candidate of
+ *      every level is kept and the entries overlap; they are ordered by first
+ *      token, the coarser entry first where two start together; a token's
+ *      output is the sum of the outputs of the entries that cover it, and
+ *      the adjoints sum likewise.
  *
  * dtype codes: 0 = bf16 (raw uint16 bit patterns), 1 = fp32.
  * Tensors q, k, v, dO, O, dq, dk, dv are [N][H][d] (token-major); the
@@ -85,18 +91,21 @@ static int check_shape(int N, int H, int d, int dtype, int p, int L, int K) {
 /* Number of kept entries S for (N, p, L, K) under reading R2: start with all
  * N/p^(L-1) top entries; each of the min(K, #candidates) selections at a
  * level replaces one entry by p children. */
-int64_t lho_subseq_len(int N, int p, int L, int K) {
-    if (N <= 0 || p < 2 || L < 1 || K < 0) return -1;
+int64_t lho_subseq_len_sel(int N, int p, int L, int K, int select_mode) {
+    if (N <= 0 || p < 2 || L < 1 || K < 0 || select_mode < 0 || select_mode > 1) return -1;
     int64_t top = ipow(p, L - 1);
     if (top > N || N % top != 0) return -1;
     int64_t n = N / top, S = n, cand = n;
     for (int l = L - 1; l >= 1; --l) {
         int64_t sel = cand < K ? cand : K;
-        S += sel * (p - 1);
+        /* partition: a selected entry gives way to its p children; parent kept: it stays */
+        S += sel * (select_mode ? p : p - 1);
         cand = sel * p;
     }
     return S;
 }
+
+int64_t lho_subseq_len(int N, int p, int L, int K) { return lho_subseq_len_sel(N, p, L, K, 0); }
 
 /* ------------------------------------------------------------- pyramid (O1) */
 
@@ -262,7 +271,8 @@ typedef struct {
 static int entry_cmp(const void* pa, const void* pb) {
     const entry_t* a = (const entry_t*)pa;
     const entry_t* b = (const entry_t*)pb;
-    return a->start < b->start ? -1 : (a->start > b->start ? 1 : 0);
+    if (a->start != b->start) return a->start < b->start ? -1 : 1;
+    return a->level > b->level ? -1 : (a->level < b->level ? 1 : 0);   /* coarser first (R2') */
 }
 
 static uint32_t f32_bits(float f) {
@@ -275,11 +285,11 @@ static uint32_t f32_bits(float f) {
  * (reading R3).  lev[l] holds the fp32 scores of level l.  Writes S entries
  * to start/level and returns S (or -1 on allocation failure).  lev64 (may be
  * NULL) gives fp64 scores for the near-tie count. */
-static int64_t head_select(float** lev, double** lev64, int N, int p, int L, int K,
+static int64_t head_select(float** lev, double** lev64, int N, int p, int L, int K, int select_mode,
                            int32_t* start_out, int8_t* level_out, int* near_ties) {
     int64_t n_top = N / ipow(p, L - 1);
     int64_t cap = n_top > (int64_t)K * p ? n_top : (int64_t)K * p;
-    int64_t S_max = lho_subseq_len(N, p, L, K);
+    int64_t S_max = lho_subseq_len_sel(N, p, L, K, select_mode);
     int64_t* cand = (int64_t*)malloc(sizeof(int64_t) * (size_t)cap);
     int64_t* next = (int64_t*)malloc(sizeof(int64_t) * (size_t)cap);
     int64_t* sel = (int64_t*)malloc(sizeof(int64_t) * (size_t)(K + 1));
@@ -304,10 +314,14 @@ static int64_t head_select(float** lev, double** lev64, int N, int p, int L, int
         }
         for (int64_t s = 0; s < nsel; ++s) sel[s] = keys[s].idx;
         qsort(sel, (size_t)nsel, sizeof(int64_t), i64_cmp);
-        /* candidates not selected are kept at this level (cand is ascending) */
+        /* candidates not selected are kept at this level (cand is ascending);
+           with the parent kept (R2') the selected ones are kept as well */
         int64_t s = 0;
         for (int64_t c = 0; c < ncand; ++c) {
-            if (s < nsel && sel[s] == cand[c]) { ++s; continue; }
+            if (s < nsel && sel[s] == cand[c]) {
+                ++s;
+                if (!select_mode) continue;
+            }
             E[nE].start = cand[c] * ipow(p, l);
             E[nE].level = l;
             ++nE;
@@ -426,6 +440,7 @@ typedef struct {
     int N, H, d, dtype, p, L, K;
     int64_t S;
     int score_mode;   /* R1 and its alternatives, see leaf_score */
+    int select_mode;  /* 0: partition (R2), 1: parent kept (R2') */
 } ctx_t;
 
 /* Scores, levels and the selection for head h.  Returns 0 or an error. */
@@ -460,7 +475,7 @@ static int head_scores_select(const ctx_t* c, int h, float* levels_out, int32_t*
         }
     }
     if (st) {
-        int64_t S = head_select(lev, lev64, c->N, c->p, L, c->K, st, lv, near_ties);
+        int64_t S = head_select(lev, lev64, c->N, c->p, L, c->K, c->select_mode, st, lv, near_ties);
         if (S != c->S) rc = LHO_ERR_MEM;
     }
 done:
@@ -497,14 +512,15 @@ static void head_gather(const ctx_t* c, const void* x, int h, const int32_t* st,
  *       1e-6 relative (reported, not an error)
  */
 int lho_forward(const void* q, const void* k, const void* v, int N, int H, int d, int dtype,
-                int p, int L, int K, int score_mode, int given_sel, float* score_levels,
+                int p, int L, int K, int score_mode, int select_mode, int given_sel, float* score_levels,
                 int32_t* sel_start, int8_t* sel_level, double* Qt, double* Kt, double* Vt,
                 double* Ot, double* lse, double* O, int* near_ties, int nthreads) {
     int rc = check_shape(N, H, d, dtype, p, L, K);
     if (rc) return rc;
     if (d > 512 || !sel_start || !sel_level) return LHO_ERR_ARG;
-    if (score_mode < 0 || score_mode > 3) return LHO_ERR_ARG;
-    ctx_t c = {q, k, v, NULL, N, H, d, dtype, p, L, K, lho_subseq_len(N, p, L, K), score_mode};
+    if (score_mode < 0 || score_mode > 3 || select_mode < 0 || select_mode > 1) return LHO_ERR_ARG;
+    ctx_t c = {q, k, v, NULL, N, H, d, dtype, p, L, K, lho_subseq_len_sel(N, p, L, K, select_mode), score_mode,
+               select_mode};
     int64_t S = c.S;
     int err = 0;
 #ifdef _OPENMP
@@ -548,11 +564,14 @@ int lho_forward(const void* q, const void* k, const void* v, int N, int H, int d
                 if (Ot) memcpy(Ot + (int64_t)h * S * d, Oh, sizeof(double) * sd);
                 if (lse) memcpy(lse + (int64_t)h * S, lh, sizeof(double) * (size_t)S);
                 if (O) {
-                    /* scatter (O7): every token of entry i receives row i */
+                    /* scatter (O7): every token of entry i receives row i; with
+                       overlapping entries (R2') a token sums the rows it receives */
+                    for (int64_t t = 0; t < N; ++t)
+                        for (int e = 0; e < d; ++e) O[(t * H + h) * (int64_t)d + e] = 0.0;
                     for (int64_t i = 0; i < S; ++i) {
                         int64_t len = ipow(p, lv[i]);
                         for (int64_t t = st[i]; t < st[i] + len; ++t)
-                            memcpy(O + (t * H + h) * (int64_t)d, Oh + i * d, sizeof(double) * (size_t)d);
+                            for (int e = 0; e < d; ++e) O[(t * H + h) * (int64_t)d + e] += Oh[i * d + e];
                     }
                 }
             }
@@ -571,13 +590,15 @@ int lho_forward(const void* q, const void* k, const void* v, int N, int H, int d
  *   head_attention_bwd); a tolerance aid, not part of the layer.
  */
 int lho_backward(const void* q, const void* k, const void* v, const void* dout, int N, int H, int d,
-                 int dtype, int p, int L, int K, const int32_t* sel_start, const int8_t* sel_level,
+                 int dtype, int p, int L, int K, int select_mode, const int32_t* sel_start, const int8_t* sel_level,
                  double* dOt, double* dQt, double* dKt, double* dVt, double* dq, double* dk, double* dv,
                  double* cond, int nthreads) {
     int rc = check_shape(N, H, d, dtype, p, L, K);
     if (rc) return rc;
     if (d > 512 || !sel_start || !sel_level || !dout) return LHO_ERR_ARG;
-    ctx_t c = {q, k, v, dout, N, H, d, dtype, p, L, K, lho_subseq_len(N, p, L, K), 0};
+    if (select_mode < 0 || select_mode > 1) return LHO_ERR_ARG;
+    ctx_t c = {q, k, v, dout, N, H, d, dtype, p, L, K, lho_subseq_len_sel(N, p, L, K, select_mode), 0,
+               select_mode};
     int64_t S = c.S;
     int err = 0;
 #ifdef _OPENMP
@@ -625,15 +646,24 @@ int lho_backward(const void* q, const void* k, const void* v, const void* dout, 
         if (dQt) memcpy(dQt + (int64_t)h * S * d, dQh, sizeof(double) * sd);
         if (dKt) memcpy(dKt + (int64_t)h * S * d, dKh, sizeof(double) * sd);
         if (dVt) memcpy(dVt + (int64_t)h * S * d, dVh, sizeof(double) * sd);
-        /* adjoint of the mean-pool: each of the p^l tokens gets 1/p^l of it */
+        /* adjoint of the mean-pool: each of the p^l tokens gets 1/p^l of it,
+           summed over the entries that cover the token (one of them unless R2') */
+        for (int64_t t = 0; t < N; ++t) {
+            int64_t base = (t * H + h) * (int64_t)d;
+            for (int e = 0; e < d; ++e) {
+                if (dq) dq[base + e] = 0.0;
+                if (dk) dk[base + e] = 0.0;
+                if (dv) dv[base + e] = 0.0;
+            }
+        }
         for (int64_t i = 0; i < S; ++i) {
             int64_t len = ipow(p, lv[i]);
             for (int64_t t = st[i]; t < st[i] + len; ++t) {
                 int64_t base = (t * H + h) * (int64_t)d;
                 for (int e = 0; e < d; ++e) {
-                    if (dq) dq[base + e] = dQh[i * d + e] / (double)len;
-                    if (dk) dk[base + e] = dKh[i * d + e] / (double)len;
-                    if (dv) dv[base + e] = dVh[i * d + e] / (double)len;
+                    if (dq) dq[base + e] += dQh[i * d + e] / (double)len;
+                    if (dk) dk[base + e] += dKh[i * d + e] / (double)len;
+                    if (dv) dv[base + e] += dVh[i * d + e] / (double)len;
                 }
             }
         }
