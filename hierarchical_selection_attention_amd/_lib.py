@@ -17,13 +17,16 @@ LH_OK, LH_ERR_ARG, LH_ERR_SHAPE, LH_ERR_DTYPE, LH_ERR_WORKSPACE, LH_ERR_HIP, LH_
 LH_BF16, LH_FP32 = 0, 1
 LH_SCATTER_FP_ATOMIC, LH_SCATTER_INT_ATOMIC = 0, 1
 LH_SCORE_QK, LH_SCORE_K, LH_SCORE_Q, LH_SCORE_QK_PRODUCT = 0, 1, 2, 3
+LH_SELECT_PARTITION, LH_SELECT_PARENT_KEPT = 0, 1
 VIEWS = {"scores": 0, "sel_start": 1, "sel_level": 2, "qsub": 3, "ksub": 4, "vsub": 5, "osub": 6,
          "lse": 7, "dosub": 8, "dqsub": 9, "dksub": 10, "dvsub": 11, "block_first": 12}
 
 EXPORTS = ("lh_subseq_len", "lh_workspace_bytes", "lh_forward", "lh_backward", "lh_workspace_view",
            "lh_dense_workspace_bytes", "lh_dense_attn_fwd", "lh_dense_attn_bwd", "lh_stage_timing",
            "lh_stage_timing_read", "lh_stage_name", "lh_status_str", "lh_read_selection", "lh_peak_probe",
-           "lh_block_workspace_bytes", "lh_block_forward", "lh_block_backward", "lh_forward_scored")
+           "lh_block_workspace_bytes", "lh_block_forward", "lh_block_backward", "lh_forward_scored",
+           "lh_subseq_len_sel", "lh_workspace_bytes_sel", "lh_forward_sel", "lh_backward_sel",
+           "lh_workspace_view_sel", "lh_read_selection_sel")
 
 
 class LighthouseError(RuntimeError):
@@ -40,6 +43,12 @@ def _load():
         "lh_workspace_bytes": (sz, [i, i, i, i, i, i, i]),
         "lh_forward": (i, [vp, vp, vp, vp, i, i, i, i, i, i, i, vp, sz, vp]),
         "lh_forward_scored": (i, [vp, vp, vp, vp, i, i, i, i, i, i, i, i, vp, sz, vp]),
+        "lh_subseq_len_sel": (i64, [i, i, i, i, i]),
+        "lh_workspace_bytes_sel": (sz, [i, i, i, i, i, i, i, i]),
+        "lh_forward_sel": (i, [vp, vp, vp, vp, i, i, i, i, i, i, i, i, i, vp, sz, vp]),
+        "lh_backward_sel": (i, [vp, vp, vp, vp, i, i, i, i, i, i, i, i, i, vp, sz, vp]),
+        "lh_workspace_view_sel": (i, [vp, i, i, i, i, i, i, i, i, i, C.POINTER(vp), C.POINTER(sz)]),
+        "lh_read_selection_sel": (i, [vp, i, i, i, i, i, i, i, i, vp, vp, vp]),
         "lh_backward": (i, [vp, vp, vp, vp, i, i, i, i, i, i, i, i, vp, sz, vp]),
         "lh_workspace_view": (i, [vp, i, i, i, i, i, i, i, i, C.POINTER(vp), C.POINTER(sz)]),
         "lh_read_selection": (i, [vp, i, i, i, i, i, i, i, vp, vp, vp]),
@@ -69,6 +78,10 @@ lh_subseq_len = _L.lh_subseq_len
 lh_workspace_bytes = _L.lh_workspace_bytes
 lh_forward = _L.lh_forward
 lh_forward_scored = _L.lh_forward_scored
+lh_subseq_len_sel = _L.lh_subseq_len_sel
+lh_workspace_bytes_sel = _L.lh_workspace_bytes_sel
+lh_forward_sel = _L.lh_forward_sel
+lh_backward_sel = _L.lh_backward_sel
 lh_backward = _L.lh_backward
 lh_dense_workspace_bytes = _L.lh_dense_workspace_bytes
 lh_dense_attn_fwd = _L.lh_dense_attn_fwd
@@ -89,9 +102,10 @@ def lh_stage_name(stage: int) -> str:
     return _L.lh_stage_name(stage).decode()
 
 
-def lh_workspace_view(ws_ptr, N, H, d, p, L, K, dtype, view):
+def lh_workspace_view(ws_ptr, N, H, d, p, L, K, dtype, view, select_mode=LH_SELECT_PARTITION):
     ptr, nbytes = C.c_void_p(), C.c_size_t()
-    rc = _L.lh_workspace_view(ws_ptr, N, H, d, p, L, K, dtype, view, C.byref(ptr), C.byref(nbytes))
+    rc = _L.lh_workspace_view_sel(ws_ptr, N, H, d, p, L, K, dtype, select_mode, view, C.byref(ptr),
+                                  C.byref(nbytes))
     _check(rc, "lh_workspace_view")
     return ptr.value, nbytes.value
 
@@ -137,27 +151,32 @@ def _dev_tensor_check(*ts):
             raise LighthouseError("tensors must be contiguous device tensors")
 
 
-def alloc_workspace(N, H, d, p, L, K, dtype, device="cuda"):
+def alloc_workspace(N, H, d, p, L, K, dtype, device="cuda", select_mode=LH_SELECT_PARTITION):
     torch = _torch()
-    nbytes = lh_workspace_bytes(N, H, d, p, L, K, dtype)
+    nbytes = lh_workspace_bytes_sel(N, H, d, p, L, K, dtype, select_mode)
     if nbytes == 0:
         raise LighthouseError("invalid layer parameters")
     return torch.empty(nbytes, dtype=torch.uint8, device=device)
 
 
-def forward(q, k, v, p, L, K, ws=None, out=None, stream=None, score_mode=LH_SCORE_QK):
+def forward(q, k, v, p, L, K, ws=None, out=None, stream=None, score_mode=LH_SCORE_QK,
+            select_mode=LH_SELECT_PARTITION):
     """o = Lighthouse layer(q, k, v) for [N, H, d] tensors.  Returns (o, ws).
 
-    score_mode other than LH_SCORE_QK selects with an alternative score (lh_forward_scored)."""
+    score_mode / select_mode other than the defaults use the alternative readings
+    (lh_forward_scored / lh_forward_sel)."""
     torch = _torch()
     _dev_tensor_check(q, k, v)
     N, H, d = q.shape
     dt = dtype_code(q)
     if ws is None:
-        ws = alloc_workspace(N, H, d, p, L, K, dt, q.device)
+        ws = alloc_workspace(N, H, d, p, L, K, dt, q.device, select_mode)
     if out is None:
         out = torch.empty_like(q)
-    if score_mode == LH_SCORE_QK:
+    if select_mode != LH_SELECT_PARTITION:
+        rc = lh_forward_sel(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), N, H, d, p, L, K, dt,
+                            score_mode, select_mode, ws.data_ptr(), ws.numel(), _stream_handle(stream))
+    elif score_mode == LH_SCORE_QK:
         rc = lh_forward(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), N, H, d, p, L, K, dt,
                         ws.data_ptr(), ws.numel(), _stream_handle(stream))
     else:
@@ -167,7 +186,8 @@ def forward(q, k, v, p, L, K, ws=None, out=None, stream=None, score_mode=LH_SCOR
     return out, ws
 
 
-def backward(dout, p, L, K, ws, mode=LH_SCATTER_FP_ATOMIC, grads=None, stream=None):
+def backward(dout, p, L, K, ws, mode=LH_SCATTER_FP_ATOMIC, grads=None, stream=None,
+             select_mode=LH_SELECT_PARTITION):
     """(dq, dk, dv) of the Lighthouse layer; ws must come from the matching forward()."""
     torch = _torch()
     _dev_tensor_check(dout)
@@ -176,20 +196,24 @@ def backward(dout, p, L, K, ws, mode=LH_SCATTER_FP_ATOMIC, grads=None, stream=No
     if grads is None:
         grads = tuple(torch.empty_like(dout) for _ in range(3))
     dq, dk, dv = grads
-    rc = lh_backward(dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), N, H, d, p, L, K, dt, mode,
-                     ws.data_ptr(), ws.numel(), _stream_handle(stream))
+    if select_mode == LH_SELECT_PARTITION:
+        rc = lh_backward(dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), N, H, d, p, L, K, dt, mode,
+                         ws.data_ptr(), ws.numel(), _stream_handle(stream))
+    else:
+        rc = lh_backward_sel(dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), N, H, d, p, L, K, dt,
+                             mode, select_mode, ws.data_ptr(), ws.numel(), _stream_handle(stream))
     _check(rc, "lh_backward")
     return dq, dk, dv
 
 
-def workspace_tensor(ws, N, H, d, p, L, K, dtype, view):
+def workspace_tensor(ws, N, H, d, p, L, K, dtype, view, select_mode=LH_SELECT_PARTITION):
     """A typed torch view of one intermediate inside the workspace (see lh_view)."""
     torch = _torch()
     vid = VIEWS[view] if isinstance(view, str) else int(view)
-    ptr, nbytes = lh_workspace_view(ws.data_ptr(), N, H, d, p, L, K, dtype, vid)
+    ptr, nbytes = lh_workspace_view(ws.data_ptr(), N, H, d, p, L, K, dtype, vid, select_mode)
     off = ptr - ws.data_ptr()
     raw = ws[off: off + nbytes]
-    S = int(lh_subseq_len(N, p, L, K))
+    S = int(lh_subseq_len_sel(N, p, L, K, select_mode))
     Sp = (S + 63) // 64 * 64
     name = [k for k, v in VIEWS.items() if v == vid][0]
     if name == "scores":
@@ -209,16 +233,16 @@ def workspace_tensor(ws, N, H, d, p, L, K, dtype, view):
     raise LighthouseError(f"unknown view {view}")
 
 
-def read_selection(ws, N, H, d, p, L, K, dtype, stream=None):
+def read_selection(ws, N, H, d, p, L, K, dtype, stream=None, select_mode=LH_SELECT_PARTITION):
     """Copies of the kept entries' (start int32 [H][S], level uint8 [H][S])."""
     torch = _torch()
-    S = int(lh_subseq_len(N, p, L, K))
+    S = int(lh_subseq_len_sel(N, p, L, K, select_mode))
     if S < 0:
         raise LighthouseError("invalid layer parameters")
     start = torch.empty((H, S), dtype=torch.int32, device=ws.device)
     level = torch.empty((H, S), dtype=torch.uint8, device=ws.device)
-    rc = lh_read_selection(ws.data_ptr(), N, H, d, p, L, K, dtype, start.data_ptr(), level.data_ptr(),
-                           _stream_handle(stream))
+    rc = _L.lh_read_selection_sel(ws.data_ptr(), N, H, d, p, L, K, dtype, select_mode, start.data_ptr(),
+                                  level.data_ptr(), _stream_handle(stream))
     _check(rc, "lh_read_selection")
     return start, level
 

@@ -15,8 +15,9 @@ namespace lh {
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-int64_t subseq_len(int N, int p, int L, int K) {
+int64_t subseq_len(int N, int p, int L, int K, int select_mode) {
     if (N <= 0 || p < 2 || L < 1 || L > kMaxLevels || K < 0) return LH_ERR_ARG;
+    if (select_mode != LH_SELECT_PARTITION && select_mode != LH_SELECT_PARENT_KEPT) return LH_ERR_DTYPE;
     int64_t top = 1;
     for (int l = 0; l < L - 1; ++l) {
         top *= p;
@@ -26,21 +27,26 @@ int64_t subseq_len(int N, int p, int L, int K) {
     int64_t n = N / top, S = n, cand = n;
     for (int l = L - 1; l >= 1; --l) {
         const int64_t sel = cand < K ? cand : K;
-        S += sel * (p - 1);
+        // a selected entry gives way to its p children, or stays beside them (parent kept)
+        S += sel * (select_mode == LH_SELECT_PARENT_KEPT ? p : p - 1);
         cand = sel * p;
     }
     return S;
 }
 
-int make_plan(int N, int H, int d, int p, int L, int K, int dtype, Plan* P) {
+int make_plan(int N, int H, int d, int p, int L, int K, int dtype, Plan* P, int select_mode) {
     if (dtype != BF16 && dtype != FP32) return LH_ERR_DTYPE;
+    if (select_mode != LH_SELECT_PARTITION && select_mode != LH_SELECT_PARENT_KEPT) return LH_ERR_DTYPE;
+    if (select_mode == LH_SELECT_PARENT_KEPT && dtype != BF16) return LH_ERR_DTYPE;
     if (N <= 0 || H <= 0 || p < 2 || L < 1 || L > kMaxLevels || K < 0) return LH_ERR_ARG;
     if (d != 64 && d != 128) return LH_ERR_SHAPE;
     if ((int64_t)H * d > 8192) return LH_ERR_SHAPE;
-    const int64_t S = subseq_len(N, p, L, K);
+    const int64_t S = subseq_len(N, p, L, K, select_mode);
     if (S < 0) return (int)S;
+    if (S > INT32_MAX - 1) return LH_ERR_SHAPE;
     Plan& pl = *P;
     pl = Plan{};
+    pl.pk = select_mode == LH_SELECT_PARENT_KEPT;
     pl.N = N; pl.H = H; pl.d = d; pl.p = p; pl.L = L; pl.K = K; pl.dtype = dtype;
     pl.esz = dtype == BF16 ? 2 : 4;
     pl.S = S;
@@ -106,9 +112,15 @@ int make_plan(int N, int H, int d, int p, int L, int K, int dtype, Plan* P) {
     pl.off_dq = take(sizeof(float) * HSd);
     pl.off_dk = take(sizeof(float) * HSd);
     pl.off_dv = take(sizeof(float) * HSd);
-    pl.rowcopy = dtype == BF16;
+    pl.rowcopy = dtype == BF16 && !pl.pk;
     pl.off_otab = take(pl.rowcopy ? 2 * HSd : 0);
     pl.off_gtab = take(pl.rowcopy ? 3 * 2 * HSd : 0);
+    size_t nmap = 0;
+    for (int l = 0; l < L; ++l) {
+        pl.lmap_off[l] = nmap;
+        nmap += (size_t)H * pl.n[l];
+    }
+    pl.off_lmap = take(pl.pk ? sizeof(int32_t) * nmap : 0);
     pl.total = off;
     return LH_OK;
 }
@@ -238,8 +250,14 @@ int lh_forward(const void* q, const void* k, const void* v, void* o, int N, int 
 
 int lh_forward_scored(const void* q, const void* k, const void* v, void* o, int N, int H, int d, int p, int L,
                       int K, int dtype, int score_mode, void* ws, size_t ws_bytes, void* stream) {
+    return lh_forward_sel(q, k, v, o, N, H, d, p, L, K, dtype, score_mode, LH_SELECT_PARTITION, ws, ws_bytes,
+                          stream);
+}
+
+int lh_forward_sel(const void* q, const void* k, const void* v, void* o, int N, int H, int d, int p, int L, int K,
+                   int dtype, int score_mode, int select_mode, void* ws, size_t ws_bytes, void* stream) {
     Plan P;
-    int rc = make_plan(N, H, d, p, L, K, dtype, &P);
+    int rc = make_plan(N, H, d, p, L, K, dtype, &P, select_mode);
     if (rc) return rc;
     if (score_mode < LH_SCORE_QK || score_mode > LH_SCORE_QK_PRODUCT) return LH_ERR_DTYPE;
     P.score_mode = score_mode;
@@ -250,7 +268,13 @@ int lh_forward_scored(const void* q, const void* k, const void* v, void* o, int 
     char* w = reinterpret_cast<char*>(ws);
     LH_TRY(stage(ST_POOL_SCORE, s, [&] { return launch_pool_score(P, q, k, v, w, s); }));
     if (L > 1 && P.m < L - 1) LH_TRY(stage(ST_POOL_UP, s, [&] { return launch_pool_up(P, w, s); }));
-    LH_TRY(stage(ST_TOPK, s, [&] { return launch_topk(P, w, s); }));
+    LH_TRY(stage(ST_TOPK, s, [&] {
+        // parent kept: the level maps start empty; the selector fills in the kept entries
+        // (rounded up to 16 bytes, inside the segment's 256-byte alignment)
+        const size_t mb = (P.off_lmap_bytes() + 15) & ~(size_t)15;
+        hipError_t e = P.pk ? launch_fill_zero(w + P.off_lmap, mb, s) : hipSuccess;
+        return e == hipSuccess ? launch_topk(P, w, s) : e;
+    }));
     LH_TRY(stage(ST_GATHER, s, [&] { return launch_gather(P, q, k, v, w, s); }));
     unsigned int* hmax = reinterpret_cast<unsigned int*>(w + P.off_hmax);
     LH_TRY(stage(ST_SUB_PREP, s, [&] {
@@ -275,6 +299,12 @@ int lh_forward_scored(const void* q, const void* k, const void* v, void* o, int 
     }
     LH_TRY(stage(ST_ATTN_FWD, s, [&] { return launch_attn_fwd(a, s); }));
     LH_TRY(stage(ST_SCATTER_FWD, s, [&] {
+        if (P.pk) {
+            // overlapping entries: every token sums the outputs of the entries that cover it
+            const float* tab[1] = {f32(w, P.off_os)};
+            void* out[1] = {o};
+            return launch_sum_copy(P, w, tab, out, 1, false, (int64_t)H * d, s);
+        }
         if (!P.rowcopy) return launch_scatter_fwd(P, w, o, s);
         const uint16_t* tab[1] = {u16(w, P.off_otab)};
         void* out[1] = {o};
@@ -287,12 +317,15 @@ int lh_forward_scored(const void* q, const void* k, const void* v, void* o, int 
 
 namespace lh {
 int backward_strided(const void* dout, void* dq, void* dk, void* dv, int N, int H, int d, int p, int L, int K,
-                         int dtype, int scatter_mode, void* ws, size_t ws_bytes, void* stream, int64_t grad_ld) {
+                     int dtype, int scatter_mode, void* ws, size_t ws_bytes, void* stream, int64_t grad_ld,
+                     int select_mode) {
     Plan P;
-    int rc = make_plan(N, H, d, p, L, K, dtype, &P);
+    int rc = make_plan(N, H, d, p, L, K, dtype, &P, select_mode);
     if (rc) return rc;
     if (scatter_mode != LH_SCATTER_FP_ATOMIC && scatter_mode != LH_SCATTER_INT_ATOMIC) return LH_ERR_DTYPE;
-    if (grad_ld != (int64_t)H * d && (!P.rowcopy || grad_ld < (int64_t)H * d || grad_ld % 8 != 0)) return LH_ERR_ARG;
+    if (grad_ld != (int64_t)H * d &&
+        (!(P.rowcopy || P.pk) || grad_ld < (int64_t)H * d || grad_ld % 8 != 0))
+        return LH_ERR_ARG;
     if (!dout || !dq || !dk || !dv) return LH_ERR_ARG;
     if (!aligned16(dout) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv)) return LH_ERR_ARG;
     if ((rc = check_ws(P, ws, ws_bytes))) return rc;
@@ -302,12 +335,17 @@ int backward_strided(const void* dout, void* dq, void* dk, void* dv, int N, int 
     unsigned int* hmax = reinterpret_cast<unsigned int*>(w + P.off_hmax);
     unsigned int* hmax_b = hmax + 4 * (size_t)H;
     LH_TRY(stage(ST_ZERO_ACC, s, [&] { return launch_fill_zero(w + P.off_acc, 8 * HSd, s); }));
-    LH_TRY(stage(ST_SCATTER_BWD, s, [&] { return launch_scatter_bwd(P, dout, scatter_mode, w, s); }));
+    // parent kept: each entry's sum of dO is taken by one wavefront (no atomics), in the
+    // fp32 layout of the fp-atomic accumulators
+    const int acc_mode = P.pk ? LH_SCATTER_FP_ATOMIC : scatter_mode;
+    LH_TRY(stage(ST_SCATTER_BWD, s, [&] {
+        return P.pk ? launch_entry_sum(P, dout, w, s) : launch_scatter_bwd(P, dout, scatter_mode, w, s);
+    }));
     LH_TRY(stage(ST_BWD_PREP, s, [&] {
         RowPrepSpec rp{};
         rp.acc = w + P.off_acc; rp.o = w + P.off_os;
         rp.dos = f32(w, P.off_dos); rp.D = f32(w, P.off_D); rp.rowdown = f32(w, P.off_rowdown);
-        rp.vmax = hmax; rp.S = P.S; rp.Sp = P.Sp; rp.H = H; rp.d = d; rp.mode = scatter_mode; rp.dense = 0;
+        rp.vmax = hmax; rp.S = P.S; rp.Sp = P.Sp; rp.H = H; rp.d = d; rp.mode = acc_mode; rp.dense = 0;
         hipError_t e = launch_row_prep(rp, s);
         if (e != hipSuccess || dtype != BF16) return e;
         e = launch_fill_zero(hmax_b, sizeof(uint32_t) * 4 * (size_t)H, s);
@@ -331,6 +369,12 @@ int backward_strided(const void* dout, void* dq, void* dk, void* dv, int N, int 
     LH_TRY(stage(ST_ATTN_BWD_DKDV, s, [&] { return launch_attn_bwd(a, s, 0); }));
     if (dtype == BF16) LH_TRY(stage(ST_ATTN_BWD_DQ, s, [&] { return launch_attn_bwd(a, s, 1); }));
     LH_TRY(stage(ST_POOL_BWD, s, [&] {
+        if (P.pk) {
+            // a token sums dX~ / p^level over the entries that cover it
+            const float* tab[3] = {f32(w, P.off_dq), f32(w, P.off_dk), f32(w, P.off_dv)};
+            void* out[3] = {dq, dk, dv};
+            return launch_sum_copy(P, w, tab, out, 3, true, grad_ld, s);
+        }
         if (!P.rowcopy) return launch_pool_bwd(P, w, dq, dk, dv, s);
         const uint16_t* tab[3] = {u16(w, P.off_gtab), u16(w, P.off_gtab + HSd2), u16(w, P.off_gtab + 2 * HSd2)};
         void* out[3] = {dq, dk, dv};
@@ -345,13 +389,34 @@ extern "C" {
 int lh_backward(const void* dout, void* dq, void* dk, void* dv, int N, int H, int d, int p, int L, int K,
                 int dtype, int scatter_mode, void* ws, size_t ws_bytes, void* stream) {
     return backward_strided(dout, dq, dk, dv, N, H, d, p, L, K, dtype, scatter_mode, ws, ws_bytes, stream,
-                         (int64_t)H * d);
+                            (int64_t)H * d);
+}
+
+int lh_backward_sel(const void* dout, void* dq, void* dk, void* dv, int N, int H, int d, int p, int L, int K,
+                    int dtype, int scatter_mode, int select_mode, void* ws, size_t ws_bytes, void* stream) {
+    return backward_strided(dout, dq, dk, dv, N, H, d, p, L, K, dtype, scatter_mode, ws, ws_bytes, stream,
+                            (int64_t)H * d, select_mode);
+}
+
+int64_t lh_subseq_len_sel(int N, int p, int L, int K, int select_mode) {
+    return subseq_len(N, p, L, K, select_mode);
+}
+
+size_t lh_workspace_bytes_sel(int N, int H, int d, int p, int L, int K, int dtype, int select_mode) {
+    Plan P;
+    if (make_plan(N, H, d, p, L, K, dtype, &P, select_mode) != LH_OK) return 0;
+    return P.total;
 }
 
 int lh_workspace_view(void* ws, int N, int H, int d, int p, int L, int K, int dtype, int view, void** ptr,
                       size_t* bytes) {
+    return lh_workspace_view_sel(ws, N, H, d, p, L, K, dtype, LH_SELECT_PARTITION, view, ptr, bytes);
+}
+
+int lh_workspace_view_sel(void* ws, int N, int H, int d, int p, int L, int K, int dtype, int select_mode, int view,
+                          void** ptr, size_t* bytes) {
     Plan P;
-    int rc = make_plan(N, H, d, p, L, K, dtype, &P);
+    int rc = make_plan(N, H, d, p, L, K, dtype, &P, select_mode);
     if (rc) return rc;
     if (!ws || !ptr || !bytes) return LH_ERR_ARG;
     char* w = reinterpret_cast<char*>(ws);
@@ -386,8 +451,13 @@ int lh_workspace_view(void* ws, int N, int H, int d, int p, int L, int K, int dt
 
 int lh_read_selection(const void* ws, int N, int H, int d, int p, int L, int K, int dtype, int32_t* start,
                       uint8_t* level, void* stream) {
+    return lh_read_selection_sel(ws, N, H, d, p, L, K, dtype, LH_SELECT_PARTITION, start, level, stream);
+}
+
+int lh_read_selection_sel(const void* ws, int N, int H, int d, int p, int L, int K, int dtype, int select_mode,
+                          int32_t* start, uint8_t* level, void* stream) {
     Plan P;
-    int rc = make_plan(N, H, d, p, L, K, dtype, &P);
+    int rc = make_plan(N, H, d, p, L, K, dtype, &P, select_mode);
     if (rc) return rc;
     if (!ws || (!start && !level)) return LH_ERR_ARG;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);

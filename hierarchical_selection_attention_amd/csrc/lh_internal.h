@@ -44,7 +44,8 @@ hipError_t stage(int id, hipStream_t s, F&& fn) {
 // lh_backward with dq, dk, dv rows grad_ld elements apart (grad_ld = H*d for
 // [N][H][d] tensors; larger strides need the bf16 path, grad_ld % 8 == 0)
 int backward_strided(const void* dout, void* dq, void* dk, void* dv, int N, int H, int d, int p, int L, int K,
-                     int dtype, int scatter_mode, void* ws, size_t ws_bytes, void* stream, int64_t grad_ld);
+                     int dtype, int scatter_mode, void* ws, size_t ws_bytes, void* stream, int64_t grad_ld,
+                     int select_mode = 0);
 
 struct Plan {
     int N, H, d, p, L, K, dtype, esz;
@@ -52,6 +53,7 @@ struct Plan {
     int64_t S, Sp;
     int m;                  // pyramid level produced per workgroup by the pooling pass
     int rowcopy;            // bf16: back-scatter and pool adjoint copy bf16 rows the attention leaves
+    int pk;                 // "parent kept": selected entries stay beside their children (bf16 only)
     int64_t tok;            // p^m tokens per pooling workgroup
     int64_t ntop;           // N / p^(L-1)
     int64_t n[kMaxLevels];  // entries at level l
@@ -81,12 +83,22 @@ struct Plan {
     // already rounded to bf16
     size_t off_otab;              // bf16 [H][Sp][d]: O~
     size_t off_gtab;              // bf16 [3][H][Sp][d]: dQ~, dK~, dV~ divided by p^level
+    // parent kept: int32 [sum_l H * n_l], 1 + the slot of entry (l, j) of head h
+    // at lmap_off[l] + h * n_l + j, 0 when that entry is not kept
+    size_t off_lmap;
+    size_t lmap_off[kMaxLevels];
     size_t total;
+    size_t off_lmap_bytes() const {
+        size_t n = 0;
+        for (int l = 0; l < L; ++l) n += (size_t)H * this->n[l];
+        return sizeof(int32_t) * n;
+    }
 };
 
-// Fills `pl`; returns 0 or a negative lh_status.
-int make_plan(int N, int H, int d, int p, int L, int K, int dtype, Plan* pl);
-int64_t subseq_len(int N, int p, int L, int K);
+// Fills `pl`; returns 0 or a negative lh_status.  select_mode 0: the kept
+// entries partition [0, N); 1: parent kept (bf16 only).
+int make_plan(int N, int H, int d, int p, int L, int K, int dtype, Plan* pl, int select_mode = 0);
+int64_t subseq_len(int N, int p, int L, int K, int select_mode = 0);
 
 // ------------------------------------------------------------ launchers
 // Each returns hipSuccess or the launch error.  All pointers are device
@@ -107,6 +119,12 @@ hipError_t launch_pool_bwd(const Plan& P, char* ws, void* dq, void* dk, void* dv
 // row of out[z] starts t * out_ld elements in (out_ld >= H*d, a multiple of 8)
 hipError_t launch_row_copy(const Plan& P, const char* ws, const uint16_t* const* tab, void* const* out, int Z,
                            int64_t out_ld, hipStream_t s);
+// parent kept: out[z][t][h] = sum over the kept entries covering t of tab[z][h][slot]
+// (divided by p^level when `divide`), fp32 tables, bf16 output rows out_ld apart
+hipError_t launch_sum_copy(const Plan& P, const char* ws, const float* const* tab, void* const* out, int Z,
+                           bool divide, int64_t out_ld, hipStream_t s);
+// parent kept: fp32 acc[h][slot] = sum of dO over the entry's tokens (bf16 dO)
+hipError_t launch_entry_sum(const Plan& P, const void* dout, char* ws, hipStream_t s);
 
 // Attention operands: 16-bit copies laid out [H][Sp][d] (rows) and
 // [H][d][Sp] (transposed); lo parts are used when `split`.

@@ -746,6 +746,101 @@ static int pick_mt(int rows_threads, int limit) {
     return mt;
 }
 
+// ------------------------------------------------ overlapping entries
+// The "parent kept" reading of the selection (Fig. 2 step 3): a selected entry
+// stays in the sub-sequence beside its p children, so up to L kept entries
+// cover a token, one per level.  lmap[l][h][j] holds 1 + the slot of entry
+// (level l, index j) when it is kept, else 0.
+
+// out[z][t][h] = sum over the levels l whose entry covering t is kept of
+// tab[z][h][slot] / p^l (z = 1: the scatter of O~, divided by 1; z = 3: the
+// pool adjoint of dQ~, dK~, dV~).  fp32 tables, one rounding to bf16.  One
+// thread per (token, head, 8-element chunk), token-major, so a wavefront
+// writes consecutive 16-byte pieces of the output rows.
+struct SumCopyArgs {
+    const int32_t* lmap;          // [sum_l H * n_l] int32, level l at lmap_off[l]
+    const float* tab[3];          // fp32 [H][Sp][d]
+    uint16_t* out[3];             // bf16; token t, head h at element t * ld + h * d
+    int64_t lmap_off[kMaxLevels];
+    int64_t n[kMaxLevels], pw[kMaxLevels];
+    int64_t N, Sp, ld;
+    int H, L, Z, divide;
+};
+
+template <int G>
+__global__ void __launch_bounds__(256) k_sum_copy(SumCopyArgs a) {
+    constexpr int d = G * 8;
+    const int64_t total = a.N * a.H * G;
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total; i += (int64_t)gridDim.x * 256) {
+        const int c = (int)(i % G);
+        const int64_t th = i / G;
+        const int h = (int)(th % a.H);
+        const int64_t t = th / a.H;
+        float acc[3][8];
+        for (int z = 0; z < 3; ++z)
+            for (int e = 0; e < 8; ++e) acc[z][e] = 0.f;
+        for (int l = 0; l < a.L; ++l) {
+            const int32_t s1 = a.lmap[a.lmap_off[l] + (int64_t)h * a.n[l] + t / a.pw[l]];
+            if (s1 == 0) continue;
+            const int64_t el = ((int64_t)h * a.Sp + (s1 - 1)) * d + 8 * c;
+            const float inv = a.divide ? 1.0f / (float)a.pw[l] : 1.0f;
+            for (int z = 0; z < a.Z; ++z) {
+                float x[8];
+                load8f(a.tab[z], el, x);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) acc[z][e] += a.divide ? x[e] * inv : x[e];
+            }
+        }
+        for (int z = 0; z < a.Z; ++z) {
+            u32x4 w;
+            w[0] = pack_bf16x2(acc[z][0], acc[z][1]);
+            w[1] = pack_bf16x2(acc[z][2], acc[z][3]);
+            w[2] = pack_bf16x2(acc[z][4], acc[z][5]);
+            w[3] = pack_bf16x2(acc[z][6], acc[z][7]);
+            __builtin_nontemporal_store(w, reinterpret_cast<u32x4*>(a.out[z] + t * a.ld + (int64_t)h * d + 8 * c));
+        }
+    }
+}
+
+// Adjoint of the summed scatter: acc[h][slot] = sum of dO over the p^level
+// tokens of the entry, fp32 (the layout the row preparation reads as fp32
+// accumulators).  One wavefront per (head, slot): 64 / G token rows per step,
+// lane group r takes rows r, r + 64/G, ...; the row groups are added with
+// xor shuffles at the end.  Every slot is summed by one wavefront in a fixed
+// order, so the result is the same on every run.
+struct EntrySumArgs {
+    const int32_t* start;   // [H][S]
+    const uint8_t* level;   // [H][S]
+    const uint16_t* dout;   // bf16 [N][H][d]
+    float* acc;             // fp32 [H][Sp][d]
+    int64_t S, Sp, pw[kMaxLevels];
+    int H;
+};
+
+template <int G>
+__global__ void __launch_bounds__(256) k_entry_sum(EntrySumArgs a) {
+    constexpr int d = G * 8, R = 64 / G;
+    const int lane = threadIdx.x & 63;
+    const int64_t slot = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int h = blockIdx.y;
+    if (slot >= a.S) return;
+    const int c = lane % G, r = lane / G;
+    const int64_t t0 = a.start[(int64_t)h * a.S + slot];
+    const int64_t len = a.pw[a.level[(int64_t)h * a.S + slot]];
+    float x[8], acc[8];
+    for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+    for (int64_t t = t0 + r; t < t0 + len; t += R) {
+        load8<0>(a.dout, (t * a.H + h) * d + 8 * c, x);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] += x[e];
+    }
+#pragma unroll
+    for (int off = G; off < 64; off <<= 1)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] += shfl_xor_f(acc[e], off);
+    if (r == 0) store8f(a.acc, ((int64_t)h * a.Sp + slot) * d + 8 * c, acc);
+}
+
 hipError_t launch_pool_score(const Plan& P, const void* q, const void* k, const void* v, char* ws,
                              hipStream_t s) {
     PoolScoreArgs a{};
@@ -900,6 +995,48 @@ hipError_t launch_pool_bwd(const Plan& P, char* ws, void* dq, void* dk, void* dv
         if (G == 16) hipLaunchKernelGGL((k_pool_bwd<1, 16>), grid, dim3(threads), 0, s, a);
         else hipLaunchKernelGGL((k_pool_bwd<1, 8>), grid, dim3(threads), 0, s, a);
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_sum_copy(const Plan& P, const char* ws, const float* const* tab, void* const* out, int Z,
+                           bool divide, int64_t out_ld, hipStream_t s) {
+    if (Z < 1 || Z > 3 || P.dtype != BF16 || !P.pk) return hipErrorInvalidValue;
+    if (out_ld < (int64_t)P.H * P.d || out_ld % 8 != 0) return hipErrorInvalidValue;
+    SumCopyArgs a{};
+    a.lmap = reinterpret_cast<const int32_t*>(ws + P.off_lmap);
+    for (int z = 0; z < Z; ++z) {
+        a.tab[z] = tab[z];
+        a.out[z] = reinterpret_cast<uint16_t*>(out[z]);
+    }
+    for (int l = 0; l < P.L; ++l) {
+        a.lmap_off[l] = (int64_t)P.lmap_off[l];
+        a.n[l] = P.n[l];
+        a.pw[l] = P.pw[l];
+    }
+    a.N = P.N; a.Sp = P.Sp; a.ld = out_ld;
+    a.H = P.H; a.L = P.L; a.Z = Z; a.divide = divide ? 1 : 0;
+    const int G = P.d / 8;
+    const int64_t total = (int64_t)P.N * P.H * G;
+    const int64_t blocks = (total + 255) / 256;
+    const unsigned grid = (unsigned)(blocks < 8192 ? blocks : 8192);
+    if (G == 16) hipLaunchKernelGGL((k_sum_copy<16>), dim3(grid), dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((k_sum_copy<8>), dim3(grid), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_entry_sum(const Plan& P, const void* dout, char* ws, hipStream_t s) {
+    if (P.dtype != BF16 || !P.pk) return hipErrorInvalidValue;
+    EntrySumArgs a{};
+    a.start = reinterpret_cast<const int32_t*>(ws + P.off_start);
+    a.level = reinterpret_cast<const uint8_t*>(ws + P.off_level);
+    a.dout = reinterpret_cast<const uint16_t*>(dout);
+    a.acc = reinterpret_cast<float*>(ws + P.off_acc);
+    a.S = P.S; a.Sp = P.Sp; a.H = P.H;
+    for (int l = 0; l < P.L; ++l) a.pw[l] = P.pw[l];
+    if (P.S == 0) return hipSuccess;
+    dim3 grid((unsigned)((P.S + 3) / 4), (unsigned)P.H);
+    if (P.d == 128) hipLaunchKernelGGL((k_entry_sum<16>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((k_entry_sum<8>), grid, dim3(256), 0, s, a);
     return hipGetLastError();
 }
 

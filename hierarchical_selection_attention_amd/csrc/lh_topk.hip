@@ -10,7 +10,10 @@
 // digit) -- the set an argsort would select, without sorting.  Selected
 // entries are replaced by their p children, the others are kept; finally
 // every kept entry gets its slot in the position-ordered sub-sequence from
-// entry counts (bottom-up) and prefix offsets (top-down).
+// entry counts (bottom-up) and prefix offsets (top-down).  In the "parent
+// kept" reading a selected entry is kept as well, in the slot just before its
+// children's (the coarser entry first where two start together), and the
+// slot of every kept entry is also written to a per-level map.
 #include "lh_device.h"
 #include "lh_internal.h"
 
@@ -24,6 +27,9 @@ struct TopkArgs {
     uint8_t* level;                 // [H][S]
     int32_t* bfirst;                // [H][ntop + 1]
     int32_t* scratch;               // [H][L][5][cap]
+    int32_t* lmap;                  // parent kept: [sum_l H * n_l], 1 + slot of kept entries (zeroed)
+    int64_t lmap_off[kMaxLevels];
+    int pk;                         // 1: parent kept
     int64_t n[kMaxLevels];
     int64_t pw[kMaxLevels];
     int64_t ncand[kMaxLevels];      // candidates at level l: ntop at the top, p*min(K, .) below
@@ -195,7 +201,7 @@ __global__ void __launch_bounds__(kTopkThreads) k_topk(TopkArgs a) {
         for (int64_t i = tid; i < ncand[l]; i += blockDim.x) {
             int32_t c = 1;
             if (flag[i]) {
-                c = 0;
+                c = a.pk;   // the entry itself, when it stays beside its children
                 const int64_t r = rank[i];
                 for (int z = 0; z < p; ++z) c += ccnt[r * p + z];
             }
@@ -215,7 +221,7 @@ __global__ void __launch_bounds__(kTopkThreads) k_topk(TopkArgs a) {
         for (int64_t i = tid; i < ncand[l]; i += blockDim.x) {
             if (flag[i]) {
                 const int64_t r = rank[i];
-                int32_t f = first[i];
+                int32_t f = first[i] + a.pk;
                 for (int z = 0; z < p; ++z) {
                     cfirst[r * p + z] = f;
                     f += ccnt[r * p + z];
@@ -231,11 +237,13 @@ __global__ void __launch_bounds__(kTopkThreads) k_topk(TopkArgs a) {
         const int32_t* idx = arr(l, 0);
         const int32_t* flag = arr(l, 1);
         const int32_t* first = arr(l, 4);
+        int32_t* lm = a.pk ? a.lmap + a.lmap_off[l] + (int64_t)h * a.n[l] : nullptr;
         for (int64_t i = tid; i < ncand[l]; i += blockDim.x) {
-            if (l == 0 || !flag[i]) {
+            if (l == 0 || !flag[i] || a.pk) {
                 const int32_t s = first[i];
                 st[s] = (int32_t)(idx[i] * a.pw[l]);
                 lv[s] = (uint8_t)l;
+                if (lm) lm[idx[i]] = s + 1;
             }
         }
     }
@@ -259,6 +267,11 @@ hipError_t launch_topk(const Plan& P, char* ws, hipStream_t s) {
     a.scratch = reinterpret_cast<int32_t*>(ws + P.off_tk);
     a.S = P.S; a.cap = P.tk_cap; a.ntop = P.ntop;
     a.L = P.L; a.p = P.p; a.K = P.K;
+    a.pk = P.pk;
+    if (P.pk) {
+        a.lmap = reinterpret_cast<int32_t*>(ws + P.off_lmap);
+        for (int l = 0; l < P.L; ++l) a.lmap_off[l] = (int64_t)P.lmap_off[l];
+    }
     int64_t nc = P.ntop;
     for (int l = P.L - 1; l >= 0; --l) {
         a.ncand[l] = nc;

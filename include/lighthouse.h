@@ -106,6 +106,38 @@ int lh_forward_scored(const void* q, const void* k, const void* v, void* o,
                       int N, int H, int d, int p, int L, int K, int dtype, int score_mode,
                       void* ws, size_t ws_bytes, void* stream);
 
+/* Which entries the selection keeps (Fig. 2 step 3 "tree-prune", "parent
+ * kept").  LH_SELECT_PARTITION, the reading of lh_forward: a selected entry
+ * is replaced by its p children, so the kept entries partition [0, N) and
+ * every token takes the output of the one entry covering it.
+ * LH_SELECT_PARENT_KEPT: a selected entry stays in the sub-sequence beside its
+ * children, so every candidate of every level is kept (S = N/p^(L-1) plus
+ * p * min(K, #candidates) per selecting level, lh_subseq_len_sel); entries
+ * are ordered by first token, the coarser first where two start together; a
+ * token's output is the sum of the outputs of the (up to L) entries covering
+ * it, and the adjoints sum likewise (the gradient of an entry is the sum of
+ * dO over its tokens; a token's dq, dk, dv sum dX~ / p^level over its
+ * entries).  Both sums are taken by one thread or wavefront per output in a
+ * fixed order, so the result does not depend on scatter_mode and is the same
+ * on every run.  Parent kept is bf16 only (LH_ERR_DTYPE otherwise). */
+typedef enum {
+    LH_SELECT_PARTITION = 0,
+    LH_SELECT_PARENT_KEPT = 1
+} lh_select_mode;
+
+/* The entry points of the layer with a selection mode (lh_select_mode;
+ * LH_ERR_DTYPE for an unknown one).  A workspace filled by lh_forward_sel
+ * must be read with the same select_mode (lh_backward_sel,
+ * lh_read_selection_sel, lh_workspace_view_sel). */
+int64_t lh_subseq_len_sel(int N, int p, int L, int K, int select_mode);
+size_t lh_workspace_bytes_sel(int N, int H, int d, int p, int L, int K, int dtype, int select_mode);
+int lh_forward_sel(const void* q, const void* k, const void* v, void* o,
+                   int N, int H, int d, int p, int L, int K, int dtype, int score_mode,
+                   int select_mode, void* ws, size_t ws_bytes, void* stream);
+int lh_backward_sel(const void* dout, void* dq, void* dk, void* dv,
+                    int N, int H, int d, int p, int L, int K, int dtype, int scatter_mode,
+                    int select_mode, void* ws, size_t ws_bytes, void* stream);
+
 /* Backward pass through the scatter, the attention, the gather and the pool
  * (Fig. 1 gradient path).  q, k, v are not needed: everything is read from
  * the workspace of the matching lh_forward.  Writes dq, dk, dv [N][H][d]. */
@@ -134,6 +166,8 @@ typedef enum {
 /* Sp = S rounded up to a multiple of 64 (row padding of the sub-sequence). */
 int lh_workspace_view(void* ws, int N, int H, int d, int p, int L, int K, int dtype,
                       int view, void** ptr, size_t* bytes);
+int lh_workspace_view_sel(void* ws, int N, int H, int d, int p, int L, int K, int dtype,
+                          int select_mode, int view, void** ptr, size_t* bytes);
 
 /* Copy the kept entries' descriptors out of a workspace that lh_forward
  * filled: start (int32 [H][S], first token of each entry of the causal
@@ -146,6 +180,8 @@ int lh_workspace_view(void* ws, int N, int H, int d, int p, int L, int K, int dt
  * arguments (nothing enqueued), or LH_ERR_HIP. */
 int lh_read_selection(const void* ws, int N, int H, int d, int p, int L, int K, int dtype,
                       int32_t* start, uint8_t* level, void* stream);
+int lh_read_selection_sel(const void* ws, int N, int H, int d, int p, int L, int K, int dtype,
+                          int select_mode, int32_t* start, uint8_t* level, void* stream);
 
 /* Achievable-peak probes (not part of the layer), reported beside the vendor
  * peaks.  kind 0 reads n bytes at src in 1 MiB chunks and stores the XOR fold
