@@ -35,8 +35,9 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def stage_bytes(w, S):
-    """Algorithmic HBM bytes of one launch of each streaming stage (see design notes)."""
+def stage_bytes(w, S, pk=False):
+    """Algorithmic HBM bytes of one launch of each streaming stage (see design notes).  With the
+    parent-kept selection the scatter and the pool adjoint read fp32 rows of the sub-sequence."""
     N, H, d, p, L = w["N"], w["H"], w["d"], w["p"], w["L"]
     e = 2 if w["dtype"] == "bf16" else 4
     row = N * H * d * e                         # one [N, H, d] tensor
@@ -47,11 +48,12 @@ def stage_bytes(w, S):
         m += 1
     pool_m = (N // p ** m) * H * d * 4 * 3
     sub32 = S * H * d * 4
+    tab = sub32 if pk else S * H * d * e
     return {
         "pool_score": 3 * row + nscore + pool_m,      # read q, k, v; write scores and level-m means
-        "scatter_fwd": row + S * H * d * e,           # write o; read the rows of O~ once
+        "scatter_fwd": row + tab,                     # write o; read the rows of O~ once
         "scatter_bwd": row + sub32,                   # read dO; write dO~ once
-        "pool_bwd": 3 * row + 3 * S * H * d * e,      # write dq, dk, dv; read their sub-sequence rows once
+        "pool_bwd": 3 * row + 3 * tab,                # write dq, dk, dv; read their sub-sequence rows once
     }
 
 
@@ -107,16 +109,17 @@ def achievable_peaks(lh, torch, stream):
     return out
 
 
-def cpu_baseline(w, x, heads):
+def cpu_baseline(w, x, heads, score_mode=0, select_mode=0):
     """The oracle (fwd+bwd) on the first `heads` heads of the same inputs, scaled to all heads."""
     import numpy as np
     import oracle
     sub = {n: np.ascontiguousarray(x[n][:, :heads]) for n in ("q", "k", "v", "dout")}
     p, L, K, dt = w["p"], w["L"], w["K"], w["dtype"]
     t0 = time.perf_counter()
-    r = oracle.forward(sub["q"], sub["k"], sub["v"], p, L, K, dt, want=("sel", "o"), nthreads=heads)
+    r = oracle.forward(sub["q"], sub["k"], sub["v"], p, L, K, dt, want=("sel", "o"), nthreads=heads,
+                       score_mode=score_mode, select_mode=select_mode)
     oracle.backward(sub["q"], sub["k"], sub["v"], sub["dout"], p, L, K, (r["start"], r["level"]), dt,
-                    want=("full",), nthreads=heads)
+                    want=("full",), nthreads=heads, select_mode=select_mode)
     t = time.perf_counter() - t0
     full = t * w["H"] / heads
     return {"value": w["N"] / full, "unit": "tokens/s", "cores": heads, "kind": "oracle",
@@ -274,6 +277,10 @@ def main():
     ap.add_argument("--no-dense", action="store_true", help="skip the dense attention comparison")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-heads", type=int, default=8)
+    ap.add_argument("--select", choices=("partition", "parent_kept"), default="partition",
+                    help="selection reading (default: partition; parent_kept prints its own line)")
+    ap.add_argument("--score", choices=("qk", "k", "q", "qk_product"), default="qk",
+                    help="score reading (default: qk)")
     ap.add_argument("--block", action="store_true",
                     help="time the attention block (projections + layer) at the 530M shape instead")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -305,7 +312,9 @@ def main():
     w = si.WORKLOADS[args.workload]
     N, H, d, p, L, K = w["N"], w["H"], w["d"], w["p"], w["L"], w["K"]
     code = 0 if w["dtype"] == "bf16" else 1
-    S = int(lh.lh_subseq_len(N, p, L, K))
+    sel_mode = 1 if args.select == "parent_kept" else 0
+    score_mode = {"qk": 0, "k": 1, "q": 2, "qk_product": 3}[args.score]
+    S = int(lh.lh_subseq_len_sel(N, p, L, K, sel_mode))
     log(f"workload {w['name']}: N={N} H={H} d={d} {w['dtype']} p={p} L={L} K={K} S={S}")
     t0 = time.perf_counter()
     x = si.workload_inputs(args.workload, with_dout=True, threads=16)
@@ -317,14 +326,14 @@ def main():
         return torch.from_numpy(a).cuda()
 
     q, k, v, do = dev(x["q"]), dev(x["k"]), dev(x["v"]), dev(x["dout"])
-    ws = lh.alloc_workspace(N, H, d, p, L, K, code)
+    ws = lh.alloc_workspace(N, H, d, p, L, K, code, select_mode=sel_mode)
     o = torch.empty_like(q)
     grads = tuple(torch.empty_like(q) for _ in range(3))
     stream = torch.cuda.current_stream()
 
     def step():
-        lh.forward(q, k, v, p, L, K, ws=ws, out=o, stream=stream)
-        lh.backward(do, p, L, K, ws, mode=args.mode, grads=grads, stream=stream)
+        lh.forward(q, k, v, p, L, K, ws=ws, out=o, stream=stream, score_mode=score_mode, select_mode=sel_mode)
+        lh.backward(do, p, L, K, ws, mode=args.mode, grads=grads, stream=stream, select_mode=sel_mode)
 
     for _ in range(args.warmup):
         step()
@@ -351,7 +360,9 @@ def main():
     stages = lh.lh_stage_timing_read(32)
     lh.lh_stage_timing(0)
 
-    sb = stage_bytes(w, S)
+    sb = stage_bytes(w, S, pk=bool(sel_mode))
+    # counter summaries are per workload and kernel set: the variants have none
+    prof_name = w["name"] + (f"_{args.select}" if sel_mode else "") + (f"_score_{args.score}" if score_mode else "")
     fl = attn_flops(w, S)
     stage_rep = {}
     for name, (ms, cnt) in stages.items():
@@ -370,13 +381,13 @@ def main():
         ach = sb[dominant] / (dom_ms / 1e3) / 1e9
         roof = {"bound": "hbm", "kernel": dominant, "achieved": round(ach, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4),
-                "traffic": measured_traffic(w["name"], dominant),
+                "traffic": measured_traffic(prof_name, dominant),
                 "algorithmic_bytes_per_launch": sb[dominant], "avg_launch_ms": round(dom_ms, 4)}
     else:
         ach = fl.get(dominant, 0) / (dom_ms / 1e3) / 1e12
         roof = {"bound": "mfma", "kernel": dominant, "achieved": round(ach, 2), "peak": BF16_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(ach / BF16_PEAK_TFLOPS, 4),
-                "traffic": measured_traffic(w["name"], dominant), "avg_launch_ms": round(dom_ms, 4)}
+                "traffic": measured_traffic(prof_name, dominant), "avg_launch_ms": round(dom_ms, 4)}
 
     roof["achievable"] = achievable_peaks(lh, torch, stream)
     log(f"achievable on this GPU: {roof['achievable']}")
@@ -409,10 +420,15 @@ def main():
     if not args.no_cpu:
         heads = max(1, min(H, args.cpu_heads, os.cpu_count() or 1))
         log(f"CPU oracle on {heads} heads ...")
-        cpu = cpu_baseline(w, x, heads)
+        cpu = cpu_baseline(w, x, heads, score_mode, sel_mode)
 
+    variant = []
+    if sel_mode:
+        variant.append("parent-kept selection")
+    if score_mode:
+        variant.append(f"score {args.score}")
     out = {
-        "metric": METRIC,
+        "metric": METRIC + (f" ({', '.join(variant)})" if variant else ""),
         "value": round(tokens_per_s, 1),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -425,7 +441,8 @@ def main():
         "dtype": w["dtype"],
         "data": "synthetic (seeded, inputs resident in HBM)",
         "config": {"workload": w["name"], "N": N, "H": H, "d": d, "p": p, "L": L, "K": K, "S": S,
-                   "scatter_mode": "int_atomic" if args.mode else "fp_atomic"},
+                   "scatter_mode": "int_atomic" if args.mode else "fp_atomic",
+                   "select": args.select, "score": args.score},
         "roofline": roof,
         "cpu_baseline": cpu,
         "dense_causal_attention": dense,

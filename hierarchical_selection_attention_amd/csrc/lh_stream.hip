@@ -752,53 +752,88 @@ static int pick_mt(int rows_threads, int limit) {
 // cover a token, one per level.  lmap[l][h][j] holds 1 + the slot of entry
 // (level l, index j) when it is kept, else 0.
 
-// out[z][t][h] = sum over the levels l whose entry covering t is kept of
-// tab[z][h][slot] / p^l (z = 1: the scatter of O~, divided by 1; z = 3: the
-// pool adjoint of dQ~, dK~, dV~).  fp32 tables, one rounding to bf16.  One
-// thread per (token, head, 8-element chunk), token-major, so a wavefront
-// writes consecutive 16-byte pieces of the output rows.
+// out[z][t][h] = sum over the kept entries covering t of tab[z][h][slot], each
+// divided by p^level when `divide` (z = 1: the scatter of O~; z = 3: the pool
+// adjoint of dQ~, dK~, dV~, one tensor per workgroup).  fp32 tables, one
+// rounding to bf16.  Threads walk tokens like the partition's row copy: the
+// entries covering the first token come from the level maps; after that a
+// cursor over the position-sorted slots enters each entry where it starts (its
+// row is loaded once, into the register row of its level) and an entry leaves
+// at its end, so rows are read once per entry and thread, not per token.
 struct SumCopyArgs {
     const int32_t* lmap;          // [sum_l H * n_l] int32, level l at lmap_off[l]
+    const int32_t* start;         // [H][S]
+    const uint8_t* level;         // [H][S]
     const float* tab[3];          // fp32 [H][Sp][d]
     uint16_t* out[3];             // bf16; token t, head h at element t * ld + h * d
     int64_t lmap_off[kMaxLevels];
     int64_t n[kMaxLevels], pw[kMaxLevels];
-    int64_t N, Sp, ld;
-    int H, L, Z, divide;
+    float scale[kMaxLevels];      // 1 / p^l, or 1
+    int64_t N, S, Sp, ld;
+    int H, HG, mt, L;
 };
 
-template <int G>
+template <int G, int LMAX>
 __global__ void __launch_bounds__(256) k_sum_copy(SumCopyArgs a) {
     constexpr int d = G * 8;
-    const int64_t total = a.N * a.H * G;
-    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total; i += (int64_t)gridDim.x * 256) {
-        const int c = (int)(i % G);
-        const int64_t th = i / G;
-        const int h = (int)(th % a.H);
-        const int64_t t = th / a.H;
-        float acc[3][8];
-        for (int z = 0; z < 3; ++z)
-            for (int e = 0; e < 8; ++e) acc[z][e] = 0.f;
-        for (int l = 0; l < a.L; ++l) {
-            const int32_t s1 = a.lmap[a.lmap_off[l] + (int64_t)h * a.n[l] + t / a.pw[l]];
-            if (s1 == 0) continue;
-            const int64_t el = ((int64_t)h * a.Sp + (s1 - 1)) * d + 8 * c;
-            const float inv = a.divide ? 1.0f / (float)a.pw[l] : 1.0f;
-            for (int z = 0; z < a.Z; ++z) {
-                float x[8];
-                load8f(a.tab[z], el, x);
+    const TokMap tm = tok_map<G>(a.HG, a.mt, a.N);
+    if (tm.tb >= tm.te) return;
+    const int z = blockIdx.z;
+    const int h = tm.h;
+    const int32_t* st = a.start + (int64_t)h * a.S;
+    const uint8_t* lv = a.level + (int64_t)h * a.S;
+    const float* tab = a.tab[z] + (int64_t)h * a.Sp * d + 8 * tm.c;
+    uint16_t* ob = a.out[z] + (int64_t)h * d + 8 * tm.c;
+    float row[LMAX][8];
+    int64_t end[LMAX];   // first token after the active entry of each level (<= tm.tb: none)
+    int64_t j = tm.tb;
 #pragma unroll
-                for (int e = 0; e < 8; ++e) acc[z][e] += a.divide ? x[e] * inv : x[e];
+    for (int l = 0; l < LMAX; ++l) {
+        end[l] = 0;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) row[l][e] = 0.f;
+        if (l < a.L) {
+            const int32_t s1 = a.lmap[a.lmap_off[l] + (int64_t)h * a.n[l] + j];
+            if (s1 != 0) {
+                load8f(tab, (int64_t)(s1 - 1) * d, row[l]);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) row[l][e] *= a.scale[l];
+                end[l] = (j + 1) * a.pw[l];
             }
+            j /= a.pw[l + 1 < a.L ? l + 1 : l] / a.pw[l];
         }
-        for (int z = 0; z < a.Z; ++z) {
-            u32x4 w;
-            w[0] = pack_bf16x2(acc[z][0], acc[z][1]);
-            w[1] = pack_bf16x2(acc[z][2], acc[z][3]);
-            w[2] = pack_bf16x2(acc[z][4], acc[z][5]);
-            w[3] = pack_bf16x2(acc[z][6], acc[z][7]);
-            __builtin_nontemporal_store(w, reinterpret_cast<u32x4*>(a.out[z] + t * a.ld + (int64_t)h * d + 8 * c));
+    }
+    int64_t cur = find_slot(st, a.S, tm.tb) + 1;   // first slot starting after tm.tb
+    int64_t nstart = cur < a.S ? st[cur] : a.N;
+    for (int64_t t = tm.tb; t < tm.te; ++t) {
+        while (nstart <= t) {   // entries that start at t, coarser first
+            const int l = lv[cur];
+            float x[8];
+            load8f(tab, cur * d, x);
+#pragma unroll
+            for (int q = 0; q < LMAX; ++q) {
+                if (q == l) {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) row[q][e] = x[e] * a.scale[q];
+                    end[q] = t + a.pw[q];
+                }
+            }
+            ++cur;
+            nstart = cur < a.S ? st[cur] : a.N;
         }
+        float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int l = 0; l < LMAX; ++l)
+            if (t < end[l]) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) acc[e] += row[l][e];
+            }
+        u32x4 w;
+        w[0] = pack_bf16x2(acc[0], acc[1]);
+        w[1] = pack_bf16x2(acc[2], acc[3]);
+        w[2] = pack_bf16x2(acc[4], acc[5]);
+        w[3] = pack_bf16x2(acc[6], acc[7]);
+        __builtin_nontemporal_store(w, reinterpret_cast<u32x4*>(ob + t * a.ld));
     }
 }
 
@@ -1004,6 +1039,8 @@ hipError_t launch_sum_copy(const Plan& P, const char* ws, const float* const* ta
     if (out_ld < (int64_t)P.H * P.d || out_ld % 8 != 0) return hipErrorInvalidValue;
     SumCopyArgs a{};
     a.lmap = reinterpret_cast<const int32_t*>(ws + P.off_lmap);
+    a.start = reinterpret_cast<const int32_t*>(ws + P.off_start);
+    a.level = reinterpret_cast<const uint8_t*>(ws + P.off_level);
     for (int z = 0; z < Z; ++z) {
         a.tab[z] = tab[z];
         a.out[z] = reinterpret_cast<uint16_t*>(out[z]);
@@ -1012,15 +1049,22 @@ hipError_t launch_sum_copy(const Plan& P, const char* ws, const float* const* ta
         a.lmap_off[l] = (int64_t)P.lmap_off[l];
         a.n[l] = P.n[l];
         a.pw[l] = P.pw[l];
+        a.scale[l] = divide ? 1.0f / (float)P.pw[l] : 1.0f;
     }
-    a.N = P.N; a.Sp = P.Sp; a.ld = out_ld;
-    a.H = P.H; a.L = P.L; a.Z = Z; a.divide = divide ? 1 : 0;
+    a.N = P.N; a.S = P.S; a.Sp = P.Sp; a.ld = out_ld;
+    a.H = P.H; a.L = P.L;
     const int G = P.d / 8;
-    const int64_t total = (int64_t)P.N * P.H * G;
-    const int64_t blocks = (total + 255) / 256;
-    const unsigned grid = (unsigned)(blocks < 8192 ? blocks : 8192);
-    if (G == 16) hipLaunchKernelGGL((k_sum_copy<16>), dim3(grid), dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((k_sum_copy<8>), dim3(grid), dim3(256), 0, s, a);
+    const int threads = scatter_threads(P, &a.HG, &a.mt);
+    dim3 grid((unsigned)((P.N + kTileTok - 1) / kTileTok), (unsigned)(P.H / a.HG), (unsigned)Z);
+#define LH_SUMC(GG, LM) hipLaunchKernelGGL((k_sum_copy<GG, LM>), grid, dim3(threads), 0, s, a)
+    if (P.L <= 6) {
+        if (G == 16) LH_SUMC(16, 6); else LH_SUMC(8, 6);
+    } else if (P.L <= 12) {
+        if (G == 16) LH_SUMC(16, 12); else LH_SUMC(8, 12);
+    } else {
+        if (G == 16) LH_SUMC(16, kMaxLevels); else LH_SUMC(8, kMaxLevels);
+    }
+#undef LH_SUMC
     return hipGetLastError();
 }
 
