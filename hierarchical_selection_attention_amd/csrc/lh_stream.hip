@@ -862,9 +862,22 @@ __global__ void __launch_bounds__(256) k_entry_sum(EntrySumArgs a) {
     const int c = lane % G, r = lane / G;
     const int64_t t0 = a.start[(int64_t)h * a.S + slot];
     const int64_t len = a.pw[a.level[(int64_t)h * a.S + slot]];
-    float x[8], acc[8];
+    float acc[8];
     for (int e = 0; e < 8; ++e) acc[e] = 0.f;
-    for (int64_t t = t0 + r; t < t0 + len; t += R) {
+    // four rows per lane group in flight; the order of the additions is fixed
+    constexpr int U = 4;
+    int64_t t = t0 + r;
+    for (; t + (U - 1) * R < t0 + len; t += U * R) {
+        float x[U][8];
+#pragma unroll
+        for (int u = 0; u < U; ++u) load8<0>(a.dout, ((t + u * R) * a.H + h) * d + 8 * c, x[u]);
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[e] += x[u][e];
+    }
+    for (; t < t0 + len; t += R) {
+        float x[8];
         load8<0>(a.dout, (t * a.H + h) * d + 8 * c, x);
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc[e] += x[e];
