@@ -139,3 +139,26 @@ def test_scored_forward_rejects_unknown_score_mode():
                                 None) == lh.LH_ERR_DTYPE
     assert lh.lh_forward_scored(fake, fake, fake, fake, 2048, 2, 64, 4, 3, 16, 1, -1, fake * 256, nb,
                                 None) == lh.LH_ERR_DTYPE
+
+
+@pytest.mark.parametrize("N,p,L,K", [(2048, 4, 3, 16), (2048, 4, 3, 512), (524288, 4, 5, 128), (1080, 3, 4, 5),
+                                     (4096, 2, 8, 3), (256, 4, 4, 0), (512, 4, 1, 7)])
+def test_parent_kept_subseq_len_matches_oracle(N, p, L, K):
+    lh = _lh()
+    assert lh.lh_subseq_len_sel(N, p, L, K, 1) == oracle.subseq_len(N, p, L, K, 1)
+    assert lh.lh_subseq_len_sel(N, p, L, K, 0) == lh.lh_subseq_len(N, p, L, K)
+
+
+def test_select_mode_validation():
+    lh = _lh()
+    assert lh.lh_subseq_len_sel(2048, 4, 3, 16, 2) == lh.LH_ERR_DTYPE                  # unknown mode
+    assert lh.lh_workspace_bytes_sel(2048, 2, 64, 4, 3, 16, 1, 1) == 0                # parent kept is bf16 only
+    assert lh.lh_workspace_bytes_sel(2048, 2, 64, 4, 3, 16, 0, 1) > 0
+    fake = 1 << 20                                                                     # never dereferenced
+    nb = lh.lh_workspace_bytes_sel(2048, 2, 64, 4, 3, 16, 0, 1)
+    assert lh.lh_forward_sel(fake, fake, fake, fake, 2048, 2, 64, 4, 3, 16, 1, 0, 1, fake * 256, nb,
+                             None) == lh.LH_ERR_DTYPE
+    assert lh.lh_forward_sel(fake, fake, fake, fake, 2048, 2, 64, 4, 3, 16, 0, 0, 3, fake * 256, nb,
+                             None) == lh.LH_ERR_DTYPE
+    assert lh.lh_backward_sel(fake, fake, fake, fake, 2048, 2, 64, 4, 3, 16, 0, 0, 1, fake * 256, nb - 1,
+                              None) == lh.LH_ERR_WORKSPACE
