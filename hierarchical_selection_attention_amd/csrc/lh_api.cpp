@@ -334,7 +334,9 @@ int backward_strided(const void* dout, void* dq, void* dk, void* dv, int N, int 
     const size_t HSd = (size_t)H * P.Sp * d;
     unsigned int* hmax = reinterpret_cast<unsigned int*>(w + P.off_hmax);
     unsigned int* hmax_b = hmax + 4 * (size_t)H;
-    LH_TRY(stage(ST_ZERO_ACC, s, [&] { return launch_fill_zero(w + P.off_acc, 8 * HSd, s); }));
+    // fp32 accumulators use the first half of the segment, int64 ones all of it
+    const size_t acc_bytes = (scatter_mode == LH_SCATTER_INT_ATOMIC && !P.pk ? 8 : 4) * HSd;
+    LH_TRY(stage(ST_ZERO_ACC, s, [&] { return launch_fill_zero(w + P.off_acc, acc_bytes, s); }));
     // parent kept: each entry's sum of dO is taken by one wavefront (no atomics), in the
     // fp32 layout of the fp-atomic accumulators
     const int acc_mode = P.pk ? LH_SCATTER_FP_ATOMIC : scatter_mode;
