@@ -81,6 +81,14 @@ def test_block_small_all_outputs(mode):
     _run_block(b, N, dm, H, d, p, L, K, mode, None, None, None, "small")
 
 
+@pytest.mark.parametrize("dm", [192, 64])
+def test_block_non_square_projections(dm):
+    """d_model != H*d: every GEMM has distinct M, N and K, so a transposed operand cannot go unseen."""
+    N, H, d, p, L, K = 2048, 2, 64, 4, 3, 16
+    b = si.make_block_inputs(N, dm, H, d, seed=78 + dm, planted=0.01, with_dy=True)
+    _run_block(b, N, dm, H, d, p, L, K, 0, None, None, None, f"dm{dm}")
+
+
 def test_block_530m_shape_sampled():
     w = si.BLOCK_WORKLOAD
     N, dm, H, d, p, L, K = w["N"], w["dm"], w["H"], w["d"], w["p"], w["L"], w["K"]
