@@ -99,6 +99,7 @@ int make_plan(int N, int H, int d, int p, int L, int K, int dtype, Plan* P, int 
     pl.off_kTh = take(h16); pl.off_kTl = take(h16);
     pl.off_qTbh = take(h16); pl.off_qTbl = take(h16);
     pl.off_hmax = take(sizeof(uint32_t) * 8 * (size_t)H);
+    pl.off_rowmax = take(sizeof(float) * 4 * (size_t)H * pl.Sp);
     pl.off_hscale = take(sizeof(float) * 4 * (size_t)H);
     pl.off_os = take(sizeof(float) * HSd);
     pl.off_lse = take(sizeof(float) * (size_t)H * pl.Sp);
@@ -278,11 +279,10 @@ int lh_forward_sel(const void* q, const void* k, const void* v, void* o, int N, 
     LH_TRY(stage(ST_GATHER, s, [&] { return launch_gather(P, q, k, v, w, s); }));
     unsigned int* hmax = reinterpret_cast<unsigned int*>(w + P.off_hmax);
     LH_TRY(stage(ST_SUB_PREP, s, [&] {
-        hipError_t e = launch_fill_zero(hmax, sizeof(uint32_t) * 8 * (size_t)H, s);
-        if (e != hipSuccess || dtype != BF16) return e;
-        const void* src[3] = {w + P.off_qs, w + P.off_ks, w + P.off_vs};
+        if (dtype != BF16) return hipSuccess;
+        // per-head max |x| of q~, k~, v~ from the row maxima the gather left
         unsigned int* out[3] = {hmax, hmax + 1, hmax + 2};
-        e = launch_maxabs(src, out, 3, false, P.d, P.Sp * P.d, P.Sp, P.d, H, s);
+        hipError_t e = launch_head_max(f32(w, P.off_rowmax), out, 3, P.S, P.Sp, H, s);
         const SplitSpec sp[3] = {
             split_spec(P, w, P.off_qs, hmax, 0, P.off_qh, P.off_ql, P.off_qTbh, P.off_qTbl, 1),
             split_spec(P, w, P.off_ks, hmax, 1, P.off_kh, P.off_kl, P.off_kTh, P.off_kTl, 0),
@@ -348,12 +348,12 @@ int backward_strided(const void* dout, void* dq, void* dk, void* dv, int N, int 
         rp.acc = w + P.off_acc; rp.o = w + P.off_os;
         rp.dos = f32(w, P.off_dos); rp.D = f32(w, P.off_D); rp.rowdown = f32(w, P.off_rowdown);
         rp.vmax = hmax; rp.S = P.S; rp.Sp = P.Sp; rp.H = H; rp.d = d; rp.mode = acc_mode; rp.dense = 0;
+        float* rowmax_b = f32(w, P.off_rowmax) + 3 * (size_t)H * P.Sp;
+        rp.rowmax = dtype == BF16 ? rowmax_b : nullptr;
         hipError_t e = launch_row_prep(rp, s);
         if (e != hipSuccess || dtype != BF16) return e;
-        e = launch_fill_zero(hmax_b, sizeof(uint32_t) * 4 * (size_t)H, s);
-        const void* src[1] = {w + P.off_dos};
         unsigned int* out[1] = {hmax_b + 3};
-        if (e == hipSuccess) e = launch_maxabs(src, out, 1, false, P.d, P.Sp * P.d, P.Sp, P.d, H, s);
+        e = launch_head_max(rowmax_b, out, 1, P.S, P.Sp, H, s);
         const SplitSpec sp = split_spec(P, w, P.off_dos, hmax_b, 3, P.off_doh, P.off_dol, P.off_doTh, P.off_doTl, 0);
         if (e == hipSuccess) e = launch_split(&sp, 1, s);
         return e;

@@ -71,6 +71,7 @@ struct Plan {
     size_t off_qh, off_ql, off_kh, off_kl, off_vh, off_vl;
     size_t off_vTh, off_vTl, off_kTh, off_kTl, off_qTbh, off_qTbl;
     size_t off_hmax;              // uint32 [2][H][4]: forward (q, k, v) and backward (dO) max |x|
+    size_t off_rowmax;            // fp32 [4][H][Sp]: max |x| per row of q~, k~, v~ (gather) and dO~
     size_t off_hscale;            // fp32 [H][4]: per-head multipliers of the fp16 copies
     size_t off_os;                // fp32 [H][Sp][d]
     size_t off_lse, off_lse2;     // fp32 [H][Sp]
@@ -169,9 +170,13 @@ struct RowPrepSpec {
     const float* lse_in;       // dense: natural-log lse [H][N] -> lse2 (base 2)
     float* lse2;
     const unsigned int* vmax;
+    float* rowmax;             // optional: per-row max |dO~| [H][Sp]
     int64_t S, Sp;
     int H, d, mode, dense;
 };
+// out[t][h * 4] = max over rows of rowmax[t][h][0..rows) (rows_ld apart), T <= 4 tensors
+hipError_t launch_head_max(const float* rowmax, unsigned int* const* out, int T, int64_t rows, int64_t rows_ld,
+                           int H, hipStream_t s);
 // max |x| per head of T <= 3 tensors of one layout (out[t]: the tensor's [H][4] slot word)
 hipError_t launch_maxabs(const void* const* src, unsigned int* const* out, int T, bool src_bf16, int64_t ld,
                          int64_t hs, int64_t rows, int d, int H, hipStream_t s);

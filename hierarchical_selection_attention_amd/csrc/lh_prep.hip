@@ -44,6 +44,28 @@ __global__ void __launch_bounds__(256) k_maxabs(MaxAbsArgs a) {
     }
 }
 
+// Per-head maximum of per-row maxima: out[t][h * 4] = max over rows of
+// rowmax[t][h][0..rows), as float bits (values are >= 0).  One workgroup per
+// (head, tensor); no atomics, so the words need no clearing first.
+struct HeadMaxArgs {
+    const float* rowmax;    // [T][H][rows_ld]
+    unsigned int* out[4];   // [H][4] word of tensor t's slot
+    int64_t rows, rows_ld;
+    int H;
+};
+__global__ void __launch_bounds__(256) k_head_max(HeadMaxArgs a) {
+    const int h = blockIdx.x, t = blockIdx.y;
+    const float* r = a.rowmax + ((int64_t)t * a.H + h) * a.rows_ld;
+    float mx = 0.f;
+    for (int64_t i = threadIdx.x; i < a.rows; i += 256) mx = fmaxf(mx, r[i]);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, shfl_xor_f(mx, off));
+    __shared__ float wm[4];
+    if ((threadIdx.x & 63) == 0) wm[threadIdx.x >> 6] = mx;
+    __syncthreads();
+    if (threadIdx.x == 0) a.out[t][h * 4] = __float_as_uint(fmaxf(fmaxf(wm[0], wm[1]), fmaxf(wm[2], wm[3])));
+}
+
 // Power of two s with max|x| * s in [2^13, 2^14) (1 when max is 0).
 __device__ __forceinline__ float down_scale(float mx) {
     if (!(mx > 0.f)) return 1.0f;
@@ -166,6 +188,7 @@ struct RowPrepArgs {
     const float* lse_in;   // dense: natural-log lse [H][N], converted to base 2 in lse2
     float* lse2;
     const unsigned int* vmax;  // [H][4] slot 2: max |V|
+    float* rowmax;             // optional fp32 [H][Sp]: max |dO~| of each row
     int64_t S, Sp;
     int H, d, mode, dense;
 };
@@ -208,6 +231,14 @@ __global__ void __launch_bounds__(256) k_row_prep(RowPrepArgs a) {
     for (int off = G / 2; off >= 1; off >>= 1) {
         dot += __shfl_xor(dot, off, 64);
         nrm += __shfl_xor(nrm, off, 64);
+    }
+    if (a.rowmax) {   // the row's max |dO~| for the per-head scale of its 16-bit copies
+        float mx = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) mx = fmaxf(mx, fabsf(x[e]));
+#pragma unroll
+        for (int off = G / 2; off >= 1; off >>= 1) mx = fmaxf(mx, shfl_xor_f(mx, off));
+        if (live && c == 0) a.rowmax[r] = mx;
     }
     if (live && c == 0) {
         if (a.lse_in) a.lse2[r] = a.lse_in[r] * 1.4426950408889634f;
@@ -269,11 +300,22 @@ hipError_t launch_split(const SplitSpec* sp, int T, hipStream_t s) {
     return hipGetLastError();
 }
 
+hipError_t launch_head_max(const float* rowmax, unsigned int* const* out, int T, int64_t rows, int64_t rows_ld,
+                           int H, hipStream_t s) {
+    if (T < 1 || T > 4 || rows < 0 || rows > rows_ld) return hipErrorInvalidValue;
+    HeadMaxArgs a{};
+    a.rowmax = rowmax;
+    for (int t = 0; t < T; ++t) a.out[t] = out[t];
+    a.rows = rows; a.rows_ld = rows_ld; a.H = H;
+    hipLaunchKernelGGL(k_head_max, dim3((unsigned)H, (unsigned)T), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
 hipError_t launch_row_prep(const RowPrepSpec& sp, hipStream_t s) {
     RowPrepArgs a{};
     a.acc = sp.acc; a.dout = sp.dout; a.o = sp.o; a.ld = sp.ld; a.hs = sp.hs;
     a.dos = sp.dos; a.D = sp.D; a.rowdown = sp.rowdown; a.vmax = sp.vmax;
-    a.lse_in = sp.lse_in; a.lse2 = sp.lse2;
+    a.lse_in = sp.lse_in; a.lse2 = sp.lse2; a.rowmax = sp.rowmax;
     a.S = sp.S; a.Sp = sp.Sp; a.H = sp.H; a.d = sp.d; a.mode = sp.mode; a.dense = sp.dense;
     const int G = sp.d / 8;
     const int64_t rows = (int64_t)sp.H * sp.Sp;

@@ -325,6 +325,7 @@ struct GatherArgs {
     const int32_t* start;
     const uint8_t* level;
     float *qs, *ks, *vs;   // fp32 [H][Sp][d]
+    float* rowmax;         // fp32 [3][H][Sp]: max |x| of each written row (q, k, v)
     int64_t S, Sp, n_m, ntop;
     int64_t pw[kMaxLevels];
     int H, m, L;
@@ -347,6 +348,8 @@ __global__ void __launch_bounds__(64) k_gather(GatherArgs a) {
             store8f(a.ks, orow, z);
             store8f(a.vs, orow, z);
         }
+        if (lane == 0)
+            for (int t = 0; t < 3; ++t) a.rowmax[((int64_t)t * a.H + h) * a.Sp + i] = 0.f;
         return;
     }
     const int64_t st = a.start[h * a.S + i];
@@ -412,15 +415,21 @@ __global__ void __launch_bounds__(64) k_gather(GatherArgs a) {
 #pragma unroll
                 for (int e = 0; e < 8; ++e) acc[t][e] += shfl_xor_f(acc[t][e], off);
     }
-    if (rs == 0) {
-        float* dst[3] = {a.qs, a.ks, a.vs};
+    float* dst[3] = {a.qs, a.ks, a.vs};
 #pragma unroll
-        for (int t = 0; t < 3; ++t) {
-            float o[8];
+    for (int t = 0; t < 3; ++t) {
+        float o[8], mx = 0.f;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) o[e] = (R > 1) ? acc[t][e] / (float)R : acc[t][e];
-            store8f(dst[t], orow, o);
+        for (int e = 0; e < 8; ++e) {
+            o[e] = (R > 1) ? acc[t][e] / (float)R : acc[t][e];
+            mx = fmaxf(mx, fabsf(o[e]));
         }
+        if (rs == 0) store8f(dst[t], orow, o);
+        // the row's max |x| for the per-head scale of the 16-bit operand copies (lanes
+        // rs != 0 hold the same row after the butterfly, or zeros when R == 1)
+#pragma unroll
+        for (int off = G / 2; off >= 1; off >>= 1) mx = fmaxf(mx, shfl_xor_f(mx, off));
+        if (lane == 0) a.rowmax[((int64_t)t * a.H + h) * a.Sp + i] = mx;
     }
 }
 
@@ -950,6 +959,7 @@ hipError_t launch_gather(const Plan& P, const void* q, const void* k, const void
     a.qs = reinterpret_cast<float*>(ws + P.off_qs);
     a.ks = reinterpret_cast<float*>(ws + P.off_ks);
     a.vs = reinterpret_cast<float*>(ws + P.off_vs);
+    a.rowmax = reinterpret_cast<float*>(ws + P.off_rowmax);
     a.S = P.S; a.Sp = P.Sp; a.n_m = P.n[P.m]; a.ntop = P.ntop;
     for (int l = 0; l < P.L; ++l) a.pw[l] = P.pw[l];
     a.H = P.H; a.m = P.m; a.L = P.L;
