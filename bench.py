@@ -48,13 +48,22 @@ def stage_bytes(w, S, pk=False):
         m += 1
     pool_m = (N // p ** m) * H * d * 4 * 3
     sub32 = S * H * d * 4
-    tab = sub32 if pk else S * H * d * e
-    return {
+    out = {
         "pool_score": 3 * row + nscore + pool_m,      # read q, k, v; write scores and level-m means
-        "scatter_fwd": row + tab,                     # write o; read the rows of O~ once
         "scatter_bwd": row + sub32,                   # read dO; write dO~ once
-        "pool_bwd": 3 * row + 3 * tab,                # write dq, dk, dv; read their sub-sequence rows once
     }
+    if pk:   # summed copies from the fp32 sub-sequence rows
+        out["scatter_fwd"] = row + sub32              # write o; read the rows of O~ once
+        out["pool_bwd"] = 3 * row + 3 * sub32         # write dq, dk, dv; read their sub-sequence rows once
+    elif e == 2:
+        # the attention kernels write the token rows themselves (o; dk, dv; dq)
+        out["attn_fwd"] = row
+        out["attn_bwd_dkdv"] = 2 * row
+        out["attn_bwd_dq"] = row
+    else:
+        out["scatter_fwd"] = row + sub32
+        out["pool_bwd"] = 3 * row + 3 * sub32
+    return out
 
 
 def attn_flops(w, S):
@@ -377,7 +386,11 @@ def main():
         stage_rep[name] = rec
     dominant = max(stages, key=lambda s: stages[s][0])
     dom_ms = stages[dominant][0] / stages[dominant][1]
-    if dominant in sb:
+    # a kernel with both HBM bytes and MFMA flops (the attention kernels that write the
+    # token rows) is placed against the resource it uses the larger fraction of
+    f_hbm = sb.get(dominant, 0) / (dom_ms / 1e3) / 1e9 / HBM_PEAK_GBS
+    f_mfma = fl.get(dominant, 0) / (dom_ms / 1e3) / 1e12 / BF16_PEAK_TFLOPS
+    if dominant in sb and f_hbm >= f_mfma:
         ach = sb[dominant] / (dom_ms / 1e3) / 1e9
         roof = {"bound": "hbm", "kernel": dominant, "achieved": round(ach, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4),

@@ -114,8 +114,6 @@ int make_plan(int N, int H, int d, int p, int L, int K, int dtype, Plan* P, int 
     pl.off_dk = take(sizeof(float) * HSd);
     pl.off_dv = take(sizeof(float) * HSd);
     pl.rowcopy = dtype == BF16 && !pl.pk;
-    pl.off_otab = take(pl.rowcopy ? 2 * HSd : 0);
-    pl.off_gtab = take(pl.rowcopy ? 3 * 2 * HSd : 0);
     size_t nmap = 0;
     for (int l = 0; l < L; ++l) {
         pl.lmap_off[l] = nmap;
@@ -292,23 +290,22 @@ int lh_forward_sel(const void* q, const void* k, const void* v, void* o, int N, 
     }));
     AttnArgs a = sub_attn_args(P, w);
     if (P.rowcopy) {
-        // O~ also leaves the attention as bf16 rows, rounded as the scatter rounds them
-        a.o_bf16 = u16m(w, P.off_otab);
-        a.ld_o = d;
-        a.hs_o = P.Sp * d;
+        // the attention kernel scatters O~ to the tokens itself (stage (iv)), rounded once to bf16
+        a.o_tok = reinterpret_cast<uint16_t*>(o);
+        a.start = reinterpret_cast<const int32_t*>(w + P.off_start);
+        a.level = reinterpret_cast<const uint8_t*>(w + P.off_level);
+        a.p = p;
+        a.tok_ld = (int64_t)H * d;
     }
     LH_TRY(stage(ST_ATTN_FWD, s, [&] { return launch_attn_fwd(a, s); }));
-    LH_TRY(stage(ST_SCATTER_FWD, s, [&] {
+    if (!P.rowcopy) LH_TRY(stage(ST_SCATTER_FWD, s, [&] {
         if (P.pk) {
             // overlapping entries: every token sums the outputs of the entries that cover it
             const float* tab[1] = {f32(w, P.off_os)};
             void* out[1] = {o};
             return launch_sum_copy(P, w, tab, out, 1, false, (int64_t)H * d, s);
         }
-        if (!P.rowcopy) return launch_scatter_fwd(P, w, o, s);
-        const uint16_t* tab[1] = {u16(w, P.off_otab)};
-        void* out[1] = {o};
-        return launch_row_copy(P, w, tab, out, 1, (int64_t)H * d, s);
+        return launch_scatter_fwd(P, w, o, s);
     }));
     return LH_OK;
 }
@@ -359,28 +356,27 @@ int backward_strided(const void* dout, void* dq, void* dk, void* dv, int N, int 
         return e;
     }));
     AttnArgs a = sub_attn_args(P, w);
-    const size_t HSd2 = 2 * HSd;
     if (P.rowcopy) {
-        // the gradients also leave the attention as the pool adjoint's bf16 rows
-        a.tq = u16m(w, P.off_gtab);
-        a.tk = u16m(w, P.off_gtab + HSd2);
-        a.tv = u16m(w, P.off_gtab + 2 * HSd2);
+        // the gradient kernels apply the pool adjoint themselves: dX~ / p^level to every
+        // token of the entry, rounded once to bf16
+        a.dq_tok = reinterpret_cast<uint16_t*>(dq);
+        a.dk_tok = reinterpret_cast<uint16_t*>(dk);
+        a.dv_tok = reinterpret_cast<uint16_t*>(dv);
+        a.start = reinterpret_cast<const int32_t*>(w + P.off_start);
         a.level = reinterpret_cast<const uint8_t*>(w + P.off_level);
         a.p = p;
+        a.tok_ld = grad_ld;
     }
     LH_TRY(stage(ST_ATTN_BWD_DKDV, s, [&] { return launch_attn_bwd(a, s, 0); }));
     if (dtype == BF16) LH_TRY(stage(ST_ATTN_BWD_DQ, s, [&] { return launch_attn_bwd(a, s, 1); }));
-    LH_TRY(stage(ST_POOL_BWD, s, [&] {
+    if (!P.rowcopy) LH_TRY(stage(ST_POOL_BWD, s, [&] {
         if (P.pk) {
             // a token sums dX~ / p^level over the entries that cover it
             const float* tab[3] = {f32(w, P.off_dq), f32(w, P.off_dk), f32(w, P.off_dv)};
             void* out[3] = {dq, dk, dv};
             return launch_sum_copy(P, w, tab, out, 3, true, grad_ld, s);
         }
-        if (!P.rowcopy) return launch_pool_bwd(P, w, dq, dk, dv, s);
-        const uint16_t* tab[3] = {u16(w, P.off_gtab), u16(w, P.off_gtab + HSd2), u16(w, P.off_gtab + 2 * HSd2)};
-        void* out[3] = {dq, dk, dv};
-        return launch_row_copy(P, w, tab, out, 3, grad_ld, s);
+        return launch_pool_bwd(P, w, dq, dk, dv, s);
     }));
     return LH_OK;
 }

@@ -94,9 +94,11 @@ struct AttnK {
     const float* rowdown;   // [H][Sp]: power-of-two down-scale of dS rows (dq kernel)
     float *dq, *dk, *dv;    // fp32 [H][Sp][d] gradients, or
     uint16_t *dq_b, *dk_b, *dv_b;   // bf16 gradients with strides ld_o/hs_o
-    uint16_t *tq, *tk, *tv;         // or null: bf16 [H][Sp][d] copies of the fp32 gradients / p^level
     const uint8_t* level;           // [H][rows]
     int p;
+    uint16_t *o_tok, *dq_tok, *dk_tok, *dv_tok;   // or null: bf16 token rows [N][H][d], tok_ld apart
+    const int32_t* start;                         // [H][rows]: first token of each entry
+    int64_t tok_ld;
     int64_t rows, Sp, ld_o, hs_o;
     float scale;            // 1/sqrt(d)
     // fp32 path (double arithmetic)
@@ -263,6 +265,37 @@ __device__ __forceinline__ float level_den(const AttnK& a, int h, int64_t row) {
 // 4 fp32 values / den, rounded to bf16 (round to nearest even)
 __device__ __forceinline__ u32x2 bf16x4_div(const f32x4& x, float den) {
     return u32x2{pack_bf16x2(x[0] / den, x[1] / den), pack_bf16x2(x[2] / den, x[3] / den)};
+}
+
+// Scatter inside the attention kernels (Sec. 3 stage (iv), and the pool
+// adjoint of the gradient path): a wavefront's 16 result rows are staged in
+// LDS as bf16, then written to every token of their entries, one 16-byte
+// chunk of one token row per lane, so the kernel's HBM writes overlap the
+// other workgroups' MFMA work instead of running as a pass of their own.
+// stage_rows: lane (lq, lg) holds columns 16v + 4lg .. +3 of row lq; the row
+// is stored as bf16 of x * mul / den (den = p^level for the pool adjoint).
+template <int D>
+__device__ __forceinline__ void stage_rows(uint16_t* rows, const f32x4* acc, float mul, float den, int lq, int lg) {
+#pragma unroll
+    for (int v = 0; v < D / 16; ++v)
+        *reinterpret_cast<u32x2*>(rows + lq * D + 16 * v + 4 * lg) = bf16x4_div(acc[v] * mul, den);
+}
+template <int D>
+__device__ __forceinline__ void rows_to_tokens(const uint16_t* rows, uint16_t* tok, const AttnK& a, int h,
+                                               int64_t r0, int lane) {
+    constexpr int CPR = D / 8, TPI = 64 / CPR;   // 16-byte chunks per row, tokens per store
+    const int c = lane % CPR, r4 = lane / CPR;
+    for (int j = 0; j < 16; ++j) {
+        const int64_t row = r0 + j;
+        if (row >= a.rows) break;
+        const int64_t st = a.start[(int64_t)h * a.rows + row];
+        int64_t n = 1;
+        for (int z = a.level[(int64_t)h * a.rows + row]; z > 0; --z) n *= a.p;
+        const u32x4 x = *reinterpret_cast<const u32x4*>(rows + j * D + 8 * c);
+        uint16_t* dst = tok + st * a.tok_ld + (int64_t)h * D + 8 * c;
+        for (int64_t t = r4; t < n; t += TPI)
+            __builtin_nontemporal_store(x, reinterpret_cast<u32x4*>(dst + t * a.tok_ld));
+    }
 }
 
 // Work item -> (head, 64-row tile).  When H is a multiple of 8, the workgroups
@@ -472,6 +505,12 @@ __global__ void __launch_bounds__(256) k_attn_fwd(AttnK a) {
         a.lse2[(int64_t)h * Sp + myq] = l2;
         a.lse[(int64_t)h * Sp + myq] = l2 * kLn2;
     }
+    if (a.o_tok) {   // the LDS tiles are idle: every wave is past the loop's last barrier
+        uint16_t* rows = sm + wave * 16 * D;
+        stage_rows<D>(rows, o, mul, 1.0f, lq, lg);
+        __syncthreads();
+        rows_to_tokens<D>(rows, a.o_tok, a, h, q0, lane);
+    }
 }
 
 // ------------------------------------------------------- backward: dK, dV
@@ -648,15 +687,17 @@ __global__ void __launch_bounds__(256) k_attn_dkdv(AttnK a) {
                 __builtin_nontemporal_store(dk[v] * a.scale, reinterpret_cast<f32x4*>(a.dk + base + 16 * v));
                 __builtin_nontemporal_store(dv[v] * mdo, reinterpret_cast<f32x4*>(a.dv + base + 16 * v));
             }
-            if (a.tk) {
-                const float den = level_den(a, h, mykey);
-#pragma unroll
-                for (int v = 0; v < NV; ++v) {
-                    *reinterpret_cast<u32x2*>(a.tk + base + 16 * v) = bf16x4_div(dk[v] * a.scale, den);
-                    *reinterpret_cast<u32x2*>(a.tv + base + 16 * v) = bf16x4_div(dv[v] * mdo, den);
-                }
-            }
         }
+    }
+    if (a.dk_tok) {   // pool adjoint of k and v: dK~ / p^level, dV~ / p^level to the entry's tokens
+        uint16_t* rk = sm + wave * 16 * D;
+        uint16_t* rv = sm + (4 + wave) * 16 * D;
+        const float den = mykey < a.rows ? level_den(a, h, mykey) : 1.0f;
+        stage_rows<D>(rk, dk, a.scale, den, lq, lg);
+        stage_rows<D>(rv, dv, mdo, den, lq, lg);
+        __syncthreads();
+        rows_to_tokens<D>(rk, a.dk_tok, a, h, k0, lane);
+        rows_to_tokens<D>(rv, a.dv_tok, a, h, k0, lane);
     }
 }
 
@@ -828,13 +869,14 @@ __global__ void __launch_bounds__(256) k_attn_dq(AttnK a) {
             const int64_t base = hb + myq * D + 4 * lg;
 #pragma unroll
             for (int v = 0; v < NV; ++v) __builtin_nontemporal_store(dq[v] * mul, reinterpret_cast<f32x4*>(a.dq + base + 16 * v));
-            if (a.tq) {
-                const float den = level_den(a, h, myq);
-#pragma unroll
-                for (int v = 0; v < NV; ++v)
-                    *reinterpret_cast<u32x2*>(a.tq + base + 16 * v) = bf16x4_div(dq[v] * mul, den);
-            }
         }
+    }
+    if (a.dq_tok) {   // pool adjoint of q: dQ~ / p^level to every token of the entry
+        uint16_t* rows = sm + wave * 16 * D;
+        const float den = myq < a.rows ? level_den(a, h, myq) : 1.0f;
+        stage_rows<D>(rows, dq, a.scale * mk / down, den, lq, lg);
+        __syncthreads();
+        rows_to_tokens<D>(rows, a.dq_tok, a, h, q0, lane);
     }
 }
 
@@ -953,7 +995,9 @@ static AttnK to_k(const AttnArgs& x) {
     a.lse = x.lse; a.lse2 = x.lse2; a.D = x.D; a.rowdown = x.rowdown;
     a.dq = x.dq; a.dk = x.dk; a.dv = x.dv;
     a.dq_b = x.dq_b; a.dk_b = x.dk_b; a.dv_b = x.dv_b;
-    a.tq = x.tq; a.tk = x.tk; a.tv = x.tv; a.level = x.level; a.p = x.p;
+    a.level = x.level; a.p = x.p;
+    a.o_tok = x.o_tok; a.dq_tok = x.dq_tok; a.dk_tok = x.dk_tok; a.dv_tok = x.dv_tok;
+    a.start = x.start; a.tok_ld = x.tok_ld;
     a.rows = x.rows; a.Sp = x.Sp; a.ld_o = x.ld_o; a.hs_o = x.hs_o;
     a.scale = x.scale;
     a.qf = x.qf; a.kf = x.kf; a.vf = x.vf; a.dof = x.dof;

@@ -52,7 +52,7 @@ struct Plan {
     int score_mode;         // leaf score: 0 |q|^2+|k|^2, 1 |k|^2, 2 |q|^2, 3 |q|^2*|k|^2
     int64_t S, Sp;
     int m;                  // pyramid level produced per workgroup by the pooling pass
-    int rowcopy;            // bf16: back-scatter and pool adjoint copy bf16 rows the attention leaves
+    int rowcopy;            // bf16 partition: the attention kernels scatter their results to the tokens
     int pk;                 // "parent kept": selected entries stay beside their children (bf16 only)
     int64_t tok;            // p^m tokens per pooling workgroup
     int64_t ntop;           // N / p^(L-1)
@@ -80,10 +80,6 @@ struct Plan {
     size_t off_doh, off_dol, off_doTh, off_doTl;   // fp16 copies of dO~
     size_t off_D, off_rowdown;    // fp32 [H][Sp]
     size_t off_dq, off_dk, off_dv;   // fp32 [H][Sp][d]
-    // bf16 path: the rows the back-scatter and the pool adjoint copy out,
-    // already rounded to bf16
-    size_t off_otab;              // bf16 [H][Sp][d]: O~
-    size_t off_gtab;              // bf16 [3][H][Sp][d]: dQ~, dK~, dV~ divided by p^level
     // parent kept: int32 [sum_l H * n_l], 1 + the slot of entry (l, j) of head h
     // at lmap_off[l] + h * n_l + j, 0 when that entry is not kept
     size_t off_lmap;
@@ -115,11 +111,6 @@ hipError_t launch_scatter_fwd(const Plan& P, char* ws, void* o, hipStream_t s);
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
 hipError_t launch_scatter_bwd(const Plan& P, const void* dout, int mode, char* ws, hipStream_t s);
 hipError_t launch_pool_bwd(const Plan& P, char* ws, void* dq, void* dk, void* dv, hipStream_t s);
-// bf16 path: out[z][t][h] = tab[z][h][slot_h(t)], the back-scatter (Z = 1) and
-// the pool adjoint (Z = 3) from bf16 rows the attention kernels leave; token t's
-// row of out[z] starts t * out_ld elements in (out_ld >= H*d, a multiple of 8)
-hipError_t launch_row_copy(const Plan& P, const char* ws, const uint16_t* const* tab, void* const* out, int Z,
-                           int64_t out_ld, hipStream_t s);
 // parent kept: out[z][t][h] = sum over the kept entries covering t of tab[z][h][slot]
 // (divided by p^level when `divide`), fp32 tables, bf16 output rows out_ld apart
 hipError_t launch_sum_copy(const Plan& P, const char* ws, const float* const* tab, void* const* out, int Z,
@@ -139,11 +130,14 @@ struct AttnArgs {
     const float *D, *rowdown;
     float *dq, *dk, *dv;       // fp32 [H][Sp][d] or null
     uint16_t *dq_b, *dk_b, *dv_b;   // bf16 rows (ld_o, hs_o) or null
-    // with fp32 gradients: bf16 copies [H][Sp][d] of dQ, dK, dV divided by
-    // p^level[h][row] (the pool adjoint's rows), or null
-    uint16_t *tq, *tk, *tv;
-    const uint8_t* level;
+    const uint8_t* level;           // [H][rows] (the in-kernel scatters)
     int p;
+    // optional: the kernels scatter their results to bf16 token rows [N][H][d]
+    // (tok_ld elements apart) themselves -- O~ (forward), dQ~/p^level (dQ),
+    // dK~/p^level and dV~/p^level (dK/dV) -- for the entries start [H][rows]
+    uint16_t *o_tok, *dq_tok, *dk_tok, *dv_tok;
+    const int32_t* start;
+    int64_t tok_ld;
     int64_t rows, Sp, ld_o, hs_o;
     int H, d;
     bool split, fp32_path;

@@ -692,47 +692,6 @@ __global__ void __launch_bounds__(256) k_pool_bwd(PoolBwdArgs a) {
     }
 }
 
-// ------------------------------------------------------------- row copy
-// Stage (iv) and the pool adjoint are both "token t of head h takes row
-// slot_h(t) of an [H][Sp][d] table" (Sec. 3: the kept entries partition the
-// tokens, an entry at level l covers p^l of them).  On the bf16 path the
-// attention kernels also leave those rows as bf16 (O~, and dQ~, dK~, dV~
-// divided by p^level), rounded exactly as the per-token code would round
-// them, so both stages become the same copy: out[z][t][h] = tab[z][h][slot].
-// Each workgroup writes one tensor (blockIdx.z) over one tile of tokens:
-// HBM takes one output stream per workgroup faster than three interleaved
-// ones (measured on MI355X).
-struct RowCopyArgs {
-    const int32_t* start;     // [H][S]
-    const u32x4* tab[3];      // [H][Sp][G] words
-    u32x4* out[3];            // token t, head h at word t * ld + h * G
-    int64_t N, S, Sp, ld;
-    int H, HG, mt;
-};
-
-template <int G, bool NT>
-__global__ void __launch_bounds__(256) k_row_copy(RowCopyArgs a) {
-    const TokMap tm = tok_map<G>(a.HG, a.mt, a.N);
-    if (tm.tb >= tm.te) return;
-    const int z = blockIdx.z;
-    const int32_t* st = a.start + (int64_t)tm.h * a.S;
-    int64_t slot = find_slot(st, a.S, tm.tb);
-    int64_t nxt = slot + 1 < a.S ? st[slot + 1] : a.N;
-    const u32x4* tb = a.tab[z] + (int64_t)tm.h * a.Sp * G + tm.c;
-    u32x4* ob = a.out[z] + (int64_t)tm.h * G + tm.c;
-    const int64_t ld = a.ld;
-    u32x4 x = tb[slot * G];
-    for (int64_t t = tm.tb; t < tm.te; ++t) {
-        if (t >= nxt) {
-            ++slot;
-            nxt = slot + 1 < a.S ? st[slot + 1] : a.N;
-            x = tb[slot * G];
-        }
-        if constexpr (NT) __builtin_nontemporal_store(x, ob + t * ld);
-        else ob[t * ld] = x;
-    }
-}
-
 __global__ void k_fill_zero(u32x4* p, int64_t n16) {
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += (int64_t)gridDim.x * blockDim.x)
         p[i] = u32x4{0, 0, 0, 0};
@@ -1104,26 +1063,6 @@ hipError_t launch_entry_sum(const Plan& P, const void* dout, char* ws, hipStream
     dim3 grid((unsigned)((P.S + 3) / 4), (unsigned)P.H);
     if (P.d == 128) hipLaunchKernelGGL((k_entry_sum<16>), grid, dim3(256), 0, s, a);
     else hipLaunchKernelGGL((k_entry_sum<8>), grid, dim3(256), 0, s, a);
-    return hipGetLastError();
-}
-
-hipError_t launch_row_copy(const Plan& P, const char* ws, const uint16_t* const* tab, void* const* out, int Z,
-                           int64_t out_ld, hipStream_t s) {
-    if (Z < 1 || Z > 3 || P.dtype != BF16) return hipErrorInvalidValue;
-    if (out_ld < (int64_t)P.H * P.d || out_ld % 8 != 0) return hipErrorInvalidValue;
-    const int G = P.d / 8;
-    RowCopyArgs a{};
-    a.start = reinterpret_cast<const int32_t*>(ws + P.off_start);
-    for (int z = 0; z < Z; ++z) {
-        a.tab[z] = reinterpret_cast<const u32x4*>(tab[z]);
-        a.out[z] = reinterpret_cast<u32x4*>(out[z]);
-    }
-    a.N = P.N; a.S = P.S; a.Sp = P.Sp; a.H = P.H;
-    a.ld = out_ld / 8;
-    const int threads = scatter_threads(P, &a.HG, &a.mt);
-    dim3 grid((unsigned)((P.N + kTileTok - 1) / kTileTok), (unsigned)(P.H / a.HG), (unsigned)Z);
-    if (G == 16) hipLaunchKernelGGL((k_row_copy<16, true>), grid, dim3(threads), 0, s, a);
-    else hipLaunchKernelGGL((k_row_copy<8, true>), grid, dim3(threads), 0, s, a);
     return hipGetLastError();
 }
 
