@@ -56,10 +56,10 @@ def stage_bytes(w, S, pk=False):
         out["scatter_fwd"] = row + sub32              # write o; read the rows of O~ once
         out["pool_bwd"] = 3 * row + 3 * sub32         # write dq, dk, dv; read their sub-sequence rows once
     elif e == 2:
-        # the attention kernels write the token rows themselves (o; dk, dv; dq)
+        # the attention kernels write the token rows themselves (o; dk, dv and dq, the
+        # two backward kernels running side by side as one stage)
         out["attn_fwd"] = row
-        out["attn_bwd_dkdv"] = 2 * row
-        out["attn_bwd_dq"] = row
+        out["attn_bwd"] = 3 * row
     else:
         out["scatter_fwd"] = row + sub32
         out["pool_bwd"] = 3 * row + 3 * sub32
@@ -70,7 +70,7 @@ def attn_flops(w, S):
     """Algorithmic flops of causal attention on the sub-sequence (per launch)."""
     H, d = w["H"], w["d"]
     unit = S * S * d * H                          # one causal S x S x d product
-    return {"attn_fwd": 2 * unit, "attn_bwd_dkdv": 3 * unit, "attn_bwd_dq": 2 * unit}
+    return {"attn_fwd": 2 * unit, "attn_bwd_dkdv": 3 * unit, "attn_bwd_dq": 2 * unit, "attn_bwd": 5 * unit}
 
 
 def measured_traffic(workload, stage):

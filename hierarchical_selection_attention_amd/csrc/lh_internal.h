@@ -21,7 +21,7 @@ enum Dtype { BF16 = 0, FP32 = 1 };
 enum Stage {
     ST_POOL_SCORE = 0, ST_POOL_UP, ST_TOPK, ST_GATHER, ST_SUB_PREP, ST_ATTN_FWD,
     ST_SCATTER_FWD, ST_ZERO_ACC, ST_SCATTER_BWD, ST_BWD_PREP, ST_ATTN_BWD_DKDV,
-    ST_ATTN_BWD_DQ, ST_POOL_BWD,
+    ST_ATTN_BWD_DQ, ST_POOL_BWD, ST_ATTN_BWD,
     // projections around the layer (lh_block_*)
     ST_PROJ_QKV, ST_PROJ_OUT, ST_PROJ_OUT_DX, ST_PROJ_OUT_DW, ST_PROJ_QKV_DX, ST_PROJ_QKV_DW, ST_COUNT
 };
