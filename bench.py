@@ -143,7 +143,7 @@ BLOCK_METRIC = ("Lighthouse attention block (QKV projections + layer + output pr
 def block_gemm_flops(N, dm, hd):
     """Flops of one launch of each projection GEMM of the block."""
     one = 2 * N * dm * hd
-    return {"proj_qkv": one, "proj_out": one, "proj_out_dx": one, "proj_out_dw": one,
+    return {"proj_qkv": 3 * one, "proj_out": one, "proj_out_dx": one, "proj_out_dw": one,
             "proj_qkv_dx": 3 * one, "proj_qkv_dw": 3 * one}
 
 

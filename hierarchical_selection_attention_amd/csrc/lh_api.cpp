@@ -47,6 +47,7 @@ int make_plan(int N, int H, int d, int p, int L, int K, int dtype, Plan* P, int 
     Plan& pl = *P;
     pl = Plan{};
     pl.pk = select_mode == LH_SELECT_PARENT_KEPT;
+    pl.in_ld = (int64_t)H * d;
     pl.N = N; pl.H = H; pl.d = d; pl.p = p; pl.L = L; pl.K = K; pl.dtype = dtype;
     pl.esz = dtype == BF16 ? 2 : 4;
     pl.S = S;
@@ -291,9 +292,21 @@ int lh_forward_scored(const void* q, const void* k, const void* v, void* o, int 
 
 int lh_forward_sel(const void* q, const void* k, const void* v, void* o, int N, int H, int d, int p, int L, int K,
                    int dtype, int score_mode, int select_mode, void* ws, size_t ws_bytes, void* stream) {
+    return forward_strided(q, k, v, o, N, H, d, p, L, K, dtype, score_mode, select_mode, ws, ws_bytes, stream,
+                           (int64_t)H * d);
+}
+
+}  // extern "C"
+
+namespace lh {
+int forward_strided(const void* q, const void* k, const void* v, void* o, int N, int H, int d, int p, int L, int K,
+                    int dtype, int score_mode, int select_mode, void* ws, size_t ws_bytes, void* stream,
+                    int64_t in_ld) {
     Plan P;
     int rc = make_plan(N, H, d, p, L, K, dtype, &P, select_mode);
     if (rc) return rc;
+    if (in_ld < (int64_t)H * d || in_ld % 8 != 0) return LH_ERR_ARG;
+    P.in_ld = in_ld;
     if (score_mode < LH_SCORE_QK || score_mode > LH_SCORE_QK_PRODUCT) return LH_ERR_DTYPE;
     P.score_mode = score_mode;
     if (!q || !k || !v || !o) return LH_ERR_ARG;
@@ -346,9 +359,6 @@ int lh_forward_sel(const void* q, const void* k, const void* v, void* o, int N, 
     return LH_OK;
 }
 
-}  // extern "C"
-
-namespace lh {
 int backward_strided(const void* dout, void* dq, void* dk, void* dv, int N, int H, int d, int p, int L, int K,
                      int dtype, int scatter_mode, void* ws, size_t ws_bytes, void* stream, int64_t grad_ld,
                      int select_mode) {

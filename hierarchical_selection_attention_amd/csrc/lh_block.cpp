@@ -109,7 +109,7 @@ int gemm_rm(bool ta, bool tb, int64_t M, int64_t N, int64_t K, const void* A, in
     return st == HIPBLAS_STATUS_SUCCESS ? LH_OK : LH_ERR_GEMM;
 }
 
-// Block workspace: [layer workspace][q, k, v: 3 x N*Hd bf16, reused as the
+// Block workspace: [layer workspace][q, k, v as [N][3Hd] bf16, reused as the
 // gradient [N][3Hd] in the backward][dO: N*Hd bf16][GEMM workspace]
 struct BlockPlan {
     size_t lh_bytes, off_qkv, off_do, off_gemm, total;
@@ -163,15 +163,13 @@ int lh_block_forward(const void* x, const void* w_qkv, const void* w_o, void* o,
     if (!ws || reinterpret_cast<uintptr_t>(ws) % 256 != 0 || ws_bytes < b.total) return LH_ERR_WORKSPACE;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     char* w = reinterpret_cast<char*>(ws);
-    const int64_t hd = (int64_t)H * d, nhd = (int64_t)N * hd;
+    const int64_t hd = (int64_t)H * d;
     uint16_t* qkv = reinterpret_cast<uint16_t*>(w + b.off_qkv);
-    const uint16_t* wq = reinterpret_cast<const uint16_t*>(w_qkv);
     void* gws = w + b.off_gemm;
-    // q, k, v = x times the three column blocks of w_qkv, each [N][H][d]
-    for (int j = 0; j < 3; ++j)
-        LH_GEMM(ST_PROJ_QKV, gemm_rm(false, false, N, hd, dm, x, dm, wq + j * hd, 3 * hd, qkv + j * nhd, hd, false,
-                                     gws, s));
-    rc = lh_forward(qkv, qkv + nhd, qkv + 2 * nhd, o, N, H, d, p, L, K, LH_BF16, w, b.lh_bytes, stream);
+    // [q k v] = x w_qkv in one product: token t's q, k and v rows side by side
+    LH_GEMM(ST_PROJ_QKV, gemm_rm(false, false, N, 3 * hd, dm, x, dm, w_qkv, 3 * hd, qkv, 3 * hd, false, gws, s));
+    rc = forward_strided(qkv, qkv + hd, qkv + 2 * hd, o, N, H, d, p, L, K, LH_BF16, LH_SCORE_QK,
+                         LH_SELECT_PARTITION, w, b.lh_bytes, stream, 3 * hd);
     if (rc) return rc;
     LH_GEMM(ST_PROJ_OUT, gemm_rm(false, false, N, dm, hd, o, hd, w_o, dm, y, dm, false, gws, s));
     return LH_OK;

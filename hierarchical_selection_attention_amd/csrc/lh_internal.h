@@ -41,6 +41,10 @@ hipError_t stage(int id, hipStream_t s, F&& fn) {
     return e;
 }
 
+// lh_forward_sel with q, k, v rows in_ld elements apart (in_ld >= H*d, a multiple of 8)
+int forward_strided(const void* q, const void* k, const void* v, void* o, int N, int H, int d, int p, int L, int K,
+                    int dtype, int score_mode, int select_mode, void* ws, size_t ws_bytes, void* stream,
+                    int64_t in_ld);
 // lh_backward with dq, dk, dv rows grad_ld elements apart (grad_ld = H*d for
 // [N][H][d] tensors; larger strides need the bf16 path, grad_ld % 8 == 0)
 int backward_strided(const void* dout, void* dq, void* dk, void* dv, int N, int H, int d, int p, int L, int K,
@@ -50,6 +54,7 @@ int backward_strided(const void* dout, void* dq, void* dk, void* dv, int N, int 
 struct Plan {
     int N, H, d, p, L, K, dtype, esz;
     int score_mode;         // leaf score: 0 |q|^2+|k|^2, 1 |k|^2, 2 |q|^2, 3 |q|^2*|k|^2
+    int64_t in_ld;          // token stride of q, k, v in elements (H*d unless a caller strides them)
     int64_t S, Sp;
     int m;                  // pyramid level produced per workgroup by the pooling pass
     int rowcopy;            // bf16 partition: the attention kernels scatter their results to the tokens

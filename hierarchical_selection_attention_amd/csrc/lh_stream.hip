@@ -28,6 +28,7 @@ struct PoolScoreArgs {
     int64_t n[kMaxLevels];
     int N, H, HG, p, m, tok, mt;
     int score_mode;
+    int64_t ld;               // q, k, v: token t, head h at element t * ld + h * d
     int64_t pw[kMaxLevels];
 };
 
@@ -92,10 +93,10 @@ __global__ void __launch_bounds__(256) k_pool_score(PoolScoreArgs a) {
         // the butterflies of the U tokens are interleaved so the cross-lane moves
         // overlap.  Loads go through buffer resources over this workgroup's chunk:
         // one lane offset, and a uniform offset per token.
-        const int64_t base0 = (t0 * H + (int64_t)blockIdx.y * HG) * d;
-        const uint32_t chunk_bytes = (uint32_t)((((int64_t)a.tok - 1) * H + HG) * d * 2);
-        const uint32_t tstride = (uint32_t)(a.mt * H * d * 2);
-        const uint32_t lane_off = (uint32_t)(((ts * H + hl) * d + c * 8) * 2);
+        const int64_t base0 = t0 * a.ld + (int64_t)blockIdx.y * HG * d;
+        const uint32_t chunk_bytes = (uint32_t)((((int64_t)a.tok - 1) * a.ld + HG * d) * 2);
+        const uint32_t tstride = (uint32_t)(a.mt * a.ld * 2);
+        const uint32_t lane_off = (uint32_t)((ts * a.ld + hl * d + c * 8) * 2);
         const auto Q = make_rsrc(reinterpret_cast<const uint16_t*>(a.q) + base0, chunk_bytes);
         const auto Kp = make_rsrc(reinterpret_cast<const uint16_t*>(a.k) + base0, chunk_bytes);
         const auto V = make_rsrc(reinterpret_cast<const uint16_t*>(a.v) + base0, chunk_bytes);
@@ -186,7 +187,7 @@ __global__ void __launch_bounds__(256) k_pool_score(PoolScoreArgs a) {
     } else {
         for (int i = 0; i < iters; ++i) {
             const int64_t t = t0 + ts + (int64_t)a.mt * i;
-            const int64_t el = (t * H + h) * d + c * 8;
+            const int64_t el = t * a.ld + (int64_t)h * d + c * 8;
             float xq[8], xk[8], xv[8];
             load8_nt<DT>(a.q, el, xq);
             load8_nt<DT>(a.k, el, xk);
@@ -327,6 +328,7 @@ struct GatherArgs {
     float *qs, *ks, *vs;   // fp32 [H][Sp][d]
     float* rowmax;         // fp32 [3][H][Sp]: max |x| of each written row (q, k, v)
     int64_t S, Sp, n_m, ntop;
+    int64_t ld;            // q, k, v: token t, head h at element t * ld + h * d
     int64_t pw[kMaxLevels];
     int H, m, L;
 };
@@ -391,7 +393,7 @@ __global__ void __launch_bounds__(64) k_gather(GatherArgs a) {
             for (int u = 0; u < U; ++u) {
                 const int64_t r = r0 + (int64_t)u * NR;
                 if (r < R) {
-                    const int64_t el = ((st + r) * H + h) * d + c * 8;
+                    const int64_t el = (st + r) * a.ld + (int64_t)h * d + c * 8;
 #pragma unroll
                     for (int t = 0; t < 3; ++t) load8<DT>(src[t], el, x[u][t]);
                 }
@@ -870,6 +872,7 @@ hipError_t launch_pool_score(const Plan& P, const void* q, const void* k, const 
     a.pool_m = reinterpret_cast<float*>(ws + P.off_pool_m);
     a.N = P.N; a.H = P.H; a.p = P.p; a.m = P.m; a.tok = (int)P.tok;
     a.score_mode = P.score_mode;
+    a.ld = P.in_ld;
     const int G = P.d / 8;
     a.HG = head_group(P.H, G);
     // token lanes must divide tok (a power of p): use powers of p
@@ -920,6 +923,7 @@ hipError_t launch_gather(const Plan& P, const void* q, const void* k, const void
     a.vs = reinterpret_cast<float*>(ws + P.off_vs);
     a.rowmax = reinterpret_cast<float*>(ws + P.off_rowmax);
     a.S = P.S; a.Sp = P.Sp; a.n_m = P.n[P.m]; a.ntop = P.ntop;
+    a.ld = P.in_ld;
     for (int l = 0; l < P.L; ++l) a.pw[l] = P.pw[l];
     a.H = P.H; a.m = P.m; a.L = P.L;
     dim3 grid((unsigned)P.Sp, (unsigned)P.H);

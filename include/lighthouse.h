@@ -234,9 +234,9 @@ int lh_dense_attn_bwd(const void* q, const void* k, const void* v, const void* o
  * until the process ends).  Workspace: lh_block_workspace_bytes (256-byte
  * aligned); it begins with the layer's workspace, so lh_read_selection and
  * lh_workspace_view (dtype LH_BF16) read it directly.  At the next 256-byte
- * boundary after it the forward leaves q, k, v ([3][N][H][d] bf16), which the
- * backward overwrites with the gradients ([N][3][H][d]: dq, dk, dv of a token
- * side by side); at the next 256-byte boundary after those the backward
+ * boundary after it the forward leaves q, k, v ([N][3][H][d] bf16: the q, k
+ * and v rows of a token side by side), which the backward overwrites with the
+ * gradients in the same layout; at the next 256-byte boundary after those the backward
  * leaves dO = dy W_O^T ([N][H][d] bf16).  The workspace must stay untouched
  * between the forward and the backward.  dm must be a multiple of
  * 8; the other shape limits are the layer's.  Returns LH_OK, a negative

@@ -35,7 +35,7 @@ def _block_qkv(ws, N, H, d, p, L, K):
     lh = lib()
     off = (lh.lh_workspace_bytes(N, H, d, p, L, K, 0) + 255) // 256 * 256
     n = 3 * N * H * d
-    return ws[off: off + 2 * n].view(torch.bfloat16).view(3, N, H, d)
+    return ws[off: off + 2 * n].view(torch.bfloat16).view(N, 3, H, d).transpose(0, 1)
 
 
 def _block_dout(ws, N, H, d, p, L, K):
