@@ -300,9 +300,10 @@ __device__ __forceinline__ void rows_to_tokens(const uint16_t* rows, uint16_t* t
 
 // Work item -> (head, 64-row tile).  When H is a multiple of 8, the workgroups
 // of a head are all dispatched to the same XCD (workgroup i runs on XCD i % 8),
-// so the head's streamed operands stay in that XCD's L2.  `heavy_last_tile`
-// orders the longest causal rows first.
-__device__ __forceinline__ void work_item(int nT, int H, bool heavy_last_tile, int& h, int& tile) {
+// so the head's streamed operands stay in that XCD's L2.  `last_tile_first`
+// dispatches the head's tiles from the last one down (for query tiles, the
+// longest causal rows first; for key tiles, the shortest).
+__device__ __forceinline__ void work_item(int nT, int H, bool last_tile_first, int& h, int& tile) {
     const int i = blockIdx.x;
     int j;
     if (H % 8 == 0) {
@@ -313,7 +314,7 @@ __device__ __forceinline__ void work_item(int nT, int H, bool heavy_last_tile, i
         h = i / nT;
         j = i % nT;
     }
-    tile = heavy_last_tile ? nT - 1 - j : j;
+    tile = last_tile_first ? nT - 1 - j : j;
 }
 
 // ------------------------------------------------------------------ forward
@@ -534,7 +535,11 @@ __global__ void __launch_bounds__(256) k_attn_dkdv(AttnK a) {
     const int64_t Sp = a.Sp;
     const int nT = (int)(Sp / 64);
     int h, kt;
-    work_item(nT, gridDim.x / nT, false, h, kt);
+    // The last key tiles see the fewest queries.  When the kernel writes token rows,
+    // they go first: their writes start soon, while the dQ kernel beside this one
+    // works through its longest tiles, so HBM is not left idle at the start.
+    // Without token writes the kernel is compute-bound and the longest go first.
+    work_item(nT, gridDim.x / nT, a.dk_tok != nullptr, h, kt);
     const int64_t k0 = (int64_t)kt * 64 + wave * 16;
     const int64_t mykey = k0 + lq;
     const int64_t hb = (int64_t)h * Sp * D;
