@@ -28,6 +28,11 @@ CASES = [
     ("bf16_p2_deep", 4096, 2, 128, "bf16", 2, 8, 3, "lognormal", 0.0, True),
     ("bf16_ties_heavy_tail", 4096, 2, 128, "bf16", 4, 4, 16, "student_t3", 0.3, True),
     ("fp32_d128", 1024, 2, 128, "fp32", 4, 3, 6, "lognormal", 0.0, True),
+    # N = p^(L-1): one top entry, one head
+    ("bf16_single_top_h1", 256, 1, 128, "bf16", 4, 5, 2, "lognormal", 0.0, True),
+    # a wide pooling factor: p^2 = 64 tokens per top entry
+    ("bf16_p8", 4096, 2, 64, "bf16", 8, 3, 3, "lognormal", 0.0, True),
+    ("fp32_p8_h1", 512, 1, 64, "fp32", 8, 3, 4, "lognormal", 0.0, True),
 ]
 
 
