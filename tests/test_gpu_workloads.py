@@ -1,5 +1,5 @@
 """GPU parity on the five benchmark workloads at their full sizes, in the launch
-configuration the benchmark times.  Scores and index sets are compared bit for
+configuration the benchmark times, and on one shape whose tensors pass 2^32 bytes.  Scores and index sets are compared bit for
 bit over all tokens and heads; the gathered sub-sequence, its attention
 output and its gradients over every row; the [N, H, d] outputs over all tokens
 for the smaller workloads and on sampled token rows (plus properties that hold
@@ -17,14 +17,25 @@ pytestmark = pytest.mark.gpu
 
 _CACHE = {}
 
+# Beyond the benchmark workloads: token rows past 2^31 elements and 2^32 bytes per
+# tensor (the layer admits any N < 2^31 that fits in HBM), 4.8 GB per bf16 tensor.
+# H = 9 is not a multiple of 8, so the attention kernels take the plain head mapping.
+OVER_4GIB = dict(name="over4gib_n2097152_h9", N=2097152, H=9, d=128, dtype="bf16", p=4, L=6, K=128,
+                 scale="lognormal", planted=0.0, dup=0.0, seed=1010)
+
 
 def _workload(idx):
     """Inputs, oracle forward/backward and one GPU run per workload (computed once)."""
     if idx in _CACHE:
         return _CACHE[idx]
-    w = si.WORKLOADS[idx]
+    _CACHE.clear()
+    w = OVER_4GIB if idx == "over4gib" else si.WORKLOADS[idx]
     say(f"workload {idx} {w['name']}: generating inputs")
-    x = si.workload_inputs(idx, with_dout=True, threads=16)
+    if idx == "over4gib":
+        x = si.make_inputs(w["N"], w["H"], w["d"], w["dtype"], w["seed"], w["scale"], w["planted"], w["dup"],
+                           True, 16)
+    else:
+        x = si.workload_inputs(idx, with_dout=True, threads=16)
     N, H, d, p, L, K, dt = w["N"], w["H"], w["d"], w["p"], w["L"], w["K"], w["dtype"]
     say("  oracle forward")
     ref = oracle.forward(x["q"], x["k"], x["v"], p, L, K, dt, want=("levels", "sel", "sub", "ot"))
@@ -32,7 +43,6 @@ def _workload(idx):
     b = oracle.backward(x["q"], x["k"], x["v"], x["dout"], p, L, K, (ref["start"], ref["level"]), dt,
                         want=("sub", "cond"))
     run = Run(x, dt, p, L, K, backward=True, mode=0, label=w["name"])
-    _CACHE.clear()
     _CACHE[idx] = (w, x, ref, b, run)
     return _CACHE[idx]
 
@@ -50,7 +60,7 @@ def _check_all(idx, sample):
     for name, key, ck in (("dqsub", "dQt", "cdQ"), ("dksub", "dKt", "cdK"), ("dvsub", "dVt", "cdV")):
         compare(run.sub(name), b[key], dt, name, cond=b[ck], d=d)
     sel = (ref["start"], ref["level"])
-    rng = np.random.default_rng(idx)
+    rng = np.random.default_rng(w.get("seed", idx))
     check_full_rows(run.o, ref["Ot"], sel, p, dt, "o", cond_sub=b["cO"], sample=sample, rng=rng)
     for g, key, sub, ck in zip(run.grads, ("dq", "dk", "dv"), ("dQt", "dKt", "dVt"), ("cdQ", "cdK", "cdV")):
         check_full_rows(g, b[sub], sel, p, dt, key, divide=True, cond_sub=b[ck], sample=sample, rng=rng)
@@ -149,3 +159,10 @@ def test_workload5_heavy_tail_ties_n1048576():
     idx = torch.from_numpy(rng.integers(0, w["N"], size=200_000)).cuda()
     for g, g0, name in zip(fp, ref_grads, ("dq", "dk", "dv")):
         compare(to_f64(g[idx]), to_f64(g0[idx]), "bf16", f"{name} fp vs int (sampled)")
+
+
+@pytest.mark.timeout(900)
+def test_tensors_over_4gib_n2097152_h9():
+    run = _check_all("over4gib", sample=200_000)
+    _check_scatter_properties(run, 4)
+    _CACHE.clear()
