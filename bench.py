@@ -36,7 +36,8 @@ def log(*a):
 
 
 def stage_bytes(w, S, pk=False):
-    """Algorithmic HBM bytes of one launch of each streaming stage (see design notes).  With the
+    """Algorithmic HBM bytes of one launch of each streaming stage (each kernel's compulsory reads
+    and writes: inputs read once, outputs written once).  With the
     parent-kept selection the scatter and the pool adjoint read fp32 rows of the sub-sequence."""
     N, H, d, p, L = w["N"], w["H"], w["d"], w["p"], w["L"]
     e = 2 if w["dtype"] == "bf16" else 4
@@ -297,7 +298,7 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: the layer runs on a single MI355X here; --gpus {args.gpus} "
-              "is not supported (heads or sequence blocks would be sharded across GPUs; see the design notes).",
+              "is not supported (heads or sequence blocks would be sharded across GPUs).",
               file=sys.stderr)
         sys.exit(2)
 

@@ -15,8 +15,7 @@
  * Everything is fp64 except the selection scores, which are fp32 in a fixed
  * reduction order so that the selected index set is reproducible bit for bit.
  *
- * Readings taken where the pages leave a step open (each one is listed with
- * its reason in the design notes that ship with the repository):
+ * Readings taken where the pages leave a step open:
  *   R1 score of an entry = ||q||^2 + ||k||^2 of its leaves (no sqrt: monotone),
  *      coarser levels take the max over their p children (Fig. 2 "l2 norm +
  *      max-pool").  The other readings of what the norm is taken of (Sec. 1
