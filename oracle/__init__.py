@@ -16,6 +16,9 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "lh_oracle.c")
 _LIB = os.path.join(_HERE, "liblh_oracle.so")
+# A separately built copy of the same source (the sanitizer build in the tests)
+# can be loaded instead by naming it here; it is never built from anything else.
+_LIB_OVERRIDE = os.environ.get("LH_ORACLE_LIB")
 _lib = None
 
 DTYPES = {"bf16": 0, "fp32": 1}
@@ -35,9 +38,13 @@ def build(force: bool = True) -> str:
 def lib():
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
-            build(force=True)
-        L = C.CDLL(_LIB)
+        if _LIB_OVERRIDE:
+            path = _LIB_OVERRIDE
+        else:
+            if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+                build(force=True)
+            path = _LIB
+        L = C.CDLL(path)
         vp, i32, i64, dp, fp = C.c_void_p, C.c_int, C.c_int64, C.POINTER(C.c_double), C.c_void_p
         L.lho_subseq_len.restype = i64
         L.lho_subseq_len.argtypes = [i32, i32, i32, i32]
