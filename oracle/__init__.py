@@ -186,8 +186,10 @@ def backward(q, k, v, dout, p, L, K, selection, dtype="bf16", want=("sub",), nth
     """Oracle backward with a given selection.
 
     want: "sub" (dOt, dQt, dKt, dVt), "full" (dq, dk, dv), "cond" (absolute term sums
-    cO, cdQ, cdK, cdV [H, S, d]: the scale of the rounding error of each output, used
-    only to set comparison tolerances).
+    cO, cdQ, cdK, cdV [H, S, d]: the scale of the rounding error of each output; and
+    lO, ldQ, ldK, ldV [H, S, d]: how far each output moves, to first order, when each
+    logit q.k/sqrt(d) moves by at most sum |q||k|/sqrt(d); both used only to set
+    comparison tolerances).
     """
     q, k, v, dout = _in(q, dtype), _in(k, dtype), _in(v, dtype), _in(dout, dtype)
     N, H, d = q.shape
@@ -198,7 +200,7 @@ def backward(q, k, v, dout, p, L, K, selection, dtype="bf16", want=("sub",), nth
     full = "full" in want
     dOt, dQt, dKt, dVt = ((np.zeros((H, S, d)) if sub else None) for _ in range(4))
     dq, dk, dv = ((np.zeros((N, H, d)) if full else None) for _ in range(3))
-    cond = np.zeros((4, H, S, d)) if "cond" in want else None
+    cond = np.zeros((8, H, S, d)) if "cond" in want else None
     rc = lib().lho_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), N, H, d, DTYPES[dtype], p, L, K,
                             int(select_mode), _ptr(st), _ptr(lv), _ptr(dOt), _ptr(dQt), _ptr(dKt), _ptr(dVt),
                             _ptr(dq), _ptr(dk), _ptr(dv), _ptr(cond), nthreads)
@@ -210,7 +212,8 @@ def backward(q, k, v, dout, p, L, K, selection, dtype="bf16", want=("sub",), nth
     if full:
         res.update(dq=dq, dk=dk, dv=dv)
     if cond is not None:
-        res.update(cO=cond[0], cdQ=cond[1], cdK=cond[2], cdV=cond[3])
+        res.update(cO=cond[0], cdQ=cond[1], cdK=cond[2], cdV=cond[3],
+                   lO=cond[4], ldQ=cond[5], ldK=cond[6], ldV=cond[7])
     return res
 
 

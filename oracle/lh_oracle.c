@@ -375,13 +375,24 @@ static void head_attention_fwd(int64_t S, int d, const double* Q, const double* 
  * dS = P o (dP - rowsum(dO o O)), dQ = dS K / sqrt(d), dK = dS^T Q / sqrt(d).
  *
  * cond (may be NULL) receives, for the tolerance of finite-precision
- * comparisons only, the sums of absolute values of the terms each output is
- * made of (4 arrays of S*d: O, dQ, dK, dV).  With A_ij = sum |dO_i||V_j|,
- * B_i = sum |dO_i||O_i| and w_ij = P_ij (A_ij + B_i):
+ * comparisons only, 8 arrays of S*d.  The first four are the sums of absolute
+ * values of the terms each output is made of (O, dQ, dK, dV).  With
+ * A_ij = sum |dO_i||V_j|, B_i = sum |dO_i||O_i| and w_ij = P_ij (A_ij + B_i):
  *   cO_i = sum_j P_ij |V_j|,  cdQ_i = sum_j w_ij |K_j| / sqrt(d),
  *   cdK_j = sum_i w_ij |Q_i| / sqrt(d),  cdV_j = sum_i P_ij |dO_i|.
  * A computation in precision u with length-n dot products has error of order
- * n u times these sums (the standard forward error bound of a dot product). */
+ * n u times these sums (the standard forward error bound of a dot product).
+ * The last four bound, to first order, how far each output moves when every
+ * logit s_ij is perturbed by at most Lam_ij = sum_e |Q_ie K_je| / sqrt(d) (the
+ * size of the rounding error of a dot product computed in precision 1, scaled
+ * by u for precision u).  With M_i = sum_k P_ik Lam_ik, a_ij = |dP_ij - D_i|
+ * and R_i = sum_k P_ik Lam_ik a_ik, a perturbation of the logits moves P_ij by
+ * at most P_ij (Lam_ij + M_i), O_i by at most sum_j P_ij Lam_ij |V_j - O_i|
+ * (dO_i/ds_ij = P_ij (V_j - O_i)), D_i = dO_i . O_i by at most R_i, and dS_ij
+ * by at most W_ij = P_ij ((Lam_ij + M_i) a_ij + R_i), so:
+ *   lO_i = sum_j P_ij Lam_ij |V_j - O_i|,  ldQ_i = sum_j W_ij |K_j| / sqrt(d),
+ *   ldK_j = sum_i W_ij |Q_i| / sqrt(d),  ldV_j = sum_i P_ij (Lam_ij + M_i) |dO_i|.
+ * Where logits are large (heavy-tailed rows) these dominate the first four. */
 static void head_attention_bwd(int64_t S, int d, const double* Q, const double* K, const double* V,
                                const double* O, const double* dO, double* dQ, double* dK, double* dV,
                                double* logit, double* cond) {
@@ -389,7 +400,15 @@ static void head_attention_bwd(int64_t S, int d, const double* Q, const double* 
     memset(dQ, 0, sizeof(double) * (size_t)(S * d));
     memset(dK, 0, sizeof(double) * (size_t)(S * d));
     memset(dV, 0, sizeof(double) * (size_t)(S * d));
-    if (cond) memset(cond, 0, sizeof(double) * (size_t)(4 * S * d));
+    if (cond) memset(cond, 0, sizeof(double) * (size_t)(8 * S * d));
+    double* lam = cond ? (double*)malloc(sizeof(double) * (size_t)S) : NULL;
+    double* adp = cond ? (double*)malloc(sizeof(double) * (size_t)S) : NULL;
+    if (cond && (!lam || !adp)) {   /* no bound without scratch: report it as unbounded */
+        for (int64_t z = 0; z < 8 * S * d; ++z) cond[z] = INFINITY;
+        free(lam); free(adp);
+        lam = adp = NULL;
+        cond = NULL;
+    }
     for (int64_t i = 0; i < S; ++i) {
         double m = -INFINITY;
         for (int64_t j = 0; j <= i; ++j) {
@@ -404,6 +423,20 @@ static void head_attention_bwd(int64_t S, int d, const double* Q, const double* 
         for (int e = 0; e < d; ++e) {
             D += dO[i * d + e] * O[i * d + e];
             B += fabs(dO[i * d + e] * O[i * d + e]);
+        }
+        double M = 0.0, R = 0.0;
+        if (cond) {
+            for (int64_t j = 0; j <= i; ++j) {
+                double P = exp(logit[j] - m) / sum, la = 0.0, dP = 0.0;
+                for (int e = 0; e < d; ++e) {
+                    la += fabs(Q[i * d + e] * K[j * d + e]);
+                    dP += dO[i * d + e] * V[j * d + e];
+                }
+                lam[j] = la * scale;
+                adp[j] = fabs(dP - D);
+                M += P * lam[j];
+                R += P * lam[j] * adp[j];
+            }
         }
         for (int64_t j = 0; j <= i; ++j) {
             double P = exp(logit[j] - m) / sum;
@@ -420,16 +453,25 @@ static void head_attention_bwd(int64_t S, int d, const double* Q, const double* 
             }
             if (cond) {
                 double w = P * (A + B);
+                double wl = P * ((lam[j] + M) * adp[j] + R);
                 double *cO = cond, *cQ = cond + S * d, *cK = cond + 2 * S * d, *cV = cond + 3 * S * d;
+                double *lO = cond + 4 * S * d, *lQ = cond + 5 * S * d, *lK = cond + 6 * S * d,
+                       *lV = cond + 7 * S * d;
                 for (int e = 0; e < d; ++e) {
                     cO[i * d + e] += P * fabs(V[j * d + e]);
                     cQ[i * d + e] += w * fabs(K[j * d + e]) * scale;
                     cK[j * d + e] += w * fabs(Q[i * d + e]) * scale;
                     cV[j * d + e] += P * fabs(dO[i * d + e]);
+                    lO[i * d + e] += P * lam[j] * fabs(V[j * d + e] - O[i * d + e]);
+                    lQ[i * d + e] += wl * fabs(K[j * d + e]) * scale;
+                    lK[j * d + e] += wl * fabs(Q[i * d + e]) * scale;
+                    lV[j * d + e] += P * (lam[j] + M) * fabs(dO[i * d + e]);
                 }
             }
         }
     }
+    free(lam);
+    free(adp);
 }
 
 /* ------------------------------------------------------------- per-head work */
@@ -585,7 +627,8 @@ int lho_forward(const void* q, const void* k, const void* v, int N, int H, int d
  * pool).  The selection (sel_start, sel_level from lho_forward) is an input:
  * indices carry no gradient.  Output pointers may be NULL.
  *   dOt, dQt, dKt, dVt [H][S][d];  dq, dk, dv [N][H][d]
- *   cond [4][H][S][d]: absolute term sums of O~, dQ~, dK~, dV~ (see
+ *   cond [8][H][S][d]: absolute term sums of O~, dQ~, dK~, dV~, then their
+ *   first-order sensitivities to the rounding of the logits (see
  *   head_attention_bwd); a tolerance aid, not part of the layer.
  */
 int lho_backward(const void* q, const void* k, const void* v, const void* dout, int N, int H, int d,
@@ -634,10 +677,10 @@ int lho_backward(const void* q, const void* k, const void* v, const void* dout, 
                 for (int e = 0; e < d; ++e) dOh[i * d + e] += (double)load_f32(dout, dtype, base + e);
             }
         }
-        double* ch = cond ? (double*)malloc(sizeof(double) * sd * 4) : NULL;
+        double* ch = cond ? (double*)malloc(sizeof(double) * sd * 8) : NULL;
         head_attention_bwd(S, d, Qh, Kh, Vh, Oh, dOh, dQh, dKh, dVh, logit, ch);
         if (ch) {
-            for (int z = 0; z < 4; ++z)
+            for (int z = 0; z < 8; ++z)
                 memcpy(cond + ((int64_t)z * H + h) * S * d, ch + (int64_t)z * S * d, sizeof(double) * sd);
             free(ch);
         }
