@@ -385,11 +385,15 @@ static void head_attention_fwd(int64_t S, int d, const double* Q, const double* 
  * The last four bound, to first order, how far each output moves when every
  * logit s_ij is perturbed by at most Lam_ij = sum_e |Q_ie K_je| / sqrt(d) (the
  * size of the rounding error of a dot product computed in precision 1, scaled
- * by u for precision u).  With M_i = sum_k P_ik Lam_ik, a_ij = |dP_ij - D_i|
- * and R_i = sum_k P_ik Lam_ik a_ik, a perturbation of the logits moves P_ij by
- * at most P_ij (Lam_ij + M_i), O_i by at most sum_j P_ij Lam_ij |V_j - O_i|
- * (dO_i/ds_ij = P_ij (V_j - O_i)), D_i = dO_i . O_i by at most R_i, and dS_ij
- * by at most W_ij = P_ij ((Lam_ij + M_i) a_ij + R_i), so:
+ * by u for precision u) and, separately, the log-sum-exp of each row by at
+ * most |lse_i| (its own rounding where it is stored apart from the logits and
+ * read back by the gradient).  With M_i = sum_k P_ik Lam_ik + |lse_i|,
+ * a_ij = |dP_ij - D_i| and R_i = sum_k P_ik Lam_ik a_ik, such a perturbation
+ * moves the gradient's weights P_ij = exp(s_ij - lse_i) by at most
+ * P_ij (Lam_ij + M_i), O_i (normalised by its own sum) by at most
+ * sum_j P_ij Lam_ij |V_j - O_i| (dO_i/ds_ij = P_ij (V_j - O_i)),
+ * D_i = dO_i . O_i by at most R_i, and dS_ij by at most
+ * W_ij = P_ij ((Lam_ij + M_i) a_ij + R_i), so:
  *   lO_i = sum_j P_ij Lam_ij |V_j - O_i|,  ldQ_i = sum_j W_ij |K_j| / sqrt(d),
  *   ldK_j = sum_i W_ij |Q_i| / sqrt(d),  ldV_j = sum_i P_ij (Lam_ij + M_i) |dO_i|.
  * Where logits are large (heavy-tailed rows) these dominate the first four. */
@@ -424,7 +428,7 @@ static void head_attention_bwd(int64_t S, int d, const double* Q, const double* 
             D += dO[i * d + e] * O[i * d + e];
             B += fabs(dO[i * d + e] * O[i * d + e]);
         }
-        double M = 0.0, R = 0.0;
+        double M = fabs(m + log(sum)), R = 0.0;   /* |lse_i| + sum_k P_ik Lam_ik */
         if (cond) {
             for (int64_t j = 0; j <= i; ++j) {
                 double P = exp(logit[j] - m) / sum, la = 0.0, dP = 0.0;

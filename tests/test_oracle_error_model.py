@@ -67,11 +67,30 @@ def test_logit_sensitivity_bounds_the_change_of_every_output(seed, scale, which)
 
 
 def test_logit_terms_dominate_where_logits_are_large():
-    """Heavy-tailed rows make the logits, and so C_L, large against C; with
-    tiny inputs (logits near 0) C_L is far below C."""
+    """Heavy-tailed rows make the logits, and so C_L, large against C.  With
+    tiny inputs (logits near 0) only the rounding of each row's log-sum-exp
+    (|lse| ~ log N) is left in C_L, a few times C at most."""
     big = _inputs(3, scale="student_t3")
     _, b = _run(big["q"], big["k"], big["v"], big["dout"])
-    assert (b["ldQ"] / np.maximum(b["cdQ"], 1e-300)).max() > 10.0
+    heavy = (b["ldQ"] / np.maximum(b["cdQ"], 1e-300)).max()
     small = {k: (v * np.float32(2.0 ** -6)).astype(np.float32) if k in ("q", "k") else v for k, v in big.items()}
     _, b = _run(small["q"], small["k"], small["v"], small["dout"])
-    assert (b["ldQ"] / np.maximum(b["cdQ"], 1e-300)).max() < 1.0
+    tiny = (b["ldQ"] / np.maximum(b["cdQ"], 1e-300)).max()
+    assert heavy > 10.0 and tiny < 2 * np.log(big["q"].shape[0]) and heavy > 5 * tiny
+
+
+def test_lse_term_closed_form_at_zero_logits():
+    """q = k = 0: every logit is 0, so P_ij = 1 / (i + 1), lse_i = log(i + 1) and
+    Lam = 0.  Only the row's log-sum-exp term is left: ldV_j = sum_{i >= j}
+    log(i + 1) / (i + 1) |dO_i| elementwise, and ldQ = ldK = lO = 0."""
+    N, d = 40, 16
+    x = _inputs(9, N=N, d=d, scale="lognormal")
+    z = np.zeros_like(x["q"])
+    r, b = _run(z, z, x["v"], x["dout"])
+    i = np.arange(N, dtype=np.float64)
+    w = np.log(i + 1) / (i + 1)                               # P_ij |lse_i| for every j <= i
+    dO = np.abs(x["dout"][:, 0, :].astype(np.float64))
+    want = np.cumsum((w[:, None] * dO)[::-1], axis=0)[::-1]   # sum over i >= j
+    np.testing.assert_allclose(b["ldV"][0], want, rtol=1e-12, atol=0)
+    for key in ("ldQ", "ldK", "lO"):
+        assert np.all(b[key] == 0.0), key
