@@ -98,7 +98,7 @@ int make_plan(int N, int H, int d, int p, int L, int K, int dtype, Plan* P, int 
     pl.off_vh = take(h16); pl.off_vl = take(h16);
     pl.off_vTh = take(h16); pl.off_vTl = take(h16);
     pl.off_kTh = take(h16); pl.off_kTl = take(h16);
-    pl.off_qTbh = take(h16); pl.off_qTbl = take(h16);
+    pl.off_qTh = take(h16); pl.off_qTl = take(h16);
     pl.off_hmax = take(sizeof(uint32_t) * 8 * (size_t)H);
     pl.off_rowmax = take(sizeof(float) * 4 * (size_t)H * pl.Sp);
     pl.off_hscale = take(sizeof(float) * 4 * (size_t)H);
@@ -110,7 +110,6 @@ int make_plan(int N, int H, int d, int p, int L, int K, int dtype, Plan* P, int 
     pl.off_doh = take(h16); pl.off_dol = take(h16);
     pl.off_doTh = take(h16); pl.off_doTl = take(h16);
     pl.off_D = take(sizeof(float) * (size_t)H * pl.Sp);
-    pl.off_rowdown = take(sizeof(float) * (size_t)H * pl.Sp);
     pl.off_dq = take(sizeof(float) * HSd);
     pl.off_dk = take(sizeof(float) * HSd);
     pl.off_dv = take(sizeof(float) * HSd);
@@ -250,13 +249,12 @@ static AttnArgs sub_attn_args(const Plan& P, char* w) {
     a.vTh = u16(w, P.off_vTh); a.vTl = u16(w, P.off_vTl);
     a.kTh = u16(w, P.off_kTh); a.kTl = u16(w, P.off_kTl);
     a.doTh = u16(w, P.off_doTh); a.doTl = u16(w, P.off_doTl);
-    a.qTbh = u16(w, P.off_qTbh); a.qTbl = u16(w, P.off_qTbl);
+    a.qTh = u16(w, P.off_qTh); a.qTl = u16(w, P.off_qTl);
     a.hscale = f32(w, P.off_hscale);
     a.o = f32(w, P.off_os);
     a.lse = f32(w, P.off_lse);
     a.lse2 = f32(w, P.off_lse2);
     a.D = f32(w, P.off_D);
-    a.rowdown = f32(w, P.off_rowdown);
     a.dq = f32(w, P.off_dq); a.dk = f32(w, P.off_dk); a.dv = f32(w, P.off_dv);
     a.rows = P.S; a.Sp = P.Sp;
     a.H = P.H; a.d = P.d;
@@ -269,13 +267,12 @@ static AttnArgs sub_attn_args(const Plan& P, char* w) {
 
 // fp16 hi/lo copy of one [H][Sp][d] fp32 tensor (rows and optionally a transposed copy)
 static SplitSpec split_spec(const Plan& P, char* w, size_t src, unsigned int* hmax, int slot, size_t rh, size_t rl,
-                            size_t th, size_t tl, int t_bf16) {
+                            size_t th, size_t tl) {
     SplitSpec sp{};
     sp.src = w + src; sp.ld = P.d; sp.hs = P.Sp * P.d; sp.rows = P.Sp; sp.Sp = P.Sp;
     sp.d = P.d; sp.H = P.H; sp.src_bf16 = 0;
     sp.hmax = hmax; sp.hscale = f32(w, P.off_hscale); sp.slot = slot;
     sp.rh = u16m(w, rh); sp.rl = u16m(w, rl); sp.th = u16m(w, th); sp.tl = u16m(w, tl);
-    sp.t_bf16 = t_bf16;
     return sp;
 }
 
@@ -331,9 +328,9 @@ int forward_strided(const void* q, const void* k, const void* v, void* o, int N,
         unsigned int* out[3] = {hmax, hmax + 1, hmax + 2};
         hipError_t e = launch_head_max(f32(w, P.off_rowmax), out, 3, P.S, P.Sp, H, s);
         const SplitSpec sp[3] = {
-            split_spec(P, w, P.off_qs, hmax, 0, P.off_qh, P.off_ql, P.off_qTbh, P.off_qTbl, 1),
-            split_spec(P, w, P.off_ks, hmax, 1, P.off_kh, P.off_kl, P.off_kTh, P.off_kTl, 0),
-            split_spec(P, w, P.off_vs, hmax, 2, P.off_vh, P.off_vl, P.off_vTh, P.off_vTl, 0)};
+            split_spec(P, w, P.off_qs, hmax, 0, P.off_qh, P.off_ql, P.off_qTh, P.off_qTl),
+            split_spec(P, w, P.off_ks, hmax, 1, P.off_kh, P.off_kl, P.off_kTh, P.off_kTl),
+            split_spec(P, w, P.off_vs, hmax, 2, P.off_vh, P.off_vl, P.off_vTh, P.off_vTl)};
         if (e == hipSuccess) e = launch_split(sp, 3, s);
         return e;
     }));
@@ -389,15 +386,15 @@ int backward_strided(const void* dout, void* dq, void* dk, void* dv, int N, int 
     LH_TRY(stage(ST_BWD_PREP, s, [&] {
         RowPrepSpec rp{};
         rp.acc = w + P.off_acc; rp.o = w + P.off_os;
-        rp.dos = f32(w, P.off_dos); rp.D = f32(w, P.off_D); rp.rowdown = f32(w, P.off_rowdown);
-        rp.vmax = hmax; rp.S = P.S; rp.Sp = P.Sp; rp.H = H; rp.d = d; rp.mode = acc_mode; rp.dense = 0;
+        rp.dos = f32(w, P.off_dos); rp.D = f32(w, P.off_D);
+        rp.S = P.S; rp.Sp = P.Sp; rp.H = H; rp.d = d; rp.mode = acc_mode; rp.dense = 0;
         float* rowmax_b = f32(w, P.off_rowmax) + 3 * (size_t)H * P.Sp;
         rp.rowmax = dtype == BF16 ? rowmax_b : nullptr;
         hipError_t e = launch_row_prep(rp, s);
         if (e != hipSuccess || dtype != BF16) return e;
         unsigned int* out[1] = {hmax_b + 3};
         e = launch_head_max(rowmax_b, out, 1, P.S, P.Sp, H, s);
-        const SplitSpec sp = split_spec(P, w, P.off_dos, hmax_b, 3, P.off_doh, P.off_dol, P.off_doTh, P.off_doTl, 0);
+        const SplitSpec sp = split_spec(P, w, P.off_dos, hmax_b, 3, P.off_doh, P.off_dol, P.off_doTh, P.off_doTl);
         if (e == hipSuccess) e = launch_split(&sp, 1, s);
         return e;
     }));
@@ -525,6 +522,9 @@ int lh_peak_probe(int kind, const void* src, void* dst, size_t n, void* stream) 
     if (kind >= 0 && kind <= 2) {
         if (n % 16 != 0 || (kind != 1 && !src)) return LH_ERR_ARG;
         if ((reinterpret_cast<uintptr_t>(dst) | reinterpret_cast<uintptr_t>(src)) % 16 != 0) return LH_ERR_ARG;
+    } else if (kind == 4) {
+        if (!src || n > (1u << 20) || (reinterpret_cast<uintptr_t>(dst) | reinterpret_cast<uintptr_t>(src)) % 16 != 0)
+            return LH_ERR_ARG;
     } else if (kind != 3 || n > (1u << 30)) {
         return LH_ERR_ARG;
     }
@@ -541,7 +541,7 @@ static int dense_check(int N, int H, int d, int dtype) {
 }
 
 struct DenseLayout {
-    size_t qh, kh, vh, doh, vTh, kTh, doTh, qTbh, o32, hmax, hscale, lse2, D, rowdown, total;
+    size_t qh, kh, vh, doh, vTh, kTh, doTh, qTh, o32, hmax, hscale, lse2, D, total;
 };
 static DenseLayout dense_layout(int N, int H, int d) {
     DenseLayout L{};
@@ -554,11 +554,11 @@ static DenseLayout dense_layout(int N, int H, int d) {
         return o;
     };
     L.qh = take(t); L.kh = take(t); L.vh = take(t); L.doh = take(t);
-    L.vTh = take(t); L.kTh = take(t); L.doTh = take(t); L.qTbh = take(t);
+    L.vTh = take(t); L.kTh = take(t); L.doTh = take(t); L.qTh = take(t);
     L.o32 = take(2 * t);
     L.hmax = take(sizeof(uint32_t) * 4 * (size_t)H);
     L.hscale = take(sizeof(float) * 4 * (size_t)H);
-    L.lse2 = take(r); L.D = take(r); L.rowdown = take(r);
+    L.lse2 = take(r); L.D = take(r);
     L.total = off;
     return L;
 }
@@ -571,7 +571,7 @@ size_t lh_dense_workspace_bytes(int N, int H, int d, int dtype) {
 // Dense operands are bf16 inputs [N][H][d]: exact in the 16-bit formats, so
 // no lo parts are needed.
 static hipError_t dense_split(const void* src, int N, int H, int d, char* w, const DenseLayout& DL, int slot,
-                              size_t rh, size_t th, int t_bf16, hipStream_t s) {
+                              size_t rh, size_t th, hipStream_t s) {
     SplitSpec sp{};
     sp.src = src; sp.ld = (int64_t)H * d; sp.hs = d; sp.rows = N; sp.Sp = N;
     sp.d = d; sp.H = H; sp.src_bf16 = 1;
@@ -579,16 +579,15 @@ static hipError_t dense_split(const void* src, int N, int H, int d, char* w, con
     sp.hscale = f32(w, DL.hscale); sp.slot = slot;
     sp.rh = rh == SIZE_MAX ? nullptr : u16m(w, rh);
     sp.th = th == SIZE_MAX ? nullptr : u16m(w, th);
-    sp.t_bf16 = t_bf16;
     return launch_split(&sp, 1, s);
 }
 
 static AttnArgs dense_args(int N, int H, int d, char* w, const DenseLayout& DL) {
     AttnArgs a{};
     a.qh = u16(w, DL.qh); a.kh = u16(w, DL.kh); a.vh = u16(w, DL.vh); a.doh = u16(w, DL.doh);
-    a.vTh = u16(w, DL.vTh); a.kTh = u16(w, DL.kTh); a.doTh = u16(w, DL.doTh); a.qTbh = u16(w, DL.qTbh);
+    a.vTh = u16(w, DL.vTh); a.kTh = u16(w, DL.kTh); a.doTh = u16(w, DL.doTh); a.qTh = u16(w, DL.qTh);
     a.hscale = f32(w, DL.hscale);
-    a.lse2 = f32(w, DL.lse2); a.D = f32(w, DL.D); a.rowdown = f32(w, DL.rowdown);
+    a.lse2 = f32(w, DL.lse2); a.D = f32(w, DL.D);
     a.rows = N; a.Sp = N; a.ld_o = (int64_t)H * d; a.hs_o = d;
     a.H = H; a.d = d; a.split = false; a.fp32_path = false;
     a.scale = 1.0f / sqrtf((float)d);
@@ -624,9 +623,9 @@ int lh_dense_attn_fwd(const void* q, const void* k, const void* v, void* o, floa
     const void* src[3] = {q, k, v};
     LH_TRY(dense_maxabs(src, 3, N, H, d, w, DL, s));
     // every q/k/v copy the matching backward needs is made here
-    LH_TRY(dense_split(q, N, H, d, w, DL, 0, DL.qh, DL.qTbh, 1, s));
-    LH_TRY(dense_split(k, N, H, d, w, DL, 1, DL.kh, DL.kTh, 0, s));
-    LH_TRY(dense_split(v, N, H, d, w, DL, 2, DL.vh, DL.vTh, 0, s));
+    LH_TRY(dense_split(q, N, H, d, w, DL, 0, DL.qh, DL.qTh, s));
+    LH_TRY(dense_split(k, N, H, d, w, DL, 1, DL.kh, DL.kTh, s));
+    LH_TRY(dense_split(v, N, H, d, w, DL, 2, DL.vh, DL.vTh, s));
     AttnArgs a = dense_args(N, H, d, w, DL);
     a.o_bf16 = reinterpret_cast<uint16_t*>(o);
     a.o = f32(w, DL.o32);
@@ -651,11 +650,10 @@ int lh_dense_attn_bwd(const void* q, const void* k, const void* v, const void* o
     // q, k, v copies and the fp32 output come from the matching forward's workspace
     const void* src[4] = {nullptr, nullptr, nullptr, dout};
     LH_TRY(dense_maxabs(src, 4, N, H, d, w, DL, s, 3));
-    LH_TRY(dense_split(dout, N, H, d, w, DL, 3, DL.doh, DL.doTh, 0, s));
+    LH_TRY(dense_split(dout, N, H, d, w, DL, 3, DL.doh, DL.doTh, s));
     RowPrepSpec rp{};
     rp.dout = dout; rp.o = w + DL.o32; rp.ld = (int64_t)H * d; rp.hs = d;
-    rp.D = f32(w, DL.D); rp.rowdown = f32(w, DL.rowdown);
-    rp.vmax = reinterpret_cast<const unsigned int*>(w + DL.hmax);
+    rp.D = f32(w, DL.D);
     rp.lse_in = lse; rp.lse2 = f32(w, DL.lse2);
     rp.S = N; rp.Sp = N; rp.H = H; rp.d = d; rp.dense = 1;
     LH_TRY(launch_row_prep(rp, s));

@@ -16,15 +16,21 @@
 //
 // Precision: the pooled sub-sequence is not representable in 16 bits, and
 // the backward's dS = P o (dP - D) cancels heavily on heavy-tailed inputs, so
-// every product uses split operands x = hi + lo:
-//   * fp16 hi/lo (22 significant bits) for Q K^T, P V, dO V^T and P^T dO;
-//     stored operands carry a per-head power-of-two scale so fp16 never
-//     overflows; P lies in [0, 1];
-//   * bf16 hi/lo for dS^T Q (dS may be large; bf16 has the fp32 range);
-//   * fp16 hi/lo of dS scaled per query row by a power of two for dS K.
-// Each split product is hi*hi + hi*lo + lo*hi (lo*lo is below fp32
-// rounding).  When the stored operands are exact in 16 bits (the dense path
-// on bf16 inputs) the lo parts of stored operands are zero and skipped.
+// every product uses split operands x = hi + lo in fp16 (22 significant bits;
+// hi*hi + hi*lo + lo*hi, lo*lo being below fp32 rounding).  Every split
+// value is first brought just below 2^14 by a power of two, so that its lo
+// part stays in fp16's normal range:
+//   * stored operands (q, k, v, dO rows and transposes): one power of two per
+//     head and tensor;
+//   * P: the forward's softmax reference lags the row maximum by 2^6, so P
+//     lies in [0, 2^14] there; the backward reads lse2 = log2-sum-exp - 14, so
+//     P lies in [0, 2^14] there too (the 2^-14 is applied to dV at the end);
+//   * dS (for dS K and dS^T Q): a running power of two per output column (per
+//     query in dQ, per key in dK) that only decreases; when a block's largest
+//     |dS| of a column would pass 2^14, the column's accumulators are
+//     multiplied by the ratio of the old and new powers (exact).
+// When the stored operands are exact in 16 bits (the dense path on bf16
+// inputs) the lo parts of stored operands are zero and skipped.
 //
 // fp32 path: one wavefront per row, double-precision arithmetic.
 #include "lh_device.h"
@@ -34,25 +40,39 @@ namespace lh {
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
-// forward: the softmax reference maximum lags the row maximum by up to this
-// much (log2 units); P then lies in [0, 2^8], still split exactly into fp16 hi/lo
-constexpr float kLazyMax = 8.0f;
+// forward: the softmax reference m is set kPLag below the row maximum and
+// moves only when the row maximum passes m + kPTop (log2 units), so the
+// weights 2^(s - m) lie in [0, 2^kPTop], at least 2^kPLag for the row's
+// maximum, and the rescale of O is rare (growth by more than 2^8)
+constexpr float kPLag = 6.0f;
+constexpr float kPTop = 14.0f;
+// the backward kernels read lse2 = base-2 log-sum-exp - kPBwd, so their
+// weights are P * 2^kPBwd in [0, 2^14]
+constexpr float kPBwd = 14.0f;
+constexpr float kInvPBwd = 1.0f / 16384.0f;
+
+// Running power-of-two multiplier `mul` of one output column's dS values:
+// keeps |dS| * mul below 2^14 for the block maximum `bm` of the column (same
+// value in the column's four lanes).  Returns the factor (a power of two, or
+// 1) by which the column's accumulators must be multiplied.
+__device__ __forceinline__ float column_scale(float bm, float& mul) {
+    if (!(bm * mul >= 16384.0f)) return 1.0f;
+    int ex;
+    frexpf(bm, &ex);                          // bm < 2^ex
+    const float nm = ldexpf(1.0f, 14 - ex);   // bm * nm < 2^14
+    const float f = nm / mul;
+    mul = nm;
+    return f;
+}
 
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 
 __device__ __forceinline__ f16x8 ld_f16x8(const uint16_t* p) {
     return __builtin_bit_cast(f16x8, *reinterpret_cast<const u32x4*>(p));
 }
-__device__ __forceinline__ bf16x8 ld_b16x8(const uint16_t* p) {
-    return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p));
-}
 __device__ __forceinline__ f32x4 mma_h(const f16x8& a, const f16x8& b, const f32x4& c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
-__device__ __forceinline__ f32x4 mma_b(const bf16x8& a, const bf16x8& b, const f32x4& c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-
 // Split 8 fp32 values (two f32x4 holding elements 0..3 and 4..7) into fp16 hi/lo.
 __device__ __forceinline__ void split_h(const f32x4& a, const f32x4& b, f16x8& hi, f16x8& lo) {
 #pragma unroll
@@ -64,34 +84,18 @@ __device__ __forceinline__ void split_h(const f32x4& a, const f32x4& b, f16x8& h
         lo[4 + e] = (_Float16)(b[e] - (float)h1);
     }
 }
-__device__ __forceinline__ uint16_t bf16_rne(float f) { return (uint16_t)f32_to_bf16_bits(f); }
-__device__ __forceinline__ void split_b(const f32x4& a, const f32x4& b, bf16x8& hi, bf16x8& lo) {
-    u32x4 wh, wl;
-#pragma unroll
-    for (int e = 0; e < 2; ++e) {
-        const uint16_t a0 = bf16_rne(a[2 * e]), a1 = bf16_rne(a[2 * e + 1]);
-        const uint16_t b0 = bf16_rne(b[2 * e]), b1 = bf16_rne(b[2 * e + 1]);
-        wh[e] = (uint32_t)a0 | ((uint32_t)a1 << 16);
-        wh[2 + e] = (uint32_t)b0 | ((uint32_t)b1 << 16);
-        wl[e] = (uint32_t)bf16_rne(a[2 * e] - bf16_lo(a0)) | ((uint32_t)bf16_rne(a[2 * e + 1] - bf16_lo(a1)) << 16);
-        wl[2 + e] = (uint32_t)bf16_rne(b[2 * e] - bf16_lo(b0)) | ((uint32_t)bf16_rne(b[2 * e + 1] - bf16_lo(b1)) << 16);
-    }
-    hi = __builtin_bit_cast(bf16x8, wh);
-    lo = __builtin_bit_cast(bf16x8, wl);
-}
 
 // Operand tensors of one attention problem (all [H][rows][d] row-major or
 // [H][d][Sp] transposed, 2-byte elements; lo pointers unused when !SPLIT).
 struct AttnK {
     const uint16_t *qh, *ql, *kh, *kl, *vh, *vl, *doh, *dol;   // fp16 rows
     const uint16_t *vTh, *vTl, *kTh, *kTl, *doTh, *doTl;       // fp16 transposed
-    const uint16_t *qTbh, *qTbl;                               // bf16 transposed (unscaled)
+    const uint16_t *qTh, *qTl;
     const float* hscale;    // [H][4]: true value = stored * hscale (q, k, v, dO)
     float* o;               // fp32 [H][Sp][d] sub-sequence output, or null
     uint16_t* o_bf16;       // bf16 output with strides ld_o/hs_o (dense), or null
-    float *lse, *lse2;      // [H][Sp]: natural and base-2 log-sum-exp
+    float *lse, *lse2;      // [H][Sp]: natural log-sum-exp, base-2 log-sum-exp - kPBwd
     const float* D;         // [H][Sp]
-    const float* rowdown;   // [H][Sp]: power-of-two down-scale of dS rows (dq kernel)
     float *dq, *dk, *dv;    // fp32 [H][Sp][d] gradients, or
     uint16_t *dq_b, *dk_b, *dv_b;   // bf16 gradients with strides ld_o/hs_o
     const uint8_t* level;           // [H][rows]
@@ -395,19 +399,26 @@ __global__ void __launch_bounds__(256) k_attn_fwd(AttnK a) {
                     if constexpr (SPLIT) klr[u][st] = __builtin_bit_cast(f16x8, frag_row<D>(Kl, 16 * u + lq, 4 * st + lg));
                 }
             __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int st = 0; st < NS; ++st)
-#pragma unroll
-                for (int u = 0; u < 2; ++u) part[u][st] = mma_h(kfr[u][st], qfh[st], f32x4{0.f, 0.f, 0.f, 0.f});
+            // the small hi*lo and lo*hi products first, hi*hi last: an MFMA's
+            // rounding error scales with its largest addend, accumulator included
             if constexpr (SPLIT) {
 #pragma unroll
                 for (int st = 0; st < NS; ++st)
 #pragma unroll
-                    for (int u = 0; u < 2; ++u) part[u][st] = mma_h(kfr[u][st], qfl[st], part[u][st]);
+                    for (int u = 0; u < 2; ++u) part[u][st] = mma_h(kfr[u][st], qfl[st], f32x4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
                 for (int st = 0; st < NS; ++st)
 #pragma unroll
                     for (int u = 0; u < 2; ++u) part[u][st] = mma_h(klr[u][st], qfh[st], part[u][st]);
+#pragma unroll
+                for (int st = 0; st < NS; ++st)
+#pragma unroll
+                    for (int u = 0; u < 2; ++u) part[u][st] = mma_h(kfr[u][st], qfh[st], part[u][st]);
+            } else {
+#pragma unroll
+                for (int st = 0; st < NS; ++st)
+#pragma unroll
+                    for (int u = 0; u < 2; ++u) part[u][st] = mma_h(kfr[u][st], qfh[st], f32x4{0.f, 0.f, 0.f, 0.f});
             }
 #pragma unroll
             for (int u = 0; u < 2; ++u) {
@@ -436,12 +447,12 @@ __global__ void __launch_bounds__(256) k_attn_fwd(AttnK a) {
                     for (int r = 0; r < 4; ++r) mx = fmaxf(mx, sc[u][r]);
             }
             mx = rows4_max(mx) * c2;
-            // The reference maximum m moves only when a row maximum exceeds it by
-            // more than kLazyMax (log2 units), so P stays in [0, 2^kLazyMax] and
-            // the rescale of O is rare; alpha is exactly 1 for rows that keep m.
-            const bool grow = mx > m + kLazyMax;
+            // The reference m moves only when a row maximum passes m + kPTop; it is
+            // then set kPLag below that maximum.  alpha is exactly 1 for rows that
+            // keep m.
+            const bool grow = mx > m + kPTop;
             if (__ballot(grow) != 0) {
-                const float mnew = grow ? mx : m;
+                const float mnew = grow ? mx - kPLag : m;
                 const float alpha = grow ? fast_exp2(m - mnew) : 1.0f;
                 lsum *= alpha;
 #pragma unroll
@@ -472,14 +483,20 @@ __global__ void __launch_bounds__(256) k_attn_fwd(AttnK a) {
                 if constexpr (SPLIT) vfl[v] = __builtin_bit_cast(f16x8, frag_t(Vl, 16 * v + lq, lg));
             }
             __builtin_amdgcn_sched_barrier(0);
+            // this block's products in fresh accumulators (small terms first), added
+            // to O with fp32 adds: an MFMA that took O itself as its accumulator
+            // would round at O's magnitude once per block and per split term
+            f32x4 blk[NV];
 #pragma unroll
-            for (int v = 0; v < NV; ++v) o[v] = mma_h(vfh[v], ph, o[v]);
-#pragma unroll
-            for (int v = 0; v < NV; ++v) o[v] = mma_h(vfh[v], pl, o[v]);
+            for (int v = 0; v < NV; ++v) blk[v] = mma_h(vfh[v], pl, f32x4{0.f, 0.f, 0.f, 0.f});
             if constexpr (SPLIT) {
 #pragma unroll
-                for (int v = 0; v < NV; ++v) o[v] = mma_h(vfl[v], ph, o[v]);
+                for (int v = 0; v < NV; ++v) blk[v] = mma_h(vfl[v], ph, blk[v]);
             }
+#pragma unroll
+            for (int v = 0; v < NV; ++v) blk[v] = mma_h(vfh[v], ph, blk[v]);
+#pragma unroll
+            for (int v = 0; v < NV; ++v) o[v] += blk[v];
         }
         wait_vmem();
         __syncthreads();
@@ -503,7 +520,7 @@ __global__ void __launch_bounds__(256) k_attn_fwd(AttnK a) {
     }
     if (lg == 0) {
         const float l2 = m + log2f(lsum);
-        a.lse2[(int64_t)h * Sp + myq] = l2;
+        a.lse2[(int64_t)h * Sp + myq] = l2 - kPBwd;
         a.lse[(int64_t)h * Sp + myq] = l2 * kLn2;
     }
     if (a.o_tok) {   // the LDS tiles are idle: every wave is past the loop's last barrier
@@ -549,6 +566,7 @@ __global__ void __launch_bounds__(256) k_attn_dkdv(AttnK a) {
     const float cP = mdo * mv;
     const float* lse2 = a.lse2 + (int64_t)h * Sp;
     const float* Dv = a.D + (int64_t)h * Sp;
+    float smul = 0x1p100f;   // running power-of-two multiplier of this key's dS column
 
     f16x8 kfh[NS], kfl[NS], vfh[NS], vfl[NS];
 #pragma unroll
@@ -587,10 +605,10 @@ __global__ void __launch_bounds__(256) k_attn_dkdv(AttnK a) {
     auto loadB = [&](int b) {
         const int64_t qb = qblock(b);
         uint16_t* base = sm + ROWS;
-        dma_t<D>(a.qTbh + hb, Sp, qb, base);
+        dma_t<D>(a.qTh + hb, Sp, qb, base);
         dma_t<D>(a.doTh + hb, Sp, qb, base + NA * T::TR);
         if constexpr (SPLIT) {
-            dma_t<D>(a.qTbl + hb, Sp, qb, base + T::TR);
+            dma_t<D>(a.qTl + hb, Sp, qb, base + T::TR);
             dma_t<D>(a.doTl + hb, Sp, qb, base + 3 * T::TR);
         }
     };
@@ -641,7 +659,7 @@ __global__ void __launch_bounds__(256) k_attn_dkdv(AttnK a) {
 #pragma unroll
                 for (int r2 = 0; r2 < 4; ++r2) {
                     const int q = (int)qq + r2;
-                    float pr = fast_exp2(s[r2] * cS - l4[r2]);
+                    float pr = fast_exp2(s[r2] * cS - l4[r2]);   // P * 2^kPBwd
                     pr = (q >= (int)mykey && q < (int)a.rows) ? pr : 0.f;
                     P[u][r2] = pr;
                     dS[u][r2] = pr * (dp[r2] * cP - d4[r2]);
@@ -654,20 +672,32 @@ __global__ void __launch_bounds__(256) k_attn_dkdv(AttnK a) {
         if (active) {
             f16x8 ph, pl;
             split_h(P[0], P[1], ph, pl);
-            bf16x8 sh, sl;
-            split_b(dS[0], dS[1], sh, sl);
+            // this key's dS column, brought below 2^14 by its running power of two
+            float bm = 0.f;
+#pragma unroll
+            for (int u = 0; u < 2; ++u)
+#pragma unroll
+                for (int r2 = 0; r2 < 4; ++r2) bm = fmaxf(bm, fabsf(dS[u][r2]));
+            bm = rows4_max(bm);
+            if (__ballot(bm * smul >= 16384.0f) != 0) {
+                const float f = column_scale(bm, smul);
+#pragma unroll
+                for (int v = 0; v < NV; ++v) dk[v] *= f;
+            }
+            f16x8 sh, sl;
+            split_h(dS[0] * smul, dS[1] * smul, sh, sl);
 #pragma unroll
             for (int v = 0; v < NV; ++v) {
                 const int r = 16 * v + lq;
                 const f16x8 oth = __builtin_bit_cast(f16x8, frag_t(OTh, r, lg));
                 dv[v] = mma_h(oth, ph, dv[v]);
                 dv[v] = mma_h(oth, pl, dv[v]);
-                const bf16x8 qth = __builtin_bit_cast(bf16x8, frag_t(QTh, r, lg));
-                dk[v] = mma_b(qth, sh, dk[v]);
-                dk[v] = mma_b(qth, sl, dk[v]);
+                const f16x8 qth = __builtin_bit_cast(f16x8, frag_t(QTh, r, lg));
+                dk[v] = mma_h(qth, sh, dk[v]);
+                dk[v] = mma_h(qth, sl, dk[v]);
                 if constexpr (SPLIT) {
                     dv[v] = mma_h(__builtin_bit_cast(f16x8, frag_t(OTl, r, lg)), ph, dv[v]);
-                    dk[v] = mma_b(__builtin_bit_cast(bf16x8, frag_t(QTl, r, lg)), sh, dk[v]);
+                    dk[v] = mma_h(__builtin_bit_cast(f16x8, frag_t(QTl, r, lg)), sh, dk[v]);
                 }
             }
         }
@@ -675,13 +705,15 @@ __global__ void __launch_bounds__(256) k_attn_dkdv(AttnK a) {
         __syncthreads();
         if (more) loadB(b + 1);
     }
-    // dk[v][r], dv[v][r] hold the gradients of key mykey at d-index 16v + 4g + r
+    // dk[v][r], dv[v][r] hold the gradients of key mykey at d-index 16v + 4g + r,
+    // times smul 2^kPBwd / (scale mq) and 2^kPBwd / mdo
+    const float kmul = a.scale * mq * kInvPBwd / smul, vmul = mdo * kInvPBwd;
     if (mykey < a.rows) {
         if constexpr (OUT_BF16) {
             const int64_t base = h * a.hs_o + mykey * a.ld_o + 4 * lg;
 #pragma unroll
             for (int v = 0; v < NV; ++v) {
-                const f32x4 x = dk[v] * a.scale, y = dv[v] * mdo;
+                const f32x4 x = dk[v] * kmul, y = dv[v] * vmul;
                 *reinterpret_cast<u32x2*>(a.dk_b + base + 16 * v) = u32x2{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3])};
                 *reinterpret_cast<u32x2*>(a.dv_b + base + 16 * v) = u32x2{pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])};
             }
@@ -689,8 +721,8 @@ __global__ void __launch_bounds__(256) k_attn_dkdv(AttnK a) {
             const int64_t base = hb + mykey * D + 4 * lg;
 #pragma unroll
             for (int v = 0; v < NV; ++v) {
-                __builtin_nontemporal_store(dk[v] * a.scale, reinterpret_cast<f32x4*>(a.dk + base + 16 * v));
-                __builtin_nontemporal_store(dv[v] * mdo, reinterpret_cast<f32x4*>(a.dv + base + 16 * v));
+                __builtin_nontemporal_store(dk[v] * kmul, reinterpret_cast<f32x4*>(a.dk + base + 16 * v));
+                __builtin_nontemporal_store(dv[v] * vmul, reinterpret_cast<f32x4*>(a.dv + base + 16 * v));
             }
         }
     }
@@ -698,8 +730,8 @@ __global__ void __launch_bounds__(256) k_attn_dkdv(AttnK a) {
         uint16_t* rk = sm + wave * 16 * D;
         uint16_t* rv = sm + (4 + wave) * 16 * D;
         const float den = mykey < a.rows ? level_den(a, h, mykey) : 1.0f;
-        stage_rows<D>(rk, dk, a.scale, den, lq, lg);
-        stage_rows<D>(rv, dv, mdo, den, lq, lg);
+        stage_rows<D>(rk, dk, kmul, den, lq, lg);
+        stage_rows<D>(rv, dv, vmul, den, lq, lg);
         __syncthreads();
         rows_to_tokens<D>(rk, a.dk_tok, a, h, k0, lane);
         rows_to_tokens<D>(rv, a.dv_tok, a, h, k0, lane);
@@ -708,9 +740,8 @@ __global__ void __launch_bounds__(256) k_attn_dkdv(AttnK a) {
 
 // ---------------------------------------------------------- backward: dQ
 // Query-stationary: wave w owns queries q0..q0+15 and the key blocks up to the
-// diagonal stream through LDS.  dS rows are scaled down by a power of two
-// (rowdown) before the fp16 split, so they cannot overflow; the scale is undone
-// at the end.
+// diagonal stream through LDS.  Each query's dS row carries a running power of
+// two (column_scale) before the fp16 split; it is undone at the end.
 template <int D, bool SPLIT, bool OUT_BF16>
 __global__ void __launch_bounds__(256) k_attn_dq(AttnK a) {
     using T = Tiles<D>;
@@ -748,7 +779,7 @@ __global__ void __launch_bounds__(256) k_attn_dq(AttnK a) {
     }
     const float l2 = a.lse2[(int64_t)h * Sp + myq];
     const float Dq = a.D[(int64_t)h * Sp + myq];
-    const float down = a.rowdown[(int64_t)h * Sp + myq];
+    float smul = 0x1p100f;   // running power-of-two multiplier of this query's dS row
     f32x4 dq[NV];
 #pragma unroll
     for (int v = 0; v < NV; ++v) dq[v] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -806,11 +837,8 @@ __global__ void __launch_bounds__(256) k_attn_dq(AttnK a) {
                 f32x4 s2[2], dp2[2];
 #pragma unroll
                 for (int e = 0; e < 2; ++e) s2[e] = dp2[e] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int st = 0; st < NS; ++st) {
-                    s2[st & 1] = mma_h(kh[st], qfh[st], s2[st & 1]);
-                    dp2[st & 1] = mma_h(vh[st], dfh[st], dp2[st & 1]);
-                }
+                // small split terms first, hi*hi last (an MFMA rounds at the scale of
+                // its largest addend)
                 if constexpr (SPLIT) {
 #pragma unroll
                     for (int st = 0; st < NS; ++st) {
@@ -823,13 +851,18 @@ __global__ void __launch_bounds__(256) k_attn_dq(AttnK a) {
                         dp2[st & 1] = mma_h(vl[st], dfh[st], dp2[st & 1]);
                     }
                 }
+#pragma unroll
+                for (int st = 0; st < NS; ++st) {
+                    s2[st & 1] = mma_h(kh[st], qfh[st], s2[st & 1]);
+                    dp2[st & 1] = mma_h(vh[st], dfh[st], dp2[st & 1]);
+                }
                 const f32x4 s = s2[0] + s2[1], dp = dp2[0] + dp2[1];
 #pragma unroll
                 for (int r2 = 0; r2 < 4; ++r2) {
                     const int key = (int)kb + 16 * u + 4 * lg + r2;
-                    float pr = fast_exp2(s[r2] * cS - l2);
+                    float pr = fast_exp2(s[r2] * cS - l2);   // P * 2^kPBwd
                     pr = key <= (int)myq ? pr : 0.f;
-                    dS[u][r2] = pr * (dp[r2] * cP - Dq) * down;
+                    dS[u][r2] = pr * (dp[r2] * cP - Dq);
                 }
             }
         }
@@ -837,8 +870,19 @@ __global__ void __launch_bounds__(256) k_attn_dq(AttnK a) {
         __syncthreads();
         if (more) loadA(b + 1);
         if (active) {
+            float bm = 0.f;
+#pragma unroll
+            for (int u = 0; u < 2; ++u)
+#pragma unroll
+                for (int r2 = 0; r2 < 4; ++r2) bm = fmaxf(bm, fabsf(dS[u][r2]));
+            bm = rows4_max(bm);
+            if (__ballot(bm * smul >= 16384.0f) != 0) {
+                const float f = column_scale(bm, smul);
+#pragma unroll
+                for (int v = 0; v < NV; ++v) dq[v] *= f;
+            }
             f16x8 sh, sl;
-            split_h(dS[0], dS[1], sh, sl);
+            split_h(dS[0] * smul, dS[1] * smul, sh, sl);
             // all k^T fragments first, then the products in passes over v, so the
             // three MFMAs into one accumulator are NV issues apart
             f16x8 kth[NV], ktl[NV];
@@ -861,8 +905,8 @@ __global__ void __launch_bounds__(256) k_attn_dq(AttnK a) {
         __syncthreads();
         if (more) loadB(b + 1);
     }
+    const float mul = a.scale * mk * kInvPBwd / smul;
     if (myq < a.rows) {
-        const float mul = a.scale * mk / down;
         if constexpr (OUT_BF16) {
             const int64_t base = h * a.hs_o + myq * a.ld_o + 4 * lg;
 #pragma unroll
@@ -879,7 +923,7 @@ __global__ void __launch_bounds__(256) k_attn_dq(AttnK a) {
     if (a.dq_tok) {   // pool adjoint of q: dQ~ / p^level to every token of the entry
         uint16_t* rows = sm + wave * 16 * D;
         const float den = myq < a.rows ? level_den(a, h, myq) : 1.0f;
-        stage_rows<D>(rows, dq, a.scale * mk / down, den, lq, lg);
+        stage_rows<D>(rows, dq, mul, den, lq, lg);
         __syncthreads();
         rows_to_tokens<D>(rows, a.dq_tok, a, h, q0, lane);
     }
@@ -929,7 +973,7 @@ __global__ void __launch_bounds__(256) k_attn_fwd_f32(AttnK a) {
     if (lane == 0) {
         const double lse = m + log(l);
         a.lse[(int64_t)h * a.Sp + i] = (float)lse;
-        a.lse2[(int64_t)h * a.Sp + i] = (float)(lse * 1.4426950408889634);
+        a.lse2[(int64_t)h * a.Sp + i] = (float)(lse * 1.4426950408889634 - (double)kPBwd);
     }
 }
 
@@ -994,10 +1038,10 @@ static AttnK to_k(const AttnArgs& x) {
     a.qh = x.qh; a.ql = x.ql; a.kh = x.kh; a.kl = x.kl; a.vh = x.vh; a.vl = x.vl;
     a.doh = x.doh; a.dol = x.dol;
     a.vTh = x.vTh; a.vTl = x.vTl; a.kTh = x.kTh; a.kTl = x.kTl; a.doTh = x.doTh; a.doTl = x.doTl;
-    a.qTbh = x.qTbh; a.qTbl = x.qTbl;
+    a.qTh = x.qTh; a.qTl = x.qTl;
     a.hscale = x.hscale;
     a.o = x.o; a.o_bf16 = x.o_bf16;
-    a.lse = x.lse; a.lse2 = x.lse2; a.D = x.D; a.rowdown = x.rowdown;
+    a.lse = x.lse; a.lse2 = x.lse2; a.D = x.D;
     a.dq = x.dq; a.dk = x.dk; a.dv = x.dv;
     a.dq_b = x.dq_b; a.dk_b = x.dk_b; a.dv_b = x.dv_b;
     a.level = x.level; a.p = x.p;

@@ -74,7 +74,7 @@ struct Plan {
     size_t off_qs, off_ks, off_vs;   // fp32 [H][Sp][d] gathered sub-sequence
     // 16-bit operand copies (bf16 path): fp16 hi/lo rows [H][Sp][d], transposed [H][d][Sp]
     size_t off_qh, off_ql, off_kh, off_kl, off_vh, off_vl;
-    size_t off_vTh, off_vTl, off_kTh, off_kTl, off_qTbh, off_qTbl;
+    size_t off_vTh, off_vTl, off_kTh, off_kTl, off_qTh, off_qTl;
     size_t off_hmax;              // uint32 [2][H][4]: forward (q, k, v) and backward (dO) max |x|
     size_t off_rowmax;            // fp32 [4][H][Sp]: max |x| per row of q~, k~, v~ (gather) and dO~
     size_t off_hscale;            // fp32 [H][4]: per-head multipliers of the fp16 copies
@@ -83,7 +83,7 @@ struct Plan {
     size_t off_acc;               // 8 bytes x [H][Sp][d]: fp32 or int64 accumulators of dO~
     size_t off_dos;               // fp32 [H][Sp][d]
     size_t off_doh, off_dol, off_doTh, off_doTl;   // fp16 copies of dO~
-    size_t off_D, off_rowdown;    // fp32 [H][Sp]
+    size_t off_D;                 // fp32 [H][Sp]
     size_t off_dq, off_dk, off_dv;   // fp32 [H][Sp][d]
     // parent kept: int32 [sum_l H * n_l], 1 + the slot of entry (l, j) of head h
     // at lmap_off[l] + h * n_l + j, 0 when that entry is not kept
@@ -127,12 +127,12 @@ hipError_t launch_entry_sum(const Plan& P, const void* dout, char* ws, hipStream
 // [H][d][Sp] (transposed); lo parts are used when `split`.
 struct AttnArgs {
     const uint16_t *qh, *ql, *kh, *kl, *vh, *vl, *doh, *dol;
-    const uint16_t *vTh, *vTl, *kTh, *kTl, *doTh, *doTl, *qTbh, *qTbl;
+    const uint16_t *vTh, *vTl, *kTh, *kTl, *doTh, *doTl, *qTh, *qTl;
     const float* hscale;
     float* o;                  // fp32 [H][Sp][d] or null
     uint16_t* o_bf16;          // bf16 output rows (ld_o, hs_o) or null
     float *lse, *lse2;
-    const float *D, *rowdown;
+    const float* D;
     float *dq, *dk, *dv;       // fp32 [H][Sp][d] or null
     uint16_t *dq_b, *dk_b, *dv_b;   // bf16 rows (ld_o, hs_o) or null
     const uint8_t* level;           // [H][rows] (the in-kernel scatters)
@@ -160,15 +160,13 @@ struct SplitSpec {
     float* hscale;
     int slot;
     uint16_t *rh, *rl, *th, *tl;
-    int t_bf16;
 };
 struct RowPrepSpec {
     const void *acc, *dout, *o;
     int64_t ld, hs;
-    float *dos, *D, *rowdown;
-    const float* lse_in;       // dense: natural-log lse [H][N] -> lse2 (base 2)
+    float *dos, *D;
+    const float* lse_in;       // dense: natural-log lse [H][N] -> lse2 (base 2, minus the backward's offset)
     float* lse2;
-    const unsigned int* vmax;
     float* rowmax;             // optional: per-row max |dO~| [H][Sp]
     int64_t S, Sp;
     int H, d, mode, dense;

@@ -1,6 +1,6 @@
 // Operand preparation for the attention kernels on gfx950: per-head scale
-// exponents, hi/lo splits into 16-bit formats (row-major and transposed), and
-// the per-row quantities of the backward pass (D_i and the dS down-scale).
+// exponents, fp16 hi/lo splits (row-major and transposed), and the per-row
+// quantities of the backward pass (D_i, and for the dense path the base-2 lse).
 #include "lh_device.h"
 #include "lh_internal.h"
 
@@ -76,8 +76,8 @@ __device__ __forceinline__ float down_scale(float mx) {
 
 // ---------------------------------------------------------------- splits
 // One 64x64 tile of head h: x = src * down (down = power-of-two scale of the
-// head); writes fp16 hi/lo rows, and a transposed copy as fp16 hi/lo (scaled)
-// or bf16 hi/lo (unscaled).  Rows >= `rows` are written as zeros.
+// head); writes fp16 hi/lo rows and a transposed fp16 hi/lo copy.  Rows >=
+// `rows` are written as zeros.
 //
 // Transposed copies are [H][d][Sp] with the sequence positions of each aligned
 // block of 32 stored in MFMA-fragment order: position 16h + 4g + e (h < 2,
@@ -97,7 +97,6 @@ struct SplitArgs {
     int slot[3];
     uint16_t *rh[3], *rl[3];    // fp16 [H][Sp][d] (scaled) or null
     uint16_t *th[3], *tl[3];    // [H][d][Sp] or null
-    int t_bf16[3];              // transposed copy in bf16, unscaled
 };
 
 __device__ __forceinline__ uint16_t h16(float x) { return __builtin_bit_cast(uint16_t, (_Float16)x); }
@@ -109,13 +108,11 @@ __global__ void __launch_bounds__(256) k_split(SplitArgs a) {
     const int t = blockIdx.z / a.H, h = blockIdx.z % a.H;
     const void* src = a.src[t];
     uint16_t *rh = a.rh[t], *rl = a.rl[t], *tth = a.th[t], *ttl = a.tl[t];
-    const int tb16 = a.t_bf16[t];
     const int64_t r0 = (int64_t)blockIdx.x * 64;
     const int c0 = blockIdx.y * 64;
     const float mx = __uint_as_float(a.hmax[h * 4 + a.slot[t]]);
     const float down = down_scale(mx);
     if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) a.hscale[h * 4 + a.slot[t]] = 1.0f / down;
-    const float tdown = tb16 ? 1.0f : down;
     // each thread: 2 (row, 8-column chunk) items of the 64x64 tile
     for (int it = threadIdx.x; it < 64 * 8; it += 256) {
         const int r = it / 8, cc = (it % 8) * 8;
@@ -144,17 +141,10 @@ __global__ void __launch_bounds__(256) k_split(SplitArgs a) {
         if (tth) {
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                const float xs = x[e] * tdown;
-                uint16_t hb, lb;
-                if (tb16) {
-                    hb = (uint16_t)f32_to_bf16_bits(xs);
-                    lb = (uint16_t)f32_to_bf16_bits(xs - bf16_lo(hb));
-                } else {
-                    hb = h16(xs);
-                    lb = h16(xs - f16f(hb));
-                }
+                const float xs = x[e] * down;
+                const uint16_t hb = h16(xs);
                 th[cc + e][frag_order(r)] = hb;
-                tl[cc + e][frag_order(r)] = lb;
+                tl[cc + e][frag_order(r)] = h16(xs - f16f(hb));
             }
         }
     }
@@ -175,19 +165,18 @@ __global__ void __launch_bounds__(256) k_split(SplitArgs a) {
 }
 
 // ---------------------------------------------------------- backward rows
-// Per sub-sequence row: finish dO~ (fp32 or 64-bit fixed-point accumulator),
-// D_i = <dO~_i, O~_i> in double, and the power-of-two down-scale of row i of
-// dS, from |dS_ij| <= ||dO~_i|| * sqrt(d) * max|V~| + |D_i|.
+// Per sub-sequence row: finish dO~ (fp32 or 64-bit fixed-point accumulator)
+// and D_i = <dO~_i, O~_i> in double; for the dense path also the base-2 lse
+// minus the backward kernels' offset 14 (their weights are then P * 2^14).
 struct RowPrepArgs {
     const void* acc;       // [H][Sp][d] fp32 (mode 0) or int64 (mode 1); unused when dense
     const void* dout;      // dense: bf16 rows with strides ld/hs
     const void* o;         // fp32 [H][Sp][d] attention output
     int64_t ld, hs;        // dense strides of dout
     float* dos;            // fp32 [H][Sp][d] finished dO~ (sub-sequence) or null
-    float *D, *rowdown;    // [H][Sp]
+    float* D;              // [H][Sp]
     const float* lse_in;   // dense: natural-log lse [H][N], converted to base 2 in lse2
     float* lse2;
-    const unsigned int* vmax;  // [H][4] slot 2: max |V|
     float* rowmax;             // optional fp32 [H][Sp]: max |dO~| of each row
     int64_t S, Sp;
     int H, d, mode, dense;
@@ -221,17 +210,11 @@ __global__ void __launch_bounds__(256) k_row_prep(RowPrepArgs a) {
         }
     }
     if (live && a.dos) store8f(a.dos, r * d + c * 8, x);
-    double dot = 0.0, nrm = 0.0;
+    double dot = 0.0;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        dot = fma((double)x[e], (double)o[e], dot);
-        nrm = fma((double)x[e], (double)x[e], nrm);
-    }
+    for (int e = 0; e < 8; ++e) dot = fma((double)x[e], (double)o[e], dot);
 #pragma unroll
-    for (int off = G / 2; off >= 1; off >>= 1) {
-        dot += __shfl_xor(dot, off, 64);
-        nrm += __shfl_xor(nrm, off, 64);
-    }
+    for (int off = G / 2; off >= 1; off >>= 1) dot += __shfl_xor(dot, off, 64);
     if (a.rowmax) {   // the row's max |dO~| for the per-head scale of its 16-bit copies
         float mx = 0.f;
 #pragma unroll
@@ -241,17 +224,8 @@ __global__ void __launch_bounds__(256) k_row_prep(RowPrepArgs a) {
         if (live && c == 0) a.rowmax[r] = mx;
     }
     if (live && c == 0) {
-        if (a.lse_in) a.lse2[r] = a.lse_in[r] * 1.4426950408889634f;
+        if (a.lse_in) a.lse2[r] = (float)((double)a.lse_in[r] * 1.4426950408889634 - 14.0);
         a.D[r] = (float)dot;
-        const float vm = __uint_as_float(a.vmax[h * 4 + 2]);
-        const float bound = (float)(sqrt(nrm) * sqrt((double)d) * (double)vm + fabs(dot));
-        float down = 1.0f;
-        if (bound > 0.f) {
-            int ex;
-            frexpf(bound, &ex);
-            down = ldexpf(1.0f, 13 - ex);
-        }
-        a.rowdown[r] = down;
     }
 }
 
@@ -293,7 +267,7 @@ hipError_t launch_split(const SplitSpec* sp, int T, hipStream_t s) {
             x.src_bf16 != s0.src_bf16 || x.hmax != s0.hmax || x.hscale != s0.hscale)
             return hipErrorInvalidValue;
         a.src[t] = x.src; a.slot[t] = x.slot;
-        a.rh[t] = x.rh; a.rl[t] = x.rl; a.th[t] = x.th; a.tl[t] = x.tl; a.t_bf16[t] = x.t_bf16;
+        a.rh[t] = x.rh; a.rl[t] = x.rl; a.th[t] = x.th; a.tl[t] = x.tl;
     }
     dim3 grid((unsigned)(s0.Sp / 64), (unsigned)(s0.d / 64), (unsigned)(s0.H * T));
     hipLaunchKernelGGL(k_split, grid, dim3(256), 0, s, a);
@@ -314,7 +288,7 @@ hipError_t launch_head_max(const float* rowmax, unsigned int* const* out, int T,
 hipError_t launch_row_prep(const RowPrepSpec& sp, hipStream_t s) {
     RowPrepArgs a{};
     a.acc = sp.acc; a.dout = sp.dout; a.o = sp.o; a.ld = sp.ld; a.hs = sp.hs;
-    a.dos = sp.dos; a.D = sp.D; a.rowdown = sp.rowdown; a.vmax = sp.vmax;
+    a.dos = sp.dos; a.D = sp.D;
     a.lse_in = sp.lse_in; a.lse2 = sp.lse2; a.rowmax = sp.rowmax;
     a.S = sp.S; a.Sp = sp.Sp; a.H = sp.H; a.d = sp.d; a.mode = sp.mode; a.dense = sp.dense;
     const int G = sp.d / 8;

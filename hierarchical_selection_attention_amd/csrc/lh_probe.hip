@@ -11,6 +11,8 @@ namespace lh {
 namespace {
 
 constexpr int64_t kChunk16 = 65536;   // 16-byte words per workgroup (1 MiB)
+constexpr size_t kMfmaRoundRecord = 3072;   // bytes per trial of the rounding probe
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 constexpr int kInFlight = 8;
 
 // XOR-fold v over the workgroup and store it to this workgroup's 16 bytes of
@@ -97,6 +99,21 @@ __global__ void __launch_bounds__(256) k_probe_mfma(int iters, unsigned* out) {
     fold_out(u32x4{__float_as_uint(t[0]), __float_as_uint(t[1]), __float_as_uint(t[2]), __float_as_uint(t[3])}, out);
 }
 
+// kind 4: one v_mfma_f32_16x16x32_f16 per trial, one wavefront per trial, on
+// operands from memory (a record of 64 lanes x 8 fp16 A values, 64 x 8 fp16
+// B values and 64 x 4 fp32 accumulator values); the 64 x 4 results go to dst.
+// Lane l supplies A[l % 16][8 (l / 16) + e] and B[8 (l / 16) + e][l % 16] for
+// e < 8, and holds C and D at rows 4 (l / 16) + r, column l % 16, for r < 4.
+__global__ void __launch_bounds__(64) k_probe_mfma_round(const unsigned char* __restrict__ src, float* __restrict__ dst) {
+    const int lane = threadIdx.x;
+    const unsigned char* rec = src + (size_t)blockIdx.x * kMfmaRoundRecord;
+    const f16x8 a = *reinterpret_cast<const f16x8*>(rec + 16 * lane);
+    const f16x8 b = *reinterpret_cast<const f16x8*>(rec + 1024 + 16 * lane);
+    const f32x4 c = *reinterpret_cast<const f32x4*>(rec + 2048 + 16 * lane);
+    const f32x4 d = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+    *reinterpret_cast<f32x4*>(dst + ((size_t)blockIdx.x * 64 + lane) * 4) = d;
+}
+
 }  // namespace
 
 // Grid of the MFMA probe: 4 waves per workgroup, 4 workgroups per CU of 256.
@@ -104,6 +121,11 @@ constexpr int kMfmaGrid = 1024;
 static_assert(kMfmaGrid * 4 == 4096, "the header documents 4096 wavefronts");
 
 hipError_t launch_peak_probe(int kind, const void* src, void* dst, size_t n, hipStream_t s) {
+    if (kind == 4) {
+        hipLaunchKernelGGL(k_probe_mfma_round, dim3((unsigned)n), dim3(64), 0, s,
+                           reinterpret_cast<const unsigned char*>(src), reinterpret_cast<float*>(dst));
+        return hipGetLastError();
+    }
     if (kind == 3) {
         hipLaunchKernelGGL(k_probe_mfma, dim3(kMfmaGrid), dim3(256), 0, s, (int)n, reinterpret_cast<unsigned*>(dst));
         return hipGetLastError();

@@ -195,8 +195,14 @@ int lh_read_selection_sel(const void* ws, int N, int H, int d, int p, int L, int
  * (these three use 16-byte non-temporal accesses; n a multiple of 16, pointers
  * 16-byte aligned); kind 3 runs n rounds (n <= 2^30) of 4 independent bf16
  * 32x32x16 MFMAs in each of 4096 wavefronts (4096 * n * 4 * 32768 flops) and
- * stores a checksum per workgroup of 4 wavefronts (dst: 1024 * 16 bytes).  Device
- * pointers; enqueued on `stream`.  Returns LH_OK, LH_ERR_ARG, or LH_ERR_HIP. */
+ * stores a checksum per workgroup of 4 wavefronts (dst: 1024 * 16 bytes); kind 4
+ * measures the rounding of the attention kernels' matrix instruction: for each
+ * of n trials (n <= 2^20) one v_mfma_f32_16x16x32_f16 on the 3072-byte record
+ * src + 3072 t (lanes 0..63 of fp16 A[8], then fp16 B[8], then fp32 C[4]; lane
+ * l holds A[l % 16][8 (l / 16) + e], B[8 (l / 16) + e][l % 16] and C, D at rows
+ * 4 (l / 16) + r, column l % 16) writes D to dst + 1024 t (lanes 0..63 of fp32
+ * D[4]).  Device pointers; enqueued on `stream`.  Returns LH_OK, LH_ERR_ARG, or
+ * LH_ERR_HIP. */
 int lh_peak_probe(int kind, const void* src, void* dst, size_t n, void* stream);
 
 /* Dense causal attention over all N tokens with the same attention kernels
