@@ -161,7 +161,7 @@ def _exact_fp32_sums(a: np.ndarray, b: np.ndarray) -> bool:
 
 
 def make_block_inputs(N: int, dm: int, H: int, d: int, seed: int = 0, planted: float = 0.0,
-                      with_dy: bool = False, threads: int | None = None) -> dict:
+                      with_dy: bool = False, threads: int | None = None, grid: bool = True) -> dict:
     """Inputs of the attention block, all bf16 bit patterns (uint16).
 
     x [N, dm] = c_t z with z ~ N(0, 1) and the per-token LogNormal(0, 0.5) scale
@@ -172,6 +172,10 @@ def make_block_inputs(N: int, dm: int, H: int, d: int, seed: int = 0, planted: f
     and dy w_o^T are exact in fp32 whatever the order of summation (checked,
     see _exact_fp32_sums), so both sides round the same values to bf16 where
     they enter the layer.
+
+    grid=False draws the same distributions without the grids: each value is
+    the float32 draw rounded to bf16, so the products carry ordinary fp32
+    rounding.
     """
     threads = threads or _threads()
     hd = H * d
@@ -181,6 +185,16 @@ def make_block_inputs(N: int, dm: int, H: int, d: int, seed: int = 0, planted: f
     if planted > 0.0:
         idx = gc.choice(N, size=int(round(planted * N)), replace=False)
         c[idx] *= np.float32(4.0)
+    if not grid:
+        out = {"x": _fill_normal((N, 1, dm), ss_x, c, "bf16", threads).reshape(N, dm),
+               "w_qkv": bf16_bits(_fill_normal((dm, 1, 3 * hd), ss_w, None, "fp32", threads).reshape(dm, 3 * hd)
+                                  / np.float32(np.sqrt(dm))),
+               "w_o": bf16_bits(_fill_normal((hd, 1, dm), ss_o, None, "fp32", threads).reshape(hd, dm)
+                                / np.float32(np.sqrt(hd))),
+               "token_scale": c}
+        if with_dy:
+            out["dy"] = _fill_normal((N, 1, dm), ss_dy, None, "bf16", threads).reshape(N, dm)
+        return out
     a = _on_grid(_fill_normal((N, 1, dm), ss_x, c, "fp32", threads).reshape(N, dm), X_GRID)
     gq, go = w_grid(dm), w_grid(hd)
     b = _on_grid(_fill_normal((dm, 1, 3 * hd), ss_w, None, "fp32", threads).reshape(dm, 3 * hd) / np.sqrt(dm), gq)

@@ -11,7 +11,7 @@ import torch
 
 import oracle
 import synth_inputs as si
-from gpu_util import Run, check_full_rows, check_scores, check_selection, compare, say, to_dev, to_f64
+from gpu_util import Run, check_full_rows, check_scores, check_selection, compare, grad_allow, say, to_dev, to_f64
 
 pytestmark = pytest.mark.gpu
 
@@ -55,15 +55,16 @@ def _check_all(idx, sample):
     for name, key in (("qsub", "Qt"), ("ksub", "Kt"), ("vsub", "Vt")):
         compare(run.sub(name), ref[key], dt, name)
     compare(run.view("lse").cpu().numpy()[:, : run.S], ref["lse"], dt, "lse")
-    compare(run.sub("osub"), ref["Ot"], dt, "osub", cond=b["cO"], d=d)
+    compare(run.sub("osub"), ref["Ot"], dt, "osub")
     compare(run.sub("dosub"), b["dOt"], dt, "dosub")
-    for name, key, ck in (("dqsub", "dQt", "cdQ"), ("dksub", "dKt", "cdK"), ("dvsub", "dVt", "cdV")):
-        compare(run.sub(name), b[key], dt, name, cond=b[ck], d=d)
+    for name, key in (("dqsub", "dQt"), ("dksub", "dKt"), ("dvsub", "dVt")):
+        compare(run.sub(name), b[key], dt, name, allow=grad_allow(b, key))
     sel = (ref["start"], ref["level"])
     rng = np.random.default_rng(w.get("seed", idx))
-    check_full_rows(run.o, ref["Ot"], sel, p, dt, "o", cond_sub=b["cO"], sample=sample, rng=rng)
-    for g, key, sub, ck in zip(run.grads, ("dq", "dk", "dv"), ("dQt", "dKt", "dVt"), ("cdQ", "cdK", "cdV")):
-        check_full_rows(g, b[sub], sel, p, dt, key, divide=True, cond_sub=b[ck], sample=sample, rng=rng)
+    check_full_rows(run.o, ref["Ot"], sel, p, dt, "o", sample=sample, rng=rng)
+    for g, key, sub in zip(run.grads, ("dq", "dk", "dv"), ("dQt", "dKt", "dVt")):
+        check_full_rows(g, b[sub], sel, p, dt, key, divide=True, allow_sub=grad_allow(b, sub), sample=sample,
+                        rng=rng)
     return run
 
 
@@ -108,9 +109,9 @@ def test_workload1_k_covers_all_is_causal_attention():
     run = Run(x, "fp32", w["p"], w["L"], K, backward=True, label="workload1 K=N/p")
     check_selection(run, ref)
     tr = lambda z: np.ascontiguousarray(z.transpose(1, 0, 2))
-    compare(to_f64(run.o), tr(ref["Ot"]), "fp32", "o", cond=tr(b["cO"]), d=w["d"])
-    for g, key, ck in zip(run.grads, ("dQt", "dKt", "dVt"), ("cdQ", "cdK", "cdV")):
-        compare(to_f64(g), tr(b[key]), "fp32", key, cond=tr(b[ck]), d=w["d"])
+    compare(to_f64(run.o), tr(ref["Ot"]), "fp32", "o")
+    for g, key in zip(run.grads, ("dQt", "dKt", "dVt")):
+        compare(to_f64(g), tr(b[key]), "fp32", key, allow=tuple(tr(a) for a in grad_allow(b, key)))
 
 
 @pytest.mark.timeout(600)
