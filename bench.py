@@ -57,8 +57,8 @@ def stage_bytes(w, S, pk=False):
         out["scatter_fwd"] = row + sub32              # write o; read the rows of O~ once
         out["pool_bwd"] = 3 * row + 3 * sub32         # write dq, dk, dv; read their sub-sequence rows once
     elif e == 2:
-        # the attention kernels write the token rows themselves (o; dk, dv and dq, the
-        # two backward kernels running side by side as one stage)
+        # the attention kernels write the token rows themselves (o; dk, dv and dq from
+        # the two roles of the one backward launch)
         out["attn_fwd"] = row
         out["attn_bwd"] = 3 * row
     else:
@@ -71,7 +71,17 @@ def attn_flops(w, S):
     """Algorithmic flops of causal attention on the sub-sequence (per launch)."""
     H, d = w["H"], w["d"]
     unit = S * S * d * H                          # one causal S x S x d product
-    return {"attn_fwd": 2 * unit, "attn_bwd_dkdv": 3 * unit, "attn_bwd_dq": 2 * unit, "attn_bwd": 5 * unit}
+    return {"attn_fwd": 2 * unit, "attn_bwd": 5 * unit}
+
+
+# the kernel each stage launches (one launch per stage and step)
+STAGE_KERNEL = {"pool_score": "k_pool_score", "pool_up": "k_pool_up", "topk": "k_topk", "gather": "k_gather",
+                "attn_fwd": "k_attn_fwd", "scatter_fwd": "k_scatter_fwd", "scatter_bwd": "k_scatter_bwd",
+                "attn_bwd": "k_attn_bwd", "pool_bwd": "k_pool_bwd"}
+# MFMA products each attention launch issues per algorithmic one (split operands:
+# hi*hi + hi*lo + lo*hi; the backward recomputes S and dP in both roles: 7 products
+# for the 5 of the gradient)
+SPLIT_PRODUCTS = {"attn_fwd": 3.0, "attn_bwd": 3.0 * 7.0 / 5.0}
 
 
 def measured_traffic(workload, stage):
@@ -393,16 +403,31 @@ def main():
     f_mfma = fl.get(dominant, 0) / (dom_ms / 1e3) / 1e12 / BF16_PEAK_TFLOPS
     if dominant in sb and f_hbm >= f_mfma:
         ach = sb[dominant] / (dom_ms / 1e3) / 1e9
-        roof = {"bound": "hbm", "kernel": dominant, "achieved": round(ach, 1), "peak": HBM_PEAK_GBS,
+        roof = {"bound": "hbm", "kernel": STAGE_KERNEL.get(dominant, dominant), "stage": dominant,
+                "achieved": round(ach, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4),
                 "traffic": measured_traffic(prof_name, dominant),
                 "algorithmic_bytes_per_launch": sb[dominant], "avg_launch_ms": round(dom_ms, 4)}
     else:
         ach = fl.get(dominant, 0) / (dom_ms / 1e3) / 1e12
-        roof = {"bound": "mfma", "kernel": dominant, "achieved": round(ach, 2), "peak": BF16_PEAK_TFLOPS,
+        roof = {"bound": "mfma", "kernel": STAGE_KERNEL.get(dominant, dominant), "stage": dominant,
+                "achieved": round(ach, 2), "peak": BF16_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(ach / BF16_PEAK_TFLOPS, 4),
                 "traffic": measured_traffic(prof_name, dominant), "avg_launch_ms": round(dom_ms, 4)}
 
+    # the attention kernels against bf16 MFMA peak, in algorithmic flops (S^2 d per causal
+    # product) and in the MFMA work they issue; with every product split in three,
+    # the algorithmic fraction can reach at most 1/3 (forward) and 5/21 (backward)
+    mfma = {}
+    for name in ("attn_fwd", "attn_bwd"):
+        if name in stages and name in fl:
+            t = stages[name][0] / stages[name][1] / 1e3
+            mfma[STAGE_KERNEL[name]] = {
+                "algorithmic_TFLOPs": round(fl[name] / t / 1e12, 2),
+                "frac_bf16_peak": round(fl[name] / t / 1e12 / BF16_PEAK_TFLOPS, 4),
+                "issued_TFLOPs": round(fl[name] * SPLIT_PRODUCTS[name] / t / 1e12, 2),
+                "ceiling_frac_of_split": round(1.0 / SPLIT_PRODUCTS[name], 4)}
+    roof["attention_mfma"] = mfma
     roof["achievable"] = achievable_peaks(lh, torch, stream)
     log(f"achievable on this GPU: {roof['achievable']}")
 
@@ -413,22 +438,36 @@ def main():
         od = torch.empty_like(q)
         lse = torch.empty((H, N), dtype=torch.float32, device="cuda")
         dg = tuple(torch.empty_like(q) for _ in range(3))
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
-        ev[0].record(stream)
-        lh.dense_forward(q, k, v, ws=dws, out=od, lse=lse, stream=stream)
-        ev[1].record(stream)
+        lh.dense_forward(q, k, v, ws=dws, out=od, lse=lse, stream=stream)          # warm-up
         lh.dense_backward(q, k, v, od, lse, do, dws, grads=dg, stream=stream)
-        ev[2].record(stream)
         torch.cuda.synchronize()
-        f_ms = ev[0].elapsed_time(ev[1])
-        fb_ms = ev[0].elapsed_time(ev[2])
+        reps = 3
+        f_all, b_all = [], []
+        for _ in range(reps):
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+            ev[0].record(stream)
+            lh.dense_forward(q, k, v, ws=dws, out=od, lse=lse, stream=stream)
+            ev[1].record(stream)
+            lh.dense_backward(q, k, v, od, lse, do, dws, grads=dg, stream=stream)
+            ev[2].record(stream)
+            torch.cuda.synchronize()
+            f_all.append(ev[0].elapsed_time(ev[1]))
+            b_all.append(ev[1].elapsed_time(ev[2]))
+        f_ms, bw_ms = sorted(f_all)[reps // 2], sorted(b_all)[reps // 2]
+        fb_ms = f_ms + bw_ms
         lh_f = sum(stages[s][0] / stages[s][1] for s in stages
                    if s in ("pool_score", "pool_up", "topk", "gather", "sub_prep", "attn_fwd", "scatter_fwd"))
+        unit = N * N * d * H                       # one causal N x N x d product
         dense = {"fwd_ms": round(f_ms, 2), "fwd_bwd_ms": round(fb_ms, 2),
                  "speedup_fwd": round(f_ms / lh_f, 1), "speedup_fwd_bwd": round(fb_ms / ms_per_step, 1),
-                 "reps": 1}
+                 "reps": reps, "fwd_ms_each": [round(t, 1) for t in f_all],
+                 "bwd_ms_each": [round(t, 1) for t in b_all],
+                 "fwd_TFLOPs": round(2 * unit / (f_ms / 1e3) / 1e12, 1),
+                 "bwd_TFLOPs": round(5 * unit / (bw_ms / 1e3) / 1e12, 1),
+                 "fwd_frac_bf16_peak": round(2 * unit / (f_ms / 1e3) / 1e12 / BF16_PEAK_TFLOPS, 3),
+                 "bwd_frac_bf16_peak": round(5 * unit / (bw_ms / 1e3) / 1e12 / BF16_PEAK_TFLOPS, 3)}
         del dws, od, lse, dg
-        log(f"dense: fwd {f_ms:.1f} ms, fwd+bwd {fb_ms:.1f} ms")
+        log(f"dense: fwd {f_ms:.1f} ms, fwd+bwd {fb_ms:.1f} ms (median of {reps})")
 
     cpu = None
     if not args.no_cpu:

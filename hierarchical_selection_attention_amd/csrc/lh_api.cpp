@@ -148,46 +148,10 @@ hipEvent_t take_event() {
 
 const char* kStageNames[ST_COUNT] = {
     "pool_score", "pool_up", "topk", "gather", "sub_prep", "attn_fwd", "scatter_fwd",
-    "zero_acc", "scatter_bwd", "bwd_prep", "attn_bwd_dkdv", "attn_bwd_dq", "pool_bwd", "attn_bwd",
+    "zero_acc", "scatter_bwd", "bwd_prep", "attn_bwd", "pool_bwd",
     "proj_qkv", "proj_out", "proj_out_dx", "proj_out_dw", "proj_qkv_dx", "proj_qkv_dw"};
 
 }  // namespace
-
-// Second stream per device for the backward: dQ runs beside dK/dV (both write
-// token rows at their ends, so one kernel's writes overlap the other's MFMA
-// work).  Created on first use, default priority, kept until the process ends.
-struct ForkState {
-    hipStream_t s2 = nullptr;
-    hipEvent_t fork = nullptr, join = nullptr;
-};
-constexpr int kMaxForkDevices = 64;
-std::mutex g_fork_mu;
-ForkState g_fork[kMaxForkDevices];
-
-// Enqueues dQ on the device's second stream and dK/dV on `s`, with `s`
-// waiting for both before anything later runs.  Calls are serialised so the
-// two events always pair the right launches.
-hipError_t attn_bwd_two_streams(const AttnArgs& a, hipStream_t s) {
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxForkDevices) return hipErrorInvalidDevice;
-    std::lock_guard<std::mutex> g(g_fork_mu);
-    ForkState& f = g_fork[dev];
-    if (!f.s2) {
-        if (hipStreamCreateWithFlags(&f.s2, hipStreamNonBlocking) != hipSuccess ||
-            hipEventCreateWithFlags(&f.fork, hipEventDisableTiming) != hipSuccess ||
-            hipEventCreateWithFlags(&f.join, hipEventDisableTiming) != hipSuccess) {
-            f = ForkState{};
-            return hipErrorOutOfMemory;
-        }
-    }
-    hipError_t e = hipEventRecord(f.fork, s);
-    if (e == hipSuccess) e = hipStreamWaitEvent(f.s2, f.fork, 0);
-    if (e == hipSuccess) e = launch_attn_bwd(a, f.s2, 1);
-    if (e == hipSuccess) e = launch_attn_bwd(a, s, 0);
-    if (e == hipSuccess) e = hipEventRecord(f.join, f.s2);
-    if (e == hipSuccess) e = hipStreamWaitEvent(s, f.join, 0);
-    return e;
-}
 
 StageMark stage_open(hipStream_t s) {
     StageMark m;
@@ -410,13 +374,8 @@ int backward_strided(const void* dout, void* dq, void* dk, void* dv, int N, int 
         a.p = p;
         a.tok_ld = grad_ld;
     }
-    if (P.rowcopy) {
-        // dK/dV and dQ side by side: each kernel's token writes overlap the other's MFMA work
-        LH_TRY(stage(ST_ATTN_BWD, s, [&] { return attn_bwd_two_streams(a, s); }));
-    } else {
-        LH_TRY(stage(ST_ATTN_BWD_DKDV, s, [&] { return launch_attn_bwd(a, s, 0); }));
-        if (dtype == BF16) LH_TRY(stage(ST_ATTN_BWD_DQ, s, [&] { return launch_attn_bwd(a, s, 1); }));
-    }
+    // dK/dV and dQ in one launch: each role's token writes overlap the other's MFMA work
+    LH_TRY(stage(ST_ATTN_BWD, s, [&] { return launch_attn_bwd(a, s); }));
     if (!P.rowcopy) LH_TRY(stage(ST_POOL_BWD, s, [&] {
         if (P.pk) {
             // a token sums dX~ / p^level over the entries that cover it
@@ -661,8 +620,7 @@ int lh_dense_attn_bwd(const void* q, const void* k, const void* v, const void* o
     a.dq_b = reinterpret_cast<uint16_t*>(dq);
     a.dk_b = reinterpret_cast<uint16_t*>(dk);
     a.dv_b = reinterpret_cast<uint16_t*>(dv);
-    LH_TRY(launch_attn_bwd(a, s, 0));
-    LH_TRY(launch_attn_bwd(a, s, 1));
+    LH_TRY(launch_attn_bwd(a, s));
     return LH_OK;
 }
 

@@ -532,31 +532,28 @@ __global__ void __launch_bounds__(256) k_attn_fwd(AttnK a) {
 }
 
 // ------------------------------------------------------- backward: dK, dV
-// Key-stationary: wave w owns keys k0..k0+15 (lane column = key); the query
-// blocks at or after the workgroup's keys stream through LDS.
+// Key-stationary: wave w owns keys k0..k0+15 (lane column = key) of key tile
+// kt of head h; the query blocks at or after the workgroup's keys stream
+// through LDS.  LDS, one buffer each: q and dO rows (read by the score phase),
+// q^T and dO^T (read by the gradient phase); each group is refilled as soon as
+// every wave is past its phase: 64 KiB at d = 128 with split operands.
+template <int D, bool SPLIT>
+struct DkdvLds {
+    static constexpr int ROWS = (SPLIT ? 2 : 1) * 2 * Tiles<D>::ROW;
+    static constexpr int ELEMS = ROWS + (SPLIT ? 2 : 1) * 2 * Tiles<D>::TR;
+};
 template <int D, bool SPLIT, bool OUT_BF16>
-__global__ void __launch_bounds__(256) k_attn_dkdv(AttnK a) {
+__device__ __forceinline__ void dkdv_body(const AttnK& a, uint16_t* __restrict__ sm, float* __restrict__ qstat, int h,
+                                          int kt) {
     using T = Tiles<D>;
     constexpr int NS = D / 32, NV = D / 16;
     constexpr int NA = SPLIT ? 2 : 1;
-    // LDS, one buffer each: q and dO rows (read by the score phase), q^T (bf16)
-    // and dO^T (read by the gradient phase); each group is refilled as soon as
-    // every wave is past its phase: 64 KiB at d = 128 with split operands
-    constexpr int ROWS = NA * 2 * T::ROW;
-    __shared__ __attribute__((aligned(16))) uint16_t sm[ROWS + NA * 2 * T::TR];
-    // per-query lse2 and D of the block, copied with the rows: the score phase
-    // then waits on no global load issued after the transposed-tile copies
-    __shared__ __attribute__((aligned(16))) float qstat[2 * kBN];
+    constexpr int ROWS = DkdvLds<D, SPLIT>::ROWS;
+    // qstat: per-query lse2 and D of the block, copied with the rows: the score
+    // phase then waits on no global load issued after the transposed-tile copies
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int lq = lane & 15, lg = lane >> 4;
     const int64_t Sp = a.Sp;
-    const int nT = (int)(Sp / 64);
-    int h, kt;
-    // The last key tiles see the fewest queries.  When the kernel writes token rows,
-    // they go first: their writes start soon, while the dQ kernel beside this one
-    // works through its longest tiles, so HBM is not left idle at the start.
-    // Without token writes the kernel is compute-bound and the longest go first.
-    work_item(nT, gridDim.x / nT, a.dk_tok != nullptr, h, kt);
     const int64_t k0 = (int64_t)kt * 64 + wave * 16;
     const int64_t mykey = k0 + lq;
     const int64_t hb = (int64_t)h * Sp * D;
@@ -739,25 +736,26 @@ __global__ void __launch_bounds__(256) k_attn_dkdv(AttnK a) {
 }
 
 // ---------------------------------------------------------- backward: dQ
-// Query-stationary: wave w owns queries q0..q0+15 and the key blocks up to the
-// diagonal stream through LDS.  Each query's dS row carries a running power of
-// two (column_scale) before the fp16 split; it is undone at the end.
+// Query-stationary: wave w owns queries q0..q0+15 of query tile qt of head h,
+// and the key blocks up to the diagonal stream through LDS.  Each query's dS
+// row carries a running power of two (column_scale) before the fp16 split; it
+// is undone at the end.  LDS: k and v rows (read by the score phase) and k^T
+// (read by the dQ phase), one buffer each, refilled by direct copies while the
+// other one is in use: 48 KiB at d = 128 with split operands.
+template <int D, bool SPLIT>
+struct DqLds {
+    static constexpr int ROWS = (SPLIT ? 2 : 1) * 2 * Tiles<D>::ROW;
+    static constexpr int ELEMS = ROWS + (SPLIT ? 2 : 1) * Tiles<D>::TR;
+};
 template <int D, bool SPLIT, bool OUT_BF16>
-__global__ void __launch_bounds__(256) k_attn_dq(AttnK a) {
+__device__ __forceinline__ void dq_body(const AttnK& a, uint16_t* __restrict__ sm, int h, int qt) {
     using T = Tiles<D>;
     constexpr int NS = D / 32, NV = D / 16;
     constexpr int NA = SPLIT ? 2 : 1;
-    // LDS: k and v rows (read by the score phase) and k^T (read by the dQ
-    // phase), one buffer each, refilled by direct copies while the other one is
-    // in use: 48 KiB at d = 128 with split operands
-    constexpr int ROWS = NA * 2 * T::ROW;
-    __shared__ __attribute__((aligned(16))) uint16_t sm[ROWS + NA * T::TR];
+    constexpr int ROWS = DqLds<D, SPLIT>::ROWS;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int lq = lane & 15, lg = lane >> 4;
     const int64_t Sp = a.Sp;
-    const int nT = (int)(Sp / 64);
-    int h, qt;
-    work_item(nT, gridDim.x / nT, true, h, qt);
     const int64_t q0 = (int64_t)qt * 64 + wave * 16;
     const int64_t myq = q0 + lq;
     const int64_t hb = (int64_t)h * Sp * D;
@@ -929,6 +927,45 @@ __global__ void __launch_bounds__(256) k_attn_dq(AttnK a) {
     }
 }
 
+// ------------------------------------------------------- backward: launch
+// One launch runs both gradient roles: workgroup i takes role i & 1 (0: dK/dV
+// of a key tile, 1: dQ of a query tile) in the order a dispatch sees them, so
+// each role's token writes overlap the other role's MFMA work.  When H is a
+// multiple of 8, both roles of a head run on the XCD of that head (workgroup
+// i runs on XCD i % 8), where its operands sit in L2.  Tile order within a
+// role: dQ takes its longest query tiles first; dK/dV, when it writes token
+// rows, its shortest key tiles first (their writes start early, beside dQ's
+// long tiles), and otherwise its longest first.
+__device__ __forceinline__ void bwd_item(int nT, int H, bool dkdv_short_first, int& role, int& h, int& tile) {
+    const int i = blockIdx.x;
+    int j;
+    if (H % 8 == 0) {
+        const int x = i % 8, q = i / 8;
+        role = q & 1;
+        const int jj = q >> 1;
+        h = x + 8 * (jj / nT);
+        j = jj % nT;
+    } else {
+        role = i & 1;
+        const int jj = i >> 1;
+        h = jj / nT;
+        j = jj % nT;
+    }
+    tile = (role == 1 || dkdv_short_first) ? nT - 1 - j : j;
+}
+
+template <int D, bool SPLIT, bool OUT_BF16>
+__global__ void __launch_bounds__(256) k_attn_bwd(AttnK a) {
+    constexpr int E1 = DkdvLds<D, SPLIT>::ELEMS, E2 = DqLds<D, SPLIT>::ELEMS;
+    __shared__ __attribute__((aligned(16))) uint16_t sm[E1 > E2 ? E1 : E2];
+    __shared__ __attribute__((aligned(16))) float qstat[2 * kBN];
+    const int nT = (int)(a.Sp / 64);
+    int role, h, tile;
+    bwd_item(nT, (int)(gridDim.x / (2 * nT)), a.dk_tok != nullptr, role, h, tile);
+    if (role == 0) dkdv_body<D, SPLIT, OUT_BF16>(a, sm, qstat, h, tile);
+    else dq_body<D, SPLIT, OUT_BF16>(a, sm, h, tile);
+}
+
 // ------------------------------------------------------------- fp32 path
 // One wavefront per row; lane holds E = D/64 consecutive elements; double
 // arithmetic throughout.
@@ -1077,24 +1114,17 @@ hipError_t launch_attn_fwd(const AttnArgs& x, hipStream_t s) {
     return hipGetLastError();
 }
 
-hipError_t launch_attn_bwd(const AttnArgs& x, hipStream_t s, int part) {
+hipError_t launch_attn_bwd(const AttnArgs& x, hipStream_t s) {
     AttnK a = to_k(x);
     if (x.fp32_path) {
-        if (part != 0) return hipSuccess;   // one kernel does both
         dim3 grid((unsigned)((x.rows + 3) / 4), (unsigned)x.H, 2);
         if (x.d == 128) hipLaunchKernelGGL(k_attn_bwd_f32<128>, grid, dim3(256), 0, s, a);
         else hipLaunchKernelGGL(k_attn_bwd_f32<64>, grid, dim3(256), 0, s, a);
         return hipGetLastError();
     }
-    dim3 grid((unsigned)(x.Sp / 64 * x.H));
-    const bool ob = x.dq_b != nullptr;
-    if (part == 0) {
-        if (ob) LH_ATTN_DISPATCH(k_attn_dkdv, grid, , true);
-        else LH_ATTN_DISPATCH(k_attn_dkdv, grid, , false);
-    } else {
-        if (ob) LH_ATTN_DISPATCH(k_attn_dq, grid, , true);
-        else LH_ATTN_DISPATCH(k_attn_dq, grid, , false);
-    }
+    dim3 grid((unsigned)(2 * (x.Sp / 64) * x.H));
+    if (x.dq_b != nullptr) LH_ATTN_DISPATCH(k_attn_bwd, grid, , true);
+    else LH_ATTN_DISPATCH(k_attn_bwd, grid, , false);
     return hipGetLastError();
 }
 

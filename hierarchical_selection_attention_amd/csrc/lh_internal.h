@@ -20,8 +20,7 @@ enum Dtype { BF16 = 0, FP32 = 1 };
 // Stage ids for event timing (order of launch).
 enum Stage {
     ST_POOL_SCORE = 0, ST_POOL_UP, ST_TOPK, ST_GATHER, ST_SUB_PREP, ST_ATTN_FWD,
-    ST_SCATTER_FWD, ST_ZERO_ACC, ST_SCATTER_BWD, ST_BWD_PREP, ST_ATTN_BWD_DKDV,
-    ST_ATTN_BWD_DQ, ST_POOL_BWD, ST_ATTN_BWD,
+    ST_SCATTER_FWD, ST_ZERO_ACC, ST_SCATTER_BWD, ST_BWD_PREP, ST_ATTN_BWD, ST_POOL_BWD,
     // projections around the layer (lh_block_*)
     ST_PROJ_QKV, ST_PROJ_OUT, ST_PROJ_OUT_DX, ST_PROJ_OUT_DW, ST_PROJ_QKV_DX, ST_PROJ_QKV_DW, ST_COUNT
 };
@@ -150,7 +149,8 @@ struct AttnArgs {
     const float *qf, *kf, *vf, *dof;   // fp32 path operands [H][Sp][d]
 };
 hipError_t launch_attn_fwd(const AttnArgs& a, hipStream_t s);
-hipError_t launch_attn_bwd(const AttnArgs& a, hipStream_t s, int part);   // part 0: dK/dV, 1: dQ
+// dK/dV and dQ in one launch (bf16: the two roles of k_attn_bwd; fp32: one kernel)
+hipError_t launch_attn_bwd(const AttnArgs& a, hipStream_t s);
 
 struct SplitSpec {
     const void* src;

@@ -61,3 +61,38 @@ def test_peak_probes_move_the_right_bytes():
     lh.peak_probe(3, None, chk, 16)
     torch.cuda.synchronize()
     assert torch.equal(chk, chk[:1].expand_as(chk))
+
+
+def test_concurrent_layers_on_two_user_streams():
+    """Two independent forward + backward passes, enqueued interleaved on two
+    caller streams with two workspaces: each matches the oracle.  The library
+    keeps no per-device stream or event state; every call runs on its own
+    stream and reads and writes only its own workspace."""
+    import hierarchical_selection_attention_amd as lh
+    from gpu_util import check_full_rows, grad_allow
+    cases = [(4096, 4, 128, 4, 4, 8, 81), (2048, 8, 128, 4, 3, 5, 82)]
+    say("case two user streams: " + ", ".join(f"N={c[0]} H={c[1]}" for c in cases))
+    runs = []
+    for N, H, d, p, L, K, seed in cases:
+        x = si.make_inputs(N, H, d, "bf16", seed=seed, with_dout=True, threads=8)
+        t = {n: to_dev(x[n], "bf16") for n in ("q", "k", "v", "dout")}
+        ws = lh.alloc_workspace(N, H, d, p, L, K, 0)
+        o = torch.empty_like(t["q"])
+        g = tuple(torch.empty_like(t["q"]) for _ in range(3))
+        runs.append((x, t, ws, o, g, (N, H, d, p, L, K)))
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]          # default priority
+    for (x, t, ws, o, g, (N, H, d, p, L, K)), s in zip(runs, streams):
+        lh.forward(t["q"], t["k"], t["v"], p, L, K, ws=ws, out=o, stream=s)
+    for (x, t, ws, o, g, (N, H, d, p, L, K)), s in zip(runs, streams):
+        lh.backward(t["dout"], p, L, K, ws, grads=g, stream=s)
+    torch.cuda.synchronize()
+    for x, t, ws, o, g, (N, H, d, p, L, K) in runs:
+        ref = oracle.forward(x["q"], x["k"], x["v"], p, L, K, "bf16", want=("sel", "ot"))
+        b = oracle.backward(x["q"], x["k"], x["v"], x["dout"], p, L, K, (ref["start"], ref["level"]), "bf16",
+                            want=("sub", "cond"))
+        sel = (ref["start"], ref["level"])
+        check_full_rows(o, ref["Ot"], sel, p, "bf16", f"two streams o (N={N})")
+        for gg, key in zip(g, ("dQt", "dKt", "dVt")):
+            check_full_rows(gg, b[key], sel, p, "bf16", f"two streams d{key[1].lower()} (N={N})", divide=True,
+                            allow_sub=grad_allow(b, key))
