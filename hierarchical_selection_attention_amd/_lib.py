@@ -16,6 +16,7 @@ LIB_PATH = os.path.join(_HERE, "liblighthouse.so")
 LH_OK, LH_ERR_ARG, LH_ERR_SHAPE, LH_ERR_DTYPE, LH_ERR_WORKSPACE, LH_ERR_HIP, LH_ERR_GEMM = 0, -1, -2, -3, -4, -5, -6
 LH_BF16, LH_FP32 = 0, 1
 LH_SCATTER_FP_ATOMIC, LH_SCATTER_INT_ATOMIC = 0, 1
+LH_SCATTER_DETERMINISTIC = LH_SCATTER_INT_ATOMIC
 LH_SCORE_QK, LH_SCORE_K, LH_SCORE_Q, LH_SCORE_QK_PRODUCT = 0, 1, 2, 3
 LH_SELECT_PARTITION, LH_SELECT_PARENT_KEPT = 0, 1
 VIEWS = {"scores": 0, "sel_start": 1, "sel_level": 2, "qsub": 3, "ksub": 4, "vsub": 5, "osub": 6,

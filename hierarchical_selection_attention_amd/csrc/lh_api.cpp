@@ -105,7 +105,8 @@ int make_plan(int N, int H, int d, int p, int L, int K, int dtype, Plan* P, int 
     pl.off_os = take(sizeof(float) * HSd);
     pl.off_lse = take(sizeof(float) * (size_t)H * pl.Sp);
     pl.off_lse2 = take(sizeof(float) * (size_t)H * pl.Sp);
-    pl.off_acc = take(8 * HSd);
+    pl.off_acc = take(sizeof(float) * HSd);
+    pl.off_part = take(m < L - 1 ? sizeof(float) * (size_t)H * (size_t)(N / pl.tok) * d : 0);
     pl.off_dos = take(sizeof(float) * HSd);
     pl.off_doh = take(h16); pl.off_dol = take(h16);
     pl.off_doTh = take(h16); pl.off_doTl = take(h16);
@@ -338,9 +339,9 @@ int backward_strided(const void* dout, void* dq, void* dk, void* dv, int N, int 
     const size_t HSd = (size_t)H * P.Sp * d;
     unsigned int* hmax = reinterpret_cast<unsigned int*>(w + P.off_hmax);
     unsigned int* hmax_b = hmax + 4 * (size_t)H;
-    // fp32 accumulators use the first half of the segment, int64 ones all of it
-    const size_t acc_bytes = (scatter_mode == LH_SCATTER_INT_ATOMIC && !P.pk ? 8 : 4) * HSd;
-    LH_TRY(stage(ST_ZERO_ACC, s, [&] { return launch_fill_zero(w + P.off_acc, acc_bytes, s); }));
+    // the fp32 atomics add into cleared rows; the deterministic mode stores every row
+    if (scatter_mode == LH_SCATTER_FP_ATOMIC || P.pk)
+        LH_TRY(stage(ST_ZERO_ACC, s, [&] { return launch_fill_zero(w + P.off_acc, sizeof(float) * HSd, s); }));
     // parent kept: each entry's sum of dO is taken by one wavefront (no atomics), in the
     // fp32 layout of the fp-atomic accumulators
     const int acc_mode = P.pk ? LH_SCATTER_FP_ATOMIC : scatter_mode;
@@ -350,6 +351,10 @@ int backward_strided(const void* dout, void* dq, void* dk, void* dv, int N, int 
     LH_TRY(stage(ST_BWD_PREP, s, [&] {
         RowPrepSpec rp{};
         rp.acc = w + P.off_acc; rp.o = w + P.off_os;
+        rp.part = f32(w, P.off_part);
+        rp.start = reinterpret_cast<const int32_t*>(w + P.off_start);
+        rp.level = reinterpret_cast<const uint8_t*>(w + P.off_level);
+        rp.tok = P.tok; rp.nblk = P.N / P.tok; rp.m = P.m; rp.p = P.p;
         rp.dos = f32(w, P.off_dos); rp.D = f32(w, P.off_D);
         rp.S = P.S; rp.Sp = P.Sp; rp.H = H; rp.d = d; rp.mode = acc_mode; rp.dense = 0;
         float* rowmax_b = f32(w, P.off_rowmax) + 3 * (size_t)H * P.Sp;

@@ -79,7 +79,8 @@ struct Plan {
     size_t off_hscale;            // fp32 [H][4]: per-head multipliers of the fp16 copies
     size_t off_os;                // fp32 [H][Sp][d]
     size_t off_lse, off_lse2;     // fp32 [H][Sp]
-    size_t off_acc;               // 8 bytes x [H][Sp][d]: fp32 or int64 accumulators of dO~
+    size_t off_acc;               // fp32 [H][Sp][d]: sums of dO over each entry (dO~)
+    size_t off_part;              // fp32 [H][N / tok][d]: deterministic mode's per-block partial sums
     size_t off_dos;               // fp32 [H][Sp][d]
     size_t off_doh, off_dol, off_doTh, off_doTl;   // fp16 copies of dO~
     size_t off_D;                 // fp32 [H][Sp]
@@ -163,6 +164,12 @@ struct SplitSpec {
 };
 struct RowPrepSpec {
     const void *acc, *dout, *o;
+    // deterministic mode: entries above level m are summed from `part` (start, level: [H][S])
+    const float* part;
+    const int32_t* start;
+    const uint8_t* level;
+    int64_t tok, nblk;            // tokens per block, blocks per head (N / tok)
+    int m, p;
     int64_t ld, hs;
     float *dos, *D;
     const float* lse_in;       // dense: natural-log lse [H][N] -> lse2 (base 2, minus the backward's offset)

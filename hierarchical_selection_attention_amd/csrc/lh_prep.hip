@@ -165,11 +165,18 @@ __global__ void __launch_bounds__(256) k_split(SplitArgs a) {
 }
 
 // ---------------------------------------------------------- backward rows
-// Per sub-sequence row: finish dO~ (fp32 or 64-bit fixed-point accumulator)
-// and D_i = <dO~_i, O~_i> in double; for the dense path also the base-2 lse
-// minus the backward kernels' offset 14 (their weights are then P * 2^14).
+// Per sub-sequence row: finish dO~ and D_i = <dO~_i, O~_i> in double; for the
+// dense path also the base-2 lse minus the backward kernels' offset 14 (their
+// weights are then P * 2^14).  dO~ of an entry is its row of `acc`, except in
+// the deterministic mode for entries above level m: those are the sum, in
+// block order and in double, of the entry's per-block partial sums.
 struct RowPrepArgs {
-    const void* acc;       // [H][Sp][d] fp32 (mode 0) or int64 (mode 1); unused when dense
+    const void* acc;       // fp32 [H][Sp][d]; unused when dense
+    const float* part;     // mode 1: fp32 [H][N / tok][d]
+    const int32_t* start;  // [H][S]
+    const uint8_t* level;  // [H][S]
+    int64_t tok, nblk;
+    int m, p;
     const void* dout;      // dense: bf16 rows with strides ld/hs
     const void* o;         // fp32 [H][Sp][d] attention output
     int64_t ld, hs;        // dense strides of dout
@@ -199,12 +206,25 @@ __global__ void __launch_bounds__(256) k_row_prep(RowPrepArgs a) {
             load8f(reinterpret_cast<const float*>(a.o), r * d + c * 8, o);
         } else {
             const int64_t el = r * d + c * 8;
-            if (a.mode == 0) {
-                load8f(reinterpret_cast<const float*>(a.acc), el, x);
-            } else {
-                const long long* p = reinterpret_cast<const long long*>(a.acc) + el;
+            const int lv = a.mode == 1 ? (int)a.level[h * a.S + i] : 0;
+            if (lv > a.m) {
+                // p^(lv - m) blocks of tok tokens, from the entry's first one
+                const int64_t b0 = a.start[h * a.S + i] / a.tok;
+                int64_t nb = 1;
+                for (int z = a.m; z < lv; ++z) nb *= a.p;
+                double acc8[8];
 #pragma unroll
-                for (int e = 0; e < 8; ++e) x[e] = (float)((double)p[e] * (1.0 / 4294967296.0));
+                for (int e = 0; e < 8; ++e) acc8[e] = 0.0;
+                for (int64_t b = 0; b < nb; ++b) {
+                    float y[8];
+                    load8f(a.part, (h * a.nblk + b0 + b) * d + c * 8, y);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) acc8[e] += (double)y[e];
+                }
+#pragma unroll
+                for (int e = 0; e < 8; ++e) x[e] = (float)acc8[e];
+            } else {
+                load8f(reinterpret_cast<const float*>(a.acc), el, x);
             }
             load8f(reinterpret_cast<const float*>(a.o), el, o);
         }
@@ -288,6 +308,8 @@ hipError_t launch_head_max(const float* rowmax, unsigned int* const* out, int T,
 hipError_t launch_row_prep(const RowPrepSpec& sp, hipStream_t s) {
     RowPrepArgs a{};
     a.acc = sp.acc; a.dout = sp.dout; a.o = sp.o; a.ld = sp.ld; a.hs = sp.hs;
+    a.part = sp.part; a.start = sp.start; a.level = sp.level; a.tok = sp.tok > 0 ? sp.tok : 1;
+    a.m = sp.m; a.p = sp.p; a.nblk = sp.nblk;
     a.dos = sp.dos; a.D = sp.D;
     a.lse_in = sp.lse_in; a.lse2 = sp.lse2; a.rowmax = sp.rowmax;
     a.S = sp.S; a.Sp = sp.Sp; a.H = sp.H; a.d = sp.d; a.mode = sp.mode; a.dense = sp.dense;

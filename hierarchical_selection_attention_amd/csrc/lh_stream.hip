@@ -507,44 +507,35 @@ __global__ void __launch_bounds__(256) k_scatter_fwd(ScatterArgs a) {
 // Adjoint of the scatter: dO~[h][i] = sum over the tokens of entry i of dO.
 // A thread owns one block of p^m tokens (the pooling chunk) for one
 // (head, 8-element chunk) and sums dO over each entry in token order in fp32.
-// Entries at levels <= m lie inside one block and are stored directly; only
-// coarser entries span blocks, and their partial sums are added atomically:
-// fp32 atomics (mode 0) or exact 64-bit fixed-point integer atomics with
-// scale 2^32 (mode 1, independent of the order of the additions).
+// Entries at levels <= m lie inside one block and are stored directly (fp32,
+// both modes).  Only coarser entries span blocks; such an entry covers each
+// of its blocks whole, so a block holds at most one partial sum of one:
+//   mode 0: the partial is added to the entry's row with fp32 atomics;
+//   mode 1 (deterministic): the partial is stored, without atomics, to the
+//     block's row of `part`, and the row preparation adds an entry's partials
+//     in block order (the same bits on every run, over the whole fp32 range).
 struct ScatterBwdArgs {
     const int32_t* start;
     const void* dout;     // dtype [N][H][d]
-    void* acc;            // fp32 or int64 [H][Sp][d]
+    float* acc;           // fp32 [H][Sp][d]
+    float* part;          // mode 1: fp32 [H][N / tok][d] partial sums of entries above level m
     int64_t N, S, Sp, tok;
     int H, HG;
 };
-
-__device__ __forceinline__ long long to_fixed(float x) {
-    return (long long)__builtin_rint((double)x * 4294967296.0);
-}
 
 template <int DT, int G, int MODE>
 __device__ __forceinline__ void flush_entry(const ScatterBwdArgs& a, int h, int c, int64_t slot, bool whole,
                                             const float (&s)[8]) {
     constexpr int d = G * 8;
     const int64_t el = ((int64_t)h * a.Sp + slot) * d + c * 8;
-    if constexpr (MODE == 0) {
-        float* p = reinterpret_cast<float*>(a.acc) + el;
-        if (whole) {
-            store8f(reinterpret_cast<float*>(a.acc), el, s);
-        } else {
+    if (whole) {
+        store8f(a.acc, el, s);
+    } else if constexpr (MODE == 0) {
+        float* p = a.acc + el;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) unsafeAtomicAdd(p + e, s[e]);
-        }
+        for (int e = 0; e < 8; ++e) unsafeAtomicAdd(p + e, s[e]);
     } else {
-        unsigned long long* p = reinterpret_cast<unsigned long long*>(a.acc) + el;
-        if (whole) {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) p[e] = (unsigned long long)to_fixed(s[e]);
-        } else {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) atomicAdd(p + e, (unsigned long long)to_fixed(s[e]));
-        }
+        store8f(a.part, ((int64_t)h * (a.N / a.tok) + blockIdx.x) * d + c * 8, s);
     }
 }
 
@@ -979,7 +970,8 @@ hipError_t launch_scatter_bwd(const Plan& P, const void* dout, int mode, char* w
     ScatterBwdArgs a{};
     a.start = reinterpret_cast<const int32_t*>(ws + P.off_start);
     a.dout = dout;
-    a.acc = ws + P.off_acc;
+    a.acc = reinterpret_cast<float*>(ws + P.off_acc);
+    a.part = reinterpret_cast<float*>(ws + P.off_part);
     a.N = P.N; a.S = P.S; a.Sp = P.Sp; a.H = P.H; a.tok = P.tok;
     const int G = P.d / 8;
     a.HG = head_group(P.H, G);

@@ -62,12 +62,23 @@ typedef enum {
 
 typedef enum { LH_BF16 = 0, LH_FP32 = 1 } lh_dtype;
 
-/* How the adjoint of the scatter sums dO over the tokens of an entry when a
- * block of tokens is split over several workgroups (Sec. 1 contributions and
- * the P4 summary: fp-atomic by default, a deterministic int-atomic variant). */
+/* How the adjoint of the scatter sums dO over the tokens of an entry when the
+ * entry spans several workgroups.  "Lighthouse Attention Technique" (closing
+ * paragraph) describes an fp-atomic default and a deterministic int-atomic
+ * variant kept for reproducibility.  Here an entry at pyramid level <= m (the
+ * level one workgroup pools, p^m <= 256 tokens) is summed by one thread in
+ * token order in both modes.  A coarser entry is summed per block of p^m
+ * tokens, and the block sums are combined:
+ *   LH_SCATTER_FP_ATOMIC: with fp32 atomic adds (the order, and so the last
+ *     bits, can differ between runs);
+ *   LH_SCATTER_INT_ATOMIC (= LH_SCATTER_DETERMINISTIC): each block stores its
+ *     sum, and the sums are added in block order in double.  The bits are the
+ *     same on every run.  Unlike fixed-point integer atomics, there is no range
+ *     limit or quantum: every fp32 dO whose sums stay finite is handled. */
 typedef enum {
-    LH_SCATTER_FP_ATOMIC = 0,   /* fp32 atomic adds: fastest, not bit-reproducible   */
-    LH_SCATTER_INT_ATOMIC = 1   /* 64-bit fixed-point atomic adds: bit-reproducible  */
+    LH_SCATTER_FP_ATOMIC = 0,
+    LH_SCATTER_INT_ATOMIC = 1,
+    LH_SCATTER_DETERMINISTIC = 1
 } lh_scatter_mode;
 
 /* Length S of the gathered sub-sequence (Sec. 1: S = O(LpK + N/p^(L-1))):

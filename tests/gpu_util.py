@@ -4,7 +4,8 @@ seeded inputs, read its intermediates, and compare with the oracle.
 Tolerances (from the acceptance criteria of the layer):
   * integer / index results: bit-exact;
   * bf16 outputs: max |err| / max(1, |ref|) <= 2e-2 and mean|err| / mean|ref| <= 5e-3;
-  * fp32 outputs: max |err| / max(1, |ref|) <= 1e-5.
+  * fp32 outputs: max |err| / max(1, |ref|) <= 1e-5, and mean|err| / mean|ref| <= 1e-5
+    (the criteria give one fp32 figure; it is read as both bounds).
 The max-abs bound is applied to values scaled to unit magnitude because a
 bf16 value above 4 is spaced 2^-5 or more apart, so rounding even the exact
 result to bf16 can move it by more than 2e-2 in absolute terms.
@@ -43,7 +44,7 @@ import torch
 import oracle
 import synth_inputs as si
 
-TOL = {"bf16": dict(max_scaled=2e-2, mean_rel=5e-3), "fp32": dict(max_scaled=1e-5, mean_rel=1e-6)}
+TOL = {"bf16": dict(max_scaled=2e-2, mean_rel=5e-3), "fp32": dict(max_scaled=1e-5, mean_rel=1e-5)}
 U32 = 2.0 ** -24
 KAPPA = 128.0
 

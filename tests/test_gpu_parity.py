@@ -127,3 +127,51 @@ def test_workspace_is_reusable_across_shapes():
     o2, _ = lh.forward(qs, ks, vs, 4, 3, 5)
     torch.cuda.synchronize()
     assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+
+
+# shapes whose top entries span several pooling blocks (p^(L-1) > 256 tokens), so the
+# deterministic mode combines per-block partial sums; one fp32 case
+SCALE_CASES = [("bf16_pool_up", 8192, 2, 128, "bf16", 4, 6, 4),
+               ("bf16_p2_deep", 4096, 2, 64, "bf16", 2, 10, 3),
+               ("fp32_pool_up", 4096, 1, 64, "fp32", 4, 6, 3)]
+
+
+@pytest.mark.parametrize("case", SCALE_CASES, ids=[c[0] for c in SCALE_CASES])
+@pytest.mark.parametrize("k", [-20, 20])
+def test_deterministic_scatter_over_the_fp32_range(case, k):
+    """dO scaled by 2^k.  Every scale in the gradient path is a power of two, so
+    the deterministic mode's gradients are those of the unscaled dO times 2^k,
+    bit for bit.  Times 2^-k they match the oracle's gradients of the unscaled
+    dO at the dtype's bound, and the fp-atomic mode's at the same bound."""
+    import hierarchical_selection_attention_amd as lh
+    label, N, H, d, dtype, p, L, K = case
+    seed = 600 + SCALE_CASES.index(case)
+    say(f"case {label} dO x 2^{k} seed={seed}")
+    x = si.make_inputs(N, H, d, dtype, seed=seed, scale="student_t3", with_dout=True, threads=8)
+    f = 2.0 ** k
+    do_s = x["dout"]
+    if dtype == "bf16":
+        do_s = si.bf16_bits(si.bf16_to_f32(x["dout"]) * np.float32(f))
+        assert np.array_equal(si.bf16_to_f32(do_s), si.bf16_to_f32(x["dout"]) * np.float32(f))
+    else:
+        do_s = (x["dout"] * np.float32(f)).astype(np.float32)
+    q, k_, v, do0, do1 = (to_dev(a, dtype) for a in (x["q"], x["k"], x["v"], x["dout"], do_s))
+    o, ws = lh.forward(q, k_, v, p, L, K)
+    g0 = [t.clone() for t in lh.backward(do0, p, L, K, ws, mode=lh.LH_SCATTER_DETERMINISTIC)]
+    g1 = [t.clone() for t in lh.backward(do1, p, L, K, ws, mode=lh.LH_SCATTER_DETERMINISTIC)]
+    gf = [t.clone() for t in lh.backward(do1, p, L, K, ws, mode=lh.LH_SCATTER_FP_ATOMIC)]
+    torch.cuda.synchronize()
+    for a, b, name in zip(g0, g1, ("dq", "dk", "dv")):
+        want = (a.double() * f).to(a.dtype)
+        assert torch.equal(b, want), f"{name}: gradients of 2^{k} dO are not 2^{k} times those of dO"
+    ref = oracle.forward(x["q"], x["k"], x["v"], p, L, K, dtype, want=("sel",))
+    bw = oracle.backward(x["q"], x["k"], x["v"], x["dout"], p, L, K, (ref["start"], ref["level"]), dtype,
+                         want=("sub", "cond"))
+    sel = (ref["start"], ref["level"])
+    for gg, key in zip(g1, ("dQt", "dKt", "dVt")):
+        back = (gg.double() / f).to(gg.dtype)
+        check_full_rows(back, bw[key], sel, p, dtype, f"d{key[1].lower()} (dO x 2^{k}, deterministic)", divide=True,
+                        allow_sub=grad_allow(bw, key))
+    for a, b, name in zip(gf, g1, ("dq", "dk", "dv")):
+        compare(to_f64(a) / f, to_f64(b) / f, dtype, f"{name} fp-atomic vs deterministic (dO x 2^{k})",
+                stored=dtype)
