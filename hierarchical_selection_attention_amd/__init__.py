@@ -6,5 +6,6 @@ fallback implementation.
 """
 from ._lib import *  # noqa: F401,F403
 from ._lib import (EXPORTS, LIB_PATH, LighthouseError, alloc_workspace, backward, block_backward,  # noqa: F401
+                   forward_static,
                    block_forward, block_workspace, dense_backward, dense_forward, dtype_code, forward, peak_probe,
                    read_selection, workspace_tensor)

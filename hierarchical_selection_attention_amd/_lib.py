@@ -14,6 +14,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "liblighthouse.so")
 
 LH_OK, LH_ERR_ARG, LH_ERR_SHAPE, LH_ERR_DTYPE, LH_ERR_WORKSPACE, LH_ERR_HIP, LH_ERR_GEMM = 0, -1, -2, -3, -4, -5, -6
+LH_ERR_SCRATCH = -7
+LH_STATIC_SCRATCH_BYTES = 64 << 20
 LH_BF16, LH_FP32 = 0, 1
 LH_SCATTER_FP_ATOMIC, LH_SCATTER_INT_ATOMIC = 0, 1
 LH_SCATTER_DETERMINISTIC = LH_SCATTER_INT_ATOMIC
@@ -27,7 +29,7 @@ EXPORTS = ("lh_subseq_len", "lh_workspace_bytes", "lh_forward", "lh_backward", "
            "lh_stage_timing_read", "lh_stage_name", "lh_status_str", "lh_read_selection", "lh_peak_probe",
            "lh_block_workspace_bytes", "lh_block_forward", "lh_block_backward", "lh_forward_scored",
            "lh_subseq_len_sel", "lh_workspace_bytes_sel", "lh_forward_sel", "lh_backward_sel",
-           "lh_workspace_view_sel", "lh_read_selection_sel")
+           "lh_workspace_view_sel", "lh_read_selection_sel", "lh_forward_static")
 
 
 class LighthouseError(RuntimeError):
@@ -43,6 +45,7 @@ def _load():
         "lh_subseq_len": (i64, [i, i, i, i]),
         "lh_workspace_bytes": (sz, [i, i, i, i, i, i, i]),
         "lh_forward": (i, [vp, vp, vp, vp, i, i, i, i, i, i, i, vp, sz, vp]),
+        "lh_forward_static": (i, [vp, vp, vp, vp, i, i, i, i, i, i, i, vp]),
         "lh_forward_scored": (i, [vp, vp, vp, vp, i, i, i, i, i, i, i, i, vp, sz, vp]),
         "lh_subseq_len_sel": (i64, [i, i, i, i, i]),
         "lh_workspace_bytes_sel": (sz, [i, i, i, i, i, i, i, i]),
@@ -78,6 +81,7 @@ _L = _load()
 lh_subseq_len = _L.lh_subseq_len
 lh_workspace_bytes = _L.lh_workspace_bytes
 lh_forward = _L.lh_forward
+lh_forward_static = _L.lh_forward_static
 lh_forward_scored = _L.lh_forward_scored
 lh_subseq_len_sel = _L.lh_subseq_len_sel
 lh_workspace_bytes_sel = _L.lh_workspace_bytes_sel
@@ -185,6 +189,20 @@ def forward(q, k, v, p, L, K, ws=None, out=None, stream=None, score_mode=LH_SCOR
                                score_mode, ws.data_ptr(), ws.numel(), _stream_handle(stream))
     _check(rc, "lh_forward")
     return out, ws
+
+
+def forward_static(q, k, v, p, L, K, out=None, stream=None):
+    """lh_forward_static: o of the layer with the library's static per-device workspace
+    (no allocation in the library; the output is allocated here unless `out` is given)."""
+    torch = _torch()
+    _dev_tensor_check(q, k, v)
+    N, H, d = q.shape
+    if out is None:
+        out = torch.empty_like(q)
+    rc = lh_forward_static(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), N, H, d, p, L, K,
+                           dtype_code(q), _stream_handle(stream))
+    _check(rc, "lh_forward_static")
+    return out
 
 
 def backward(dout, p, L, K, ws, mode=LH_SCATTER_FP_ATOMIC, grads=None, stream=None,

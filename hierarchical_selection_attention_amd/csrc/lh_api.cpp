@@ -105,6 +105,14 @@ int make_plan(int N, int H, int d, int p, int L, int K, int dtype, Plan* P, int 
     pl.off_os = take(sizeof(float) * HSd);
     pl.off_lse = take(sizeof(float) * (size_t)H * pl.Sp);
     pl.off_lse2 = take(sizeof(float) * (size_t)H * pl.Sp);
+    size_t nmap = 0;
+    for (int l = 0; l < L; ++l) {
+        pl.lmap_off[l] = nmap;
+        nmap += (size_t)H * pl.n[l];
+    }
+    pl.off_lmap = take(pl.pk ? sizeof(int32_t) * nmap : 0);
+    // everything above is the forward's state; what follows only the backward uses
+    pl.fwd_total = off;
     pl.off_acc = take(sizeof(float) * HSd);
     pl.off_part = take(m < L - 1 ? sizeof(float) * (size_t)H * (size_t)(N / pl.tok) * d : 0);
     pl.off_dos = take(sizeof(float) * HSd);
@@ -115,12 +123,6 @@ int make_plan(int N, int H, int d, int p, int L, int K, int dtype, Plan* P, int 
     pl.off_dk = take(sizeof(float) * HSd);
     pl.off_dv = take(sizeof(float) * HSd);
     pl.rowcopy = dtype == BF16 && !pl.pk;
-    size_t nmap = 0;
-    for (int l = 0; l < L; ++l) {
-        pl.lmap_off[l] = nmap;
-        nmap += (size_t)H * pl.n[l];
-    }
-    pl.off_lmap = take(pl.pk ? sizeof(int32_t) * nmap : 0);
     pl.total = off;
     return LH_OK;
 }
@@ -133,6 +135,9 @@ struct TimedLaunch {
 };
 std::mutex g_mu;
 bool g_timing = false;
+// set while lh_forward_static runs on this thread: its stages take no events
+// (creating one may allocate)
+thread_local bool t_untimed = false;
 std::vector<TimedLaunch> g_recs;
 std::vector<hipEvent_t> g_pool;
 
@@ -156,6 +161,7 @@ const char* kStageNames[ST_COUNT] = {
 
 StageMark stage_open(hipStream_t s) {
     StageMark m;
+    if (t_untimed) return m;
     {
         std::lock_guard<std::mutex> g(g_mu);
         if (!g_timing) return m;
@@ -172,6 +178,34 @@ void stage_close(int id, hipStream_t s, const StageMark& m) {
     std::lock_guard<std::mutex> g(g_mu);
     g_recs.push_back({id, m.a, m.b});
 }
+
+// ------------------------------------------------ forward without allocation
+// The workspace of lh_forward_static: one array per device, allocated with the
+// library's code on each device and held until the process ends.  Host code
+// never uses the symbol itself (on the host it is only a stand-in): the device
+// address is looked up once per device and kept in g_scratch_dev.
+static __device__ __align__(256) unsigned char scratch[LH_STATIC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_dev[kMaxScratchDevices];
+
+// The array's address on the current device, looked up on the first call
+// there; null when the lookup fails.
+void* scratch_on_current_device(int* dev_out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxScratchDevices) return nullptr;
+    *dev_out = dev;
+    std::lock_guard<std::mutex> g(g_scratch_mu);
+    if (!g_scratch_dev[dev]) {
+        void* ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return nullptr;
+        g_scratch_dev[dev] = ptr;
+    }
+    return g_scratch_dev[dev];
+}
+}  // namespace
 
 }  // namespace lh
 
@@ -192,10 +226,10 @@ size_t lh_workspace_bytes(int N, int H, int d, int p, int L, int K, int dtype) {
     return P.total;
 }
 
-static int check_ws(const Plan& P, const void* ws, size_t ws_bytes) {
+static int check_ws(const Plan& P, const void* ws, size_t ws_bytes, bool fwd_only = false) {
     if (!ws) return LH_ERR_WORKSPACE;
     if (reinterpret_cast<uintptr_t>(ws) % 256 != 0) return LH_ERR_WORKSPACE;
-    if (ws_bytes < P.total) return LH_ERR_WORKSPACE;
+    if (ws_bytes < (fwd_only ? P.fwd_total : P.total)) return LH_ERR_WORKSPACE;
     return LH_OK;
 }
 
@@ -263,7 +297,7 @@ int lh_forward_sel(const void* q, const void* k, const void* v, void* o, int N, 
 namespace lh {
 int forward_strided(const void* q, const void* k, const void* v, void* o, int N, int H, int d, int p, int L, int K,
                     int dtype, int score_mode, int select_mode, void* ws, size_t ws_bytes, void* stream,
-                    int64_t in_ld) {
+                    int64_t in_ld, bool fwd_only) {
     Plan P;
     int rc = make_plan(N, H, d, p, L, K, dtype, &P, select_mode);
     if (rc) return rc;
@@ -273,7 +307,7 @@ int forward_strided(const void* q, const void* k, const void* v, void* o, int N,
     P.score_mode = score_mode;
     if (!q || !k || !v || !o) return LH_ERR_ARG;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return LH_ERR_ARG;
-    if ((rc = check_ws(P, ws, ws_bytes))) return rc;
+    if ((rc = check_ws(P, ws, ws_bytes, fwd_only))) return rc;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     char* w = reinterpret_cast<char*>(ws);
     LH_TRY(stage(ST_POOL_SCORE, s, [&] { return launch_pool_score(P, q, k, v, w, s); }));
@@ -395,6 +429,28 @@ int backward_strided(const void* dout, void* dq, void* dk, void* dv, int N, int 
 }  // namespace lh
 
 extern "C" {
+
+int lh_forward_static(const void* q, const void* k, const void* v, void* o, int N, int H, int d, int p, int L,
+                      int K, int dtype, void* stream) {
+    Plan P;
+    int rc = make_plan(N, H, d, p, L, K, dtype, &P);
+    if (rc) return rc;
+    if (P.fwd_total > (size_t)LH_STATIC_SCRATCH_BYTES) return LH_ERR_SCRATCH;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    int dev = -1;
+    void* ws = scratch_on_current_device(&dev);
+    if (!ws) return LH_ERR_HIP;
+    if (s) {   // the stream must belong to the current device, whose array is used
+        int sdev = -1;
+        if (hipStreamGetDevice(s, &sdev) != hipSuccess) return LH_ERR_HIP;
+        if (sdev != dev) return LH_ERR_ARG;
+    }
+    t_untimed = true;
+    rc = forward_strided(q, k, v, o, N, H, d, p, L, K, dtype, LH_SCORE_QK, LH_SELECT_PARTITION, ws,
+                         (size_t)LH_STATIC_SCRATCH_BYTES, stream, (int64_t)H * d, true);
+    t_untimed = false;
+    return rc;
+}
 
 int lh_backward(const void* dout, void* dq, void* dk, void* dv, int N, int H, int d, int p, int L, int K,
                 int dtype, int scatter_mode, void* ws, size_t ws_bytes, void* stream) {
@@ -679,6 +735,7 @@ const char* lh_status_str(int status) {
         case LH_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
         case LH_ERR_HIP: return "HIP launch or runtime error";
         case LH_ERR_GEMM: return "GEMM library error or no algorithm for the shape";
+        case LH_ERR_SCRATCH: return "the shape needs more forward state than lh_forward_static's static array holds";
         default: return "unknown status";
     }
 }

@@ -41,9 +41,11 @@ hipError_t stage(int id, hipStream_t s, F&& fn) {
 }
 
 // lh_forward_sel with q, k, v rows in_ld elements apart (in_ld >= H*d, a multiple of 8)
+// fwd_only: ws need only hold the forward's state (Plan::fwd_total); no matching
+// backward may then use it
 int forward_strided(const void* q, const void* k, const void* v, void* o, int N, int H, int d, int p, int L, int K,
                     int dtype, int score_mode, int select_mode, void* ws, size_t ws_bytes, void* stream,
-                    int64_t in_ld);
+                    int64_t in_ld, bool fwd_only = false);
 // lh_backward with dq, dk, dv rows grad_ld elements apart (grad_ld = H*d for
 // [N][H][d] tensors; larger strides need the bf16 path, grad_ld % 8 == 0)
 int backward_strided(const void* dout, void* dq, void* dk, void* dv, int N, int H, int d, int p, int L, int K,
@@ -89,6 +91,7 @@ struct Plan {
     // at lmap_off[l] + h * n_l + j, 0 when that entry is not kept
     size_t off_lmap;
     size_t lmap_off[kMaxLevels];
+    size_t fwd_total;             // bytes of the forward's state (a prefix of the workspace)
     size_t total;
     size_t off_lmap_bytes() const {
         size_t n = 0;

@@ -57,7 +57,8 @@ typedef enum {
     LH_ERR_DTYPE = -3,      /* unknown dtype or scatter mode                      */
     LH_ERR_WORKSPACE = -4,  /* workspace missing, misaligned or too small         */
     LH_ERR_HIP = -5,        /* a HIP launch or runtime call failed                */
-    LH_ERR_GEMM = -6        /* the GEMM library (hipBLASLt) failed or has no algorithm */
+    LH_ERR_GEMM = -6,       /* the GEMM library (hipBLASLt) failed or has no algorithm */
+    LH_ERR_SCRATCH = -7     /* lh_forward_static: the shape's forward state exceeds its array */
 } lh_status;
 
 typedef enum { LH_BF16 = 0, LH_FP32 = 1 } lh_dtype;
@@ -94,6 +95,25 @@ size_t lh_workspace_bytes(int N, int H, int d, int p, int L, int K, int dtype);
 int lh_forward(const void* q, const void* k, const void* v, void* o,
                int N, int H, int d, int p, int L, int K, int dtype,
                void* ws, size_t ws_bytes, void* stream);
+
+/* lh_forward for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.  The
+ * same computation and output as lh_forward (partition selection, default
+ * score), with its workspace in a static device array of
+ * LH_STATIC_SCRATCH_BYTES (64 MiB) that the library holds on each device it
+ * runs on until the process ends.  The first call on a device looks up that
+ * device's array; the call allocates nothing.  Its state serves no
+ * lh_backward.  Every call on one device shares that device's array: calls
+ * that overlap in time on one device (on different streams, or from other
+ * threads) race and give wrong results.  The shape must fit: its forward state
+ * (scores, selection, gathered sub-sequence and operand copies, about 53 MiB at
+ * N = 16384, H = 16, d = 128, K = 32) may not exceed the array, else
+ * LH_ERR_SCRATCH and nothing is enqueued.  `stream` must belong to the current
+ * device (LH_ERR_ARG otherwise).  Other arguments, layouts and errors as
+ * lh_forward. */
+#define LH_STATIC_SCRATCH_BYTES (64u << 20)
+int lh_forward_static(const void* q, const void* k, const void* v, void* o,
+                      int N, int H, int d, int p, int L, int K, int dtype, void* stream);
 
 /* What the parameter-free score is taken of.  The pages call the scoring
  * bidirectional (Sec. 1) and label Fig. 2's scores "qk" / "kq" without fixing

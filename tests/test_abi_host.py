@@ -163,3 +163,15 @@ def test_select_mode_validation():
                              None) == lh.LH_ERR_DTYPE
     assert lh.lh_backward_sel(fake, fake, fake, fake, 2048, 2, 64, 4, 3, 16, 0, 0, 1, fake * 256, nb - 1,
                               None) == lh.LH_ERR_WORKSPACE
+
+
+def test_forward_static_rejects_before_any_launch():
+    """lh_forward_static validates on the host: bad shapes, and shapes whose forward state
+    exceeds its static array (LH_ERR_SCRATCH), return before touching a device."""
+    import hierarchical_selection_attention_amd as lh
+    fake = 1 << 20
+    assert lh.lh_forward_static(fake, fake, fake, fake, 524288, 16, 128, 4, 5, 128, 0, None) == lh.LH_ERR_SCRATCH
+    assert lh.lh_forward_static(fake, fake, fake, fake, 2048, 2, 96, 4, 3, 16, 0, None) == lh.LH_ERR_SHAPE
+    assert lh.lh_forward_static(fake, fake, fake, fake, 2047, 2, 64, 4, 3, 16, 0, None) == lh.LH_ERR_SHAPE
+    assert lh.lh_forward_static(fake, fake, fake, fake, 2048, 2, 64, 4, 3, 16, 7, None) == lh.LH_ERR_DTYPE
+    assert "static array" in lh.lh_status_str(lh.LH_ERR_SCRATCH)
