@@ -129,22 +129,36 @@ def achievable_peaks(lh, torch, stream):
     return out
 
 
+def cpu_threads():
+    """Host threads this process may use: its CPU affinity, capped by OMP_NUM_THREADS when set
+    (the GPU machine's share of host cores)."""
+    n = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
+    env = os.environ.get("OMP_NUM_THREADS", "")
+    if env.isdigit() and int(env) > 0:
+        n = min(n, int(env))
+    return max(1, n)
+
+
 def cpu_baseline(w, x, heads, score_mode=0, select_mode=0):
-    """The oracle (fwd+bwd) on the first `heads` heads of the same inputs, scaled to all heads."""
+    """The oracle (fwd+bwd) on the first `heads` heads of the same inputs, on every host thread
+    this process may use (OpenMP over heads and over the sub-sequence's rows), scaled to all
+    heads when heads < H."""
     import numpy as np
     import oracle
     sub = {n: np.ascontiguousarray(x[n][:, :heads]) for n in ("q", "k", "v", "dout")}
     p, L, K, dt = w["p"], w["L"], w["K"], w["dtype"]
+    threads = cpu_threads()
     t0 = time.perf_counter()
-    r = oracle.forward(sub["q"], sub["k"], sub["v"], p, L, K, dt, want=("sel", "o"), nthreads=heads,
+    r = oracle.forward(sub["q"], sub["k"], sub["v"], p, L, K, dt, want=("sel", "o"), nthreads=threads,
                        score_mode=score_mode, select_mode=select_mode)
     oracle.backward(sub["q"], sub["k"], sub["v"], sub["dout"], p, L, K, (r["start"], r["level"]), dt,
-                    want=("full",), nthreads=heads, select_mode=select_mode)
+                    want=("full",), nthreads=threads, select_mode=select_mode)
     t = time.perf_counter() - t0
     full = t * w["H"] / heads
-    return {"value": w["N"] / full, "unit": "tokens/s", "cores": heads, "kind": "oracle",
-            "sample": f"fwd+bwd on {heads} of {w['H']} heads (all {w['N']} tokens), {t:.1f} s, "
-                      f"scaled by {w['H']}/{heads} heads (heads are independent)"}
+    scaled = "" if heads == w["H"] else f", scaled by {w['H']}/{heads} heads (heads are independent)"
+    return {"value": w["N"] / full, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"fwd+bwd on {heads} of {w['H']} heads (all {w['N']} tokens), {t:.1f} s on {threads} "
+                      f"threads (nproc {os.cpu_count()}){scaled}"}
 
 
 BLOCK_METRIC = ("Lighthouse attention block (QKV projections + layer + output projection) "
@@ -254,7 +268,7 @@ def bench_block(args, lh, torch, np, si):
     cpu = None
     if not args.no_cpu:
         import oracle
-        threads = max(1, min(16, os.cpu_count() or 1))
+        threads = cpu_threads()
         log(f"CPU oracle block fwd+bwd on {threads} threads ...")
         t0 = time.perf_counter()
         f = oracle.block_forward(b["x"], b["w_qkv"], b["w_o"], H, d, p, L, K, nthreads=threads)
@@ -296,7 +310,7 @@ def main():
     ap.add_argument("--mode", type=int, default=0, help="scatter adjoint: 0 fp-atomic, 1 int-atomic")
     ap.add_argument("--no-dense", action="store_true", help="skip the dense attention comparison")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--cpu-heads", type=int, default=8)
+    ap.add_argument("--cpu-heads", type=int, default=0, help="heads in the CPU oracle sample (0: all)")
     ap.add_argument("--select", choices=("partition", "parent_kept"), default="partition",
                     help="selection reading (default: partition; parent_kept prints its own line)")
     ap.add_argument("--score", choices=("qk", "k", "q", "qk_product"), default="qk",
@@ -471,8 +485,8 @@ def main():
 
     cpu = None
     if not args.no_cpu:
-        heads = max(1, min(H, args.cpu_heads, os.cpu_count() or 1))
-        log(f"CPU oracle on {heads} heads ...")
+        heads = H if args.cpu_heads <= 0 else max(1, min(H, args.cpu_heads))
+        log(f"CPU oracle on {heads} heads, {cpu_threads()} threads ...")
         cpu = cpu_baseline(w, x, heads, score_mode, sel_mode)
 
     variant = []

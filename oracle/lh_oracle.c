@@ -348,27 +348,37 @@ static int64_t head_select(float** lev, double** lev64, int N, int p, int L, int
 
 /* ------------------------------------------------------------ attention (O6, O8) */
 
-/* Eq. (1) on one head's sub-sequence with the causal mask: two-pass softmax. */
-static void head_attention_fwd(int64_t S, int d, const double* Q, const double* K, const double* V,
-                               double* O, double* lse, double* logit) {
+/* The logits s_ij = Q_i . K_j / sqrt(d) of query i for every visible key
+ * j <= i (the causal mask of Eq. (1)), their maximum and the sum of
+ * exp(s_ij - max). */
+static void row_logits(int64_t i, int d, const double* Q, const double* K, double* logit, double* m_out,
+                       double* sum_out) {
     double scale = 1.0 / sqrt((double)d);
-    for (int64_t i = 0; i < S; ++i) {
-        double m = -INFINITY;
-        for (int64_t j = 0; j <= i; ++j) {
-            double acc = 0.0;
-            for (int e = 0; e < d; ++e) acc += Q[i * d + e] * K[j * d + e];
-            logit[j] = acc * scale;
-            if (logit[j] > m) m = logit[j];
-        }
-        double sum = 0.0;
-        for (int64_t j = 0; j <= i; ++j) sum += exp(logit[j] - m);
-        for (int e = 0; e < d; ++e) O[i * d + e] = 0.0;
-        for (int64_t j = 0; j <= i; ++j) {
-            double w = exp(logit[j] - m) / sum;
-            for (int e = 0; e < d; ++e) O[i * d + e] += w * V[j * d + e];
-        }
-        if (lse) lse[i] = m + log(sum);
+    double m = -INFINITY;
+    for (int64_t j = 0; j <= i; ++j) {
+        double acc = 0.0;
+        for (int e = 0; e < d; ++e) acc += Q[i * d + e] * K[j * d + e];
+        logit[j] = acc * scale;
+        if (logit[j] > m) m = logit[j];
     }
+    double sum = 0.0;
+    for (int64_t j = 0; j <= i; ++j) sum += exp(logit[j] - m);
+    *m_out = m;
+    *sum_out = sum;
+}
+
+/* Eq. (1) for query row i of one head: O_i = sum_j softmax_j(s_ij) V_j (a
+ * two-pass softmax) and lse_i. */
+static void attn_fwd_row(int64_t i, int d, const double* Q, const double* K, const double* V, double* O,
+                         double* lse, double* logit) {
+    double m, sum;
+    row_logits(i, d, Q, K, logit, &m, &sum);
+    for (int e = 0; e < d; ++e) O[i * d + e] = 0.0;
+    for (int64_t j = 0; j <= i; ++j) {
+        double w = exp(logit[j] - m) / sum;
+        for (int e = 0; e < d; ++e) O[i * d + e] += w * V[j * d + e];
+    }
+    if (lse) lse[i] = m + log(sum);
 }
 
 /* Gradient of the above: P = softmax, dV = P^T dO, dP = dO V^T,
@@ -397,85 +407,95 @@ static void head_attention_fwd(int64_t S, int d, const double* Q, const double* 
  *   lO_i = sum_j P_ij Lam_ij |V_j - O_i|,  ldQ_i = sum_j W_ij |K_j| / sqrt(d),
  *   ldK_j = sum_i W_ij |Q_i| / sqrt(d),  ldV_j = sum_i P_ij (Lam_ij + M_i) |dO_i|.
  * Where logits are large (heavy-tailed rows) these dominate the first four. */
-static void head_attention_bwd(int64_t S, int d, const double* Q, const double* K, const double* V,
-                               const double* O, const double* dO, double* dQ, double* dK, double* dV,
-                               double* logit, double* cond) {
+/* The gradient is computed in two passes, each a loop over independent rows:
+ * the query side (attn_bwd_query_row: dQ_i, the row's statistics, and P_ij,
+ * dS_ij for j <= i, stored row by row in packed lower-triangular arrays at
+ * tri(i) + j) and the key side (attn_bwd_key_row: dK_j and dV_j, adding the
+ * stored P_ij and dS_ij over i >= j in increasing i).  Every sum is taken in
+ * the same order as one loop over i then j would take it.  rs[i] holds m,
+ * sum, D, B, M, R of row i; cz the 8 condition arrays of the head (or NULL)
+ * and, with them, wt[3] the packed per-pair weights w_ij, W_ij and
+ * P_ij (Lam_ij + M_i) that the key side needs; lam, adp: scratch. */
+static int64_t tri(int64_t i) { return i * (i + 1) / 2; }
+enum { RS_M, RS_SUM, RS_D, RS_B, RS_LM, RS_R, RS_N };
+
+static void attn_bwd_query_row(int64_t i, int d, const double* Q, const double* K, const double* V,
+                               const double* O, const double* dO, double* dQ, double* rs, double* Pt,
+                               double* dSt, double* logit, double* lam, double* adp, double* const* cz,
+                               double* const* wt) {
     double scale = 1.0 / sqrt((double)d);
-    memset(dQ, 0, sizeof(double) * (size_t)(S * d));
-    memset(dK, 0, sizeof(double) * (size_t)(S * d));
-    memset(dV, 0, sizeof(double) * (size_t)(S * d));
-    if (cond) memset(cond, 0, sizeof(double) * (size_t)(8 * S * d));
-    double* lam = cond ? (double*)malloc(sizeof(double) * (size_t)S) : NULL;
-    double* adp = cond ? (double*)malloc(sizeof(double) * (size_t)S) : NULL;
-    if (cond && (!lam || !adp)) {   /* no bound without scratch: report it as unbounded */
-        for (int64_t z = 0; z < 8 * S * d; ++z) cond[z] = INFINITY;
-        free(lam); free(adp);
-        lam = adp = NULL;
-        cond = NULL;
+    double m, sum;
+    row_logits(i, d, Q, K, logit, &m, &sum);
+    double D = 0.0, B = 0.0;
+    for (int e = 0; e < d; ++e) {
+        D += dO[i * d + e] * O[i * d + e];
+        B += fabs(dO[i * d + e] * O[i * d + e]);
     }
-    for (int64_t i = 0; i < S; ++i) {
-        double m = -INFINITY;
+    double M = fabs(m + log(sum)), R = 0.0;   /* |lse_i| + sum_k P_ik Lam_ik */
+    if (cz) {
         for (int64_t j = 0; j <= i; ++j) {
-            double acc = 0.0;
-            for (int e = 0; e < d; ++e) acc += Q[i * d + e] * K[j * d + e];
-            logit[j] = acc * scale;
-            if (logit[j] > m) m = logit[j];
-        }
-        double sum = 0.0;
-        for (int64_t j = 0; j <= i; ++j) sum += exp(logit[j] - m);
-        double D = 0.0, B = 0.0;
-        for (int e = 0; e < d; ++e) {
-            D += dO[i * d + e] * O[i * d + e];
-            B += fabs(dO[i * d + e] * O[i * d + e]);
-        }
-        double M = fabs(m + log(sum)), R = 0.0;   /* |lse_i| + sum_k P_ik Lam_ik */
-        if (cond) {
-            for (int64_t j = 0; j <= i; ++j) {
-                double P = exp(logit[j] - m) / sum, la = 0.0, dP = 0.0;
-                for (int e = 0; e < d; ++e) {
-                    la += fabs(Q[i * d + e] * K[j * d + e]);
-                    dP += dO[i * d + e] * V[j * d + e];
-                }
-                lam[j] = la * scale;
-                adp[j] = fabs(dP - D);
-                M += P * lam[j];
-                R += P * lam[j] * adp[j];
-            }
-        }
-        for (int64_t j = 0; j <= i; ++j) {
-            double P = exp(logit[j] - m) / sum;
-            double dP = 0.0, A = 0.0;
+            double P = exp(logit[j] - m) / sum, la = 0.0, dP = 0.0;
             for (int e = 0; e < d; ++e) {
+                la += fabs(Q[i * d + e] * K[j * d + e]);
                 dP += dO[i * d + e] * V[j * d + e];
-                A += fabs(dO[i * d + e] * V[j * d + e]);
             }
-            double dS = P * (dP - D);
+            lam[j] = la * scale;
+            adp[j] = fabs(dP - D);
+            M += P * lam[j];
+            R += P * lam[j] * adp[j];
+        }
+    }
+    for (int e = 0; e < d; ++e) dQ[i * d + e] = 0.0;
+    for (int64_t j = 0; j <= i; ++j) {
+        double P = exp(logit[j] - m) / sum;
+        double dP = 0.0, A = 0.0;
+        for (int e = 0; e < d; ++e) {
+            dP += dO[i * d + e] * V[j * d + e];
+            A += fabs(dO[i * d + e] * V[j * d + e]);
+        }
+        double dS = P * (dP - D);
+        Pt[tri(i) + j] = P;
+        dSt[tri(i) + j] = dS;
+        for (int e = 0; e < d; ++e) dQ[i * d + e] += dS * K[j * d + e] * scale;
+        if (cz) {
+            double w = P * (A + B);
+            double wl = P * ((lam[j] + M) * adp[j] + R);
+            wt[0][tri(i) + j] = w;
+            wt[1][tri(i) + j] = wl;
+            wt[2][tri(i) + j] = P * (lam[j] + M);
             for (int e = 0; e < d; ++e) {
-                dQ[i * d + e] += dS * K[j * d + e] * scale;
-                dK[j * d + e] += dS * Q[i * d + e] * scale;
-                dV[j * d + e] += P * dO[i * d + e];
-            }
-            if (cond) {
-                double w = P * (A + B);
-                double wl = P * ((lam[j] + M) * adp[j] + R);
-                double *cO = cond, *cQ = cond + S * d, *cK = cond + 2 * S * d, *cV = cond + 3 * S * d;
-                double *lO = cond + 4 * S * d, *lQ = cond + 5 * S * d, *lK = cond + 6 * S * d,
-                       *lV = cond + 7 * S * d;
-                for (int e = 0; e < d; ++e) {
-                    cO[i * d + e] += P * fabs(V[j * d + e]);
-                    cQ[i * d + e] += w * fabs(K[j * d + e]) * scale;
-                    cK[j * d + e] += w * fabs(Q[i * d + e]) * scale;
-                    cV[j * d + e] += P * fabs(dO[i * d + e]);
-                    lO[i * d + e] += P * lam[j] * fabs(V[j * d + e] - O[i * d + e]);
-                    lQ[i * d + e] += wl * fabs(K[j * d + e]) * scale;
-                    lK[j * d + e] += wl * fabs(Q[i * d + e]) * scale;
-                    lV[j * d + e] += P * (lam[j] + M) * fabs(dO[i * d + e]);
-                }
+                cz[0][i * d + e] += P * fabs(V[j * d + e]);
+                cz[1][i * d + e] += w * fabs(K[j * d + e]) * scale;
+                cz[4][i * d + e] += P * lam[j] * fabs(V[j * d + e] - O[i * d + e]);
+                cz[5][i * d + e] += wl * fabs(K[j * d + e]) * scale;
             }
         }
     }
-    free(lam);
-    free(adp);
+    double* r = rs + i * RS_N;
+    r[RS_M] = m; r[RS_SUM] = sum; r[RS_D] = D; r[RS_B] = B; r[RS_LM] = M; r[RS_R] = R;
+}
+
+static void attn_bwd_key_row(int64_t j, int64_t S, int d, const double* Q, const double* dO, const double* Pt,
+                             const double* dSt, double* dK, double* dV, double* const* cz,
+                             const double* const* wt) {
+    double scale = 1.0 / sqrt((double)d);
+    for (int e = 0; e < d; ++e) dK[j * d + e] = dV[j * d + e] = 0.0;
+    for (int64_t i = j; i < S; ++i) {
+        double P = Pt[tri(i) + j], dS = dSt[tri(i) + j];
+        for (int e = 0; e < d; ++e) {
+            dK[j * d + e] += dS * Q[i * d + e] * scale;
+            dV[j * d + e] += P * dO[i * d + e];
+        }
+        if (cz) {
+            double w = wt[0][tri(i) + j], wl = wt[1][tri(i) + j], plm = wt[2][tri(i) + j];
+            for (int e = 0; e < d; ++e) {
+                cz[2][j * d + e] += w * fabs(Q[i * d + e]) * scale;
+                cz[3][j * d + e] += P * fabs(dO[i * d + e]);
+                cz[6][j * d + e] += wl * fabs(Q[i * d + e]) * scale;
+                cz[7][j * d + e] += plm * fabs(dO[i * d + e]);
+            }
+        }
+    }
 }
 
 /* ------------------------------------------------------------- per-head work */
@@ -567,12 +587,26 @@ int lho_forward(const void* q, const void* k, const void* v, int N, int H, int d
     ctx_t c = {q, k, v, NULL, N, H, d, dtype, p, L, K, lho_subseq_len_sel(N, p, L, K, select_mode), score_mode,
                select_mode};
     int64_t S = c.S;
+    size_t sd = (size_t)(S * d);
     int err = 0;
 #ifdef _OPENMP
     if (nthreads > 0) omp_set_num_threads(nthreads);
 #else
     (void)nthreads;
 #endif
+    int need_attn = Ot || lse || O;
+    int need_rows = Qt || Kt || Vt || need_attn;
+    /* every head's gathered rows, output rows and lse, for the row-parallel attention */
+    double* Qa = need_rows ? (double*)malloc(sizeof(double) * sd * (size_t)H) : NULL;
+    double* Ka = need_rows ? (double*)malloc(sizeof(double) * sd * (size_t)H) : NULL;
+    double* Va = need_rows ? (double*)malloc(sizeof(double) * sd * (size_t)H) : NULL;
+    double* Oa = need_attn ? (double*)malloc(sizeof(double) * sd * (size_t)H) : NULL;
+    double* la = need_attn ? (double*)malloc(sizeof(double) * (size_t)S * (size_t)H) : NULL;
+    if (need_rows && (!Qa || !Ka || !Va || (need_attn && (!Oa || !la)))) {
+        free(Qa); free(Ka); free(Va); free(Oa); free(la);
+        return LHO_ERR_MEM;
+    }
+    /* scores, selection (O2-O4) and gather (O5), one head at a time */
 #pragma omp parallel for schedule(dynamic, 1) reduction(| : err)
     for (int h = 0; h < H; ++h) {
         int32_t* st = sel_start + (int64_t)h * S;
@@ -585,44 +619,58 @@ int lho_forward(const void* q, const void* k, const void* v, int N, int H, int d
                 continue;
             }
         }
-        int need_attn = Ot || lse || O;
-        if (!(Qt || Kt || Vt || need_attn)) continue;
-        size_t sd = (size_t)(S * d);
+        if (!need_rows) continue;
         double* scratch = (double*)malloc(sizeof(double) * (size_t)d * (size_t)(L + 1));
-        double* Qh = (double*)malloc(sizeof(double) * sd);
-        double* Kh = (double*)malloc(sizeof(double) * sd);
-        double* Vh = (double*)malloc(sizeof(double) * sd);
-        double* Oh = (double*)malloc(sizeof(double) * sd);
-        double* lh = (double*)malloc(sizeof(double) * (size_t)S);
-        double* logit = (double*)malloc(sizeof(double) * (size_t)S);
-        if (!scratch || !Qh || !Kh || !Vh || !Oh || !lh || !logit) {
+        if (!scratch) {
             err |= 1;
-        } else {
-            head_gather(&c, q, h, st, lv, Qh, scratch);
-            head_gather(&c, k, h, st, lv, Kh, scratch);
-            head_gather(&c, v, h, st, lv, Vh, scratch);
-            if (Qt) memcpy(Qt + (int64_t)h * S * d, Qh, sizeof(double) * sd);
-            if (Kt) memcpy(Kt + (int64_t)h * S * d, Kh, sizeof(double) * sd);
-            if (Vt) memcpy(Vt + (int64_t)h * S * d, Vh, sizeof(double) * sd);
-            if (need_attn) {
-                head_attention_fwd(S, d, Qh, Kh, Vh, Oh, lh, logit);
-                if (Ot) memcpy(Ot + (int64_t)h * S * d, Oh, sizeof(double) * sd);
-                if (lse) memcpy(lse + (int64_t)h * S, lh, sizeof(double) * (size_t)S);
-                if (O) {
-                    /* scatter (O7): every token of entry i receives row i; with
-                       overlapping entries (R2') a token sums the rows it receives */
-                    for (int64_t t = 0; t < N; ++t)
-                        for (int e = 0; e < d; ++e) O[(t * H + h) * (int64_t)d + e] = 0.0;
-                    for (int64_t i = 0; i < S; ++i) {
-                        int64_t len = ipow(p, lv[i]);
-                        for (int64_t t = st[i]; t < st[i] + len; ++t)
-                            for (int e = 0; e < d; ++e) O[(t * H + h) * (int64_t)d + e] += Oh[i * d + e];
-                    }
+            continue;
+        }
+        head_gather(&c, q, h, st, lv, Qa + (size_t)h * sd, scratch);
+        head_gather(&c, k, h, st, lv, Ka + (size_t)h * sd, scratch);
+        head_gather(&c, v, h, st, lv, Va + (size_t)h * sd, scratch);
+        free(scratch);
+    }
+    /* attention (O6), one query row of one head at a time */
+    if (!err && need_attn) {
+#pragma omp parallel reduction(| : err)
+        {
+            double* logit = (double*)malloc(sizeof(double) * (size_t)(S > 0 ? S : 1));
+            if (!logit) err |= 1;
+#pragma omp for schedule(dynamic, 16)
+            for (int64_t r = 0; r < (int64_t)H * S; ++r) {
+                if (!logit) continue;
+                int64_t h = r / S, i = r % S;
+                attn_fwd_row(i, d, Qa + h * sd, Ka + h * sd, Va + h * sd, Oa + h * sd, la + h * S, logit);
+            }
+            free(logit);
+        }
+    }
+    /* outputs and the scatter (O7), one head at a time */
+    if (!err && need_rows) {
+#pragma omp parallel for schedule(dynamic, 1)
+        for (int h = 0; h < H; ++h) {
+            const int32_t* st = sel_start + (int64_t)h * S;
+            const int8_t* lv = sel_level + (int64_t)h * S;
+            if (Qt) memcpy(Qt + (int64_t)h * S * d, Qa + (size_t)h * sd, sizeof(double) * sd);
+            if (Kt) memcpy(Kt + (int64_t)h * S * d, Ka + (size_t)h * sd, sizeof(double) * sd);
+            if (Vt) memcpy(Vt + (int64_t)h * S * d, Va + (size_t)h * sd, sizeof(double) * sd);
+            if (Ot) memcpy(Ot + (int64_t)h * S * d, Oa + (size_t)h * sd, sizeof(double) * sd);
+            if (lse) memcpy(lse + (int64_t)h * S, la + (size_t)h * S, sizeof(double) * (size_t)S);
+            if (O) {
+                /* every token of entry i receives row i; with overlapping entries
+                   (R2') a token sums the rows it receives */
+                const double* Oh = Oa + (size_t)h * sd;
+                for (int64_t t = 0; t < N; ++t)
+                    for (int e = 0; e < d; ++e) O[(t * H + h) * (int64_t)d + e] = 0.0;
+                for (int64_t i = 0; i < S; ++i) {
+                    int64_t len = ipow(p, lv[i]);
+                    for (int64_t t = st[i]; t < st[i] + len; ++t)
+                        for (int e = 0; e < d; ++e) O[(t * H + h) * (int64_t)d + e] += Oh[i * d + e];
                 }
             }
         }
-        free(scratch); free(Qh); free(Kh); free(Vh); free(Oh); free(lh); free(logit);
     }
+    free(Qa); free(Ka); free(Va); free(Oa); free(la);
     return err ? LHO_ERR_MEM : LHO_OK;
 }
 
@@ -646,33 +694,38 @@ int lho_backward(const void* q, const void* k, const void* v, const void* dout, 
     ctx_t c = {q, k, v, dout, N, H, d, dtype, p, L, K, lho_subseq_len_sel(N, p, L, K, select_mode), 0,
                select_mode};
     int64_t S = c.S;
+    size_t sd = (size_t)(S * d), hsd = sd * (size_t)H;
     int err = 0;
 #ifdef _OPENMP
     if (nthreads > 0) omp_set_num_threads(nthreads);
 #else
     (void)nthreads;
 #endif
+    /* every head's rows: Q, K, V, O, dO, dQ, dK, dV, and the query rows' statistics */
+    double* buf = (double*)malloc(sizeof(double) * hsd * 8);
+    double* rs = (double*)malloc(sizeof(double) * (size_t)(H * S * RS_N > 0 ? H * S * RS_N : 1));
+    if (!buf || !rs) {
+        free(buf); free(rs);
+        return LHO_ERR_MEM;
+    }
+    double *Qa = buf, *Ka = buf + hsd, *Va = buf + 2 * hsd, *Oa = buf + 3 * hsd;
+    double *dOa = buf + 4 * hsd, *dQa = buf + 5 * hsd, *dKa = buf + 6 * hsd, *dVa = buf + 7 * hsd;
+    if (cond) memset(cond, 0, sizeof(double) * hsd * 8);
+    /* gather (O5) and the adjoint of the scatter (O8): an entry's dO is the sum
+       over its tokens; one head at a time */
 #pragma omp parallel for schedule(dynamic, 1) reduction(| : err)
     for (int h = 0; h < H; ++h) {
         const int32_t* st = sel_start + (int64_t)h * S;
         const int8_t* lv = sel_level + (int64_t)h * S;
-        size_t sd = (size_t)(S * d);
         double* scratch = (double*)malloc(sizeof(double) * (size_t)d * (size_t)(L + 1));
-        double* buf = (double*)malloc(sizeof(double) * sd * 8);
-        double* lse = (double*)malloc(sizeof(double) * (size_t)S);
-        double* logit = (double*)malloc(sizeof(double) * (size_t)S);
-        if (!scratch || !buf || !lse || !logit) {
+        if (!scratch) {
             err |= 1;
-            free(scratch); free(buf); free(lse); free(logit);
             continue;
         }
-        double *Qh = buf, *Kh = buf + sd, *Vh = buf + 2 * sd, *Oh = buf + 3 * sd;
-        double *dOh = buf + 4 * sd, *dQh = buf + 5 * sd, *dKh = buf + 6 * sd, *dVh = buf + 7 * sd;
-        head_gather(&c, q, h, st, lv, Qh, scratch);
-        head_gather(&c, k, h, st, lv, Kh, scratch);
-        head_gather(&c, v, h, st, lv, Vh, scratch);
-        head_attention_fwd(S, d, Qh, Kh, Vh, Oh, lse, logit);
-        /* adjoint of the scatter: an entry's gradient is the sum over its tokens */
+        head_gather(&c, q, h, st, lv, Qa + (size_t)h * sd, scratch);
+        head_gather(&c, k, h, st, lv, Ka + (size_t)h * sd, scratch);
+        head_gather(&c, v, h, st, lv, Va + (size_t)h * sd, scratch);
+        double* dOh = dOa + (size_t)h * sd;
         for (int64_t i = 0; i < S; ++i) {
             int64_t len = ipow(p, lv[i]);
             for (int e = 0; e < d; ++e) dOh[i * d + e] = 0.0;
@@ -681,39 +734,82 @@ int lho_backward(const void* q, const void* k, const void* v, const void* dout, 
                 for (int e = 0; e < d; ++e) dOh[i * d + e] += (double)load_f32(dout, dtype, base + e);
             }
         }
-        double* ch = cond ? (double*)malloc(sizeof(double) * sd * 8) : NULL;
-        head_attention_bwd(S, d, Qh, Kh, Vh, Oh, dOh, dQh, dKh, dVh, logit, ch);
-        if (ch) {
-            for (int z = 0; z < 8; ++z)
-                memcpy(cond + ((int64_t)z * H + h) * S * d, ch + (int64_t)z * S * d, sizeof(double) * sd);
-            free(ch);
+        free(scratch);
+    }
+    /* attention forward (O6) for O, then the gradient (O8): the query side and
+       the key side; one head after the other, its rows in parallel */
+    size_t ntri = (size_t)(tri(S) > 0 ? tri(S) : 1);
+    double* Pt = (double*)malloc(sizeof(double) * ntri);
+    double* dSt = (double*)malloc(sizeof(double) * ntri);
+    double* wt[3] = {NULL, NULL, NULL};
+    for (int z = 0; z < 3 && cond; ++z) {
+        wt[z] = (double*)malloc(sizeof(double) * ntri);
+        if (!wt[z]) err |= 1;
+    }
+    if (!Pt || !dSt) err |= 1;
+    for (int64_t h = 0; h < H && !err; ++h) {
+        double* cz[8];
+        for (int z = 0; z < 8; ++z) cz[z] = cond ? cond + ((size_t)z * H + (size_t)h) * sd : NULL;
+        const double *Qh = Qa + h * sd, *Kh = Ka + h * sd, *Vh = Va + h * sd, *dOh = dOa + h * sd;
+        double* Oh = Oa + h * sd;
+        double* rh = rs + h * S * RS_N;
+#pragma omp parallel reduction(| : err)
+        {
+            double* tmp = (double*)malloc(sizeof(double) * 3 * (size_t)(S > 0 ? S : 1));
+            if (!tmp) err |= 1;
+#pragma omp for schedule(dynamic, 16)
+            for (int64_t i = 0; i < S; ++i)
+                if (tmp) attn_fwd_row(i, d, Qh, Kh, Vh, Oh, NULL, tmp);
+#pragma omp for schedule(dynamic, 16)
+            for (int64_t i = 0; i < S; ++i)
+                if (tmp)
+                    attn_bwd_query_row(i, d, Qh, Kh, Vh, Oh, dOh, dQa + h * sd, rh, Pt, dSt, tmp, tmp + S, tmp + 2 * S,
+                                       cond ? cz : NULL, wt);
+#pragma omp for schedule(dynamic, 16)
+            for (int64_t j = 0; j < S; ++j)
+                attn_bwd_key_row(j, S, d, Qh, dOh, Pt, dSt, dKa + h * sd, dVa + h * sd, cond ? cz : NULL,
+                                 (const double* const*)wt);
+            free(tmp);
         }
-        if (dOt) memcpy(dOt + (int64_t)h * S * d, dOh, sizeof(double) * sd);
-        if (dQt) memcpy(dQt + (int64_t)h * S * d, dQh, sizeof(double) * sd);
-        if (dKt) memcpy(dKt + (int64_t)h * S * d, dKh, sizeof(double) * sd);
-        if (dVt) memcpy(dVt + (int64_t)h * S * d, dVh, sizeof(double) * sd);
-        /* adjoint of the mean-pool: each of the p^l tokens gets 1/p^l of it,
-           summed over the entries that cover the token (one of them unless R2') */
-        for (int64_t t = 0; t < N; ++t) {
-            int64_t base = (t * H + h) * (int64_t)d;
-            for (int e = 0; e < d; ++e) {
-                if (dq) dq[base + e] = 0.0;
-                if (dk) dk[base + e] = 0.0;
-                if (dv) dv[base + e] = 0.0;
-            }
-        }
-        for (int64_t i = 0; i < S; ++i) {
-            int64_t len = ipow(p, lv[i]);
-            for (int64_t t = st[i]; t < st[i] + len; ++t) {
+    }
+    free(Pt);
+    free(dSt);
+    for (int z = 0; z < 3; ++z) free(wt[z]);
+    /* outputs and the adjoint of the mean-pool: each of the p^l tokens gets
+       1/p^l of it, summed over the entries that cover the token (one of them
+       unless R2'); one head at a time */
+    if (!err) {
+#pragma omp parallel for schedule(dynamic, 1)
+        for (int h = 0; h < H; ++h) {
+            const int32_t* st = sel_start + (int64_t)h * S;
+            const int8_t* lv = sel_level + (int64_t)h * S;
+            const double *dQh = dQa + (size_t)h * sd, *dKh = dKa + (size_t)h * sd, *dVh = dVa + (size_t)h * sd;
+            if (dOt) memcpy(dOt + (int64_t)h * S * d, dOa + (size_t)h * sd, sizeof(double) * sd);
+            if (dQt) memcpy(dQt + (int64_t)h * S * d, dQh, sizeof(double) * sd);
+            if (dKt) memcpy(dKt + (int64_t)h * S * d, dKh, sizeof(double) * sd);
+            if (dVt) memcpy(dVt + (int64_t)h * S * d, dVh, sizeof(double) * sd);
+            for (int64_t t = 0; t < N; ++t) {
                 int64_t base = (t * H + h) * (int64_t)d;
                 for (int e = 0; e < d; ++e) {
-                    if (dq) dq[base + e] += dQh[i * d + e] / (double)len;
-                    if (dk) dk[base + e] += dKh[i * d + e] / (double)len;
-                    if (dv) dv[base + e] += dVh[i * d + e] / (double)len;
+                    if (dq) dq[base + e] = 0.0;
+                    if (dk) dk[base + e] = 0.0;
+                    if (dv) dv[base + e] = 0.0;
+                }
+            }
+            for (int64_t i = 0; i < S; ++i) {
+                int64_t len = ipow(p, lv[i]);
+                for (int64_t t = st[i]; t < st[i] + len; ++t) {
+                    int64_t base = (t * H + h) * (int64_t)d;
+                    for (int e = 0; e < d; ++e) {
+                        if (dq) dq[base + e] += dQh[i * d + e] / (double)len;
+                        if (dk) dk[base + e] += dKh[i * d + e] / (double)len;
+                        if (dv) dv[base + e] += dVh[i * d + e] / (double)len;
+                    }
                 }
             }
         }
-        free(scratch); free(buf); free(lse); free(logit);
     }
+    free(buf);
+    free(rs);
     return err ? LHO_ERR_MEM : LHO_OK;
 }
