@@ -272,10 +272,10 @@ __device__ __forceinline__ u32x2 bf16x4_div(const f32x4& x, float den) {
 }
 
 // Scatter inside the attention kernels (Sec. 3 stage (iv), and the pool
-// adjoint of the gradient path): a wavefront's 16 result rows are staged in
-// LDS as bf16, then written to every token of their entries, one 16-byte
-// chunk of one token row per lane, so the kernel's HBM writes overlap the
-// other workgroups' MFMA work instead of running as a pass of their own.
+// adjoint of the gradient path): the workgroup's 64 result rows are staged in
+// LDS as bf16, then written to every token of their entries, so the kernel's
+// HBM writes overlap the other workgroups' MFMA work instead of running as a
+// pass of their own.
 // stage_rows: lane (lq, lg) holds columns 16v + 4lg .. +3 of row lq; the row
 // is stored as bf16 of x * mul / den (den = p^level for the pool adjoint).
 template <int D>
@@ -284,21 +284,60 @@ __device__ __forceinline__ void stage_rows(uint16_t* rows, const f32x4* acc, flo
     for (int v = 0; v < D / 16; ++v)
         *reinterpret_cast<u32x2*>(rows + lq * D + 16 * v + 4 * lg) = bf16x4_div(acc[v] * mul, den);
 }
-template <int D>
-__device__ __forceinline__ void rows_to_tokens(const uint16_t* rows, uint16_t* tok, const AttnK& a, int h,
-                                               int64_t r0, int lane) {
-    constexpr int CPR = D / 8, TPI = 64 / CPR;   // 16-byte chunks per row, tokens per store
-    const int c = lane % CPR, r4 = lane / CPR;
-    for (int j = 0; j < 16; ++j) {
-        const int64_t row = r0 + j;
-        if (row >= a.rows) break;
-        const int64_t st = a.start[(int64_t)h * a.rows + row];
-        int64_t n = 1;
+// Token table of the workgroup's 64 entries (rows r0 .. r0+63 of head h), by
+// the first wavefront: tab[e] is the number of tokens of entries 0 .. e-1
+// (tab[64] the total) and tab[65 + e] the first token of entry e.  Rows past
+// the sub-sequence have no tokens.  Published by the caller's next barrier.
+constexpr int kTokTab = 129;
+__device__ __forceinline__ void token_table(const AttnK& a, int h, int64_t r0, int64_t* tab) {
+    if (threadIdx.x >= 64) return;
+    const int e = threadIdx.x;
+    const int64_t row = r0 + e;
+    int64_t n = 0, first = 0;
+    if (row < a.rows) {
+        first = a.start[(int64_t)h * a.rows + row];
+        n = 1;
         for (int z = a.level[(int64_t)h * a.rows + row]; z > 0; --z) n *= a.p;
-        const u32x4 x = *reinterpret_cast<const u32x4*>(rows + j * D + 8 * c);
-        uint16_t* dst = tok + st * a.tok_ld + (int64_t)h * D + 8 * c;
-        for (int64_t t = r4; t < n; t += TPI)
-            __builtin_nontemporal_store(x, reinterpret_cast<u32x4*>(dst + t * a.tok_ld));
+    }
+    int64_t incl = n;   // inclusive prefix sum over the wavefront
+#pragma unroll
+    for (int k = 1; k < 64; k <<= 1) {
+        const int64_t u = __shfl_up(incl, k);
+        if (e >= k) incl += u;
+    }
+    tab[e + 1] = incl;
+    if (e == 0) tab[0] = 0;
+    tab[65 + e] = first;
+}
+// Writes the staged rows (NT tensors; entry e's row at rows_j + e * D) to
+// their tokens.  The work is flattened over (token, 16-byte chunk), so all
+// four wavefronts share it evenly whatever the entries' sizes: thread t keeps
+// chunk t % (D/8) and walks the workgroup's tokens 256/(D/8) apart, loading
+// its chunk from LDS only when it crosses into the next entry.
+template <int D, int NT>
+__device__ __forceinline__ void tile_to_tokens(const uint16_t* rows0, const uint16_t* rows1, uint16_t* tok0,
+                                               uint16_t* tok1, const AttnK& a, int h, const int64_t* tab) {
+    constexpr int CPR = D / 8, TPI = 256 / CPR;   // 16-byte chunks per row, tokens per pass
+    const int c = threadIdx.x % CPR;
+    const int64_t total = tab[64];
+    const int64_t col = (int64_t)h * D + 8 * c;
+    int e = -1;
+    int64_t end = 0;          // flat index one past entry e's last token
+    int64_t shift = 0;        // first token of entry e minus its flat offset
+    u32x4 x0 = {0u, 0u, 0u, 0u}, x1 = {0u, 0u, 0u, 0u};
+    for (int64_t t = threadIdx.x / CPR; t < total; t += TPI) {
+        if (t >= end) {
+            do {
+                ++e;
+                end = tab[e + 1];
+            } while (t >= end);
+            shift = tab[65 + e] - tab[e];
+            x0 = *reinterpret_cast<const u32x4*>(rows0 + e * D + 8 * c);
+            if constexpr (NT == 2) x1 = *reinterpret_cast<const u32x4*>(rows1 + e * D + 8 * c);
+        }
+        const int64_t o = (shift + t) * a.tok_ld + col;
+        __builtin_nontemporal_store(x0, reinterpret_cast<u32x4*>(tok0 + o));
+        if constexpr (NT == 2) __builtin_nontemporal_store(x1, reinterpret_cast<u32x4*>(tok1 + o));
     }
 }
 
@@ -331,6 +370,7 @@ __global__ void __launch_bounds__(256) k_attn_fwd(AttnK a) {
     // buffer each, refilled by direct copies while the other one is in use
     constexpr int KR = NA * T::ROW;
     __shared__ __attribute__((aligned(16))) uint16_t sm[KR + NA * T::TR];
+    __shared__ int64_t ttab[kTokTab];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int lq = lane & 15, lg = lane >> 4;
     const int64_t Sp = a.Sp;
@@ -524,10 +564,10 @@ __global__ void __launch_bounds__(256) k_attn_fwd(AttnK a) {
         a.lse[(int64_t)h * Sp + myq] = l2 * kLn2;
     }
     if (a.o_tok) {   // the LDS tiles are idle: every wave is past the loop's last barrier
-        uint16_t* rows = sm + wave * 16 * D;
-        stage_rows<D>(rows, o, mul, 1.0f, lq, lg);
+        token_table(a, h, (int64_t)qt * 64, ttab);
+        stage_rows<D>(sm + wave * 16 * D, o, mul, 1.0f, lq, lg);
         __syncthreads();
-        rows_to_tokens<D>(rows, a.o_tok, a, h, q0, lane);
+        tile_to_tokens<D, 1>(sm, nullptr, a.o_tok, nullptr, a, h, ttab);
     }
 }
 
@@ -543,7 +583,8 @@ struct DkdvLds {
     static constexpr int ELEMS = ROWS + (SPLIT ? 2 : 1) * 2 * Tiles<D>::TR;
 };
 template <int D, bool SPLIT, bool OUT_BF16>
-__device__ __forceinline__ void dkdv_body(const AttnK& a, uint16_t* __restrict__ sm, float* __restrict__ qstat, int h,
+__device__ __forceinline__ void dkdv_body(const AttnK& a, uint16_t* __restrict__ sm, float* __restrict__ qstat,
+                                          int64_t* __restrict__ ttab, int h,
                                           int kt) {
     using T = Tiles<D>;
     constexpr int NS = D / 32, NV = D / 16;
@@ -724,14 +765,12 @@ __device__ __forceinline__ void dkdv_body(const AttnK& a, uint16_t* __restrict__
         }
     }
     if (a.dk_tok) {   // pool adjoint of k and v: dK~ / p^level, dV~ / p^level to the entry's tokens
-        uint16_t* rk = sm + wave * 16 * D;
-        uint16_t* rv = sm + (4 + wave) * 16 * D;
+        token_table(a, h, (int64_t)kt * 64, ttab);
         const float den = mykey < a.rows ? level_den(a, h, mykey) : 1.0f;
-        stage_rows<D>(rk, dk, kmul, den, lq, lg);
-        stage_rows<D>(rv, dv, vmul, den, lq, lg);
+        stage_rows<D>(sm + wave * 16 * D, dk, kmul, den, lq, lg);
+        stage_rows<D>(sm + (4 + wave) * 16 * D, dv, vmul, den, lq, lg);
         __syncthreads();
-        rows_to_tokens<D>(rk, a.dk_tok, a, h, k0, lane);
-        rows_to_tokens<D>(rv, a.dv_tok, a, h, k0, lane);
+        tile_to_tokens<D, 2>(sm, sm + 64 * D, a.dk_tok, a.dv_tok, a, h, ttab);
     }
 }
 
@@ -748,7 +787,8 @@ struct DqLds {
     static constexpr int ELEMS = ROWS + (SPLIT ? 2 : 1) * Tiles<D>::TR;
 };
 template <int D, bool SPLIT, bool OUT_BF16>
-__device__ __forceinline__ void dq_body(const AttnK& a, uint16_t* __restrict__ sm, int h, int qt) {
+__device__ __forceinline__ void dq_body(const AttnK& a, uint16_t* __restrict__ sm, int64_t* __restrict__ ttab, int h,
+                                        int qt) {
     using T = Tiles<D>;
     constexpr int NS = D / 32, NV = D / 16;
     constexpr int NA = SPLIT ? 2 : 1;
@@ -919,39 +959,39 @@ __device__ __forceinline__ void dq_body(const AttnK& a, uint16_t* __restrict__ s
         }
     }
     if (a.dq_tok) {   // pool adjoint of q: dQ~ / p^level to every token of the entry
-        uint16_t* rows = sm + wave * 16 * D;
+        token_table(a, h, (int64_t)qt * 64, ttab);
         const float den = myq < a.rows ? level_den(a, h, myq) : 1.0f;
-        stage_rows<D>(rows, dq, mul, den, lq, lg);
+        stage_rows<D>(sm + wave * 16 * D, dq, mul, den, lq, lg);
         __syncthreads();
-        rows_to_tokens<D>(rows, a.dq_tok, a, h, q0, lane);
+        tile_to_tokens<D, 1>(sm, nullptr, a.dq_tok, nullptr, a, h, ttab);
     }
 }
 
 // ------------------------------------------------------- backward: launch
-// One launch runs both gradient roles: workgroup i takes role i & 1 (0: dK/dV
-// of a key tile, 1: dQ of a query tile) in the order a dispatch sees them, so
-// each role's token writes overlap the other role's MFMA work.  When H is a
-// multiple of 8, both roles of a head run on the XCD of that head (workgroup
-// i runs on XCD i % 8), where its operands sit in L2.  Tile order within a
-// role: dQ takes its longest query tiles first; dK/dV, when it writes token
-// rows, its shortest key tiles first (their writes start early, beside dQ's
-// long tiles), and otherwise its longest first.
-__device__ __forceinline__ void bwd_item(int nT, int H, bool dkdv_short_first, int& role, int& h, int& tile) {
+// One launch runs both gradient roles: 0, dK/dV of a key tile, and 1, dQ of a
+// query tile.  Key tile t of the dK/dV role and query tile nT-1-t of the dQ
+// role both sweep nT - t tiles: rank r = t.  Workgroups are dispatched in
+// order of rank, longest first, the two roles of one rank side by side, so
+// a workgroup that frees its slot late in the launch takes a short item
+// (longest-processing-time-first list scheduling) and the token writes of
+// short items fill the end of the launch.  When H is a multiple of 8, head h
+// runs on XCD h % 8 (workgroup i runs on XCD i % 8), where its operands sit
+// in that XCD's L2.
+__device__ __forceinline__ void bwd_item(int nT, int H, int& role, int& h, int& tile) {
     const int i = blockIdx.x;
-    int j;
+    int r;
     if (H % 8 == 0) {
-        const int x = i % 8, q = i / 8;
+        const int G = H / 8, x = i % 8, q = i / 8;
         role = q & 1;
-        const int jj = q >> 1;
-        h = x + 8 * (jj / nT);
-        j = jj % nT;
+        r = q / (2 * G);
+        h = x + 8 * ((q >> 1) % G);
     } else {
         role = i & 1;
         const int jj = i >> 1;
-        h = jj / nT;
-        j = jj % nT;
+        r = jj / H;
+        h = jj % H;
     }
-    tile = (role == 1 || dkdv_short_first) ? nT - 1 - j : j;
+    tile = role == 0 ? r : nT - 1 - r;
 }
 
 template <int D, bool SPLIT, bool OUT_BF16>
@@ -959,11 +999,12 @@ __global__ void __launch_bounds__(256) k_attn_bwd(AttnK a) {
     constexpr int E1 = DkdvLds<D, SPLIT>::ELEMS, E2 = DqLds<D, SPLIT>::ELEMS;
     __shared__ __attribute__((aligned(16))) uint16_t sm[E1 > E2 ? E1 : E2];
     __shared__ __attribute__((aligned(16))) float qstat[2 * kBN];
+    __shared__ int64_t ttab[kTokTab];
     const int nT = (int)(a.Sp / 64);
     int role, h, tile;
-    bwd_item(nT, (int)(gridDim.x / (2 * nT)), a.dk_tok != nullptr, role, h, tile);
-    if (role == 0) dkdv_body<D, SPLIT, OUT_BF16>(a, sm, qstat, h, tile);
-    else dq_body<D, SPLIT, OUT_BF16>(a, sm, h, tile);
+    bwd_item(nT, (int)(gridDim.x / (2 * nT)), role, h, tile);
+    if (role == 0) dkdv_body<D, SPLIT, OUT_BF16>(a, sm, qstat, ttab, h, tile);
+    else dq_body<D, SPLIT, OUT_BF16>(a, sm, ttab, h, tile);
 }
 
 // ------------------------------------------------------------- fp32 path
