@@ -126,7 +126,15 @@ struct Tiles {
     static constexpr int CH_T = D * 4 / 256;
 };
 
-__device__ __forceinline__ int swz_row(int r, int slot, int nslot) { return slot ^ (r & (nslot - 1)); }
+// Row tiles: slot s of row r holds the row's 16-byte chunk s ^ f(r).  At d = 128
+// (16 slots) f rotates the row's low four bits left by one, so that both reads
+// of a row tile touch distinct banks: a fragment read (16 rows, one slot each)
+// and a transposed read (frag_tr: 8 rows per half-wave, a pair of adjacent
+// slots each, and rows 2i and 2i+1 land in different pairs).
+__device__ __forceinline__ int swz_row(int r, int slot, int nslot) {
+    const int f = nslot == 16 ? (((r << 1) | ((r >> 3) & 1)) & 15) : (r & (nslot - 1));
+    return slot ^ f;
+}
 // Transposed tiles have 64-byte rows (4 slots).  A ds_read_b128 of rows
 // r0..r0+15 (r0 a multiple of 16) at one slot per 16-lane group runs at the
 // full 256 B/clk on gfx950 with this XOR (measured; (r >> 2) & 3 and no
@@ -250,6 +258,25 @@ __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70)
 template <int D>
 __device__ __forceinline__ u32x4 frag_row(const uint16_t* lds, int r, int c) {
     return *reinterpret_cast<const u32x4*>(lds + r * D + swz_row(r, c, Tiles<D>::NSLOT) * 8);
+}
+// Fragment of a row tile read across its rows (gfx950 ds_read_b64_tr_b16): lane
+// (lq, g) receives column c0 + lq of rows 4g..4g+3 and 16+4g..16+4g+3, the
+// contraction order in which the score fragments hold a block's positions.
+// Within each 16-lane group the instruction hands lane t element t % 4 of the
+// 8 bytes addressed by lane 4k + t / 4 as its k-th value; so lane s addresses
+// row 4g + s / 4 (then 16 + 4g + s / 4), columns c0 + 4 (s % 4) .. + 3.
+typedef __fp16 f16x4t __attribute__((__vector_size__(4 * sizeof(__fp16))));
+template <int D>
+__device__ __forceinline__ u32x4 frag_tr(const uint16_t* lds, int c0, int lq, int g) {
+    const int r = 4 * g + (lq >> 2);
+    const int col = c0 + 4 * (lq & 3);
+    const int ch = col >> 3, e = col & 7;
+    const uint16_t* p0 = lds + r * D + swz_row(r, ch, Tiles<D>::NSLOT) * 8 + e;
+    const uint16_t* p1 = lds + (r + 16) * D + swz_row(r + 16, ch, Tiles<D>::NSLOT) * 8 + e;
+    const f16x4t x0 = __builtin_amdgcn_ds_read_tr16_b64_v4f16((__attribute__((address_space(3))) f16x4t*)(p0));
+    const f16x4t x1 = __builtin_amdgcn_ds_read_tr16_b64_v4f16((__attribute__((address_space(3))) f16x4t*)(p1));
+    const u32x2 a = __builtin_bit_cast(u32x2, x0), b = __builtin_bit_cast(u32x2, x1);
+    return u32x4{a[0], a[1], b[0], b[1]};
 }
 // fragment of transposed tile: row r, sequence positions {4g..4g+3} and
 // {16+4g..16+4g+3} of the block, which the split stores as the 16-byte run g
@@ -574,24 +601,24 @@ __global__ void __launch_bounds__(256) k_attn_fwd(AttnK a) {
 // ------------------------------------------------------- backward: dK, dV
 // Key-stationary: wave w owns keys k0..k0+15 (lane column = key) of key tile
 // kt of head h; the query blocks at or after the workgroup's keys stream
-// through LDS.  LDS, one buffer each: q and dO rows (read by the score phase),
-// q^T and dO^T (read by the gradient phase); each group is refilled as soon as
-// every wave is past its phase: 64 KiB at d = 128 with split operands.
+// through LDS as row tiles (q and dO, hi and lo), two blocks' worth: the copy
+// of block b + 1 is in flight during all of block b's work, and one barrier
+// per block orders it.  The score phase reads the rows directly, the gradient
+// phase reads them across (frag_tr): no transposed copies.  64 KiB at d = 128
+// with split operands.
 template <int D, bool SPLIT>
 struct DkdvLds {
-    static constexpr int ROWS = (SPLIT ? 2 : 1) * 2 * Tiles<D>::ROW;
-    static constexpr int ELEMS = ROWS + (SPLIT ? 2 : 1) * 2 * Tiles<D>::TR;
+    static constexpr int STAGE = (SPLIT ? 2 : 1) * 2 * Tiles<D>::ROW;
+    static constexpr int ELEMS = 2 * STAGE;
 };
 template <int D, bool SPLIT, bool OUT_BF16>
 __device__ __forceinline__ void dkdv_body(const AttnK& a, uint16_t* __restrict__ sm, float* __restrict__ qstat,
-                                          int64_t* __restrict__ ttab, int h,
-                                          int kt) {
+                                          int64_t* __restrict__ ttab, int h, int kt) {
     using T = Tiles<D>;
     constexpr int NS = D / 32, NV = D / 16;
     constexpr int NA = SPLIT ? 2 : 1;
-    constexpr int ROWS = DkdvLds<D, SPLIT>::ROWS;
-    // qstat: per-query lse2 and D of the block, copied with the rows: the score
-    // phase then waits on no global load issued after the transposed-tile copies
+    constexpr int STAGE = DkdvLds<D, SPLIT>::STAGE;
+    // qstat: per stage, the block's per-query lse2 and D, copied with the rows
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int lq = lane & 15, lg = lane >> 4;
     const int64_t Sp = a.Sp;
@@ -626,123 +653,99 @@ __device__ __forceinline__ void dkdv_body(const AttnK& a, uint16_t* __restrict__
     // query blocks run from the last one down, so the workgroups of a head read
     // the same block at about the same time (one L2 working set per head)
     auto qblock = [&](int b) { return qfirst + (int64_t)(nblk - 1 - b) * kBN; };
-    // layout: [qh][ql?][doh][dol?] rows, then [qTh][qTl?][doTh][doTl?]
-    auto loadA = [&](int b) {
+    // stage layout: [qh][ql?][doh][dol?] row tiles
+    auto load = [&](int b) {
         const int64_t qb = qblock(b);
+        uint16_t* base = sm + (b & 1) * STAGE;
         if (wave == 0) {   // lanes 0..31: lse2, lanes 32..63: D (qb + 32 <= Sp)
             const float* src = (lane < kBN ? lse2 : Dv) + qb + (lane & (kBN - 1));
-            __builtin_amdgcn_global_load_lds(src, LH_LDS_PTR(qstat), 4, 0, 0);
+            __builtin_amdgcn_global_load_lds(src, LH_LDS_PTR(qstat + (b & 1) * 2 * kBN), 4, 0, 0);
         }
-        dma_row<D>(a.qh + hb, qb, sm);
-        dma_row<D>(a.doh + hb, qb, sm + NA * T::ROW);
+        dma_row<D>(a.qh + hb, qb, base);
+        dma_row<D>(a.doh + hb, qb, base + NA * T::ROW);
         if constexpr (SPLIT) {
-            dma_row<D>(a.ql + hb, qb, sm + T::ROW);
-            dma_row<D>(a.dol + hb, qb, sm + 3 * T::ROW);
+            dma_row<D>(a.ql + hb, qb, base + T::ROW);
+            dma_row<D>(a.dol + hb, qb, base + 3 * T::ROW);
         }
     };
-    auto loadB = [&](int b) {
-        const int64_t qb = qblock(b);
-        uint16_t* base = sm + ROWS;
-        dma_t<D>(a.qTh + hb, Sp, qb, base);
-        dma_t<D>(a.doTh + hb, Sp, qb, base + NA * T::TR);
-        if constexpr (SPLIT) {
-            dma_t<D>(a.qTl + hb, Sp, qb, base + T::TR);
-            dma_t<D>(a.doTl + hb, Sp, qb, base + 3 * T::TR);
-        }
-    };
-    if (nblk > 0) {
-        loadA(0);
-        loadB(0);
-    }
-    wait_vmem();
-    __syncthreads();
-    const uint16_t* Qh = sm;
-    const uint16_t* Ql = sm + T::ROW;
-    const uint16_t* Oh = sm + NA * T::ROW;
-    const uint16_t* Ol = Oh + T::ROW;
-    const uint16_t* QTh = sm + ROWS;
-    const uint16_t* QTl = QTh + T::TR;
-    const uint16_t* OTh = QTh + NA * T::TR;
-    const uint16_t* OTl = OTh + T::TR;
-    // Per block: the score phase reads the rows while this block's transposed
-    // tiles may still be arriving; the barrier after it publishes them and frees
-    // the rows, which are refilled during the gradient phase; the second barrier
-    // publishes the rows and frees the transposed tiles for the next block.
+    if (nblk > 0) load(0);
     for (int b = 0; b < nblk; ++b) {
-        const bool more = b + 1 < nblk;
+        // block b has landed (this wave's copies; the barrier covers the others')
+        // and every wave is past block b - 1, whose stage the next copy refills
+        wait_vmem();
+        __syncthreads();
+        if (b + 1 < nblk) load(b + 1);
         const int64_t qb = qblock(b);
         const bool active = qb + kBN > k0;   // some query of the block sees some key of the wave
+        if (!active) continue;
+        const uint16_t* Qh = sm + (b & 1) * STAGE;
+        const uint16_t* Ql = Qh + T::ROW;
+        const uint16_t* Oh = Qh + NA * T::ROW;
+        const uint16_t* Ol = Oh + T::ROW;
+        const float* qs = qstat + (b & 1) * 2 * kBN;
         f32x4 P[2], dS[2];
-        if (active) {
 #pragma unroll
-            for (int u = 0; u < 2; ++u) {
-                f32x4 s = {0.f, 0.f, 0.f, 0.f}, dp = {0.f, 0.f, 0.f, 0.f};
-                const int r = 16 * u + lq;
+        for (int u = 0; u < 2; ++u) {
+            f32x4 s = {0.f, 0.f, 0.f, 0.f}, dp = {0.f, 0.f, 0.f, 0.f};
+            const int r = 16 * u + lq;
 #pragma unroll
-                for (int st = 0; st < NS; ++st) {
-                    const f16x8 qh = __builtin_bit_cast(f16x8, frag_row<D>(Qh, r, 4 * st + lg));
-                    const f16x8 oh = __builtin_bit_cast(f16x8, frag_row<D>(Oh, r, 4 * st + lg));
-                    s = mma_h(qh, kfh[st], s);
-                    dp = mma_h(oh, vfh[st], dp);
-                    if constexpr (SPLIT) {
-                        s = mma_h(qh, kfl[st], s);
-                        s = mma_h(__builtin_bit_cast(f16x8, frag_row<D>(Ql, r, 4 * st + lg)), kfh[st], s);
-                        dp = mma_h(oh, vfl[st], dp);
-                        dp = mma_h(__builtin_bit_cast(f16x8, frag_row<D>(Ol, r, 4 * st + lg)), vfh[st], dp);
-                    }
-                }
-                const int64_t qq = qb + 16 * u + 4 * lg;
-                const f32x4 l4 = *reinterpret_cast<const f32x4*>(qstat + 16 * u + 4 * lg);
-                const f32x4 d4 = *reinterpret_cast<const f32x4*>(qstat + kBN + 16 * u + 4 * lg);
-#pragma unroll
-                for (int r2 = 0; r2 < 4; ++r2) {
-                    const int q = (int)qq + r2;
-                    float pr = fast_exp2(s[r2] * cS - l4[r2]);   // P * 2^kPBwd
-                    pr = (q >= (int)mykey && q < (int)a.rows) ? pr : 0.f;
-                    P[u][r2] = pr;
-                    dS[u][r2] = pr * (dp[r2] * cP - d4[r2]);
-                }
-            }
-        }
-        wait_vmem();
-        __syncthreads();
-        if (more) loadA(b + 1);
-        if (active) {
-            f16x8 ph, pl;
-            split_h(P[0], P[1], ph, pl);
-            // this key's dS column, brought below 2^14 by its running power of two
-            float bm = 0.f;
-#pragma unroll
-            for (int u = 0; u < 2; ++u)
-#pragma unroll
-                for (int r2 = 0; r2 < 4; ++r2) bm = fmaxf(bm, fabsf(dS[u][r2]));
-            bm = rows4_max(bm);
-            if (__ballot(bm * smul >= 16384.0f) != 0) {
-                const float f = column_scale(bm, smul);
-#pragma unroll
-                for (int v = 0; v < NV; ++v) dk[v] *= f;
-            }
-            f16x8 sh, sl;
-            split_h(dS[0] * smul, dS[1] * smul, sh, sl);
-#pragma unroll
-            for (int v = 0; v < NV; ++v) {
-                const int r = 16 * v + lq;
-                const f16x8 oth = __builtin_bit_cast(f16x8, frag_t(OTh, r, lg));
-                dv[v] = mma_h(oth, ph, dv[v]);
-                dv[v] = mma_h(oth, pl, dv[v]);
-                const f16x8 qth = __builtin_bit_cast(f16x8, frag_t(QTh, r, lg));
-                dk[v] = mma_h(qth, sh, dk[v]);
-                dk[v] = mma_h(qth, sl, dk[v]);
+            for (int st = 0; st < NS; ++st) {
+                const f16x8 qh = __builtin_bit_cast(f16x8, frag_row<D>(Qh, r, 4 * st + lg));
+                const f16x8 oh = __builtin_bit_cast(f16x8, frag_row<D>(Oh, r, 4 * st + lg));
                 if constexpr (SPLIT) {
-                    dv[v] = mma_h(__builtin_bit_cast(f16x8, frag_t(OTl, r, lg)), ph, dv[v]);
-                    dk[v] = mma_h(__builtin_bit_cast(f16x8, frag_t(QTl, r, lg)), sh, dk[v]);
+                    s = mma_h(qh, kfl[st], s);
+                    s = mma_h(__builtin_bit_cast(f16x8, frag_row<D>(Ql, r, 4 * st + lg)), kfh[st], s);
+                    dp = mma_h(oh, vfl[st], dp);
+                    dp = mma_h(__builtin_bit_cast(f16x8, frag_row<D>(Ol, r, 4 * st + lg)), vfh[st], dp);
                 }
+                s = mma_h(qh, kfh[st], s);
+                dp = mma_h(oh, vfh[st], dp);
+            }
+            const int64_t qq = qb + 16 * u + 4 * lg;
+            const f32x4 l4 = *reinterpret_cast<const f32x4*>(qs + 16 * u + 4 * lg);
+            const f32x4 d4 = *reinterpret_cast<const f32x4*>(qs + kBN + 16 * u + 4 * lg);
+#pragma unroll
+            for (int r2 = 0; r2 < 4; ++r2) {
+                const int q = (int)qq + r2;
+                float pr = fast_exp2(s[r2] * cS - l4[r2]);   // P * 2^kPBwd
+                pr = (q >= (int)mykey && q < (int)a.rows) ? pr : 0.f;
+                P[u][r2] = pr;
+                dS[u][r2] = pr * (dp[r2] * cP - d4[r2]);
             }
         }
-        wait_vmem();
-        __syncthreads();
-        if (more) loadB(b + 1);
+        f16x8 ph, pl;
+        split_h(P[0], P[1], ph, pl);
+        // this key's dS column, brought below 2^14 by its running power of two
+        float bm = 0.f;
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+            for (int r2 = 0; r2 < 4; ++r2) bm = fmaxf(bm, fabsf(dS[u][r2]));
+        bm = rows4_max(bm);
+        if (__ballot(bm * smul >= 16384.0f) != 0) {
+            const float f = column_scale(bm, smul);
+#pragma unroll
+            for (int v = 0; v < NV; ++v) dk[v] *= f;
+        }
+        f16x8 sh, sl;
+        split_h(dS[0] * smul, dS[1] * smul, sh, sl);
+        // dV^T += dO^T P and dK^T += Q^T dS: the transposed operands are the
+        // rows read across; small split terms first, hi * hi last
+#pragma unroll
+        for (int v = 0; v < NV; ++v) {
+            const f16x8 oth = __builtin_bit_cast(f16x8, frag_tr<D>(Oh, 16 * v, lq, lg));
+            const f16x8 qth = __builtin_bit_cast(f16x8, frag_tr<D>(Qh, 16 * v, lq, lg));
+            if constexpr (SPLIT) {
+                dv[v] = mma_h(__builtin_bit_cast(f16x8, frag_tr<D>(Ol, 16 * v, lq, lg)), ph, dv[v]);
+                dk[v] = mma_h(__builtin_bit_cast(f16x8, frag_tr<D>(Ql, 16 * v, lq, lg)), sh, dk[v]);
+            }
+            dv[v] = mma_h(oth, pl, dv[v]);
+            dk[v] = mma_h(qth, sl, dk[v]);
+            dv[v] = mma_h(oth, ph, dv[v]);
+            dk[v] = mma_h(qth, sh, dk[v]);
+        }
     }
+    __syncthreads();   // every wave is done with the last stage before the LDS is reused
     // dk[v][r], dv[v][r] hold the gradients of key mykey at d-index 16v + 4g + r,
     // times smul 2^kPBwd / (scale mq) and 2^kPBwd / mdo
     const float kmul = a.scale * mq * kInvPBwd / smul, vmul = mdo * kInvPBwd;
@@ -776,15 +779,14 @@ __device__ __forceinline__ void dkdv_body(const AttnK& a, uint16_t* __restrict__
 
 // ---------------------------------------------------------- backward: dQ
 // Query-stationary: wave w owns queries q0..q0+15 of query tile qt of head h,
-// and the key blocks up to the diagonal stream through LDS.  Each query's dS
-// row carries a running power of two (column_scale) before the fp16 split; it
-// is undone at the end.  LDS: k and v rows (read by the score phase) and k^T
-// (read by the dQ phase), one buffer each, refilled by direct copies while the
-// other one is in use: 48 KiB at d = 128 with split operands.
+// and the key blocks up to the diagonal stream through LDS as row tiles (k and
+// v, hi and lo), two blocks' worth, like dK/dV.  dQ = dS K reads the k rows
+// across (frag_tr).  Each query's dS row carries a running power of two
+// (column_scale) before the fp16 split; it is undone at the end.
 template <int D, bool SPLIT>
 struct DqLds {
-    static constexpr int ROWS = (SPLIT ? 2 : 1) * 2 * Tiles<D>::ROW;
-    static constexpr int ELEMS = ROWS + (SPLIT ? 2 : 1) * Tiles<D>::TR;
+    static constexpr int STAGE = (SPLIT ? 2 : 1) * 2 * Tiles<D>::ROW;
+    static constexpr int ELEMS = 2 * STAGE;
 };
 template <int D, bool SPLIT, bool OUT_BF16>
 __device__ __forceinline__ void dq_body(const AttnK& a, uint16_t* __restrict__ sm, int64_t* __restrict__ ttab, int h,
@@ -792,7 +794,7 @@ __device__ __forceinline__ void dq_body(const AttnK& a, uint16_t* __restrict__ s
     using T = Tiles<D>;
     constexpr int NS = D / 32, NV = D / 16;
     constexpr int NA = SPLIT ? 2 : 1;
-    constexpr int ROWS = DqLds<D, SPLIT>::ROWS;
+    constexpr int STAGE = DqLds<D, SPLIT>::STAGE;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int lq = lane & 15, lg = lane >> 4;
     const int64_t Sp = a.Sp;
@@ -823,126 +825,109 @@ __device__ __forceinline__ void dq_body(const AttnK& a, uint16_t* __restrict__ s
     for (int v = 0; v < NV; ++v) dq[v] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     const int nblk = (int)(((int64_t)qt * 64 + 64) / kBN);
-    auto loadA = [&](int b) {
+    // stage layout: [kh][kl?][vh][vl?] row tiles
+    auto load = [&](int b) {
         const int64_t kb = (int64_t)b * kBN;
-        dma_row<D>(a.kh + hb, kb, sm);
-        dma_row<D>(a.vh + hb, kb, sm + NA * T::ROW);
+        uint16_t* base = sm + (b & 1) * STAGE;
+        dma_row<D>(a.kh + hb, kb, base);
+        dma_row<D>(a.vh + hb, kb, base + NA * T::ROW);
         if constexpr (SPLIT) {
-            dma_row<D>(a.kl + hb, kb, sm + T::ROW);
-            dma_row<D>(a.vl + hb, kb, sm + 3 * T::ROW);
+            dma_row<D>(a.kl + hb, kb, base + T::ROW);
+            dma_row<D>(a.vl + hb, kb, base + 3 * T::ROW);
         }
     };
-    auto loadB = [&](int b) {
-        const int64_t kb = (int64_t)b * kBN;
-        dma_t<D>(a.kTh + hb, Sp, kb, sm + ROWS);
-        if constexpr (SPLIT) dma_t<D>(a.kTl + hb, Sp, kb, sm + ROWS + T::TR);
-    };
-    loadA(0);
-    loadB(0);
-    wait_vmem();
-    __syncthreads();
-    const uint16_t* Kh = sm;
-    const uint16_t* Kl = sm + T::ROW;
-    const uint16_t* Vh = sm + NA * T::ROW;
-    const uint16_t* Vl = Vh + T::ROW;
-    const uint16_t* KTh = sm + ROWS;
-    const uint16_t* KTl = KTh + T::TR;
-    // Per block: scores from the rows while this block's k^T may still be
-    // arriving; the barrier publishes k^T and frees the rows, refilled during the
-    // dQ phase; the second barrier publishes the rows and frees k^T.
+    load(0);
     for (int b = 0; b < nblk; ++b) {
-        const bool more = b + 1 < nblk;
+        wait_vmem();
+        __syncthreads();
+        if (b + 1 < nblk) load(b + 1);
         const int64_t kb = (int64_t)b * kBN;
         const bool active = kb < q0 + 16;
+        if (!active) continue;
+        const uint16_t* Kh = sm + (b & 1) * STAGE;
+        const uint16_t* Kl = Kh + T::ROW;
+        const uint16_t* Vh = Kh + NA * T::ROW;
+        const uint16_t* Vl = Vh + T::ROW;
         f32x4 dS[2];
-        if (active) {
 #pragma unroll
-            for (int u = 0; u < 2; ++u) {
-                // the key tile's fragments first, then its products in four
-                // independent chains (s and dp, by parity of the d step)
-                const int r = 16 * u + lq;
-                f16x8 kh[NS], kl[NS], vh[NS], vl[NS];
+        for (int u = 0; u < 2; ++u) {
+            // the key tile's fragments first, then its products in four
+            // independent chains (s and dp, by parity of the d step)
+            const int r = 16 * u + lq;
+            f16x8 kh[NS], kl[NS], vh[NS], vl[NS];
 #pragma unroll
-                for (int st = 0; st < NS; ++st) {
-                    kh[st] = __builtin_bit_cast(f16x8, frag_row<D>(Kh, r, 4 * st + lg));
-                    vh[st] = __builtin_bit_cast(f16x8, frag_row<D>(Vh, r, 4 * st + lg));
-                    if constexpr (SPLIT) {
-                        kl[st] = __builtin_bit_cast(f16x8, frag_row<D>(Kl, r, 4 * st + lg));
-                        vl[st] = __builtin_bit_cast(f16x8, frag_row<D>(Vl, r, 4 * st + lg));
-                    }
-                }
-                __builtin_amdgcn_sched_barrier(0);
-                f32x4 s2[2], dp2[2];
-#pragma unroll
-                for (int e = 0; e < 2; ++e) s2[e] = dp2[e] = f32x4{0.f, 0.f, 0.f, 0.f};
-                // small split terms first, hi*hi last (an MFMA rounds at the scale of
-                // its largest addend)
+            for (int st = 0; st < NS; ++st) {
+                kh[st] = __builtin_bit_cast(f16x8, frag_row<D>(Kh, r, 4 * st + lg));
+                vh[st] = __builtin_bit_cast(f16x8, frag_row<D>(Vh, r, 4 * st + lg));
                 if constexpr (SPLIT) {
-#pragma unroll
-                    for (int st = 0; st < NS; ++st) {
-                        s2[st & 1] = mma_h(kh[st], qfl[st], s2[st & 1]);
-                        dp2[st & 1] = mma_h(vh[st], dfl[st], dp2[st & 1]);
-                    }
-#pragma unroll
-                    for (int st = 0; st < NS; ++st) {
-                        s2[st & 1] = mma_h(kl[st], qfh[st], s2[st & 1]);
-                        dp2[st & 1] = mma_h(vl[st], dfh[st], dp2[st & 1]);
-                    }
+                    kl[st] = __builtin_bit_cast(f16x8, frag_row<D>(Kl, r, 4 * st + lg));
+                    vl[st] = __builtin_bit_cast(f16x8, frag_row<D>(Vl, r, 4 * st + lg));
                 }
-#pragma unroll
-                for (int st = 0; st < NS; ++st) {
-                    s2[st & 1] = mma_h(kh[st], qfh[st], s2[st & 1]);
-                    dp2[st & 1] = mma_h(vh[st], dfh[st], dp2[st & 1]);
-                }
-                const f32x4 s = s2[0] + s2[1], dp = dp2[0] + dp2[1];
-#pragma unroll
-                for (int r2 = 0; r2 < 4; ++r2) {
-                    const int key = (int)kb + 16 * u + 4 * lg + r2;
-                    float pr = fast_exp2(s[r2] * cS - l2);   // P * 2^kPBwd
-                    pr = key <= (int)myq ? pr : 0.f;
-                    dS[u][r2] = pr * (dp[r2] * cP - Dq);
-                }
-            }
-        }
-        wait_vmem();
-        __syncthreads();
-        if (more) loadA(b + 1);
-        if (active) {
-            float bm = 0.f;
-#pragma unroll
-            for (int u = 0; u < 2; ++u)
-#pragma unroll
-                for (int r2 = 0; r2 < 4; ++r2) bm = fmaxf(bm, fabsf(dS[u][r2]));
-            bm = rows4_max(bm);
-            if (__ballot(bm * smul >= 16384.0f) != 0) {
-                const float f = column_scale(bm, smul);
-#pragma unroll
-                for (int v = 0; v < NV; ++v) dq[v] *= f;
-            }
-            f16x8 sh, sl;
-            split_h(dS[0] * smul, dS[1] * smul, sh, sl);
-            // all k^T fragments first, then the products in passes over v, so the
-            // three MFMAs into one accumulator are NV issues apart
-            f16x8 kth[NV], ktl[NV];
-#pragma unroll
-            for (int v = 0; v < NV; ++v) {
-                kth[v] = __builtin_bit_cast(f16x8, frag_t(KTh, 16 * v + lq, lg));
-                if constexpr (SPLIT) ktl[v] = __builtin_bit_cast(f16x8, frag_t(KTl, 16 * v + lq, lg));
             }
             __builtin_amdgcn_sched_barrier(0);
+            f32x4 s2[2], dp2[2];
 #pragma unroll
-            for (int v = 0; v < NV; ++v) dq[v] = mma_h(kth[v], sh, dq[v]);
-#pragma unroll
-            for (int v = 0; v < NV; ++v) dq[v] = mma_h(kth[v], sl, dq[v]);
+            for (int e = 0; e < 2; ++e) s2[e] = dp2[e] = f32x4{0.f, 0.f, 0.f, 0.f};
+            // small split terms first, hi*hi last (an MFMA rounds at the scale of
+            // its largest addend)
             if constexpr (SPLIT) {
 #pragma unroll
-                for (int v = 0; v < NV; ++v) dq[v] = mma_h(ktl[v], sh, dq[v]);
+                for (int st = 0; st < NS; ++st) {
+                    s2[st & 1] = mma_h(kh[st], qfl[st], s2[st & 1]);
+                    dp2[st & 1] = mma_h(vh[st], dfl[st], dp2[st & 1]);
+                }
+#pragma unroll
+                for (int st = 0; st < NS; ++st) {
+                    s2[st & 1] = mma_h(kl[st], qfh[st], s2[st & 1]);
+                    dp2[st & 1] = mma_h(vl[st], dfh[st], dp2[st & 1]);
+                }
+            }
+#pragma unroll
+            for (int st = 0; st < NS; ++st) {
+                s2[st & 1] = mma_h(kh[st], qfh[st], s2[st & 1]);
+                dp2[st & 1] = mma_h(vh[st], dfh[st], dp2[st & 1]);
+            }
+            const f32x4 s = s2[0] + s2[1], dp = dp2[0] + dp2[1];
+#pragma unroll
+            for (int r2 = 0; r2 < 4; ++r2) {
+                const int key = (int)kb + 16 * u + 4 * lg + r2;
+                float pr = fast_exp2(s[r2] * cS - l2);   // P * 2^kPBwd
+                pr = key <= (int)myq ? pr : 0.f;
+                dS[u][r2] = pr * (dp[r2] * cP - Dq);
             }
         }
-        wait_vmem();
-        __syncthreads();
-        if (more) loadB(b + 1);
+        float bm = 0.f;
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+            for (int r2 = 0; r2 < 4; ++r2) bm = fmaxf(bm, fabsf(dS[u][r2]));
+        bm = rows4_max(bm);
+        if (__ballot(bm * smul >= 16384.0f) != 0) {
+            const float f = column_scale(bm, smul);
+#pragma unroll
+            for (int v = 0; v < NV; ++v) dq[v] *= f;
+        }
+        f16x8 sh, sl;
+        split_h(dS[0] * smul, dS[1] * smul, sh, sl);
+        // all k^T fragments first (the k rows read across), then the products in
+        // passes over v, so the three MFMAs into one accumulator are NV issues apart
+        f16x8 kth[NV], ktl[NV];
+#pragma unroll
+        for (int v = 0; v < NV; ++v) {
+            kth[v] = __builtin_bit_cast(f16x8, frag_tr<D>(Kh, 16 * v, lq, lg));
+            if constexpr (SPLIT) ktl[v] = __builtin_bit_cast(f16x8, frag_tr<D>(Kl, 16 * v, lq, lg));
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int v = 0; v < NV; ++v) dq[v] = mma_h(kth[v], sl, dq[v]);
+        if constexpr (SPLIT) {
+#pragma unroll
+            for (int v = 0; v < NV; ++v) dq[v] = mma_h(ktl[v], sh, dq[v]);
+        }
+#pragma unroll
+        for (int v = 0; v < NV; ++v) dq[v] = mma_h(kth[v], sh, dq[v]);
     }
+    __syncthreads();   // every wave is done with the last stage before the LDS is reused
     const float mul = a.scale * mk * kInvPBwd / smul;
     if (myq < a.rows) {
         if constexpr (OUT_BF16) {
@@ -970,27 +955,29 @@ __device__ __forceinline__ void dq_body(const AttnK& a, uint16_t* __restrict__ s
 // ------------------------------------------------------- backward: launch
 // One launch runs both gradient roles: 0, dK/dV of a key tile, and 1, dQ of a
 // query tile.  Key tile t of the dK/dV role and query tile nT-1-t of the dQ
-// role both sweep nT - t tiles: rank r = t.  Workgroups are dispatched in
-// order of rank, longest first, the two roles of one rank side by side, so
-// a workgroup that frees its slot late in the launch takes a short item
-// (longest-processing-time-first list scheduling) and the token writes of
-// short items fill the end of the launch.  When H is a multiple of 8, head h
-// runs on XCD h % 8 (workgroup i runs on XCD i % 8), where its operands sit
-// in that XCD's L2.
+// role both sweep nT - t tiles: rank t.  Workgroups are dispatched by rank in
+// the order 0, nT-1, 1, nT-2, ... (a long rank, then a short one), the two
+// roles of a rank side by side, so the workgroups resident at any time mix
+// long and short items: their token writes, which start when an item's MFMA
+// work ends, are spread over the whole launch instead of bunching where many
+// similar items end together.  (Measured at 512K: 1.53 ms longest first, 1.37
+// ms alternating.)  When H is a multiple of 8, head h runs on XCD h % 8
+// (workgroup i runs on XCD i % 8), where its operands sit in that XCD's L2.
 __device__ __forceinline__ void bwd_item(int nT, int H, int& role, int& h, int& tile) {
     const int i = blockIdx.x;
-    int r;
+    int j;
     if (H % 8 == 0) {
         const int G = H / 8, x = i % 8, q = i / 8;
         role = q & 1;
-        r = q / (2 * G);
+        j = q / (2 * G);
         h = x + 8 * ((q >> 1) % G);
     } else {
         role = i & 1;
         const int jj = i >> 1;
-        r = jj / H;
+        j = jj / H;
         h = jj % H;
     }
+    const int r = (j & 1) ? nT - 1 - (j >> 1) : (j >> 1);   // rank of the j-th position
     tile = role == 0 ? r : nT - 1 - r;
 }
 
@@ -998,7 +985,7 @@ template <int D, bool SPLIT, bool OUT_BF16>
 __global__ void __launch_bounds__(256) k_attn_bwd(AttnK a) {
     constexpr int E1 = DkdvLds<D, SPLIT>::ELEMS, E2 = DqLds<D, SPLIT>::ELEMS;
     __shared__ __attribute__((aligned(16))) uint16_t sm[E1 > E2 ? E1 : E2];
-    __shared__ __attribute__((aligned(16))) float qstat[2 * kBN];
+    __shared__ __attribute__((aligned(16))) float qstat[4 * kBN];
     __shared__ int64_t ttab[kTokTab];
     const int nT = (int)(a.Sp / 64);
     int role, h, tile;
