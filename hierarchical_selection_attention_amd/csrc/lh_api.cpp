@@ -96,9 +96,6 @@ int make_plan(int N, int H, int d, int p, int L, int K, int dtype, Plan* P, int 
     pl.off_qh = take(h16); pl.off_ql = take(h16);
     pl.off_kh = take(h16); pl.off_kl = take(h16);
     pl.off_vh = take(h16); pl.off_vl = take(h16);
-    pl.off_vTh = take(h16); pl.off_vTl = take(h16);
-    pl.off_kTh = take(h16); pl.off_kTl = take(h16);
-    pl.off_qTh = take(h16); pl.off_qTl = take(h16);
     pl.off_hmax = take(sizeof(uint32_t) * 8 * (size_t)H);
     pl.off_rowmax = take(sizeof(float) * 4 * (size_t)H * pl.Sp);
     pl.off_hscale = take(sizeof(float) * 4 * (size_t)H);
@@ -117,7 +114,6 @@ int make_plan(int N, int H, int d, int p, int L, int K, int dtype, Plan* P, int 
     pl.off_part = take(m < L - 1 ? sizeof(float) * (size_t)H * (size_t)(N / pl.tok) * d : 0);
     pl.off_dos = take(sizeof(float) * HSd);
     pl.off_doh = take(h16); pl.off_dol = take(h16);
-    pl.off_doTh = take(h16); pl.off_doTl = take(h16);
     pl.off_D = take(sizeof(float) * (size_t)H * pl.Sp);
     pl.off_dq = take(sizeof(float) * HSd);
     pl.off_dk = take(sizeof(float) * HSd);
@@ -245,10 +241,6 @@ static AttnArgs sub_attn_args(const Plan& P, char* w) {
     a.kh = u16(w, P.off_kh); a.kl = u16(w, P.off_kl);
     a.vh = u16(w, P.off_vh); a.vl = u16(w, P.off_vl);
     a.doh = u16(w, P.off_doh); a.dol = u16(w, P.off_dol);
-    a.vTh = u16(w, P.off_vTh); a.vTl = u16(w, P.off_vTl);
-    a.kTh = u16(w, P.off_kTh); a.kTl = u16(w, P.off_kTl);
-    a.doTh = u16(w, P.off_doTh); a.doTl = u16(w, P.off_doTl);
-    a.qTh = u16(w, P.off_qTh); a.qTl = u16(w, P.off_qTl);
     a.hscale = f32(w, P.off_hscale);
     a.o = f32(w, P.off_os);
     a.lse = f32(w, P.off_lse);
@@ -264,14 +256,13 @@ static AttnArgs sub_attn_args(const Plan& P, char* w) {
     return a;
 }
 
-// fp16 hi/lo copy of one [H][Sp][d] fp32 tensor (rows and optionally a transposed copy)
-static SplitSpec split_spec(const Plan& P, char* w, size_t src, unsigned int* hmax, int slot, size_t rh, size_t rl,
-                            size_t th, size_t tl) {
+// fp16 hi/lo rows of one [H][Sp][d] fp32 tensor
+static SplitSpec split_spec(const Plan& P, char* w, size_t src, unsigned int* hmax, int slot, size_t rh, size_t rl) {
     SplitSpec sp{};
     sp.src = w + src; sp.ld = P.d; sp.hs = P.Sp * P.d; sp.rows = P.Sp; sp.Sp = P.Sp;
     sp.d = P.d; sp.H = P.H; sp.src_bf16 = 0;
     sp.hmax = hmax; sp.hscale = f32(w, P.off_hscale); sp.slot = slot;
-    sp.rh = u16m(w, rh); sp.rl = u16m(w, rl); sp.th = u16m(w, th); sp.tl = u16m(w, tl);
+    sp.rh = u16m(w, rh); sp.rl = u16m(w, rl);
     return sp;
 }
 
@@ -327,9 +318,9 @@ int forward_strided(const void* q, const void* k, const void* v, void* o, int N,
         unsigned int* out[3] = {hmax, hmax + 1, hmax + 2};
         hipError_t e = launch_head_max(f32(w, P.off_rowmax), out, 3, P.S, P.Sp, H, s);
         const SplitSpec sp[3] = {
-            split_spec(P, w, P.off_qs, hmax, 0, P.off_qh, P.off_ql, P.off_qTh, P.off_qTl),
-            split_spec(P, w, P.off_ks, hmax, 1, P.off_kh, P.off_kl, P.off_kTh, P.off_kTl),
-            split_spec(P, w, P.off_vs, hmax, 2, P.off_vh, P.off_vl, P.off_vTh, P.off_vTl)};
+            split_spec(P, w, P.off_qs, hmax, 0, P.off_qh, P.off_ql),
+            split_spec(P, w, P.off_ks, hmax, 1, P.off_kh, P.off_kl),
+            split_spec(P, w, P.off_vs, hmax, 2, P.off_vh, P.off_vl)};
         if (e == hipSuccess) e = launch_split(sp, 3, s);
         return e;
     }));
@@ -397,7 +388,7 @@ int backward_strided(const void* dout, void* dq, void* dk, void* dv, int N, int 
         if (e != hipSuccess || dtype != BF16) return e;
         unsigned int* out[1] = {hmax_b + 3};
         e = launch_head_max(rowmax_b, out, 1, P.S, P.Sp, H, s);
-        const SplitSpec sp = split_spec(P, w, P.off_dos, hmax_b, 3, P.off_doh, P.off_dol, P.off_doTh, P.off_doTl);
+        const SplitSpec sp = split_spec(P, w, P.off_dos, hmax_b, 3, P.off_doh, P.off_dol);
         if (e == hipSuccess) e = launch_split(&sp, 1, s);
         return e;
     }));
@@ -561,7 +552,7 @@ static int dense_check(int N, int H, int d, int dtype) {
 }
 
 struct DenseLayout {
-    size_t qh, kh, vh, doh, vTh, kTh, doTh, qTh, o32, hmax, hscale, lse2, D, total;
+    size_t qh, kh, vh, doh, o32, hmax, hscale, lse2, D, total;
 };
 static DenseLayout dense_layout(int N, int H, int d) {
     DenseLayout L{};
@@ -574,7 +565,6 @@ static DenseLayout dense_layout(int N, int H, int d) {
         return o;
     };
     L.qh = take(t); L.kh = take(t); L.vh = take(t); L.doh = take(t);
-    L.vTh = take(t); L.kTh = take(t); L.doTh = take(t); L.qTh = take(t);
     L.o32 = take(2 * t);
     L.hmax = take(sizeof(uint32_t) * 4 * (size_t)H);
     L.hscale = take(sizeof(float) * 4 * (size_t)H);
@@ -591,21 +581,19 @@ size_t lh_dense_workspace_bytes(int N, int H, int d, int dtype) {
 // Dense operands are bf16 inputs [N][H][d]: exact in the 16-bit formats, so
 // no lo parts are needed.
 static hipError_t dense_split(const void* src, int N, int H, int d, char* w, const DenseLayout& DL, int slot,
-                              size_t rh, size_t th, hipStream_t s) {
+                              size_t rh, hipStream_t s) {
     SplitSpec sp{};
     sp.src = src; sp.ld = (int64_t)H * d; sp.hs = d; sp.rows = N; sp.Sp = N;
     sp.d = d; sp.H = H; sp.src_bf16 = 1;
     sp.hmax = reinterpret_cast<const unsigned int*>(w + DL.hmax);
     sp.hscale = f32(w, DL.hscale); sp.slot = slot;
-    sp.rh = rh == SIZE_MAX ? nullptr : u16m(w, rh);
-    sp.th = th == SIZE_MAX ? nullptr : u16m(w, th);
+    sp.rh = u16m(w, rh);
     return launch_split(&sp, 1, s);
 }
 
 static AttnArgs dense_args(int N, int H, int d, char* w, const DenseLayout& DL) {
     AttnArgs a{};
     a.qh = u16(w, DL.qh); a.kh = u16(w, DL.kh); a.vh = u16(w, DL.vh); a.doh = u16(w, DL.doh);
-    a.vTh = u16(w, DL.vTh); a.kTh = u16(w, DL.kTh); a.doTh = u16(w, DL.doTh); a.qTh = u16(w, DL.qTh);
     a.hscale = f32(w, DL.hscale);
     a.lse2 = f32(w, DL.lse2); a.D = f32(w, DL.D);
     a.rows = N; a.Sp = N; a.ld_o = (int64_t)H * d; a.hs_o = d;
@@ -643,9 +631,9 @@ int lh_dense_attn_fwd(const void* q, const void* k, const void* v, void* o, floa
     const void* src[3] = {q, k, v};
     LH_TRY(dense_maxabs(src, 3, N, H, d, w, DL, s));
     // every q/k/v copy the matching backward needs is made here
-    LH_TRY(dense_split(q, N, H, d, w, DL, 0, DL.qh, DL.qTh, s));
-    LH_TRY(dense_split(k, N, H, d, w, DL, 1, DL.kh, DL.kTh, s));
-    LH_TRY(dense_split(v, N, H, d, w, DL, 2, DL.vh, DL.vTh, s));
+    LH_TRY(dense_split(q, N, H, d, w, DL, 0, DL.qh, s));
+    LH_TRY(dense_split(k, N, H, d, w, DL, 1, DL.kh, s));
+    LH_TRY(dense_split(v, N, H, d, w, DL, 2, DL.vh, s));
     AttnArgs a = dense_args(N, H, d, w, DL);
     a.o_bf16 = reinterpret_cast<uint16_t*>(o);
     a.o = f32(w, DL.o32);
@@ -670,7 +658,7 @@ int lh_dense_attn_bwd(const void* q, const void* k, const void* v, const void* o
     // q, k, v copies and the fp32 output come from the matching forward's workspace
     const void* src[4] = {nullptr, nullptr, nullptr, dout};
     LH_TRY(dense_maxabs(src, 4, N, H, d, w, DL, s, 3));
-    LH_TRY(dense_split(dout, N, H, d, w, DL, 3, DL.doh, DL.doTh, s));
+    LH_TRY(dense_split(dout, N, H, d, w, DL, 3, DL.doh, s));
     RowPrepSpec rp{};
     rp.dout = dout; rp.o = w + DL.o32; rp.ld = (int64_t)H * d; rp.hs = d;
     rp.D = f32(w, DL.D);

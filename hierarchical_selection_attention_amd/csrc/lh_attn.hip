@@ -10,9 +10,9 @@
 // Scores are computed transposed (S^T = K Q^T, one query per lane column) so
 // the online-softmax statistics of a query live in the lanes that own its
 // output column (O^T = V^T P^T).  Operands whose contraction index is the
-// sequence position come from [H][d][Sp] transposed copies whose blocks of 32
-// positions are stored in fragment order, so every operand load is one
-// contiguous 16-byte vector.
+// sequence position (V^T in P V, dO^T and Q^T in dV and dK, K^T in dQ) are
+// read across the same row tiles with gfx950's transposed LDS read, which
+// hands each lane its 8 positions in the order the score fragments hold them.
 //
 // Precision: the pooled sub-sequence is not representable in 16 bits, and
 // the backward's dS = P o (dP - D) cancels heavily on heavy-tailed inputs, so
@@ -20,8 +20,7 @@
 // hi*hi + hi*lo + lo*hi, lo*lo being below fp32 rounding).  Every split
 // value is first brought just below 2^14 by a power of two, so that its lo
 // part stays in fp16's normal range:
-//   * stored operands (q, k, v, dO rows and transposes): one power of two per
-//     head and tensor;
+//   * stored operands (q, k, v, dO rows): one power of two per head and tensor;
 //   * P: the forward's softmax reference lags the row maximum by 2^6, so P
 //     lies in [0, 2^14] there; the backward reads lse2 = log2-sum-exp - 14, so
 //     P lies in [0, 2^14] there too (the 2^-14 is applied to dV at the end);
@@ -89,8 +88,6 @@ __device__ __forceinline__ void split_h(const f32x4& a, const f32x4& b, f16x8& h
 // [H][d][Sp] transposed, 2-byte elements; lo pointers unused when !SPLIT).
 struct AttnK {
     const uint16_t *qh, *ql, *kh, *kl, *vh, *vl, *doh, *dol;   // fp16 rows
-    const uint16_t *vTh, *vTl, *kTh, *kTl, *doTh, *doTl;       // fp16 transposed
-    const uint16_t *qTh, *qTl;
     const float* hscale;    // [H][4]: true value = stored * hscale (q, k, v, dO)
     float* o;               // fp32 [H][Sp][d] sub-sequence output, or null
     uint16_t* o_bf16;       // bf16 output with strides ld_o/hs_o (dense), or null
@@ -110,78 +107,34 @@ struct AttnK {
 };
 
 // ------------------------------------------------------------ LDS tiles
-// Streamed operands move through double-buffered LDS in blocks of kBN
-// sequence positions, shared by the 4 wavefronts of a workgroup.  Row tiles
-// hold kBN rows of d elements; transposed tiles hold d rows of kBN elements.
-// 16-byte slots are XOR-swizzled by row so a fragment read is free of LDS
-// bank conflicts.
+// Streamed operands move through LDS in blocks of kBN sequence positions,
+// shared by the 4 wavefronts of a workgroup: row tiles of kBN rows of d
+// elements, two stages (the copy of the next block lands in one while the
+// current block is read from the other).  A tile is read along its rows
+// (frag_row) or across them (frag_tr).
 constexpr int kBN = 32;
 
 template <int D>
 struct Tiles {
     static constexpr int NSLOT = D / 8;              // 16-byte slots per row-tile row
     static constexpr int ROW = kBN * D;              // elements of a row tile
-    static constexpr int TR = D * kBN;               // elements of a transposed tile
     static constexpr int CH_ROW = kBN * NSLOT / 256; // 16-byte chunks per thread
-    static constexpr int CH_T = D * 4 / 256;
 };
 
 // Row tiles: slot s of row r holds the row's 16-byte chunk s ^ f(r).  At d = 128
 // (16 slots) f rotates the row's low four bits left by one, so that both reads
 // of a row tile touch distinct banks: a fragment read (16 rows, one slot each)
-// and a transposed read (frag_tr: 8 rows per half-wave, a pair of adjacent
-// slots each, and rows 2i and 2i+1 land in different pairs).
+// and a read across (frag_tr: 8 rows per half-wave, a pair of adjacent slots
+// each, and rows 2i and 2i+1 land in different pairs).
 __device__ __forceinline__ int swz_row(int r, int slot, int nslot) {
     const int f = nslot == 16 ? (((r << 1) | ((r >> 3) & 1)) & 15) : (r & (nslot - 1));
     return slot ^ f;
 }
-// Transposed tiles have 64-byte rows (4 slots).  A ds_read_b128 of rows
-// r0..r0+15 (r0 a multiple of 16) at one slot per 16-lane group runs at the
-// full 256 B/clk on gfx950 with this XOR (measured; (r >> 2) & 3 and no
-// swizzle both run at half rate).
-__device__ __forceinline__ int swz_t(int r, int slot) { return slot ^ ((r >> 1) & 3); }
 
-// global [rows][D] (head base `g`, first row r0) -> registers
-template <int D>
-__device__ __forceinline__ void fetch_row(const uint16_t* g, int64_t r0, u32x4 (&reg)[Tiles<D>::CH_ROW]) {
-    constexpr int NSLOT = Tiles<D>::NSLOT;
-#pragma unroll
-    for (int i = 0; i < Tiles<D>::CH_ROW; ++i) {
-        const int c = threadIdx.x + 256 * i;
-        const int r = c / NSLOT, slot = c % NSLOT;
-        reg[i] = *reinterpret_cast<const u32x4*>(g + (r0 + r) * D + swz_row(r, slot, NSLOT) * 8);
-    }
-}
-template <int D>
-__device__ __forceinline__ void store_row(uint16_t* lds, const u32x4 (&reg)[Tiles<D>::CH_ROW]) {
-#pragma unroll
-    for (int i = 0; i < Tiles<D>::CH_ROW; ++i) {
-        const int c = threadIdx.x + 256 * i;
-        *reinterpret_cast<u32x4*>(lds + c * 8) = reg[i];
-    }
-}
-// global transposed [D][Sp] (head base `g`), columns c0..c0+kBN-1 -> registers
-template <int D>
-__device__ __forceinline__ void fetch_t(const uint16_t* g, int64_t Sp, int64_t c0, u32x4 (&reg)[Tiles<D>::CH_T]) {
-#pragma unroll
-    for (int i = 0; i < Tiles<D>::CH_T; ++i) {
-        const int c = threadIdx.x + 256 * i;
-        const int r = c / 4, slot = c % 4;
-        reg[i] = *reinterpret_cast<const u32x4*>(g + (int64_t)r * Sp + c0 + swz_t(r, slot) * 8);
-    }
-}
-template <int D>
-__device__ __forceinline__ void store_t(uint16_t* lds, const u32x4 (&reg)[Tiles<D>::CH_T]) {
-#pragma unroll
-    for (int i = 0; i < Tiles<D>::CH_T; ++i) {
-        const int c = threadIdx.x + 256 * i;
-        *reinterpret_cast<u32x4*>(lds + c * 8) = reg[i];
-    }
-}
-// Direct global -> LDS copies of the same tiles (no staging registers): thread
-// c fetches the 16-byte chunk that fetch_row / fetch_t would give it, and the
-// load writes it at wave base + 16 * lane, i.e. at chunk c of the LDS tile.
-// The data is in LDS once the issuing wave's vmcnt has drained.
+// Direct global -> LDS copies of a row tile (no staging registers): thread c
+// fetches row c / NSLOT's chunk swz_row(r, c % NSLOT), and the load writes it
+// at wave base + 16 * lane, i.e. at slot c of the LDS tile.  The data is in
+// LDS once the issuing wave's vmcnt has drained.
 #define LH_LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
 template <int D>
 __device__ __forceinline__ void dma_row(const uint16_t* g, int64_t r0, uint16_t* lds) {
@@ -195,21 +148,10 @@ __device__ __forceinline__ void dma_row(const uint16_t* g, int64_t r0, uint16_t*
                                          LH_LDS_PTR(lds + (256 * i + wbase) * 8), 16, 0, 0);
     }
 }
-template <int D>
-__device__ __forceinline__ void dma_t(const uint16_t* g, int64_t Sp, int64_t c0, uint16_t* lds) {
-    const int wbase = threadIdx.x & ~63;
-#pragma unroll
-    for (int i = 0; i < Tiles<D>::CH_T; ++i) {
-        const int c = threadIdx.x + 256 * i;
-        const int r = c / 4, slot = c % 4;
-        __builtin_amdgcn_global_load_lds(g + (int64_t)r * Sp + c0 + swz_t(r, slot) * 8,
-                                         LH_LDS_PTR(lds + (256 * i + wbase) * 8), 16, 0, 0);
-    }
-}
 // The same copies through a buffer resource over one head's operand: the
-// per-lane byte offsets are computed once (row_voff / t_voff), the block's
-// offset is a scalar, and `wofs` (the wave's byte offset inside a tile,
-// wave * 1024) is uniform.
+// per-lane byte offsets are computed once (row_voff), the block's offset is a
+// scalar, and `wofs` (the wave's byte offset inside a tile, wave * 1024) is
+// uniform.
 template <int D>
 __device__ __forceinline__ void row_voff(uint32_t (&voff)[Tiles<D>::CH_ROW]) {
     constexpr int NSLOT = Tiles<D>::NSLOT;
@@ -218,15 +160,6 @@ __device__ __forceinline__ void row_voff(uint32_t (&voff)[Tiles<D>::CH_ROW]) {
         const int c = threadIdx.x + 256 * i;
         const int r = c / NSLOT, slot = c % NSLOT;
         voff[i] = (uint32_t)(r * D + swz_row(r, slot, NSLOT) * 8) * 2u;
-    }
-}
-template <int D>
-__device__ __forceinline__ void t_voff(uint32_t (&voff)[Tiles<D>::CH_T], int64_t Sp) {
-#pragma unroll
-    for (int i = 0; i < Tiles<D>::CH_T; ++i) {
-        const int c = threadIdx.x + 256 * i;
-        const int r = c / 4, slot = c % 4;
-        voff[i] = (uint32_t)((int64_t)r * Sp + swz_t(r, slot) * 8) * 2u;
     }
 }
 // rows r0 .. r0 + kBN - 1 of a head's [rows][D] operand -> LDS row tile
@@ -238,16 +171,6 @@ __device__ __forceinline__ void bdma_row(const uint16_t* head, uint32_t bytes, c
     for (int i = 0; i < Tiles<D>::CH_ROW; ++i)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, LH_LDS_PTR(reinterpret_cast<char*>(tile) + 4096 * i + wofs), 16,
                                                  voff[i], (uint32_t)(r0 * D * 2), 0, 0);
-}
-// columns c0 .. c0 + kBN - 1 of a head's [D][Sp] operand -> LDS transposed tile
-template <int D>
-__device__ __forceinline__ void bdma_t(const uint16_t* head, uint32_t bytes, const uint32_t* voff,
-                                       int64_t c0, uint16_t* tile, uint32_t wofs) {
-    const auto rs = make_rsrc(head, bytes);
-#pragma unroll
-    for (int i = 0; i < Tiles<D>::CH_T; ++i)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, LH_LDS_PTR(reinterpret_cast<char*>(tile) + 4096 * i + wofs), 16,
-                                                 voff[i], (uint32_t)(c0 * 2), 0, 0);
 }
 
 // wait until this wave's outstanding vector-memory operations (its tile
@@ -277,12 +200,6 @@ __device__ __forceinline__ u32x4 frag_tr(const uint16_t* lds, int c0, int lq, in
     const f16x4t x1 = __builtin_amdgcn_ds_read_tr16_b64_v4f16((__attribute__((address_space(3))) f16x4t*)(p1));
     const u32x2 a = __builtin_bit_cast(u32x2, x0), b = __builtin_bit_cast(u32x2, x1);
     return u32x4{a[0], a[1], b[0], b[1]};
-}
-// fragment of transposed tile: row r, sequence positions {4g..4g+3} and
-// {16+4g..16+4g+3} of the block, which the split stores as the 16-byte run g
-// (fragment order); one read, conflict-free over the 16 rows of a fragment
-__device__ __forceinline__ u32x4 frag_t(const uint16_t* lds, int r, int g) {
-    return *reinterpret_cast<const u32x4*>(lds + r * kBN + swz_t(r, g) * 8);
 }
 
 // p^level of row `row` of head h as a float (exact for every level that fits
@@ -393,10 +310,12 @@ __global__ void __launch_bounds__(256) k_attn_fwd(AttnK a) {
     using T = Tiles<D>;
     constexpr int NS = D / 32, NV = D / 16;
     constexpr int NA = SPLIT ? 2 : 1;
-    // K rows (read by the score phase) and V^T (read by the P V phase): one LDS
-    // buffer each, refilled by direct copies while the other one is in use
-    constexpr int KR = NA * T::ROW;
-    __shared__ __attribute__((aligned(16))) uint16_t sm[KR + NA * T::TR];
+    // Per key block, one stage of row tiles: k (hi, lo) for the score phase and
+    // v (hi, lo), read across (frag_tr) by the P V phase.  Two stages: the copy
+    // of block b + 1 is in flight during all of block b's work, and one barrier
+    // per block orders it.
+    constexpr int STAGE = NA * 2 * T::ROW;
+    __shared__ __attribute__((aligned(16))) uint16_t sm[2 * STAGE];
     __shared__ int64_t ttab[kTokTab];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int lq = lane & 15, lg = lane >> 4;
@@ -423,36 +342,35 @@ __global__ void __launch_bounds__(256) k_attn_fwd(AttnK a) {
     float m = -INFINITY, lsum = 0.f;
 
     const int nblk = (int)(((int64_t)qt * 64 + 64) / kBN);
-    const uint16_t* Kh = sm;
-    const uint16_t* Kl = sm + T::ROW;
-    const uint16_t* Vh = sm + KR;
-    const uint16_t* Vl = Vh + T::TR;
     const uint32_t wofs = __builtin_amdgcn_readfirstlane((uint32_t)wave * 1024u);
     const uint32_t hbytes = (uint32_t)(Sp * D * 2);
-    uint32_t rvo[T::CH_ROW], tvo[T::CH_T];
+    uint32_t rvo[T::CH_ROW];
     row_voff<D>(rvo);
-    t_voff<D>(tvo, Sp);
-    auto loadK = [&](int b) {
-        bdma_row<D>(a.kh + hb, hbytes, rvo, (int64_t)b * kBN, sm, wofs);
-        if constexpr (SPLIT) bdma_row<D>(a.kl + hb, hbytes, rvo, (int64_t)b * kBN, sm + T::ROW, wofs);
+    // stage layout: [kh][kl?][vh][vl?] row tiles
+    auto load = [&](int b) {
+        uint16_t* base = sm + (b & 1) * STAGE;
+        bdma_row<D>(a.kh + hb, hbytes, rvo, (int64_t)b * kBN, base, wofs);
+        bdma_row<D>(a.vh + hb, hbytes, rvo, (int64_t)b * kBN, base + NA * T::ROW, wofs);
+        if constexpr (SPLIT) {
+            bdma_row<D>(a.kl + hb, hbytes, rvo, (int64_t)b * kBN, base + T::ROW, wofs);
+            bdma_row<D>(a.vl + hb, hbytes, rvo, (int64_t)b * kBN, base + 3 * T::ROW, wofs);
+        }
     };
-    auto loadV = [&](int b) {
-        bdma_t<D>(a.vTh + hb, hbytes, tvo, (int64_t)b * kBN, sm + KR, wofs);
-        if constexpr (SPLIT) bdma_t<D>(a.vTl + hb, hbytes, tvo, (int64_t)b * kBN, sm + KR + T::TR, wofs);
-    };
-    loadK(0);
-    loadV(0);
-    wait_vmem();
-    __syncthreads();
-    // Per block: scores and softmax from K while this block's V^T may still be
-    // arriving; the barrier publishes V^T and frees K, which is refilled during
-    // the P V phase; the second barrier publishes K and frees V^T.
+    load(0);
     for (int b = 0; b < nblk; ++b) {
-        const bool more = b + 1 < nblk;
+        // block b has landed (this wave's copies; the barrier covers the others')
+        // and every wave is past block b - 1, whose stage the next copy refills
+        wait_vmem();
+        __syncthreads();
+        if (b + 1 < nblk) load(b + 1);
         const int64_t kb = (int64_t)b * kBN;
-        const bool active = kb < q0 + 16;
+        if (!(kb < q0 + 16)) continue;   // no key of the block is visible to the wave
+        const uint16_t* Kh = sm + (b & 1) * STAGE;
+        const uint16_t* Kl = Kh + T::ROW;
+        const uint16_t* Vh = Kh + NA * T::ROW;
+        const uint16_t* Vl = Vh + T::ROW;
         f32x4 sc[2];
-        if (active) {
+        {
             // one accumulator per (key tile u, d step st), so consecutive MFMAs are
             // independent (a 16x16x32 MFMA chain needs many in flight); the partial
             // sums are added at the end
@@ -535,19 +453,17 @@ __global__ void __launch_bounds__(256) k_attn_fwd(AttnK a) {
                     sc[u][r] = pr;
                 }
         }
-        wait_vmem();
-        __syncthreads();
-        if (more) loadK(b + 1);
-        if (active) {
+        {
             f16x8 ph, pl;
             split_h(sc[0], sc[1], ph, pl);
-            // all V^T fragments first, then the products in passes over v, so the
-            // three MFMAs into one accumulator are NV issues apart
+            // all V^T fragments first (the v rows read across), then the products
+            // in passes over v, so the three MFMAs into one accumulator are NV
+            // issues apart
             f16x8 vfh[NV], vfl[NV];
 #pragma unroll
             for (int v = 0; v < NV; ++v) {
-                vfh[v] = __builtin_bit_cast(f16x8, frag_t(Vh, 16 * v + lq, lg));
-                if constexpr (SPLIT) vfl[v] = __builtin_bit_cast(f16x8, frag_t(Vl, 16 * v + lq, lg));
+                vfh[v] = __builtin_bit_cast(f16x8, frag_tr<D>(Vh, 16 * v, lq, lg));
+                if constexpr (SPLIT) vfl[v] = __builtin_bit_cast(f16x8, frag_tr<D>(Vl, 16 * v, lq, lg));
             }
             __builtin_amdgcn_sched_barrier(0);
             // this block's products in fresh accumulators (small terms first), added
@@ -565,9 +481,6 @@ __global__ void __launch_bounds__(256) k_attn_fwd(AttnK a) {
 #pragma unroll
             for (int v = 0; v < NV; ++v) o[v] += blk[v];
         }
-        wait_vmem();
-        __syncthreads();
-        if (more) loadV(b + 1);
     }
     lsum = rows4_sum(lsum);
     const float mul = mv / lsum;
@@ -590,7 +503,8 @@ __global__ void __launch_bounds__(256) k_attn_fwd(AttnK a) {
         a.lse2[(int64_t)h * Sp + myq] = l2 - kPBwd;
         a.lse[(int64_t)h * Sp + myq] = l2 * kLn2;
     }
-    if (a.o_tok) {   // the LDS tiles are idle: every wave is past the loop's last barrier
+    if (a.o_tok) {
+        __syncthreads();   // every wave is done with the last stage before the LDS is reused
         token_table(a, h, (int64_t)qt * 64, ttab);
         stage_rows<D>(sm + wave * 16 * D, o, mul, 1.0f, lq, lg);
         __syncthreads();
@@ -1102,8 +1016,6 @@ static AttnK to_k(const AttnArgs& x) {
     AttnK a{};
     a.qh = x.qh; a.ql = x.ql; a.kh = x.kh; a.kl = x.kl; a.vh = x.vh; a.vl = x.vl;
     a.doh = x.doh; a.dol = x.dol;
-    a.vTh = x.vTh; a.vTl = x.vTl; a.kTh = x.kTh; a.kTl = x.kTl; a.doTh = x.doTh; a.doTl = x.doTl;
-    a.qTh = x.qTh; a.qTl = x.qTl;
     a.hscale = x.hscale;
     a.o = x.o; a.o_bf16 = x.o_bf16;
     a.lse = x.lse; a.lse2 = x.lse2; a.D = x.D;

@@ -73,9 +73,8 @@ struct Plan {
     size_t off_start, off_level, off_bfirst;
     size_t off_tk;                // selection scratch: [H][L][5][tk_cap] int32
     size_t off_qs, off_ks, off_vs;   // fp32 [H][Sp][d] gathered sub-sequence
-    // 16-bit operand copies (bf16 path): fp16 hi/lo rows [H][Sp][d], transposed [H][d][Sp]
+    // 16-bit operand copies (bf16 path): fp16 hi/lo rows [H][Sp][d]
     size_t off_qh, off_ql, off_kh, off_kl, off_vh, off_vl;
-    size_t off_vTh, off_vTl, off_kTh, off_kTl, off_qTh, off_qTl;
     size_t off_hmax;              // uint32 [2][H][4]: forward (q, k, v) and backward (dO) max |x|
     size_t off_rowmax;            // fp32 [4][H][Sp]: max |x| per row of q~, k~, v~ (gather) and dO~
     size_t off_hscale;            // fp32 [H][4]: per-head multipliers of the fp16 copies
@@ -84,7 +83,7 @@ struct Plan {
     size_t off_acc;               // fp32 [H][Sp][d]: sums of dO over each entry (dO~)
     size_t off_part;              // fp32 [H][N / tok][d]: deterministic mode's per-block partial sums
     size_t off_dos;               // fp32 [H][Sp][d]
-    size_t off_doh, off_dol, off_doTh, off_doTl;   // fp16 copies of dO~
+    size_t off_doh, off_dol;      // fp16 hi/lo rows of dO~
     size_t off_D;                 // fp32 [H][Sp]
     size_t off_dq, off_dk, off_dv;   // fp32 [H][Sp][d]
     // parent kept: int32 [sum_l H * n_l], 1 + the slot of entry (l, j) of head h
@@ -126,11 +125,10 @@ hipError_t launch_sum_copy(const Plan& P, const char* ws, const float* const* ta
 // parent kept: fp32 acc[h][slot] = sum of dO over the entry's tokens (bf16 dO)
 hipError_t launch_entry_sum(const Plan& P, const void* dout, char* ws, hipStream_t s);
 
-// Attention operands: 16-bit copies laid out [H][Sp][d] (rows) and
-// [H][d][Sp] (transposed); lo parts are used when `split`.
+// Attention operands: 16-bit copies laid out [H][Sp][d]; lo parts are used
+// when `split`.
 struct AttnArgs {
     const uint16_t *qh, *ql, *kh, *kl, *vh, *vl, *doh, *dol;
-    const uint16_t *vTh, *vTl, *kTh, *kTl, *doTh, *doTl, *qTh, *qTl;
     const float* hscale;
     float* o;                  // fp32 [H][Sp][d] or null
     uint16_t* o_bf16;          // bf16 output rows (ld_o, hs_o) or null
@@ -163,7 +161,7 @@ struct SplitSpec {
     const unsigned int* hmax;
     float* hscale;
     int slot;
-    uint16_t *rh, *rl, *th, *tl;
+    uint16_t *rh, *rl;
 };
 struct RowPrepSpec {
     const void *acc, *dout, *o;

@@ -1,5 +1,5 @@
 // Operand preparation for the attention kernels on gfx950: per-head scale
-// exponents, fp16 hi/lo splits (row-major and transposed), and the per-row
+// exponents, fp16 hi/lo row splits, and the per-row
 // quantities of the backward pass (D_i, and for the dense path the base-2 lse).
 #include "lh_device.h"
 #include "lh_internal.h"
@@ -76,17 +76,7 @@ __device__ __forceinline__ float down_scale(float mx) {
 
 // ---------------------------------------------------------------- splits
 // One 64x64 tile of head h: x = src * down (down = power-of-two scale of the
-// head); writes fp16 hi/lo rows and a transposed fp16 hi/lo copy.  Rows >=
-// `rows` are written as zeros.
-//
-// Transposed copies are [H][d][Sp] with the sequence positions of each aligned
-// block of 32 stored in MFMA-fragment order: position 16h + 4g + e (h < 2,
-// g < 4, e < 4) sits at 8g + 4h + e, so the 8 positions {4g..4g+3, 16+4g..
-// 16+4g+3} that lane group g of a 16x16x32 MFMA supplies are one 16-byte run.
-__device__ __forceinline__ int frag_order(int r) {
-    const int k = r & 31;
-    return (r & ~31) | (((k >> 2) & 3) << 3) | ((k >> 4) << 2) | (k & 3);
-}
+// head); writes fp16 hi/lo rows.  Rows >= `rows` are written as zeros.
 // Up to three tensors of the same layout per launch: blockIdx.z = tensor * H + head.
 struct SplitArgs {
     const void* src[3];
@@ -95,19 +85,16 @@ struct SplitArgs {
     const unsigned int* hmax;   // [H][4], slot `slot`
     float* hscale;              // [H][4]: stored * hscale = true value
     int slot[3];
-    uint16_t *rh[3], *rl[3];    // fp16 [H][Sp][d] (scaled) or null
-    uint16_t *th[3], *tl[3];    // [H][d][Sp] or null
+    uint16_t *rh[3], *rl[3];    // fp16 [H][Sp][d] (scaled); rl may be null
 };
 
 __device__ __forceinline__ uint16_t h16(float x) { return __builtin_bit_cast(uint16_t, (_Float16)x); }
 __device__ __forceinline__ float f16f(uint16_t b) { return (float)__builtin_bit_cast(_Float16, b); }
 
 __global__ void __launch_bounds__(256) k_split(SplitArgs a) {
-    __shared__ uint16_t th[64][64 + 2];
-    __shared__ uint16_t tl[64][64 + 2];
     const int t = blockIdx.z / a.H, h = blockIdx.z % a.H;
     const void* src = a.src[t];
-    uint16_t *rh = a.rh[t], *rl = a.rl[t], *tth = a.th[t], *ttl = a.tl[t];
+    uint16_t *rh = a.rh[t], *rl = a.rl[t];
     const int64_t r0 = (int64_t)blockIdx.x * 64;
     const int c0 = blockIdx.y * 64;
     const float mx = __uint_as_float(a.hmax[h * 4 + a.slot[t]]);
@@ -125,42 +112,17 @@ __global__ void __launch_bounds__(256) k_split(SplitArgs a) {
 #pragma unroll
             for (int e = 0; e < 8; ++e) x[e] = 0.f;
         }
-        if (rh) {
-            u32x4 wh, wl;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const float x0 = x[2 * e] * down, x1 = x[2 * e + 1] * down;
-                const uint16_t h0 = h16(x0), h1 = h16(x1);
-                wh[e] = (uint32_t)h0 | ((uint32_t)h1 << 16);
-                wl[e] = (uint32_t)h16(x0 - f16f(h0)) | ((uint32_t)h16(x1 - f16f(h1)) << 16);
-            }
-            const int64_t o = ((int64_t)h * a.Sp + r0 + r) * a.d + c0 + cc;
-            *reinterpret_cast<u32x4*>(rh + o) = wh;
-            if (rl) *reinterpret_cast<u32x4*>(rl + o) = wl;
-        }
-        if (tth) {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float xs = x[e] * down;
-                const uint16_t hb = h16(xs);
-                th[cc + e][frag_order(r)] = hb;
-                tl[cc + e][frag_order(r)] = h16(xs - f16f(hb));
-            }
-        }
-    }
-    if (!tth) return;
-    __syncthreads();
-    for (int it = threadIdx.x; it < 64 * 8; it += 256) {
-        const int col = it / 8, rr = (it % 8) * 8;
         u32x4 wh, wl;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            wh[e] = (uint32_t)th[col][rr + 2 * e] | ((uint32_t)th[col][rr + 2 * e + 1] << 16);
-            wl[e] = (uint32_t)tl[col][rr + 2 * e] | ((uint32_t)tl[col][rr + 2 * e + 1] << 16);
+            const float x0 = x[2 * e] * down, x1 = x[2 * e + 1] * down;
+            const uint16_t h0 = h16(x0), h1 = h16(x1);
+            wh[e] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+            wl[e] = (uint32_t)h16(x0 - f16f(h0)) | ((uint32_t)h16(x1 - f16f(h1)) << 16);
         }
-        const int64_t o = ((int64_t)h * a.d + c0 + col) * a.Sp + r0 + rr;
-        *reinterpret_cast<u32x4*>(tth + o) = wh;
-        if (ttl) *reinterpret_cast<u32x4*>(ttl + o) = wl;
+        const int64_t o = ((int64_t)h * a.Sp + r0 + r) * a.d + c0 + cc;
+        *reinterpret_cast<u32x4*>(rh + o) = wh;
+        if (rl) *reinterpret_cast<u32x4*>(rl + o) = wl;
     }
 }
 
@@ -287,7 +249,8 @@ hipError_t launch_split(const SplitSpec* sp, int T, hipStream_t s) {
             x.src_bf16 != s0.src_bf16 || x.hmax != s0.hmax || x.hscale != s0.hscale)
             return hipErrorInvalidValue;
         a.src[t] = x.src; a.slot[t] = x.slot;
-        a.rh[t] = x.rh; a.rl[t] = x.rl; a.th[t] = x.th; a.tl[t] = x.tl;
+        if (!x.rh) return hipErrorInvalidValue;
+        a.rh[t] = x.rh; a.rl[t] = x.rl;
     }
     dim3 grid((unsigned)(s0.Sp / 64), (unsigned)(s0.d / 64), (unsigned)(s0.H * T));
     hipLaunchKernelGGL(k_split, grid, dim3(256), 0, s, a);
