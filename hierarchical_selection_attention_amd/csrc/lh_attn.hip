@@ -122,12 +122,14 @@ struct Tiles {
 };
 
 // Row tiles: slot s of row r holds the row's 16-byte chunk s ^ f(r).  At d = 128
-// (16 slots) f rotates the row's low four bits left by one, so that both reads
-// of a row tile touch distinct banks: a fragment read (16 rows, one slot each)
-// and a read across (frag_tr: 8 rows per half-wave, a pair of adjacent slots
-// each, and rows 2i and 2i+1 land in different pairs).
+// (16 slots) f is the linear map of r's low four bits b0..b3 to
+// (b0 << 1) | (b1 << 2) | b2 | ((b2 ^ b3) << 3), chosen by measurement: with it
+// both reads of a row tile, along (frag_row) and across (frag_tr), run free of
+// LDS bank conflicts on gfx950 (r & 15 leaves the read across 2-way
+// conflicted, a rotation of r the read along; 240 bit-linear maps were timed).
 __device__ __forceinline__ int swz_row(int r, int slot, int nslot) {
-    const int f = nslot == 16 ? (((r << 1) | ((r >> 3) & 1)) & 15) : (r & (nslot - 1));
+    const int f = nslot == 16 ? (((r & 3) << 1) | ((r >> 2) & 1) | ((((r >> 2) ^ (r >> 3)) & 1) << 3))
+                              : (r & (nslot - 1));
     return slot ^ f;
 }
 
