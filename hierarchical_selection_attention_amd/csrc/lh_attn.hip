@@ -877,9 +877,12 @@ __device__ __forceinline__ void dq_body(const AttnK& a, uint16_t* __restrict__ s
 // long and short items: their token writes, which start when an item's MFMA
 // work ends, are spread over the whole launch instead of bunching where many
 // similar items end together.  (Measured at 512K: 1.53 ms longest first, 1.37
-// ms alternating.)  When H is a multiple of 8, head h runs on XCD h % 8
-// (workgroup i runs on XCD i % 8), where its operands sit in that XCD's L2.
-__device__ __forceinline__ void bwd_item(int nT, int H, int& role, int& h, int& tile) {
+// ms alternating.)  A launch that writes no token rows (dense comparison,
+// parent-kept selection) is bound by its MFMA work alone and takes the ranks
+// longest first (dense at 128K: 401 TFLOP/s against 328 alternating).  When H
+// is a multiple of 8, head h runs on XCD h % 8 (workgroup i runs on XCD i % 8),
+// where its operands sit in that XCD's L2.
+__device__ __forceinline__ void bwd_item(int nT, int H, bool alternate, int& role, int& h, int& tile) {
     const int i = blockIdx.x;
     int j;
     if (H % 8 == 0) {
@@ -893,7 +896,7 @@ __device__ __forceinline__ void bwd_item(int nT, int H, int& role, int& h, int& 
         j = jj / H;
         h = jj % H;
     }
-    const int r = (j & 1) ? nT - 1 - (j >> 1) : (j >> 1);   // rank of the j-th position
+    const int r = !alternate ? j : (j & 1) ? nT - 1 - (j >> 1) : (j >> 1);   // rank of the j-th position
     tile = role == 0 ? r : nT - 1 - r;
 }
 
@@ -905,7 +908,7 @@ __global__ void __launch_bounds__(256) k_attn_bwd(AttnK a) {
     __shared__ int64_t ttab[kTokTab];
     const int nT = (int)(a.Sp / 64);
     int role, h, tile;
-    bwd_item(nT, (int)(gridDim.x / (2 * nT)), role, h, tile);
+    bwd_item(nT, (int)(gridDim.x / (2 * nT)), a.dk_tok != nullptr, role, h, tile);
     if (role == 0) dkdv_body<D, SPLIT, OUT_BF16>(a, sm, qstat, ttab, h, tile);
     else dq_body<D, SPLIT, OUT_BF16>(a, sm, ttab, h, tile);
 }
