@@ -84,8 +84,8 @@ __device__ __forceinline__ void split_h(const f32x4& a, const f32x4& b, f16x8& h
     }
 }
 
-// Operand tensors of one attention problem (all [H][rows][d] row-major or
-// [H][d][Sp] transposed, 2-byte elements; lo pointers unused when !SPLIT).
+// Operand tensors of one attention problem (16-bit operands [H][Sp][d]
+// row-major; lo pointers unused when !SPLIT).
 struct AttnK {
     const uint16_t *qh, *ql, *kh, *kl, *vh, *vl, *doh, *dol;   // fp16 rows
     const float* hscale;    // [H][4]: true value = stored * hscale (q, k, v, dO)
