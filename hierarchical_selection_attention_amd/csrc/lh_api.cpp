@@ -364,8 +364,10 @@ int backward_strided(const void* dout, void* dq, void* dk, void* dv, int N, int 
     const size_t HSd = (size_t)H * P.Sp * d;
     unsigned int* hmax = reinterpret_cast<unsigned int*>(w + P.off_hmax);
     unsigned int* hmax_b = hmax + 4 * (size_t)H;
-    // the fp32 atomics add into cleared rows; the deterministic mode stores every row
-    if (scatter_mode == LH_SCATTER_FP_ATOMIC || P.pk)
+    // the fp32 atomics add into cleared rows.  They only run for entries above level m,
+    // which span several blocks; with m = L-1 every entry is stored whole, as in the
+    // deterministic mode, and row preparation reads no row it has not written
+    if ((scatter_mode == LH_SCATTER_FP_ATOMIC && P.m < P.L - 1) || P.pk)
         LH_TRY(stage(ST_ZERO_ACC, s, [&] { return launch_fill_zero(w + P.off_acc, sizeof(float) * HSd, s); }));
     // parent kept: each entry's sum of dO is taken by one wavefront (no atomics), in the
     // fp32 layout of the fp-atomic accumulators

@@ -258,8 +258,8 @@ __device__ __forceinline__ void token_table(const AttnK& a, int h, int64_t r0, i
 // Writes the staged rows (NT tensors; entry e's row at rows_j + e * D) to
 // their tokens.  The work is flattened over (token, 16-byte chunk), so all
 // four wavefronts share it evenly whatever the entries' sizes: thread t keeps
-// chunk t % (D/8) and walks the workgroup's tokens 256/(D/8) apart, loading
-// its chunk from LDS only when it crosses into the next entry.
+// chunk t % (D/8) and walks the workgroup's tokens 256/(D/8) apart, entry by
+// entry, loading its chunk once per entry and stepping a pointer per token.
 template <int D, int NT>
 __device__ __forceinline__ void tile_to_tokens(const uint16_t* rows0, const uint16_t* rows1, uint16_t* tok0,
                                                uint16_t* tok1, const AttnK& a, int h, const int64_t* tab) {
@@ -267,23 +267,25 @@ __device__ __forceinline__ void tile_to_tokens(const uint16_t* rows0, const uint
     const int c = threadIdx.x % CPR;
     const int64_t total = tab[64];
     const int64_t col = (int64_t)h * D + 8 * c;
-    int e = -1;
-    int64_t end = 0;          // flat index one past entry e's last token
-    int64_t shift = 0;        // first token of entry e minus its flat offset
-    u32x4 x0 = {0u, 0u, 0u, 0u}, x1 = {0u, 0u, 0u, 0u};
-    for (int64_t t = threadIdx.x / CPR; t < total; t += TPI) {
-        if (t >= end) {
-            do {
-                ++e;
-                end = tab[e + 1];
-            } while (t >= end);
-            shift = tab[65 + e] - tab[e];
-            x0 = *reinterpret_cast<const u32x4*>(rows0 + e * D + 8 * c);
-            if constexpr (NT == 2) x1 = *reinterpret_cast<const u32x4*>(rows1 + e * D + 8 * c);
+    const int64_t step = (int64_t)TPI * a.tok_ld;
+    int64_t t = threadIdx.x / CPR;   // this thread's next token (flat index over the 64 entries)
+    for (int e = 0; e < 64 && t < total; ++e) {
+        const int64_t end = tab[e + 1];
+        if (t >= end) continue;
+        const u32x4 x0 = *reinterpret_cast<const u32x4*>(rows0 + e * D + 8 * c);
+        u32x4 x1 = {0u, 0u, 0u, 0u};
+        if constexpr (NT == 2) x1 = *reinterpret_cast<const u32x4*>(rows1 + e * D + 8 * c);
+        const int64_t o = (tab[65 + e] - tab[e] + t) * a.tok_ld + col;
+        uint16_t* p0 = tok0 + o;
+        uint16_t* p1 = NT == 2 ? tok1 + o : nullptr;
+        for (; t < end; t += TPI) {
+            __builtin_nontemporal_store(x0, reinterpret_cast<u32x4*>(p0));
+            p0 += step;
+            if constexpr (NT == 2) {
+                __builtin_nontemporal_store(x1, reinterpret_cast<u32x4*>(p1));
+                p1 += step;
+            }
         }
-        const int64_t o = (shift + t) * a.tok_ld + col;
-        __builtin_nontemporal_store(x0, reinterpret_cast<u32x4*>(tok0 + o));
-        if constexpr (NT == 2) __builtin_nontemporal_store(x1, reinterpret_cast<u32x4*>(tok1 + o));
     }
 }
 
