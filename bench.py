@@ -291,7 +291,7 @@ def bench_block(args, lh, torch, np, si):
         "dtype": "bf16",
         "data": "synthetic (seeded, inputs resident in HBM)",
         "config": {"workload": w["name"], "N": N, "d_model": dm, "H": H, "d": d, "p": p, "L": L, "K": K, "S": S,
-                   "scatter_mode": "int_atomic" if args.mode else "fp_atomic"},
+                   "scatter_mode": "deterministic" if args.mode else "fp_atomic"},
         "layer_ms_per_step": round(layer_ms, 3),
         "roofline": roof,
         "cpu_baseline": cpu,
@@ -307,7 +307,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", type=int, default=4)
-    ap.add_argument("--mode", type=int, default=0, help="scatter adjoint: 0 fp-atomic, 1 int-atomic")
+    ap.add_argument("--mode", type=int, default=0, help="scatter adjoint: 0 fp-atomic, 1 deterministic (partial sums added in a fixed order)")
     ap.add_argument("--no-dense", action="store_true", help="skip the dense attention comparison")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-heads", type=int, default=0, help="heads in the CPU oracle sample (0: all)")
@@ -508,7 +508,7 @@ def main():
         "dtype": w["dtype"],
         "data": "synthetic (seeded, inputs resident in HBM)",
         "config": {"workload": w["name"], "N": N, "H": H, "d": d, "p": p, "L": L, "K": K, "S": S,
-                   "scatter_mode": "int_atomic" if args.mode else "fp_atomic",
+                   "scatter_mode": "deterministic" if args.mode else "fp_atomic",
                    "select": args.select, "score": args.score},
         "roofline": roof,
         "cpu_baseline": cpu,

@@ -42,7 +42,7 @@ def _inputs(case, seed):
 
 
 @pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
-@pytest.mark.parametrize("mode", [0, 1], ids=["fp_atomic", "int_atomic"])
+@pytest.mark.parametrize("mode", [0, 1], ids=["fp_atomic", "deterministic"])
 def test_parity_small(case, mode):
     label, N, H, d, dtype, p, L, K, scale, dup, bwd = case
     seed = 500 + CASES.index(case)
@@ -70,11 +70,11 @@ def test_parity_small(case, mode):
             check_full_rows(g, b[sub], sel, p, dtype, key, divide=True, allow_sub=grad_allow(b, sub))
 
 
-def test_int_atomic_scatter_is_bit_reproducible():
+def test_deterministic_scatter_is_bit_reproducible():
     """Deterministic mode: identical bits over repeated runs (and close to the fp-atomic mode)."""
     case = ("rep", 8192, 4, 128, "bf16", 4, 4, 16, "lognormal", 0.0, True)
     x = _inputs(case, 77)
-    say("case int-atomic reproducibility N=8192 H=4 d=128 p=4 L=4 K=16")
+    say("case deterministic-mode reproducibility N=8192 H=4 d=128 p=4 L=4 K=16")
     runs = [Run(x, "bf16", 4, 4, 16, backward=True, mode=1, label=f"rep{i}") for i in range(5)]
     ref = [g.view(torch.int16).cpu() for g in runs[0].grads]
     dos = runs[0].view("dosub").cpu()
