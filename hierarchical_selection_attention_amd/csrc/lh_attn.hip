@@ -289,23 +289,33 @@ __device__ __forceinline__ void tile_to_tokens(const uint16_t* rows0, const uint
     }
 }
 
-// Work item -> (head, 64-row tile).  When H is a multiple of 8, the workgroups
-// of a head are all dispatched to the same XCD (workgroup i runs on XCD i % 8),
-// so the head's streamed operands stay in that XCD's L2.  `last_tile_first`
-// dispatches the head's tiles from the last one down (for query tiles, the
-// longest causal rows first; for key tiles, the shortest).
-__device__ __forceinline__ void work_item(int nT, int H, bool last_tile_first, int& h, int& tile) {
+// Work item -> (head, 64-row tile) of the forward.  When H is a multiple of
+// 8, head h runs on XCD h % 8 (workgroup i runs on XCD i % 8), where its
+// operands stay in that XCD's L2.  With token writes (`alternate`) the heads
+// of an XCD are interleaved tile by tile and the query tiles go out in the
+// order nT-1, 0, nT-2, 1, ... (the longest causal rows, then the shortest),
+// so the workgroups resident at any time mix long and short rows and their
+// token writes spread over the launch (at 512K: 0.507 -> 0.498 ms against the
+// order below).  Without them (dense comparison, parent kept) the launch is
+// bound by its MFMA work: heads one after the other, longest rows first.
+__device__ __forceinline__ void work_item(int nT, int H, bool alternate, int& h, int& tile) {
     const int i = blockIdx.x;
     int j;
     if (H % 8 == 0) {
-        const int x = i % 8, q = i / 8;
-        h = x + 8 * (q / nT);
-        j = q % nT;
+        const int G = H / 8, x = i % 8, q = i / 8;
+        if (alternate) {
+            h = x + 8 * (q % G);
+            j = q / G;
+        } else {
+            h = x + 8 * (q / nT);
+            j = q % nT;
+        }
     } else {
         h = i / nT;
         j = i % nT;
     }
-    tile = last_tile_first ? nT - 1 - j : j;
+    if (alternate) j = (j & 1) ? nT - 1 - (j >> 1) : (j >> 1);
+    tile = nT - 1 - j;
 }
 
 // ------------------------------------------------------------------ forward
@@ -326,7 +336,7 @@ __global__ void __launch_bounds__(256) k_attn_fwd(AttnK a) {
     const int64_t Sp = a.Sp;
     const int nT = (int)(Sp / 64);
     int h, qt;
-    work_item(nT, gridDim.x / nT, true, h, qt);
+    work_item(nT, gridDim.x / nT, a.o_tok != nullptr, h, qt);
     const int64_t q0 = (int64_t)qt * 64 + wave * 16;
     const int64_t myq = q0 + lq;
     const int64_t hb = (int64_t)h * Sp * D;
