@@ -172,11 +172,9 @@ int lh_backward_sel(const void* dout, void* dq, void* dk, void* dv,
 /* Backward pass through the scatter, the attention, the gather and the pool
  * (Fig. 1 gradient path).  q, k, v are not needed: everything is read from
  * the workspace of the matching lh_forward.  Writes dq, dk, dv [N][H][d].
- * On the bf16 path the dQ kernel runs on a second stream of the device (one
- * per device, default priority, created on the first call and kept until the
- * process ends) forked from and joined back into `stream` with events, so the
- * work still completes in `stream`'s order; calls on one device serialise
- * their use of that stream. */
+ * Every kernel is enqueued on `stream`; the library keeps no stream or
+ * buffer of its own (events only while lh_stage_timing is on), so calls with
+ * distinct workspaces on distinct streams may run concurrently. */
 int lh_backward(const void* dout, void* dq, void* dk, void* dv,
                 int N, int H, int d, int p, int L, int K, int dtype, int scatter_mode,
                 void* ws, size_t ws_bytes, void* stream);
