@@ -20,6 +20,7 @@ LH_BF16, LH_FP32 = 0, 1
 LH_SCATTER_FP_ATOMIC, LH_SCATTER_INT_ATOMIC = 0, 1
 LH_SCATTER_DETERMINISTIC = LH_SCATTER_INT_ATOMIC
 LH_SCORE_QK, LH_SCORE_K, LH_SCORE_Q, LH_SCORE_QK_PRODUCT = 0, 1, 2, 3
+LH_SCORE_KEEP_LEAVES = 0x100   # option bit: also store the level-0 scores (score view)
 LH_SELECT_PARTITION, LH_SELECT_PARENT_KEPT = 0, 1
 VIEWS = {"scores": 0, "sel_start": 1, "sel_level": 2, "qsub": 3, "ksub": 4, "vsub": 5, "osub": 6,
          "lse": 7, "dosub": 8, "dqsub": 9, "dksub": 10, "dvsub": 11, "block_first": 12}
@@ -165,11 +166,12 @@ def alloc_workspace(N, H, d, p, L, K, dtype, device="cuda", select_mode=LH_SELEC
 
 
 def forward(q, k, v, p, L, K, ws=None, out=None, stream=None, score_mode=LH_SCORE_QK,
-            select_mode=LH_SELECT_PARTITION):
+            select_mode=LH_SELECT_PARTITION, keep_leaf_scores=False):
     """o = Lighthouse layer(q, k, v) for [N, H, d] tensors.  Returns (o, ws).
 
     score_mode / select_mode other than the defaults use the alternative readings
-    (lh_forward_scored / lh_forward_sel)."""
+    (lh_forward_scored / lh_forward_sel); keep_leaf_scores also stores level 0 of
+    the score view (LH_SCORE_KEEP_LEAVES)."""
     torch = _torch()
     _dev_tensor_check(q, k, v)
     N, H, d = q.shape
@@ -178,10 +180,12 @@ def forward(q, k, v, p, L, K, ws=None, out=None, stream=None, score_mode=LH_SCOR
         ws = alloc_workspace(N, H, d, p, L, K, dt, q.device, select_mode)
     if out is None:
         out = torch.empty_like(q)
+    if keep_leaf_scores:
+        score_mode |= LH_SCORE_KEEP_LEAVES
     if select_mode != LH_SELECT_PARTITION:
         rc = lh_forward_sel(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), N, H, d, p, L, K, dt,
                             score_mode, select_mode, ws.data_ptr(), ws.numel(), _stream_handle(stream))
-    elif score_mode == LH_SCORE_QK:
+    elif score_mode == LH_SCORE_QK and not keep_leaf_scores:
         rc = lh_forward(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), N, H, d, p, L, K, dt,
                         ws.data_ptr(), ws.numel(), _stream_handle(stream))
     else:

@@ -294,6 +294,8 @@ int forward_strided(const void* q, const void* k, const void* v, void* o, int N,
     if (rc) return rc;
     if (in_ld < (int64_t)H * d || in_ld % 8 != 0) return LH_ERR_ARG;
     P.in_ld = in_ld;
+    P.keep_leaves = (score_mode & LH_SCORE_KEEP_LEAVES) ? 1 : 0;
+    score_mode &= ~LH_SCORE_KEEP_LEAVES;
     if (score_mode < LH_SCORE_QK || score_mode > LH_SCORE_QK_PRODUCT) return LH_ERR_DTYPE;
     P.score_mode = score_mode;
     if (!q || !k || !v || !o) return LH_ERR_ARG;

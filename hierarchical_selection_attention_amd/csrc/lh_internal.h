@@ -55,6 +55,7 @@ int backward_strided(const void* dout, void* dq, void* dk, void* dv, int N, int 
 struct Plan {
     int N, H, d, p, L, K, dtype, esz;
     int score_mode;         // leaf score: 0 |q|^2+|k|^2, 1 |k|^2, 2 |q|^2, 3 |q|^2*|k|^2
+    int keep_leaves;        // store the level-0 scores (inspection only; the selection ranks levels >= 1)
     int64_t in_ld;          // token stride of q, k, v in elements (H*d unless a caller strides them)
     int64_t S, Sp;
     int m;                  // pyramid level produced per workgroup by the pooling pass

@@ -28,6 +28,7 @@ struct PoolScoreArgs {
     int64_t n[kMaxLevels];
     int N, H, HG, p, m, tok, mt;
     int score_mode;
+    int store_l0;             // store level 0 too (else levels 1..m only)
     int64_t ld;               // q, k, v: token t, head h at element t * ld + h * d
     int64_t pw[kMaxLevels];
 };
@@ -136,6 +137,12 @@ __global__ void __launch_bounds__(256) k_pool_score(PoolScoreArgs a) {
                     av[e] += xv[e];
                 }
             }
+            // Materialise the sums here.  Left to itself the compiler sinks them past
+            // the score store's branch, so the loaded registers stay live across the
+            // next prefetch; it then loads into other registers and copies them back
+            // at the loop end behind a wait for every load in flight.
+#pragma unroll
+            for (int e = 0; e < 8; ++e) asm volatile("" : "+v"(aq[e]), "+v"(ak[e]), "+v"(av[e]));
             // a_g <- a_g + a_(g^off), off = G/2 .. 1
 #define LH_BFLY(OFF)                                                        \
             if constexpr (G / 2 >= OFF) {                                   \
@@ -210,8 +217,11 @@ __global__ void __launch_bounds__(256) k_pool_score(PoolScoreArgs a) {
             float* out = a.lev[l] + (int64_t)blockIdx.y * HG * a.n[l] + j0;
             // non-temporal stores: nothing reads the scores until the selection,
             // and cached lines written inside this read stream cost more (16-byte
-            // stores when every head's run is 16-byte aligned)
-            if ((per & 3) == 0 && (a.n[l] & 3) == 0 && (reinterpret_cast<uintptr_t>(out) & 15) == 0) {
+            // stores when every head's run is 16-byte aligned).  Leaves are stored
+            // only on request: writes inside this read stream cost several times
+            // their bytes, and the selection does not rank leaves.
+            if (l == 0 && !a.store_l0) {
+            } else if ((per & 3) == 0 && (a.n[l] & 3) == 0 && (reinterpret_cast<uintptr_t>(out) & 15) == 0) {
                 for (int idx = tid; idx < HG * per / 4; idx += blockDim.x) {
                     const int i4 = idx * 4, hh = i4 / per, j = i4 - hh * per;
                     const f32x4 x = *reinterpret_cast<const f32x4*>(src + i4);
@@ -549,9 +559,18 @@ __global__ void __launch_bounds__(256) k_scatter_bwd(ScatterBwdArgs a) {
     const int64_t tb = (int64_t)blockIdx.x * a.tok;
     const int64_t te = tb + a.tok;
     const int32_t* st = a.start + (int64_t)h * a.S;
-    int64_t slot = find_slot(st, a.S, tb);
-    int64_t beg = st[slot];
-    int64_t nxt = slot + 1 < a.S ? st[slot + 1] : a.N;
+    const int64_t slot0 = find_slot(st, a.S, tb);
+    // First tokens of the entries from slot0 on, for this head's walk: at most tok
+    // entries start inside the chunk, so tok + 2 values cover every entry met and
+    // the start of the one after the last (N past the end).  Kept in LDS: a load
+    // from memory at each entry boundary would wait for every dO load in flight.
+    extern __shared__ int32_t stab_mem[];
+    int32_t* stab = stab_mem + hl * (int)(a.tok + 2);
+    for (int i = c; i < (int)a.tok + 2; i += G) stab[i] = slot0 + i < a.S ? st[slot0 + i] : (int32_t)a.N;
+    __syncthreads();
+    int ls = 0;   // current entry: slot0 + ls
+    int64_t beg = stab[0];
+    int64_t nxt = stab[1];
     float s[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) s[e] = 0.f;
@@ -560,12 +579,12 @@ __global__ void __launch_bounds__(256) k_scatter_bwd(ScatterBwdArgs a) {
     // flushed when the next one starts
     auto add_token = [&](int64_t t, const float (&x)[8]) {
         if (t >= nxt) {
-            flush_entry<DT, G, MODE>(a, h, c, slot, beg >= tb && nxt <= te, s);
+            flush_entry<DT, G, MODE>(a, h, c, slot0 + ls, beg >= tb && nxt <= te, s);
 #pragma unroll
             for (int e = 0; e < 8; ++e) s[e] = 0.f;
-            ++slot;
+            ++ls;
             beg = nxt;
-            nxt = slot + 1 < a.S ? st[slot + 1] : a.N;
+            nxt = stab[ls + 1];
         }
 #pragma unroll
         for (int e = 0; e < 8; ++e) s[e] += x[e];
@@ -633,7 +652,7 @@ __global__ void __launch_bounds__(256) k_scatter_bwd(ScatterBwdArgs a) {
                 if (t0 + u < te) add_token(t0 + u, x[u]);
         }
     }
-    flush_entry<DT, G, MODE>(a, h, c, slot, beg >= tb && nxt <= te, s);
+    flush_entry<DT, G, MODE>(a, h, c, slot0 + ls, beg >= tb && nxt <= te, s);
 }
 
 // Adjoint of gather + mean-pool: dX[t][h] = dX~[h][slot_h(t)] / p^level.
@@ -863,6 +882,9 @@ hipError_t launch_pool_score(const Plan& P, const void* q, const void* k, const 
     a.pool_m = reinterpret_cast<float*>(ws + P.off_pool_m);
     a.N = P.N; a.H = P.H; a.p = P.p; a.m = P.m; a.tok = (int)P.tok;
     a.score_mode = P.score_mode;
+    // level 0 is read by the selection only when it is the top level, and by
+    // the upper pooling pass only when it is the level this pass ends at
+    a.store_l0 = (P.keep_leaves || P.L == 1 || P.m == 0) ? 1 : 0;
     a.ld = P.in_ld;
     const int G = P.d / 8;
     a.HG = head_group(P.H, G);
@@ -977,7 +999,8 @@ hipError_t launch_scatter_bwd(const Plan& P, const void* dout, int mode, char* w
     a.HG = head_group(P.H, G);
     const int threads = a.HG * G;
     dim3 grid((unsigned)(P.N / P.tok), (unsigned)(P.H / a.HG));
-#define LH_SB(DT, GG, MD) hipLaunchKernelGGL((k_scatter_bwd<DT, GG, MD>), grid, dim3(threads), 0, s, a)
+    const size_t lds = (size_t)a.HG * (size_t)(P.tok + 2) * sizeof(int32_t);   // entry starts per head
+#define LH_SB(DT, GG, MD) hipLaunchKernelGGL((k_scatter_bwd<DT, GG, MD>), grid, dim3(threads), lds, s, a)
     if (P.dtype == BF16) {
         if (G == 16) { if (mode == 0) LH_SB(0, 16, 0); else LH_SB(0, 16, 1); }
         else { if (mode == 0) LH_SB(0, 8, 0); else LH_SB(0, 8, 1); }

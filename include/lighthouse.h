@@ -131,8 +131,17 @@ typedef enum {
     LH_SCORE_QK_PRODUCT = 3
 } lh_score_mode;
 
-/* lh_forward with the score of `score_mode` (lh_score_mode; LH_ERR_DTYPE for
- * an unknown mode).  Everything else, lh_backward included, is unchanged. */
+/* Option bit for the score_mode argument of lh_forward_scored / lh_forward_sel:
+ * also store the leaf scores (level 0 of LH_VIEW_SCORES).  The selection never
+ * ranks leaves -- the p children of a selected level-1 entry are all kept -- so
+ * the layer itself needs only levels 1..L-1, and without this bit level 0 of
+ * the score view is left unwritten (except when L = 1, where level 0 is the
+ * top).  Leaf scores are computed either way: level 1 is their max-pool. */
+#define LH_SCORE_KEEP_LEAVES 0x100
+
+/* lh_forward with the score of `score_mode` (lh_score_mode, optionally ORed
+ * with LH_SCORE_KEEP_LEAVES; LH_ERR_DTYPE for an unknown mode).  Everything
+ * else, lh_backward included, is unchanged. */
 int lh_forward_scored(const void* q, const void* k, const void* v, void* o,
                       int N, int H, int d, int p, int L, int K, int dtype, int score_mode,
                       void* ws, size_t ws_bytes, void* stream);
@@ -182,7 +191,8 @@ int lh_backward(const void* dout, void* dq, void* dk, void* dv,
 /* Locations of intermediate results inside a workspace, for inspection.
  * Host only; pure address arithmetic on `ws`. */
 typedef enum {
-    LH_VIEW_SCORES = 0,     /* fp32, levels 0..L-1 concatenated, each [H][N/p^l]   */
+    LH_VIEW_SCORES = 0,     /* fp32, levels 0..L-1 concatenated, each [H][N/p^l]
+                               (level 0 only with LH_SCORE_KEEP_LEAVES or L = 1) */
     LH_VIEW_SEL_START = 1,  /* int32 [H][S]: first token of each kept entry        */
     LH_VIEW_SEL_LEVEL = 2,  /* uint8 [H][S]: pyramid level of each kept entry      */
     LH_VIEW_QSUB = 3,       /* fp32 [H][Sp][d]: gathered q (rows >= S are zero)    */
