@@ -35,7 +35,12 @@ struct TopkArgs {
     int64_t ncand[kMaxLevels];      // candidates at level l: ntop at the top, p*min(K, .) below
     int64_t S, cap, ntop;
     int L, p, K;
+    // per-level arrays in LDS when they fit (lds = 1): level l's five arrays of llen[l]
+    // words each from word loff[l]; the candidates' scores of the level being ranked from ks_off
+    int lds;
+    int64_t loff[kMaxLevels], llen[kMaxLevels], ks_off;
 };
+constexpr size_t kTopkLdsMax = 144 * 1024;   // gfx950: 160 KiB of LDS per workgroup
 
 __device__ __forceinline__ uint64_t make_key(float s, int32_t idx) {
     return ((uint64_t)__float_as_uint(s) << 32) | (uint64_t)(uint32_t)(~idx);
@@ -47,8 +52,10 @@ __device__ __forceinline__ uint64_t make_key(float s, int32_t idx) {
 // of the next digit is counted, and wavefront 0 walks it from the top to the
 // bin that holds the k-th largest, which becomes the next digit of the answer.
 // When that bin holds a single key, one more pass reads the key itself.
-__device__ uint64_t kth_largest_key(const float* sc, const int32_t* idx, int64_t nc, int64_t k, int32_t* hist,
-                                    int64_t* bcast) {
+__device__ uint64_t kth_largest_key(const float* sc, const int32_t* idx, const float* ks, int64_t nc, int64_t k,
+                                    int32_t* hist, int64_t* bcast) {
+    // candidate i's score: from the level's scores, or from the copy ks[i] made for this level
+    auto score = [&](int64_t i) { return ks ? ks[i] : sc[idx[i]]; };
     const int tid = threadIdx.x, lane = tid & 63;
     uint64_t pre = 0, mask = 0;
     int64_t krem = k;   // rank of the answer among the keys that match `pre`
@@ -56,8 +63,7 @@ __device__ uint64_t kth_largest_key(const float* sc, const int32_t* idx, int64_t
         for (int i = tid; i < 256; i += blockDim.x) hist[i] = 0;
         __syncthreads();
         for (int64_t i = tid; i < nc; i += blockDim.x) {
-            const int32_t j = idx[i];
-            const uint64_t key = make_key(sc[j], j);
+            const uint64_t key = make_key(score(i), idx[i]);
             if ((key & mask) == pre) atomicAdd(&hist[(key >> shift) & 0xFF], 1);
         }
         __syncthreads();
@@ -97,8 +103,7 @@ __device__ uint64_t kth_largest_key(const float* sc, const int32_t* idx, int64_t
         __syncthreads();                     // bcast is rewritten below
         if (unique) {
             for (int64_t i = tid; i < nc; i += blockDim.x) {
-                const int32_t j = idx[i];
-                const uint64_t key = make_key(sc[j], j);
+                const uint64_t key = make_key(score(i), idx[i]);
                 if ((key & mask) == pre) bcast[3] = (int64_t)key;
             }
             __syncthreads();
@@ -151,7 +156,13 @@ __global__ void __launch_bounds__(kTopkThreads) k_topk(TopkArgs a) {
     const int L = a.L, p = a.p, K = a.K;
     const int64_t cap = a.cap;
     int32_t* base = a.scratch + (int64_t)h * L * 5 * cap;
-    auto arr = [&](int l, int which) { return base + ((int64_t)l * 5 + which) * cap; };
+    // The selection is a chain of dependent passes over small arrays: kept in LDS
+    // (when they fit) every pass waits for LDS instead of memory.
+    extern __shared__ int32_t tk_lds[];
+    auto arr = [&](int l, int which) -> int32_t* {
+        return a.lds ? tk_lds + a.loff[l] + which * a.llen[l] : base + ((int64_t)l * 5 + which) * cap;
+    };
+    float* ks = a.lds ? reinterpret_cast<float*>(tk_lds + a.ks_off) : nullptr;
     // which: 0 idx, 1 flag, 2 rank, 3 cnt, 4 first
     const int64_t* ncand = a.ncand;
 
@@ -168,10 +179,14 @@ __global__ void __launch_bounds__(kTopkThreads) k_topk(TopkArgs a) {
             const int32_t all = nc <= K ? 1 : 0;
             for (int64_t i = tid; i < nc; i += blockDim.x) flag[i] = all;
         } else {
-            const uint64_t tau = kth_largest_key(sc, idx, nc, K, hist, bcast);
+            if (ks) {
+                for (int64_t i = tid; i < nc; i += blockDim.x) ks[i] = sc[idx[i]];
+                __syncthreads();
+            }
+            const uint64_t tau = kth_largest_key(sc, idx, ks, nc, K, hist, bcast);
             for (int64_t i = tid; i < nc; i += blockDim.x) {
-                const int32_t j = idx[i];
-                flag[i] = make_key(sc[j], j) >= tau ? 1 : 0;
+                const float v = ks ? ks[i] : sc[idx[i]];
+                flag[i] = make_key(v, idx[i]) >= tau ? 1 : 0;
             }
         }
         __syncthreads();
@@ -277,7 +292,20 @@ hipError_t launch_topk(const Plan& P, char* ws, hipStream_t s) {
         a.ncand[l] = nc;
         nc = (nc < P.K ? nc : P.K) * P.p;
     }
-    hipLaunchKernelGGL(k_topk, dim3((unsigned)P.H), dim3(kTopkThreads), 0, s, a);
+    // LDS layout: each level's five arrays (lengths rounded up to 4 words), then the
+    // score copy of the largest ranked level
+    int64_t words = 0, ksw = 0;
+    for (int l = P.L - 1; l >= 0; --l) {
+        a.llen[l] = (a.ncand[l] + 3) & ~(int64_t)3;
+        a.loff[l] = words;
+        words += 5 * a.llen[l];
+        if (l >= 1 && a.llen[l] > ksw) ksw = a.llen[l];
+    }
+    a.ks_off = words;
+    words += ksw;
+    const size_t lds = (size_t)words * sizeof(int32_t);
+    a.lds = lds <= kTopkLdsMax ? 1 : 0;
+    hipLaunchKernelGGL(k_topk, dim3((unsigned)P.H), dim3(kTopkThreads), a.lds ? lds : 0, s, a);
     return hipGetLastError();
 }
 
