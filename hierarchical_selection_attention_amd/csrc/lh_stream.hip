@@ -29,6 +29,8 @@ struct PoolScoreArgs {
     int N, H, HG, p, m, tok, mt;
     int score_mode;
     int store_l0;             // store level 0 too (else levels 1..m only)
+    int tpc;                  // threads per chunk; a workgroup of ng * tpc threads takes ng chunks
+    int lds_chunk;            // floats of LDS per chunk
     int64_t ld;               // q, k, v: token t, head h at element t * ld + h * d
     int64_t pw[kMaxLevels];
 };
@@ -48,11 +50,21 @@ __device__ __forceinline__ float leaf_score(float sq, float sk, int mode) {
 #define LH_SCATTER_U 3
 #endif
 
+#ifndef LH_POOL_NG
+#define LH_POOL_NG 4
+#endif
 template <int DT, int G>
-__global__ void __launch_bounds__(256) k_pool_score(PoolScoreArgs a) {
-    extern __shared__ float smem[];
+__global__ void __launch_bounds__(1024) k_pool_score(PoolScoreArgs a) {
+    extern __shared__ float smem_all[];
     const int d = G * 8;
-    const int tid = threadIdx.x;
+    // Chunk group: a workgroup may take several chunks side by side (one per group of
+    // tpc threads) and store all their results after one barrier.  The group index is
+    // uniform over a wavefront: several chunks per workgroup only when tpc is a
+    // multiple of 64.
+    const int grp = __builtin_amdgcn_readfirstlane(threadIdx.x / a.tpc);
+    const int tid = threadIdx.x - grp * a.tpc;
+    const int64_t chunk = (int64_t)blockIdx.x * (blockDim.x / a.tpc) + grp;
+    float* smem = smem_all + (size_t)grp * a.lds_chunk;
     const int c = tid % G;
     const int row = tid / G;
     const int HG = a.HG;              // heads handled by this workgroup
@@ -60,7 +72,7 @@ __global__ void __launch_bounds__(256) k_pool_score(PoolScoreArgs a) {
     const int h = blockIdx.y * HG + hl;
     const int ts = row / HG;
     const int H = a.H;
-    const int64_t t0 = (int64_t)blockIdx.x * a.tok;
+    const int64_t t0 = chunk * a.tok;
     const int iters = a.tok / a.mt;
     float* sc = smem;   // [HG][tok] leaf scores of this chunk (head-major)
 
@@ -222,20 +234,20 @@ __global__ void __launch_bounds__(256) k_pool_score(PoolScoreArgs a) {
             // their bytes, and the selection does not rank leaves.
             if (l == 0 && !a.store_l0) {
             } else if ((per & 3) == 0 && (a.n[l] & 3) == 0 && (reinterpret_cast<uintptr_t>(out) & 15) == 0) {
-                for (int idx = tid; idx < HG * per / 4; idx += blockDim.x) {
+                for (int idx = tid; idx < HG * per / 4; idx += a.tpc) {
                     const int i4 = idx * 4, hh = i4 / per, j = i4 - hh * per;
                     const f32x4 x = *reinterpret_cast<const f32x4*>(src + i4);
                     __builtin_nontemporal_store(x, reinterpret_cast<f32x4*>(out + (int64_t)hh * a.n[l] + j));
                 }
             } else {
-                for (int idx = tid; idx < HG * per; idx += blockDim.x) {
+                for (int idx = tid; idx < HG * per; idx += a.tpc) {
                     const int hh = idx / per, j = idx - hh * per;
                     __builtin_nontemporal_store(src[idx], out + (int64_t)hh * a.n[l] + j);
                 }
             }
             if (l == a.m) break;
             const int nper = per / a.p;
-            for (int idx = tid; idx < HG * nper; idx += blockDim.x) {
+            for (int idx = tid; idx < HG * nper; idx += a.tpc) {
                 const float* g = src + (int64_t)idx * a.p;   // entries idx*p .. idx*p+p-1 of [HG][per]
                 float mx = g[0];
                 for (int k = 1; k < a.p; ++k) mx = fmaxf(mx, g[k]);
@@ -251,7 +263,7 @@ __global__ void __launch_bounds__(256) k_pool_score(PoolScoreArgs a) {
     if (a.m >= 1) {
         float* red = smem + (size_t)a.tok * HG + (size_t)(a.tok / a.p) * HG;   // [mt][HG][d]
         const float inv = 1.0f / (float)a.tok;
-        const int64_t blk = blockIdx.x;
+        const int64_t blk = chunk;
         float* accs[3] = {aq, ak, av};
 #pragma unroll
         for (int t = 0; t < 3; ++t) {
@@ -897,13 +909,25 @@ hipError_t launch_pool_score(const Plan& P, const void* q, const void* k, const 
     size_t lds = sizeof(float) * (size_t)P.tok * a.HG;
     if (P.m >= 1) lds += sizeof(float) * (size_t)(P.tok / P.p) * a.HG;
     if (P.m >= 1 && mt > 1) lds += sizeof(float) * (size_t)mt * a.HG * P.d;
-    dim3 grid((unsigned)(P.N / P.tok), (unsigned)(P.H / a.HG));
+    // Chunks per workgroup: up to LH_POOL_NG side by side, so that one workgroup fills a
+    // CU.  Workgroups sharing a CU progress unevenly (the oldest is served first) and
+    // their result stores then trickle into the read stream, where writes cost several
+    // times their bytes; with one workgroup per CU they all finish together.
+    const int64_t nchunks = P.N / P.tok;
+    int ng = 1;
+    while (threads % 64 == 0 && ng * 2 <= LH_POOL_NG && ng * 2 * threads <= 1024 && nchunks % (ng * 2) == 0 &&
+           (size_t)(ng * 2) * lds <= 96 * 1024)
+        ng *= 2;
+    a.tpc = threads;
+    a.lds_chunk = (int)(lds / sizeof(float));
+    lds *= (size_t)ng;
+    dim3 grid((unsigned)(nchunks / ng), (unsigned)(P.H / a.HG));
     if (P.dtype == BF16) {
-        if (G == 16) hipLaunchKernelGGL((k_pool_score<0, 16>), grid, dim3(threads), lds, s, a);
-        else hipLaunchKernelGGL((k_pool_score<0, 8>), grid, dim3(threads), lds, s, a);
+        if (G == 16) hipLaunchKernelGGL((k_pool_score<0, 16>), grid, dim3(threads * ng), lds, s, a);
+        else hipLaunchKernelGGL((k_pool_score<0, 8>), grid, dim3(threads * ng), lds, s, a);
     } else {
-        if (G == 16) hipLaunchKernelGGL((k_pool_score<1, 16>), grid, dim3(threads), lds, s, a);
-        else hipLaunchKernelGGL((k_pool_score<1, 8>), grid, dim3(threads), lds, s, a);
+        if (G == 16) hipLaunchKernelGGL((k_pool_score<1, 16>), grid, dim3(threads * ng), lds, s, a);
+        else hipLaunchKernelGGL((k_pool_score<1, 8>), grid, dim3(threads * ng), lds, s, a);
     }
     return hipGetLastError();
 }
