@@ -40,10 +40,10 @@ __device__ __forceinline__ float leaf_score(float sq, float sk, int mode) {
 }
 
 // Tokens per load batch of the bf16 pooling pass (two batches in flight per wave).
-// One is fastest on MI355X at d = 128: 90 VGPRs, five waves per SIMD; the read
-// stream is not latency bound at that depth, larger batches only cost occupancy.
+// Two at d = 128: 110 VGPRs, four waves per SIMD, which is exactly one workgroup
+// of four chunks per CU (0.961 -> 0.950 ms at 512K against one token per batch).
 #ifndef LH_POOL_U
-#define LH_POOL_U 1
+#define LH_POOL_U 2
 #endif
 // Tokens per load batch of the bf16 scatter adjoint (one tensor streamed).
 #ifndef LH_SCATTER_U
