@@ -42,11 +42,13 @@ def stage_bytes(w, S, pk=False):
     N, H, d, p, L = w["N"], w["H"], w["d"], w["p"], w["L"]
     e = 2 if w["dtype"] == "bf16" else 4
     row = N * H * d * e                         # one [N, H, d] tensor
-    nscore = sum(N // p ** l for l in range(L)) * H * 4
     top = (N // p ** (L - 1)) * H * d * 4
     m = 0
     while m + 1 <= L - 1 and p ** (m + 1) <= 256 and p ** (m + 1) * H <= 8192:
         m += 1
+    # the pooling pass stores the scores of levels 1..m (level 0 too when it is the top level
+    # or the pass ends there: the selection never ranks leaves)
+    nscore = sum(N // p ** l for l in range(0 if (L == 1 or m == 0) else 1, m + 1)) * H * 4
     pool_m = (N // p ** m) * H * d * 4 * 3
     sub32 = S * H * d * 4
     out = {
