@@ -140,6 +140,17 @@ def test_scored_forward_rejects_unknown_score_mode():
                                 None) == lh.LH_ERR_DTYPE
     assert lh.lh_forward_scored(fake, fake, fake, fake, 2048, 2, 64, 4, 3, 16, 1, -1, fake * 256, nb,
                                 None) == lh.LH_ERR_DTYPE
+    # the keep-leaves option bit does not make an unknown mode valid
+    assert lh.lh_forward_scored(fake, fake, fake, fake, 2048, 2, 64, 4, 3, 16, 1, lh.LH_SCORE_KEEP_LEAVES | 7,
+                                fake * 256, nb, None) == lh.LH_ERR_DTYPE
+
+
+def test_keep_leaves_bit_matches_the_header():
+    lh = _lh()
+    hdr = open(os.path.join(ROOT, "include", "lighthouse.h")).read()
+    m = re.search(r"#define\s+LH_SCORE_KEEP_LEAVES\s+(0x[0-9a-fA-F]+|\d+)", hdr)
+    assert m and int(m.group(1), 0) == lh.LH_SCORE_KEEP_LEAVES
+    assert lh.LH_SCORE_KEEP_LEAVES & 0xff == 0   # clear of every score mode
 
 
 @pytest.mark.parametrize("N,p,L,K", [(2048, 4, 3, 16), (2048, 4, 3, 512), (524288, 4, 5, 128), (1080, 3, 4, 5),
