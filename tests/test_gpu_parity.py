@@ -33,6 +33,9 @@ CASES = [
     # a wide pooling factor: p^2 = 64 tokens per top entry
     ("bf16_p8", 4096, 2, 64, "bf16", 8, 3, 3, "lognormal", 0.0, True),
     ("fp32_p8_h1", 512, 1, 64, "fp32", 8, 3, 4, "lognormal", 0.0, True),
+    # 8192 top-level candidates: the selection's per-level arrays exceed what it keeps in
+    # LDS, so it works on the workspace arrays instead
+    ("bf16_topk_arrays_in_memory", 32768, 1, 64, "bf16", 4, 2, 64, "lognormal", 0.0, True),
 ]
 
 
