@@ -13,9 +13,11 @@ namespace lh {
 
 // ---------------------------------------------------------------------------
 // Pooling + scoring pass (stage (i) and the scorer of stage (ii)).
-// One workgroup per chunk of `tok` = p^m tokens, all heads.  Thread
-// (ts, h, c): token lane ts, head h, 8-element chunk c.  Outputs: leaf scores
-// and their max-pool for levels 0..m, and the level-m means of q, k, v (fp32).
+// Chunks of `tok` = p^m tokens, all heads of a head group; a workgroup takes
+// up to four chunks side by side (one group of threads each).  Thread (ts, h, c)
+// of a group: token lane ts, head h, 8-element chunk c.  Outputs: the max-pool
+// of the leaf scores for levels 1..m (and the leaf scores themselves on
+// request), and the level-m means of q, k, v (fp32).
 // The leaf score is ||q||^2 + ||k||^2 in fp32 in a fixed order: fma over the 8
 // elements of a lane from +0, then a xor butterfly over the G lanes of the row,
 // then one add of the q and k parts.  The other readings of what the norm is
