@@ -104,7 +104,9 @@ def measured_traffic(workload, stage):
 
 def achievable_peaks(lh, torch, stream):
     """What plain in-repo kernels reach on this GPU (lh_peak_probe): 2 GiB read, write and
-    copy streams, and a register-only bf16 MFMA loop.  Reported beside the vendor peaks."""
+    copy streams, 2 GiB written in the token-row pattern of the attention kernels' scatter
+    (one head's 256-byte pieces, 4 KiB apart), and a register-only bf16 MFMA loop.
+    Reported beside the vendor peaks."""
     nbytes = 2 << 30
     src = torch.empty(nbytes // 4, dtype=torch.int32, device="cuda")
     dst = torch.empty_like(src)
@@ -114,7 +116,7 @@ def achievable_peaks(lh, torch, stream):
     mfma_flops = 4096 * iters * 4 * 32768
     out = {}
     for kind, name, moved in ((0, "read_GBs", nbytes), (1, "write_GBs", nbytes), (2, "copy_GBs", 2 * nbytes),
-                              (3, "mfma_bf16_TFLOPs", mfma_flops)):
+                              (5, "token_write_GBs", nbytes), (3, "mfma_bf16_TFLOPs", mfma_flops)):
         a = src if kind in (0, 2) else None
         b = acc if kind in (0, 3) else dst
         n = iters if kind == 3 else nbytes

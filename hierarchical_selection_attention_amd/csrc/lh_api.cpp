@@ -537,6 +537,10 @@ int lh_peak_probe(int kind, const void* src, void* dst, size_t n, void* stream) 
     if (kind >= 0 && kind <= 2) {
         if (n % 16 != 0 || (kind != 1 && !src)) return LH_ERR_ARG;
         if ((reinterpret_cast<uintptr_t>(dst) | reinterpret_cast<uintptr_t>(src)) % 16 != 0) return LH_ERR_ARG;
+    } else if (kind == 5) {
+        // whole 64 MiB groups (16 heads x 16384 tokens x 256 bytes), within a 32-bit grid
+        if (n % ((size_t)64 << 20) != 0 || n > ((size_t)1 << 40) || reinterpret_cast<uintptr_t>(dst) % 16 != 0)
+            return LH_ERR_ARG;
     } else if (kind == 4) {
         if (!src || n > (1u << 20) || (reinterpret_cast<uintptr_t>(dst) | reinterpret_cast<uintptr_t>(src)) % 16 != 0)
             return LH_ERR_ARG;

@@ -73,6 +73,25 @@ __global__ void __launch_bounds__(256) k_probe_write(u32x4* __restrict__ dst, in
     for (int64_t i = b0 + threadIdx.x; i < b1; i += 256) __builtin_nontemporal_store(z, dst + i);
 }
 
+// kind 5: the token-row write pattern of the attention kernels' scatter: bf16
+// rows [T][16 heads][128], each workgroup writing one head's 256-byte pieces
+// (4 KiB apart) for 16384 consecutive tokens (4 MiB, about what one work item
+// of the backward writes), 16 tokens per pass of its 256 threads, one pointer
+// step per store.  Thread t's store i goes to token tb + t / 16 + 16 i, chunk
+// t % 16; its value is {1.0f bits, workgroup, thread, 0}.  n16 is a multiple of
+// 16 heads x 16384 tokens x 16 words.
+constexpr int kTokHeads = 16, kTokPerWg = 16384;
+__global__ void __launch_bounds__(256) k_probe_token_write(u32x4* __restrict__ dst) {
+    const int64_t g = blockIdx.x;
+    const int h = (int)(g % kTokHeads);
+    const int64_t tb = (g / kTokHeads) * kTokPerWg;
+    const int c = threadIdx.x % 16;
+    const u32x4 z = {0x3f800000u, (unsigned)blockIdx.x, (unsigned)threadIdx.x, 0u};
+    u32x4* p = dst + ((tb + threadIdx.x / 16) * kTokHeads + h) * 16 + c;
+    const int64_t step = (int64_t)16 * kTokHeads * 16;   // 16 tokens, in 16-byte words
+    for (int i = 0; i < kTokPerWg / 16; ++i, p += step) __builtin_nontemporal_store(z, p);
+}
+
 // kind 3: every wave issues `iters` rounds of 4 independent
 // v_mfma_f32_32x32x16_bf16 on register operands (32768 flops each); four
 // accumulation chains per wave keep the matrix pipe full
@@ -128,6 +147,12 @@ hipError_t launch_peak_probe(int kind, const void* src, void* dst, size_t n, hip
     }
     if (kind == 3) {
         hipLaunchKernelGGL(k_probe_mfma, dim3(kMfmaGrid), dim3(256), 0, s, (int)n, reinterpret_cast<unsigned*>(dst));
+        return hipGetLastError();
+    }
+    if (kind == 5) {
+        const int64_t words = (int64_t)(n / 16);
+        hipLaunchKernelGGL(k_probe_token_write, dim3((unsigned)(words / (16 * kTokPerWg))), dim3(256), 0, s,
+                           reinterpret_cast<u32x4*>(dst));
         return hipGetLastError();
     }
     const int64_t n16 = (int64_t)(n / 16);

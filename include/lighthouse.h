@@ -240,8 +240,14 @@ int lh_read_selection_sel(const void* ws, int N, int H, int d, int p, int L, int
  * src + 3072 t (lanes 0..63 of fp16 A[8], then fp16 B[8], then fp32 C[4]; lane
  * l holds A[l % 16][8 (l / 16) + e], B[8 (l / 16) + e][l % 16] and C, D at rows
  * 4 (l / 16) + r, column l % 16) writes D to dst + 1024 t (lanes 0..63 of fp32
- * D[4]).  Device pointers; enqueued on `stream`.  Returns LH_OK, LH_ERR_ARG, or
- * LH_ERR_HIP. */
+ * D[4]); kind 5 writes n bytes at dst (n a multiple of 64 MiB, at most 2^40,
+ * dst 16-byte aligned) in the token-row pattern of the attention kernels'
+ * scatter: dst read as bf16 rows [n / 4096][16][128], each workgroup of 256
+ * threads writing one head's 256-byte pieces of 16384 consecutive tokens, 16
+ * tokens per pass, in 16-byte non-temporal stores (the 16-byte word of token t,
+ * head h, chunk c holds {1.0f bits, workgroup 16 (t / 16384) + h, thread
+ * 16 (t % 16) + c, 0}).  Device pointers; enqueued on `stream`.  Returns LH_OK,
+ * LH_ERR_ARG, or LH_ERR_HIP. */
 int lh_peak_probe(int kind, const void* src, void* dst, size_t n, void* stream);
 
 /* Dense causal attention over all N tokens with the same attention kernels

@@ -79,7 +79,10 @@ def test_entry_points_validate_before_launching():
     assert lh.lh_read_selection(aligned_ws, N, H, d, p, L, K, 1, None, None, None) == lh.LH_ERR_ARG
     assert lh.lh_read_selection(aligned_ws, 2047, H, d, p, L, K, 1, fake, fake, None) == lh.LH_ERR_SHAPE
     assert lh.lh_read_selection(aligned_ws, N, H, d, p, L, K, 7, fake, fake, None) == lh.LH_ERR_DTYPE
-    assert lh.lh_peak_probe(5, fake, fake, 1 << 20, None) == lh.LH_ERR_ARG        # unknown kind
+    assert lh.lh_peak_probe(6, fake, fake, 1 << 20, None) == lh.LH_ERR_ARG        # unknown kind
+    assert lh.lh_peak_probe(5, None, fake, 16 << 20, None) == lh.LH_ERR_ARG       # token rows: whole 64 MiB groups
+    assert lh.lh_peak_probe(5, None, fake + 8, 64 << 20, None) == lh.LH_ERR_ARG   # misaligned
+    assert lh.lh_peak_probe(5, None, fake, (1 << 40) + (64 << 20), None) == lh.LH_ERR_ARG
     assert lh.lh_peak_probe(4, fake, fake, (1 << 20) + 1, None) == lh.LH_ERR_ARG  # too many rounding trials
     assert lh.lh_peak_probe(0, fake, fake, 17, None) == lh.LH_ERR_ARG             # not a multiple of 16
     assert lh.lh_peak_probe(0, None, fake, 1 << 20, None) == lh.LH_ERR_ARG        # read needs a source

@@ -56,6 +56,20 @@ def test_peak_probes_move_the_right_bytes():
     assert np.array_equal(words[:, 1], (idx // 16384).astype(np.uint32))
     assert np.array_equal(words[:, 2], (idx % 256).astype(np.uint32))
     assert np.all(words[:, 3] == 0)
+    # token-row write pattern: the word of token t, head h, chunk c holds
+    # {1.0f bits, workgroup 16 (t / 16384) + h, thread 16 (t % 16) + c, 0}
+    nt = 128 << 20
+    tokw = torch.zeros(nt // 4, dtype=torch.int32, device="cuda")
+    lh.peak_probe(5, None, tokw, nt)
+    torch.cuda.synchronize()
+    words = tokw.cpu().numpy().view(np.uint32).reshape(-1, 16, 16, 4)   # [token][head][chunk]
+    t = np.arange(words.shape[0])[:, None, None]
+    h = np.arange(16)[None, :, None]
+    c = np.arange(16)[None, None, :]
+    assert np.all(words[..., 0] == 0x3F800000)
+    assert np.array_equal(words[..., 1], np.broadcast_to(16 * (t // 16384) + h, words.shape[:3]).astype(np.uint32))
+    assert np.array_equal(words[..., 2], np.broadcast_to(16 * (t % 16) + c, words.shape[:3]).astype(np.uint32))
+    assert np.all(words[..., 3] == 0)
     # MFMA loop: every workgroup runs the same operands, so all 1024 checksums agree
     chk = torch.zeros((1024, 4), dtype=torch.int32, device="cuda")
     lh.peak_probe(3, None, chk, 16)
