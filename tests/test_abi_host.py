@@ -189,3 +189,26 @@ def test_forward_static_rejects_before_any_launch():
     assert lh.lh_forward_static(fake, fake, fake, fake, 2047, 2, 64, 4, 3, 16, 0, None) == lh.LH_ERR_SHAPE
     assert lh.lh_forward_static(fake, fake, fake, fake, 2048, 2, 64, 4, 3, 16, 7, None) == lh.LH_ERR_DTYPE
     assert "static array" in lh.lh_status_str(lh.LH_ERR_SCRATCH)
+
+
+def test_workspace_plan_accepts_every_valid_shape():
+    """Every shape lh_subseq_len accepts gets a workspace in both selection modes, over a
+    sweep that includes K = 0, K above every candidate count, one level and deep
+    pyramids."""
+    lh = _lh()
+    n_ok = 0
+    for p in (2, 3, 4, 8):
+        for L in range(1, 9):
+            top = p ** (L - 1)
+            for mult in (1, 3, 16):
+                N = top * mult * (64 if top < 64 else 1)
+                if N > (1 << 22):
+                    continue
+                for K in (0, 1, 5, 64, 300, N):
+                    if lh.lh_subseq_len(N, p, L, K) < 0:
+                        continue
+                    for H, d in ((1, 64), (3, 64), (16, 128)):
+                        assert lh.lh_workspace_bytes(N, H, d, p, L, K, 0) > 0, (N, H, d, p, L, K)
+                        assert lh.lh_workspace_bytes_sel(N, H, d, p, L, K, 0, 1) > 0, (N, H, d, p, L, K)
+                        n_ok += 1
+    assert n_ok > 500
