@@ -133,6 +133,14 @@ int block_plan(int N, int H, int d, int dm, int p, int L, int K, BlockPlan* b) {
 
 bool al16(const void* p) { return reinterpret_cast<uintptr_t>(p) % 16 == 0; }
 
+// The GEMM handle is the current device's: a stream of another device is refused.
+int check_stream_device(hipStream_t s) {
+    if (!s) return LH_OK;
+    int cur = -1, sdev = -1;
+    if (hipGetDevice(&cur) != hipSuccess || hipStreamGetDevice(s, &sdev) != hipSuccess) return LH_ERR_HIP;
+    return sdev == cur ? LH_OK : LH_ERR_ARG;
+}
+
 }  // namespace
 }  // namespace lh
 
@@ -162,6 +170,7 @@ int lh_block_forward(const void* x, const void* w_qkv, const void* w_o, void* o,
     if (!al16(x) || !al16(w_qkv) || !al16(w_o) || !al16(o) || !al16(y)) return LH_ERR_ARG;
     if (!ws || reinterpret_cast<uintptr_t>(ws) % 256 != 0 || ws_bytes < b.total) return LH_ERR_WORKSPACE;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    if ((rc = check_stream_device(s))) return rc;
     char* w = reinterpret_cast<char*>(ws);
     const int64_t hd = (int64_t)H * d;
     uint16_t* qkv = reinterpret_cast<uint16_t*>(w + b.off_qkv);
@@ -188,6 +197,7 @@ int lh_block_backward(const void* x, const void* w_qkv, const void* w_o, const v
     if (!ws || reinterpret_cast<uintptr_t>(ws) % 256 != 0 || ws_bytes < b.total) return LH_ERR_WORKSPACE;
     if (scatter_mode != LH_SCATTER_FP_ATOMIC && scatter_mode != LH_SCATTER_INT_ATOMIC) return LH_ERR_DTYPE;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    if ((rc = check_stream_device(s))) return rc;
     char* w = reinterpret_cast<char*>(ws);
     const int64_t hd = (int64_t)H * d;
     uint16_t* g = reinterpret_cast<uint16_t*>(w + b.off_qkv);   // [N][3Hd]: dq | dk | dv per token

@@ -290,8 +290,10 @@ int lh_dense_attn_bwd(const void* q, const void* k, const void* v, const void* o
  * gradients in the same layout; at the next 256-byte boundary after those the backward
  * leaves dO = dy W_O^T ([N][H][d] bf16).  The workspace must stay untouched
  * between the forward and the backward.  dm must be a multiple of
- * 8; the other shape limits are the layer's.  Returns LH_OK, a negative
- * lh_status for bad arguments (nothing enqueued), LH_ERR_HIP or LH_ERR_GEMM. */
+ * 8; the other shape limits are the layer's.  `stream` must belong to the
+ * current device, whose hipBLASLt handle runs the products (LH_ERR_ARG
+ * otherwise).  Returns LH_OK, a negative lh_status for bad arguments (nothing
+ * enqueued), LH_ERR_HIP or LH_ERR_GEMM. */
 size_t lh_block_workspace_bytes(int N, int H, int d, int dm, int p, int L, int K);
 int lh_block_forward(const void* x, const void* w_qkv, const void* w_o, void* o, void* y,
                      int N, int H, int d, int dm, int p, int L, int K,
