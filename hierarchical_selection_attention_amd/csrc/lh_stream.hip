@@ -450,7 +450,7 @@ __global__ void __launch_bounds__(64) k_gather(GatherArgs a) {
             o[e] = (R > 1) ? acc[t][e] / (float)R : acc[t][e];
             mx = fmaxf(mx, fabsf(o[e]));
         }
-        if (rs == 0) store8f(dst[t], orow, o);
+        if (rs == 0) store8f_nt(dst[t], orow, o);
         // the row's max |x| for the per-head scale of the 16-bit operand copies (lanes
         // rs != 0 hold the same row after the butterfly, or zeros when R == 1)
 #pragma unroll
@@ -553,13 +553,13 @@ __device__ __forceinline__ void flush_entry(const ScatterBwdArgs& a, int h, int 
     constexpr int d = G * 8;
     const int64_t el = ((int64_t)h * a.Sp + slot) * d + c * 8;
     if (whole) {
-        store8f(a.acc, el, s);
+        store8f_nt(a.acc, el, s);
     } else if constexpr (MODE == 0) {
         float* p = a.acc + el;
 #pragma unroll
         for (int e = 0; e < 8; ++e) unsafeAtomicAdd(p + e, s[e]);
     } else {
-        store8f(a.part, ((int64_t)h * (a.N / a.tok) + blockIdx.x) * d + c * 8, s);
+        store8f_nt(a.part, ((int64_t)h * (a.N / a.tok) + blockIdx.x) * d + c * 8, s);
     }
 }
 
