@@ -398,7 +398,7 @@ __global__ void __launch_bounds__(64) k_gather(GatherArgs a) {
         if (rs == 0) {
             const int64_t el = ((st / a.pw[l]) * H + h) * d + c * 8;
 #pragma unroll
-            for (int t = 0; t < 3; ++t) load8f(a.pool_top + t * a.ntop * H * d, el, acc[t]);
+            for (int t = 0; t < 3; ++t) load8_nt<1>(a.pool_top + t * a.ntop * H * d, el, acc[t]);
         }
     } else if (l >= 1 && l >= a.m) {
         R = a.pw[l] / a.pw[a.m];
@@ -408,7 +408,7 @@ __global__ void __launch_bounds__(64) k_gather(GatherArgs a) {
 #pragma unroll
             for (int t = 0; t < 3; ++t) {
                 float x[8];
-                load8f(a.pool_m + t * a.n_m * H * d, el, x);
+                load8_nt<1>(a.pool_m + t * a.n_m * H * d, el, x);
 #pragma unroll
                 for (int e = 0; e < 8; ++e) acc[t][e] += x[e];
             }
@@ -425,7 +425,7 @@ __global__ void __launch_bounds__(64) k_gather(GatherArgs a) {
                 if (r < R) {
                     const int64_t el = (st + r) * a.ld + (int64_t)h * d + c * 8;
 #pragma unroll
-                    for (int t = 0; t < 3; ++t) load8<DT>(src[t], el, x[u][t]);
+                    for (int t = 0; t < 3; ++t) load8_nt<DT>(src[t], el, x[u][t]);
                 }
             }
 #pragma unroll
