@@ -53,17 +53,33 @@ struct HeadMaxArgs {
     int64_t rows, rows_ld;
     int H;
 };
-__global__ void __launch_bounds__(256) k_head_max(HeadMaxArgs a) {
+// 1024 threads, four independent loads in flight per thread per pass.
+constexpr int kHeadMaxThreads = 1024;
+__global__ void __launch_bounds__(kHeadMaxThreads) k_head_max(HeadMaxArgs a) {
     const int h = blockIdx.x, t = blockIdx.y;
     const float* r = a.rowmax + ((int64_t)t * a.H + h) * a.rows_ld;
     float mx = 0.f;
-    for (int64_t i = threadIdx.x; i < a.rows; i += 256) mx = fmaxf(mx, r[i]);
+    for (int64_t i0 = threadIdx.x; i0 < a.rows; i0 += 4 * kHeadMaxThreads) {
+        float v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int64_t i = i0 + (int64_t)u * kHeadMaxThreads;
+            v[u] = i < a.rows ? r[i] : 0.f;
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) mx = fmaxf(mx, v[u]);
+    }
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, shfl_xor_f(mx, off));
-    __shared__ float wm[4];
+    constexpr int NW = kHeadMaxThreads / 64;
+    __shared__ float wm[NW];
     if ((threadIdx.x & 63) == 0) wm[threadIdx.x >> 6] = mx;
     __syncthreads();
-    if (threadIdx.x == 0) a.out[t][h * 4] = __float_as_uint(fmaxf(fmaxf(wm[0], wm[1]), fmaxf(wm[2], wm[3])));
+    if (threadIdx.x == 0) {
+        float m = wm[0];
+        for (int w = 1; w < NW; ++w) m = fmaxf(m, wm[w]);
+        a.out[t][h * 4] = __float_as_uint(m);
+    }
 }
 
 // Power of two s with max|x| * s in [2^13, 2^14) (1 when max is 0).
@@ -264,7 +280,7 @@ hipError_t launch_head_max(const float* rowmax, unsigned int* const* out, int T,
     a.rowmax = rowmax;
     for (int t = 0; t < T; ++t) a.out[t] = out[t];
     a.rows = rows; a.rows_ld = rows_ld; a.H = H;
-    hipLaunchKernelGGL(k_head_max, dim3((unsigned)H, (unsigned)T), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(k_head_max, dim3((unsigned)H, (unsigned)T), dim3(kHeadMaxThreads), 0, s, a);
     return hipGetLastError();
 }
 
