@@ -112,7 +112,9 @@ int make_plan(int N, int H, int d, int p, int L, int K, int dtype, Plan* P, int 
     pl.fwd_total = off;
     pl.off_acc = take(sizeof(float) * HSd);
     pl.off_part = take(m < L - 1 ? sizeof(float) * (size_t)H * (size_t)(N / pl.tok) * d : 0);
-    pl.off_dos = take(sizeof(float) * HSd);
+    // the finished dO~ is the accumulator itself: the row preparation completes its
+    // rows in place
+    pl.off_dos = pl.off_acc;
     pl.off_doh = take(h16); pl.off_dol = take(h16);
     pl.off_D = take(sizeof(float) * (size_t)H * pl.Sp);
     pl.off_dq = take(sizeof(float) * HSd);
@@ -385,6 +387,7 @@ int backward_strided(const void* dout, void* dq, void* dk, void* dv, int N, int 
         rp.level = reinterpret_cast<const uint8_t*>(w + P.off_level);
         rp.tok = P.tok; rp.nblk = P.N / P.tok; rp.m = P.m; rp.p = P.p;
         rp.dos = f32(w, P.off_dos); rp.D = f32(w, P.off_D);
+        rp.in_place = 1;
         rp.S = P.S; rp.Sp = P.Sp; rp.H = H; rp.d = d; rp.mode = acc_mode; rp.dense = 0;
         float* rowmax_b = f32(w, P.off_rowmax) + 3 * (size_t)H * P.Sp;
         rp.rowmax = dtype == BF16 ? rowmax_b : nullptr;

@@ -83,7 +83,7 @@ struct Plan {
     size_t off_lse, off_lse2;     // fp32 [H][Sp]
     size_t off_acc;               // fp32 [H][Sp][d]: sums of dO over each entry (dO~)
     size_t off_part;              // fp32 [H][N / tok][d]: deterministic mode's per-block partial sums
-    size_t off_dos;               // fp32 [H][Sp][d]
+    size_t off_dos;               // fp32 [H][Sp][d] finished dO~: the rows of off_acc, completed in place
     size_t off_doh, off_dol;      // fp16 hi/lo rows of dO~
     size_t off_D;                 // fp32 [H][Sp]
     size_t off_dq, off_dk, off_dv;   // fp32 [H][Sp][d]
@@ -179,6 +179,7 @@ struct RowPrepSpec {
     float* rowmax;             // optional: per-row max |dO~| [H][Sp]
     int64_t S, Sp;
     int H, d, mode, dense;
+    int in_place;              // dos is acc: only the rows that change are stored
 };
 // out[t][h * 4] = max over rows of rowmax[t][h][0..rows) (rows_ld apart), T <= 4 tensors
 hipError_t launch_head_max(const float* rowmax, unsigned int* const* out, int T, int64_t rows, int64_t rows_ld,

@@ -147,7 +147,9 @@ __global__ void __launch_bounds__(256) k_split(SplitArgs a) {
 // dense path also the base-2 lse minus the backward kernels' offset 14 (their
 // weights are then P * 2^14).  dO~ of an entry is its row of `acc`, except in
 // the deterministic mode for entries above level m: those are the sum, in
-// block order and in double, of the entry's per-block partial sums.
+// block order and in double, of the entry's per-block partial sums.  In place
+// (dos == acc), only the rows that change are written: those sums, and zeros
+// for the padding rows S .. Sp-1.
 struct RowPrepArgs {
     const void* acc;       // fp32 [H][Sp][d]; unused when dense
     const float* part;     // mode 1: fp32 [H][N / tok][d]
@@ -165,6 +167,7 @@ struct RowPrepArgs {
     float* rowmax;             // optional fp32 [H][Sp]: max |dO~| of each row
     int64_t S, Sp;
     int H, d, mode, dense;
+    int in_place;              // dos is acc: store only the rows that change
 };
 
 template <int G>
@@ -178,6 +181,7 @@ __global__ void __launch_bounds__(256) k_row_prep(RowPrepArgs a) {
     float x[8], o[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) x[e] = o[e] = 0.f;
+    bool changed = i >= a.S;   // rows whose dO~ differs from what `acc` holds
     if (live && i < a.S) {
         if (a.dense) {
             load8<0>(a.dout, h * a.hs + i * a.ld + c * 8, x);
@@ -186,6 +190,7 @@ __global__ void __launch_bounds__(256) k_row_prep(RowPrepArgs a) {
             const int64_t el = r * d + c * 8;
             const int lv = a.mode == 1 ? (int)a.level[h * a.S + i] : 0;
             if (lv > a.m) {
+                changed = true;
                 // p^(lv - m) blocks of tok tokens, from the entry's first one
                 const int64_t b0 = a.start[h * a.S + i] / a.tok;
                 int64_t nb = 1;
@@ -207,7 +212,7 @@ __global__ void __launch_bounds__(256) k_row_prep(RowPrepArgs a) {
             load8f(reinterpret_cast<const float*>(a.o), el, o);
         }
     }
-    if (live && a.dos) store8f(a.dos, r * d + c * 8, x);
+    if (live && a.dos && (changed || !a.in_place)) store8f(a.dos, r * d + c * 8, x);
     double dot = 0.0;
 #pragma unroll
     for (int e = 0; e < 8; ++e) dot = fma((double)x[e], (double)o[e], dot);
@@ -292,6 +297,7 @@ hipError_t launch_row_prep(const RowPrepSpec& sp, hipStream_t s) {
     a.dos = sp.dos; a.D = sp.D;
     a.lse_in = sp.lse_in; a.lse2 = sp.lse2; a.rowmax = sp.rowmax;
     a.S = sp.S; a.Sp = sp.Sp; a.H = sp.H; a.d = sp.d; a.mode = sp.mode; a.dense = sp.dense;
+    a.in_place = sp.in_place;
     const int G = sp.d / 8;
     const int64_t rows = (int64_t)sp.H * sp.Sp;
     dim3 grid((unsigned)((rows + (256 / G) - 1) / (256 / G)));
