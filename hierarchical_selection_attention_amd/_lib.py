@@ -21,6 +21,7 @@ LH_SCATTER_FP_ATOMIC, LH_SCATTER_INT_ATOMIC = 0, 1
 LH_SCATTER_DETERMINISTIC = LH_SCATTER_INT_ATOMIC
 LH_SCORE_QK, LH_SCORE_K, LH_SCORE_Q, LH_SCORE_QK_PRODUCT = 0, 1, 2, 3
 LH_SCORE_KEEP_LEAVES = 0x100   # option bit: also store the level-0 scores (score view)
+LH_BWD_KEEP_SUB = 0x100        # option bit of scatter_mode: also store dQ~, dK~, dV~ (fp32 views)
 LH_SELECT_PARTITION, LH_SELECT_PARENT_KEPT = 0, 1
 VIEWS = {"scores": 0, "sel_start": 1, "sel_level": 2, "qsub": 3, "ksub": 4, "vsub": 5, "osub": 6,
          "lse": 7, "dosub": 8, "dqsub": 9, "dksub": 10, "dvsub": 11, "block_first": 12}
@@ -210,12 +211,15 @@ def forward_static(q, k, v, p, L, K, out=None, stream=None):
 
 
 def backward(dout, p, L, K, ws, mode=LH_SCATTER_FP_ATOMIC, grads=None, stream=None,
-             select_mode=LH_SELECT_PARTITION):
-    """(dq, dk, dv) of the Lighthouse layer; ws must come from the matching forward()."""
+             select_mode=LH_SELECT_PARTITION, keep_sub_grads=False):
+    """(dq, dk, dv) of the Lighthouse layer; ws must come from the matching forward().
+    keep_sub_grads: also store dQ~, dK~, dV~ in the workspace (LH_BWD_KEEP_SUB)."""
     torch = _torch()
     _dev_tensor_check(dout)
     N, H, d = dout.shape
     dt = dtype_code(dout)
+    if keep_sub_grads:
+        mode |= LH_BWD_KEEP_SUB
     if grads is None:
         grads = tuple(torch.empty_like(dout) for _ in range(3))
     dq, dk, dv = grads

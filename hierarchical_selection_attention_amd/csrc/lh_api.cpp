@@ -356,6 +356,8 @@ int backward_strided(const void* dout, void* dq, void* dk, void* dv, int N, int 
     Plan P;
     int rc = make_plan(N, H, d, p, L, K, dtype, &P, select_mode);
     if (rc) return rc;
+    const bool keep_sub = (scatter_mode & LH_BWD_KEEP_SUB) != 0;
+    scatter_mode &= ~LH_BWD_KEEP_SUB;
     if (scatter_mode != LH_SCATTER_FP_ATOMIC && scatter_mode != LH_SCATTER_INT_ATOMIC) return LH_ERR_DTYPE;
     if (grad_ld != (int64_t)H * d &&
         (!(P.rowcopy || P.pk) || grad_ld < (int64_t)H * d || grad_ld % 8 != 0))
@@ -410,6 +412,9 @@ int backward_strided(const void* dout, void* dq, void* dk, void* dv, int N, int 
         a.level = reinterpret_cast<const uint8_t*>(w + P.off_level);
         a.p = p;
         a.tok_ld = grad_ld;
+        // the fp32 dQ~, dK~, dV~ rows are read by nothing after the attention here:
+        // stored only on request
+        if (!keep_sub) a.dq = a.dk = a.dv = nullptr;
     }
     // dK/dV and dQ in one launch: each role's token writes overlap the other's MFMA work
     LH_TRY(stage(ST_ATTN_BWD, s, [&] { return launch_attn_bwd(a, s); }));

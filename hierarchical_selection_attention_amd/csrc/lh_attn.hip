@@ -686,7 +686,7 @@ __device__ __forceinline__ void dkdv_body(const AttnK& a, uint16_t* __restrict__
                 *reinterpret_cast<u32x2*>(a.dk_b + base + 16 * v) = u32x2{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3])};
                 *reinterpret_cast<u32x2*>(a.dv_b + base + 16 * v) = u32x2{pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])};
             }
-        } else {
+        } else if (a.dk) {   // fp32 dK~, dV~ rows (null when only the token rows are wanted)
             const int64_t base = hb + mykey * D + 4 * lg;
 #pragma unroll
             for (int v = 0; v < NV; ++v) {
@@ -865,7 +865,7 @@ __device__ __forceinline__ void dq_body(const AttnK& a, uint16_t* __restrict__ s
                 const f32x4 x = dq[v] * mul;
                 *reinterpret_cast<u32x2*>(a.dq_b + base + 16 * v) = u32x2{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3])};
             }
-        } else {
+        } else if (a.dq) {   // fp32 dQ~ rows (null when only the token rows are wanted)
             const int64_t base = hb + myq * D + 4 * lg;
 #pragma unroll
             for (int v = 0; v < NV; ++v) __builtin_nontemporal_store(dq[v] * mul, reinterpret_cast<f32x4*>(a.dq + base + 16 * v));

@@ -178,9 +178,19 @@ int lh_backward_sel(const void* dout, void* dq, void* dk, void* dv,
                     int N, int H, int d, int p, int L, int K, int dtype, int scatter_mode,
                     int select_mode, void* ws, size_t ws_bytes, void* stream);
 
+/* Option bit for the scatter_mode argument of lh_backward / lh_backward_sel:
+ * also store the fp32 gradients of the gathered sub-sequence, dQ~, dK~, dV~
+ * (LH_VIEW_DQSUB .. LH_VIEW_DVSUB).  On the bf16 partition path the attention
+ * kernels write dq, dk, dv to the tokens themselves and nothing reads these
+ * rows, so without the bit they are not stored and those views keep whatever
+ * the workspace held.  The fp32 path and the parent-kept selection store them
+ * either way (their pool adjoint reads them). */
+#define LH_BWD_KEEP_SUB 0x100
+
 /* Backward pass through the scatter, the attention, the gather and the pool
  * (Fig. 1 gradient path).  q, k, v are not needed: everything is read from
  * the workspace of the matching lh_forward.  Writes dq, dk, dv [N][H][d].
+ * scatter_mode is an lh_scatter_mode, optionally ORed with LH_BWD_KEEP_SUB.
  * Every kernel is enqueued on `stream`; the library keeps no stream or
  * buffer of its own (events only while lh_stage_timing is on), so calls with
  * distinct workspaces on distinct streams may run concurrently. */
@@ -201,7 +211,8 @@ typedef enum {
     LH_VIEW_OSUB = 6,       /* fp32 [H][Sp][d]: attention output on the sub-seq.   */
     LH_VIEW_LSE = 7,        /* fp32 [H][Sp]: natural-log log-sum-exp per row       */
     LH_VIEW_DOSUB = 8,      /* fp32 [H][Sp][d]: dO summed over each entry's tokens */
-    LH_VIEW_DQSUB = 9,      /* fp32 [H][Sp][d]: gradient of the gathered q         */
+    LH_VIEW_DQSUB = 9,      /* fp32 [H][Sp][d]: gradient of the gathered q (bf16
+                               partition path: only with LH_BWD_KEEP_SUB)          */
     LH_VIEW_DKSUB = 10,     /* fp32 [H][Sp][d]                                     */
     LH_VIEW_DVSUB = 11,     /* fp32 [H][Sp][d]                                     */
     LH_VIEW_BLOCK_FIRST = 12 /* int32 [H][N/p^(L-1)+1]: first slot of each top block */

@@ -211,7 +211,7 @@ class Run:
                                      keep_leaf_scores=keep_leaves)
         if backward:
             self.dout = to_dev(x["dout"], dtype)
-            self.grads = lh.backward(self.dout, p, L, K, self.ws, mode=mode)
+            self.grads = lh.backward(self.dout, p, L, K, self.ws, mode=mode, keep_sub_grads=True)
         torch.cuda.synchronize()
         say("  GPU run done")
 

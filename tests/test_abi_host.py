@@ -71,6 +71,12 @@ def test_entry_points_validate_before_launching():
     assert lh.lh_backward(fake, fake, fake, fake, N, H, d, p, L, K, 1, 2, aligned_ws, nb, None) == lh.LH_ERR_DTYPE
     assert lh.lh_backward(fake, None, fake, fake, N, H, d, p, L, K, 1, 0, aligned_ws, nb, None) == lh.LH_ERR_ARG
     assert lh.lh_backward(fake, fake, fake, fake, N, H, d, p, L, K, 1, 0, aligned_ws, 0, None) == lh.LH_ERR_WORKSPACE
+    # the keep-sub-gradients bit is accepted beside either scatter mode (the call then fails
+    # at the workspace check); other bits are not
+    for mode in (0, 1):
+        assert lh.lh_backward(fake, fake, fake, fake, N, H, d, p, L, K, 1, mode | lh.LH_BWD_KEEP_SUB, aligned_ws, 0,
+                              None) == lh.LH_ERR_WORKSPACE
+    assert lh.lh_backward(fake, fake, fake, fake, N, H, d, p, L, K, 1, 0x200, aligned_ws, nb, None) == lh.LH_ERR_DTYPE
     assert lh.lh_dense_workspace_bytes(1000, 2, 64, 0) == 0          # N not a multiple of 64
     assert lh.lh_dense_workspace_bytes(1024, 2, 64, 1) == 0          # dense path is bf16
     assert lh.lh_dense_attn_fwd(fake, fake, fake, fake, fake, 1000, 2, 64, 0, aligned_ws, 1 << 30, None) \
@@ -154,6 +160,14 @@ def test_keep_leaves_bit_matches_the_header():
     m = re.search(r"#define\s+LH_SCORE_KEEP_LEAVES\s+(0x[0-9a-fA-F]+|\d+)", hdr)
     assert m and int(m.group(1), 0) == lh.LH_SCORE_KEEP_LEAVES
     assert lh.LH_SCORE_KEEP_LEAVES & 0xff == 0   # clear of every score mode
+
+
+def test_keep_sub_gradients_bit_matches_the_header():
+    lh = _lh()
+    hdr = open(os.path.join(ROOT, "include", "lighthouse.h")).read()
+    m = re.search(r"#define\s+LH_BWD_KEEP_SUB\s+(0x[0-9a-fA-F]+|\d+)", hdr)
+    assert m and int(m.group(1), 0) == lh.LH_BWD_KEEP_SUB
+    assert lh.LH_BWD_KEEP_SUB & (lh.LH_SCATTER_FP_ATOMIC | lh.LH_SCATTER_INT_ATOMIC) == 0
 
 
 @pytest.mark.parametrize("N,p,L,K", [(2048, 4, 3, 16), (2048, 4, 3, 512), (524288, 4, 5, 128), (1080, 3, 4, 5),

@@ -1,5 +1,6 @@
-"""GPU checks of the descriptor read-out and of the achievable-peak probes,
-called through the C ABI."""
+"""GPU checks of the descriptor read-out, the achievable-peak probes, concurrent
+layers on two streams and the backward's optional sub-sequence gradients, called
+through the C ABI."""
 import numpy as np
 import pytest
 import torch
@@ -110,3 +111,27 @@ def test_concurrent_layers_on_two_user_streams():
         for gg, key in zip(g, ("dQt", "dKt", "dVt")):
             check_full_rows(gg, b[key], sel, p, "bf16", f"two streams d{key[1].lower()} (N={N})", divide=True,
                             allow_sub=grad_allow(b, key))
+
+
+def test_backward_without_sub_gradients_writes_the_same_tokens():
+    """The default backward stores no fp32 dQ~, dK~, dV~ rows on the bf16 partition path
+    (LH_BWD_KEEP_SUB asks for them): its dq, dk, dv token rows equal, bit for bit, those of
+    a backward that stores them, and the views it does not write keep their contents."""
+    import hierarchical_selection_attention_amd as lh
+    N, H, d, p, L, K = 8192, 4, 128, 4, 4, 16
+    say(f"case backward keep-sub N={N} H={H} d={d} p={p} L={L} K={K}")
+    x = si.make_inputs(N, H, d, "bf16", seed=910, with_dout=True, threads=8)
+    q, k, v, do = (to_dev(x[n], "bf16") for n in ("q", "k", "v", "dout"))
+    o, ws = lh.forward(q, k, v, p, L, K)
+    for mode in (lh.LH_SCATTER_FP_ATOMIC, lh.LH_SCATTER_DETERMINISTIC):
+        kept = [g.clone() for g in lh.backward(do, p, L, K, ws, mode=mode, keep_sub_grads=True)]
+        subs = [lh.workspace_tensor(ws, N, H, d, p, L, K, 0, n) for n in ("dqsub", "dksub", "dvsub")]
+        for t in subs:
+            t.fill_(1234.5)
+        plain = lh.backward(do, p, L, K, ws, mode=mode)
+        torch.cuda.synchronize()
+        for a, b, name in zip(kept, plain, ("dq", "dk", "dv")):
+            assert torch.equal(a.view(torch.int16), b.view(torch.int16)), f"{name} differs (mode {mode})"
+        for t, name in zip(subs, ("dqsub", "dksub", "dvsub")):
+            assert bool((t == 1234.5).all()), f"{name} was written without LH_BWD_KEEP_SUB"
+
