@@ -213,8 +213,8 @@ typedef enum {
     LH_VIEW_DOSUB = 8,      /* fp32 [H][Sp][d]: dO summed over each entry's tokens */
     LH_VIEW_DQSUB = 9,      /* fp32 [H][Sp][d]: gradient of the gathered q (bf16
                                partition path: only with LH_BWD_KEEP_SUB)          */
-    LH_VIEW_DKSUB = 10,     /* fp32 [H][Sp][d]                                     */
-    LH_VIEW_DVSUB = 11,     /* fp32 [H][Sp][d]                                     */
+    LH_VIEW_DKSUB = 10,     /* fp32 [H][Sp][d], as LH_VIEW_DQSUB                 */
+    LH_VIEW_DVSUB = 11,     /* fp32 [H][Sp][d], as LH_VIEW_DQSUB                 */
     LH_VIEW_BLOCK_FIRST = 12 /* int32 [H][N/p^(L-1)+1]: first slot of each top block */
 } lh_view;
 
